@@ -1,0 +1,28 @@
+"""CPU oracle for the block-sparse spatiotemporal attention path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU
+baseline leg of the benchmark may import this package.  It is plain numpy in
+float64, shares no code with the HIP library, and is written from the method
+descriptions on the five pages:
+
+* "[논문리뷰] LVSA: Training-Free Sparse Attention for Long Video Diffusion"
+  (blog review), section 1 Key Terms and section 3 Method & Key Results:
+  block-sparse attention where each frame attends to a local window of frames
+  and to global anchor frames whose positions rotate at every denoising step.
+* "라디얼 어텐션, 비디오 확산 모델에서 비용 4.4배 절감하며 품질 유지" (hyper.ai
+  headline on Radial Attention): a static mask whose attention window shrinks
+  exponentially with temporal distance, O(n log n).
+* "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video Generation via
+  Error-aware Routing", technical summary section 2 Method: centroid linear
+  compensation of skipped blocks, error estimation with query-cluster
+  centroids as proxies, error-to-cost routing under a density budget.
+* "LinVideo: A Post-Training Framework towards O(n) Attention in Efficient
+  Video Generation", technical summary sections 1-2: O(n) linear attention.
+
+Modules: ``mask`` (block rule and CSR), ``attention`` (block-sparse softmax
+attention), ``svg_ear`` (centroids, routing scores, budget selection,
+compensated attention; the score formula is "parity unpinned" as far as the
+pages go, see that module), ``linear`` (elu+1 linear attention).
+"""
+
+from . import mask, attention, linear, svg_ear  # noqa: F401

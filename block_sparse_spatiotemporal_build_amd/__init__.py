@@ -1,0 +1,157 @@
+"""Python binding of libbsa.so (block-sparse spatiotemporal attention, gfx950).
+
+Argument marshalling only: every computation runs in the HIP kernels behind
+the C ABI declared in ``include/bsa.h``.  PyTorch supplies device memory and
+the current stream.  There is no fallback: if the library is not built, or a
+call fails, an exception is raised.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libbsa.so")
+
+MASK_ALL, MASK_WINDOW_ANCHOR, MASK_RADIAL = 0, 1, 2
+DT_BF16, DT_F32 = 0, 1
+
+_lib = None
+
+
+class BsaError(RuntimeError):
+    pass
+
+
+class MaskDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("kind", "frames", "frame_tokens", "block", "window", "anchor_period",
+                 "anchor_step", "anchor_rows", "radial_w")]
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("stride_b", ctypes.c_int64),
+                ("stride_h", ctypes.c_int64), ("stride_n", ctypes.c_int64)]
+
+
+_P = ctypes.c_void_p
+_SIGNATURES = {
+    "bsa_mask_num_blocks": (ctypes.c_int32, [ctypes.POINTER(MaskDesc)]),
+    "bsa_build_block_mask": (ctypes.c_int, [ctypes.POINTER(MaskDesc), _P, _P, ctypes.c_int64, _P]),
+    "bsa_block_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int,
+                                                 ctypes.POINTER(Shape), _P, _P, ctypes.c_int32,
+                                                 ctypes.c_float, _P]),
+    "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "bsa_last_error": (ctypes.c_char_p, []),
+}
+
+
+def load(path: str = LIB_PATH):
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise BsaError(f"{path} not found: build it first (python -c 'import __graft_entry__ as g; g.build()')")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def exported_names():
+    return list(_SIGNATURES)
+
+
+def _check(status: int, fn: str):
+    if status != 0:
+        lib = load()
+        raise BsaError(f"{fn}: {lib.bsa_status_string(status).decode()}: {lib.bsa_last_error().decode()}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def mask_desc(params: dict) -> MaskDesc:
+    return MaskDesc(**{k: int(params[k]) for k, _ in MaskDesc._fields_})
+
+
+def num_blocks(params: dict) -> int:
+    nb = load().bsa_mask_num_blocks(ctypes.byref(mask_desc(params)))
+    if nb < 0:
+        raise BsaError(f"invalid mask description: {load().bsa_last_error().decode()}")
+    return nb
+
+
+def build_block_mask(params: dict, device="cuda", row_ptr=None, col_idx=None):
+    """CSR (row_ptr int32[nb+1], col_idx int32[nb*nb]) of the block mask, on the device.
+
+    Only the first row_ptr[nb] entries of col_idx are meaningful.
+    """
+    lib = load()
+    desc = mask_desc(params)
+    nb = num_blocks(params)
+    if row_ptr is None:
+        row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=device)
+    if col_idx is None:
+        col_idx = torch.empty(nb * nb, dtype=torch.int32, device=device)
+    assert row_ptr.dtype == torch.int32 and row_ptr.numel() >= nb + 1 and row_ptr.is_cuda
+    assert col_idx.dtype == torch.int32 and col_idx.is_cuda
+    _check(lib.bsa_build_block_mask(ctypes.byref(desc), _ptr(row_ptr), _ptr(col_idx),
+                                    col_idx.numel(), _stream(row_ptr.device)),
+           "bsa_build_block_mask")
+    return row_ptr, col_idx
+
+
+def _shape_of(q: torch.Tensor) -> Shape:
+    if q.dim() != 4:
+        raise BsaError("tensors must be [B, H, N, D]")
+    B, H, N, D = q.shape
+    if q.stride(3) != 1:
+        raise BsaError("the D axis must be contiguous")
+    return Shape(B, H, N, D, q.stride(0), q.stride(1), q.stride(2))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DT_BF16
+    if t.dtype == torch.float32:
+        return DT_F32
+    raise BsaError(f"unsupported dtype {t.dtype}")
+
+
+def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out=None,
+                          return_lse: bool = True):
+    """O (and LSE, fp32 [B, H, N]) of block-sparse softmax attention on the device."""
+    lib = load()
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise BsaError("q, k, v must be device tensors")
+    if k.shape != q.shape or v.shape != q.shape or k.stride() != q.stride() or v.stride() != q.stride():
+        raise BsaError("q, k, v must share one shape and one stride layout")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise BsaError("q, k, v must share one dtype")
+    shape = _shape_of(q)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if out.stride() != q.stride() or out.dtype != q.dtype:
+        raise BsaError("out must have the layout and dtype of q")
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[-1])
+    _check(lib.bsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                         _dtype_code(q), ctypes.byref(shape), _ptr(row_ptr),
+                                         _ptr(col_idx), int(block), float(scale), _stream(q.device)),
+           "bsa_block_sparse_attn_fwd")
+    return out, lse

@@ -1,0 +1,154 @@
+// C-ABI entry points: argument validation, dispatch, status and error text.
+//
+// Validation runs entirely on the host before any HIP call, so a rejected
+// call launches nothing and touches no output.
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "common.h"
+
+namespace bsa {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+bool launch_ok(const char* what) {
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("%s: kernel launch failed: %s", what, hipGetErrorString(e));
+    return false;
+  }
+  return true;
+}
+
+bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
+                                   hipStream_t stream);
+bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                            int block, float scale, hipStream_t stream);
+bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                           int block, float scale, hipStream_t stream);
+
+static bsa_status fail(bsa_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by the tensor calls: sizes positive, strides that keep
+// each row inside its own head, D contiguous, 16-byte aligned rows.
+static bsa_status check_shape(const bsa_shape* s, int elem_bytes, const char* fn) {
+  if (s == nullptr) return fail(BSA_ERR_ARG, "%s: shape is NULL", fn);
+  if (s->B <= 0 || s->H <= 0 || s->N <= 0 || s->D <= 0)
+    return fail(BSA_ERR_ARG, "%s: B, H, N, D must be positive (got %d, %d, %d, %d)", fn, s->B, s->H,
+                s->N, s->D);
+  if (s->stride_n < s->D || s->stride_h < 0 || s->stride_b < 0)
+    return fail(BSA_ERR_ARG, "%s: stride_n must be >= D and strides non-negative", fn);
+  if (((int64_t)s->stride_n * elem_bytes) % 16 != 0 || ((int64_t)s->stride_h * elem_bytes) % 16 != 0 ||
+      ((int64_t)s->stride_b * elem_bytes) % 16 != 0)
+    return fail(BSA_ERR_ARG, "%s: strides must be multiples of 16 bytes", fn);
+  return BSA_OK;
+}
+
+static bsa_status check_desc(const bsa_mask_desc* d, const char* fn) {
+  if (d == nullptr) return fail(BSA_ERR_ARG, "%s: desc is NULL", fn);
+  if (d->kind < BSA_MASK_ALL || d->kind > BSA_MASK_RADIAL)
+    return fail(BSA_ERR_ARG, "%s: unknown mask kind %d", fn, d->kind);
+  if (d->frames < 1 || d->frame_tokens < 1 || d->block < 1 || d->block > 4096)
+    return fail(BSA_ERR_ARG, "%s: frames, frame_tokens >= 1 and 1 <= block <= 4096 required", fn);
+  if (d->window < 0 || d->anchor_period < 0 || d->anchor_step < 0 || d->radial_w < 0)
+    return fail(BSA_ERR_ARG, "%s: window, anchor_period, anchor_step, radial_w must be >= 0", fn);
+  const int64_t N = (int64_t)d->frames * d->frame_tokens;
+  if (N > 0x7fffffffLL - 4096) return fail(BSA_ERR_ARG, "%s: frames * frame_tokens too large", fn);
+  const int64_t nb = (N + d->block - 1) / d->block;
+  if (nb > 46340) return fail(BSA_ERR_ARG, "%s: %lld blocks exceed the limit of 46340", fn, (long long)nb);
+  return BSA_OK;
+}
+
+}  // namespace bsa
+
+using namespace bsa;
+
+extern "C" {
+
+int32_t bsa_mask_num_blocks(const bsa_mask_desc* desc) {
+  if (check_desc(desc, "bsa_mask_num_blocks") != BSA_OK) return -1;
+  const int64_t N = (int64_t)desc->frames * desc->frame_tokens;
+  return (int32_t)((N + desc->block - 1) / desc->block);
+}
+
+bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
+                                int64_t col_capacity, void* stream) {
+  const char* fn = "bsa_build_block_mask";
+  bsa_status st = check_desc(desc, fn);
+  if (st != BSA_OK) return st;
+  if (row_ptr == nullptr || col_idx == nullptr) return fail(BSA_ERR_ARG, "%s: NULL output pointer", fn);
+  const int64_t nb = bsa_mask_num_blocks(desc);
+  if (col_capacity < nb * nb)
+    return fail(BSA_ERR_CAPACITY, "%s: col_capacity %lld < nb*nb = %lld", fn, (long long)col_capacity,
+                (long long)(nb * nb));
+  g_err[0] = 0;
+  return launch_build_block_mask(*desc, row_ptr, col_idx, (hipStream_t)stream);
+}
+
+bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     bsa_dtype dtype, const bsa_shape* shape, const int32_t* row_ptr,
+                                     const int32_t* col_idx, int32_t block, float scale, void* stream) {
+  const char* fn = "bsa_block_sparse_attn_fwd";
+  if (dtype != BSA_DT_BF16 && dtype != BSA_DT_F32) return fail(BSA_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
+  const int eb = dtype == BSA_DT_BF16 ? 2 : 4;
+  bsa_status st = check_shape(shape, eb, fn);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !o || !row_ptr || !col_idx) return fail(BSA_ERR_ARG, "%s: NULL tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if (!__builtin_isfinite(scale) || scale == 0.f)
+    return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+  if (block < 1) return fail(BSA_ERR_ARG, "%s: block must be >= 1", fn);
+  if (dtype == BSA_DT_BF16) {
+    if (shape->D != 64 && shape->D != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "%s: bf16 supports D in {64, 128} (got %d)", fn, shape->D);
+    if (block != 64 && block != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "%s: bf16 supports block in {64, 128} (got %d)", fn, block);
+  } else {
+    if (shape->D != 32 && shape->D != 64 && shape->D != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "%s: f32 supports D in {32, 64, 128} (got %d)", fn, shape->D);
+    if (block != 16 && block != 32 && block != 64 && block != 128)
+      return fail(BSA_ERR_UNSUPPORTED, "%s: f32 supports block in {16, 32, 64, 128} (got %d)", fn, block);
+  }
+  if ((int64_t)shape->B * shape->H > 65535 * 65535LL || shape->H > 65535 || shape->B > 65535)
+    return fail(BSA_ERR_ARG, "%s: B and H must be <= 65535", fn);
+  g_err[0] = 0;
+  if (dtype == BSA_DT_BF16)
+    return launch_attn_bf16(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
+  return launch_attn_f32(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
+}
+
+const char* bsa_status_string(bsa_status s) {
+  switch (s) {
+    case BSA_OK: return "ok";
+    case BSA_ERR_ARG: return "invalid argument";
+    case BSA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case BSA_ERR_CAPACITY: return "output capacity too small";
+    case BSA_ERR_WORKSPACE: return "workspace missing or too small";
+    case BSA_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* bsa_last_error(void) { return g_err; }
+
+}  // extern "C"

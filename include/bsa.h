@@ -1,0 +1,129 @@
+/*
+ * bsa.h - block-sparse spatiotemporal attention for MI355X (gfx950), C ABI.
+ *
+ * Conventions for every call
+ *   - Tensor pointers are DEVICE pointers owned by the caller; the library
+ *     keeps no state and allocates no device memory.  Calls that need scratch
+ *     take a caller-owned workspace whose size comes from a *_workspace query.
+ *   - Every call validates its arguments on the host first.  A failed check
+ *     returns a non-zero bsa_status, writes a message readable through
+ *     bsa_last_error() (per host thread), launches nothing and leaves every
+ *     output untouched.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     default stream).  No call synchronises.  A launch failure returns
+ *     BSA_ERR_HIP with the HIP error text in bsa_last_error().
+ *   - Results are deterministic: no floating-point atomics anywhere.
+ *   - Q, K, V, O tensors are [B, H, N, D] with element strides (stride_b,
+ *     stride_h, stride_n) and a contiguous D axis; all four share one shape.
+ *     Token t of a video latent of F frames x P patches is frame t / P,
+ *     in-frame raster position t % P (frame-major flattening).
+ */
+#ifndef BSA_H
+#define BSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bsa_status {
+  BSA_OK = 0,
+  BSA_ERR_ARG = 1,          /* invalid argument (null pointer, bad size, bad enum)   */
+  BSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. a head_dim)           */
+  BSA_ERR_CAPACITY = 3,     /* an output buffer is too small                         */
+  BSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query returned  */
+  BSA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed            */
+} bsa_status;
+
+typedef enum bsa_dtype { BSA_DT_BF16 = 0, BSA_DT_F32 = 1 } bsa_dtype;
+
+typedef enum bsa_mask_kind {
+  BSA_MASK_ALL = 0,            /* every block pair kept (dense attention)            */
+  BSA_MASK_WINDOW_ANCHOR = 1,  /* local frame window + rotating global anchor frames */
+  BSA_MASK_RADIAL = 2          /* window shrinking with temporal distance            */
+} bsa_mask_kind;
+
+/* Block-mask description.
+ *
+ * Token rule (a real token pair q, k with frames fq, fk and positions pq, pk):
+ *  WINDOW_ANCHOR - "[논문리뷰] LVSA: Training-Free Sparse Attention for Long Video
+ *    Diffusion", section 3 Method & Key Results, Figures 1 and 2: kept when
+ *    |fq - fk| <= window, or fk is an anchor frame, or (anchor_rows != 0 and fq
+ *    is an anchor frame).  Anchor frames are {f < frames : f % anchor_period ==
+ *    anchor_step % anchor_period}; anchor_step is the denoising step, so the
+ *    anchor set rotates by one frame per step.  anchor_period 0 = no anchors.
+ *  RADIAL - Radial Attention headline page (static mask, window shrinking
+ *    exponentially with temporal distance, O(n log n)): kept when fq == fk, or
+ *    |pq - pk| * 2^floor(log2 |fq - fk|) <= radial_w.
+ *  ALL - every pair kept.
+ * Block rule: blocks of `block` consecutive tokens; block pair (i, j) is kept
+ * when any real token pair (q in block i, k in block j) is kept.  The sequence
+ * has N = frames * frame_tokens real tokens and nb = ceil(N / block) blocks;
+ * the last block may be partial (tokens past N do not exist).
+ * Limits: frames, frame_tokens, block >= 1; block <= 4096; nb <= 46340;
+ * window, anchor_period, anchor_step, radial_w >= 0. */
+typedef struct bsa_mask_desc {
+  int32_t kind;
+  int32_t frames;
+  int32_t frame_tokens;
+  int32_t block;
+  int32_t window;
+  int32_t anchor_period;
+  int32_t anchor_step;
+  int32_t anchor_rows;
+  int32_t radial_w;
+} bsa_mask_desc;
+
+typedef struct bsa_shape {
+  int32_t B, H, N, D;
+  int64_t stride_b, stride_h, stride_n; /* element strides; D is contiguous */
+} bsa_shape;
+
+/* Number of blocks nb = ceil(N / block) of a valid description, else -1. */
+int32_t bsa_mask_num_blocks(const bsa_mask_desc* desc);
+
+/* Build the block mask of `desc` as CSR on the device.
+ * Operation: the block rule above (LVSA review page section 3; Radial Attention
+ * headline page).  Integer-only, bit-exact.
+ * row_ptr: int32[nb + 1] device, written with row offsets (row_ptr[0] = 0).
+ * col_idx: int32[col_capacity] device, written with the kept key-block indices
+ *          of each row in ascending order.  col_capacity must be >= nb * nb
+ *          (the largest possible count), else BSA_ERR_CAPACITY.
+ * The mask is shared by every batch and head. */
+bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
+                                int64_t col_capacity, void* stream);
+
+/* Block-sparse softmax attention forward.
+ * Operation (LVSA review page section 1 Key Terms and section 3; SVG-EAR page,
+ * technical summary section 1: compute the kept blocks, skip the rest): for a
+ * real query row q in block i, over the real keys t of kept blocks (i, j):
+ *   l_t = scale * q . k_t,  out = sum_t exp(l_t - m) v_t / sum_t exp(l_t - m),
+ *   lse = m + ln sum_t exp(l_t - m)  (m = max l_t).
+ * Skipped blocks are never read.  A row with no kept block gets out = 0 and
+ * lse = -inf.
+ * q, k, v, o: device tensors of `dtype` with `shape`.  BSA_DT_BF16: bf16
+ *   inputs, fp32 accumulation, o written in bf16 (round to nearest even);
+ *   D in {64, 128}, block in {64, 128}.  BSA_DT_F32: fp32 end to end; D in
+ *   {32, 64, 128}, block in {16, 32, 64, 128}.
+ * lse: nullable fp32 [B, H, N] contiguous device array.
+ * row_ptr, col_idx: the CSR from bsa_build_block_mask for the same N and block
+ *   (nb = ceil(N / block) rows, ascending columns < nb).
+ * scale: the softmax scale (1/sqrt(D) for standard attention). */
+bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
+                                     float* lse, bsa_dtype dtype, const bsa_shape* shape,
+                                     const int32_t* row_ptr, const int32_t* col_idx,
+                                     int32_t block, float scale, void* stream);
+
+/* Text of a status code (static storage). */
+const char* bsa_status_string(bsa_status status);
+
+/* Detail of the last failure on the calling host thread ("" if none). */
+const char* bsa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSA_H */

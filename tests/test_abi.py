@@ -1,0 +1,105 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments
+on the host before touching the device (CPU only: no kernel is launched)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_spatiotemporal_build_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    inc = os.path.join(ROOT, "include")
+    for f in sorted(os.listdir(inc)):
+        if f.endswith(".h"):
+            text = open(os.path.join(inc, f)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"\b(bsa_[a-z0-9_]+)\s*\(", text)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(bsa.LIB_PATH):
+        pytest.fail("libbsa.so is not built (run __graft_entry__.build())")
+    return bsa.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert len(declared) >= 5
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(bsa.exported_names())
+
+
+def _desc(**kw):
+    p = dict(kind=1, frames=4, frame_tokens=64, block=64, window=1, anchor_period=8,
+             anchor_step=0, anchor_rows=1, radial_w=0)
+    p.update(kw)
+    return bsa.mask_desc(p)
+
+
+def test_num_blocks(lib):
+    assert lib.bsa_mask_num_blocks(ctypes.byref(_desc())) == 4
+    assert lib.bsa_mask_num_blocks(ctypes.byref(_desc(frames=21, frame_tokens=1560, block=128))) == 256
+    assert lib.bsa_mask_num_blocks(ctypes.byref(_desc(block=0))) == -1
+    assert lib.bsa_mask_num_blocks(None) == -1
+
+
+@pytest.mark.parametrize("bad", [dict(kind=7), dict(frames=0), dict(block=0), dict(block=5000),
+                                 dict(window=-1), dict(anchor_period=-2), dict(radial_w=-1),
+                                 dict(frames=100000, frame_tokens=100000)])
+def test_mask_rejects_bad_descriptions(lib, bad):
+    st = lib.bsa_build_block_mask(ctypes.byref(_desc(**bad)), ctypes.c_void_p(16), ctypes.c_void_p(16),
+                                  1 << 40, None)
+    assert st == 1, lib.bsa_last_error()
+    assert lib.bsa_last_error().decode()
+
+
+def test_mask_rejects_small_capacity_and_null(lib):
+    d = _desc()
+    assert lib.bsa_build_block_mask(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), 15, None) == 3
+    assert b"col_capacity" in lib.bsa_last_error()
+    assert lib.bsa_build_block_mask(ctypes.byref(d), None, ctypes.c_void_p(16), 16, None) == 1
+
+
+def _shape(B=1, H=2, N=256, D=64, sn=None):
+    sn = D if sn is None else sn
+    return bsa.Shape(B, H, N, D, H * N * sn, N * sn, sn)
+
+
+def _attn(lib, dtype=0, shape=None, block=64, scale=0.125, ptr=4096, rp=4096):
+    shape = shape or _shape()
+    p = ctypes.c_void_p(ptr)
+    return lib.bsa_block_sparse_attn_fwd(p, p, p, p, None, dtype, ctypes.byref(shape),
+                                         ctypes.c_void_p(rp), ctypes.c_void_p(rp), block,
+                                         ctypes.c_float(scale), None)
+
+
+def test_attention_argument_checks(lib):
+    assert _attn(lib, dtype=5) == 1
+    assert _attn(lib, shape=_shape(D=48)) == 2                  # bf16 needs D in {64, 128}
+    assert _attn(lib, block=32) == 2                            # bf16 needs block in {64, 128}
+    assert _attn(lib, dtype=1, block=48) == 2
+    assert _attn(lib, shape=_shape(N=0)) == 1
+    assert _attn(lib, shape=_shape(D=64, sn=60)) == 1           # stride_n < D
+    assert _attn(lib, shape=_shape(D=64, sn=68)) == 1           # 136-byte rows: not 16-byte multiple
+    assert _attn(lib, ptr=4098) == 1                            # misaligned tensor
+    assert _attn(lib, ptr=0) == 1
+    assert _attn(lib, rp=0) == 1
+    assert _attn(lib, scale=0.0) == 1
+    assert _attn(lib, scale=float("inf")) == 1
+    assert _attn(lib, scale=float("nan")) == 1
+    assert b"bsa_block_sparse_attn_fwd" in lib.bsa_last_error()
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.bsa_status_string(s)
+    assert lib.bsa_status_string(99) == b"unknown status"

@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse spatiotemporal attention path on one MI355X.
+
+Workload (default ``lvsa_32k``): batch 1, 12 heads, head_dim 128, a video
+latent of 21 frames x 30x52 patches = 32,760 tokens, blocks of 128 tokens,
+bf16 Q/K/V (N(0,1) plus a per-frame AR(1) component, seeded).  One step is
+one denoising step's worth of the hot path: build the LVSA block mask for
+step s (local window +-3 frames, anchor frames every 8th frame rotated by s,
+s = step index mod 4) and run block-sparse attention with it.  Inputs are
+resident in HBM before the timed region starts.
+
+Reported (one JSON line): effective TFLOP/s over the timed steps, counting
+4 * D * (real query rows x real key columns) of kept blocks only; ms per
+attention call; the attention kernel's roofline against the bf16 MFMA peak
+(kernel time from HIP events on the launch stream); the HBM traffic measured
+by rocprofv3 counters when a profile of the current kernel source exists; and
+the CPU oracle timed on a bounded sample of the same workload.
+
+Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens).
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK_TFLOPS = 2500.0     # MI355X dense bf16 MFMA (published)
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E (published)
+KERNEL_SRC = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "attn_fwd.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="lvsa_32k", choices=["lvsa_32k", "radial_196k"])
+    ap.add_argument("--cpu-seconds", type=float, default=20.0,
+                    help="wall-clock budget of the CPU oracle sample (0 disables it)")
+    ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
+                    help="copy: run a plain device copy of known size (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path=KERNEL_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def kept_flops_from_csr(row_ptr, col_idx, N, block, D, B, H) -> int:
+    """4 * D * sum over kept (i, j) of real rows(i) * real cols(j), times B * H."""
+    import numpy as np
+    nb = len(row_ptr) - 1
+    sizes = np.minimum(block, N - np.arange(nb) * block).astype(np.int64)
+    pairs = 0
+    for i in range(nb):
+        cols = col_idx[row_ptr[i]:row_ptr[i + 1]]
+        pairs += int(sizes[i]) * int(sizes[cols].sum())
+    return 4 * D * pairs * B * H
+
+
+def read_traffic(workload: str):
+    """HBM bytes per attention launch from a committed counter profile of this kernel source."""
+    path = os.path.join(PROFILES, f"attn_bf16_{workload}.hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256") != source_hash():
+        return None
+    try:
+        return int(float(fields["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, d, params, budget_s: float):
+    """The oracle, as it stands, on a bounded sample: whole heads, query blocks in order,
+    until the wall-clock budget is spent."""
+    import numpy as np
+    from oracle import attention as oa
+    from oracle import mask as om
+    from synth import gen
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        threads = len(os.sched_getaffinity(0))
+    m = om.block_mask(om.spec_from_params(params))
+    scale = 1.0 / math.sqrt(wl.D)
+    sizes = np.minimum(wl.block, wl.N - np.arange(wl.nb) * wl.block)
+    flops, done, heads = 0, 0, 0
+    dt = 0.0
+    for h in range(wl.H):
+        q, k, v = (gen.to_f64(d[n][:, h:h + 1], wl.dtype) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        for i in range(wl.nb):
+            oa.block_sparse_attention(q, k, v, m, wl.block, scale, query_blocks=[i])
+            flops += 4 * wl.D * int(sizes[i]) * int(sizes[m[i]].sum())
+            done += 1
+            if dt + time.perf_counter() - t0 >= budget_s:
+                break
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= budget_s:
+            break
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s (effective, kept blocks)",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} of {wl.nb * wl.H} query-block rows (heads 0..{heads - 1} in order), "
+                      f"mask step 0: {flops / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy"}
+
+
+def copy_mode():
+    """Plain device-to-device copy of 1 GiB, 5 times (for counter calibration)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
+
+
+def main():
+    args = parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "the path has no multi-GPU part; heads would be sharded with no exchange.", file=sys.stderr)
+        sys.exit(2)
+    if args.mode == "copy":
+        copy_mode()
+        return
+
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen, get_workload
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    wl = get_workload(args.workload)
+    d = gen.make_qkv(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    steps_cycle = list(wl.anchor_steps) if wl.mask_kind == 1 else [0]
+    params = [wl.mask_params(s) for s in steps_cycle]
+    nb = wl.nb
+    rp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+
+    # effective FLOP of each step's mask (from the device CSR)
+    flops = []
+    for p in params:
+        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci)
+        r = rp.cpu().numpy()
+        c = ci[: int(r[-1])].cpu().numpy()
+        flops.append(kept_flops_from_csr(r, c, wl.N, wl.block, wl.D, wl.B, wl.H))
+
+    def step(i, evs=None):
+        p = params[i % len(params)]
+        if evs is not None:
+            evs[0].record()
+        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci)
+        if evs is not None:
+            evs[1].record()
+        bsa.block_sparse_attn_fwd(q, k, v, rp, ci, wl.block, out=out, lse=lse)
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+
+    total_s = t1 - t0
+    step_flops = [flops[i % len(flops)] for i in range(args.steps)]
+    attn_ms = [evs[i][1].elapsed_time(evs[i][2]) for i in range(args.steps)]
+    mask_ms = [evs[i][0].elapsed_time(evs[i][1]) for i in range(args.steps)]
+    attn_avg_ms = float(np.mean(attn_ms))
+    achieved = float(np.mean(step_flops)) / (attn_avg_ms * 1e-3) / 1e12
+    traffic = read_traffic(wl.name)
+
+    result = {
+        "metric": "ms/attn call and effective TFLOP/s at 32K video tokens; % of bf16 MFMA peak",
+        "value": round(sum(step_flops) / total_s / 1e12, 3),
+        "unit": "TFLOP/s (effective, kept blocks; mask build + attention per step)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_s * 1e3 / args.steps, 4),
+        "ms_per_attn_call": round(attn_avg_ms, 4),
+        "ms_per_attn_call_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),
+                                     round(float(np.percentile(attn_ms, 90)), 4)],
+        "ms_per_mask_build": round(float(np.mean(mask_ms)), 4),
+        "pct_of_bf16_mfma_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "frames": wl.frames, "frame_hw": [wl.frame_h, wl.frame_w], "block": wl.block,
+                   "mask": ("window +-3 frames, anchor every 8th frame rotated by step s=0..3, rows+cols"
+                            if wl.mask_kind == 1 else f"radial W={wl.radial_w}"),
+                   "gflop_per_call": [round(f / 1e9, 2) for f in flops]},
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128,128>",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(wl, d, params[0], args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -132,7 +132,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out=None,
-                          return_lse: bool = True):
+                          return_lse: bool = True, lse=None):
     """O (and LSE, fp32 [B, H, N]) of block-sparse softmax attention on the device."""
     lib = load()
     for t in (q, k, v):
@@ -147,7 +147,11 @@ def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if out.stride() != q.stride() or out.dtype != q.dtype:
         raise BsaError("out must have the layout and dtype of q")
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    if lse is None and return_lse:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
+                            or tuple(lse.shape) != tuple(q.shape[:3])):
+        raise BsaError("lse must be a contiguous float32 [B, H, N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     _check(lib.bsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),

@@ -39,20 +39,18 @@ constexpr int kBN = 64;  // keys per sub-tile
 
 template <int D>
 struct AttnCfg {
-  static constexpr int KST = D + 8;     // K stage row stride (elements): 16-byte shifted rows
-  static constexpr int VST = kBN + 8;   // V^T stage row stride (elements)
+  // K stage: row stride D + 8 elements (row step = 4 banks mod 64), so the 16 rows
+  // read by 16 consecutive lanes cover all 64 banks.
+  static constexpr int KST = D + 8;
+  // V stage: row-major, stride D + 32 elements (row step = 16 banks mod 64), so the
+  // 4-row x 64-byte footprint of a 32-lane transpose read covers all 64 banks.
+  static constexpr int VST = D + 32;
   static constexpr int K_ELEMS = kBN * KST;
-  static constexpr int V_ELEMS = D * VST;
+  static constexpr int V_ELEMS = kBN * VST;
   static constexpr int KT = D / 16;     // k-steps of the first product
   static constexpr int DT = D / 32;     // 32-wide d tiles of the output
+  static constexpr int CH = D / 8;      // 16-byte chunks per row
 };
-
-// Position of key offset w (0..15) inside its 16-key group of the V^T stage:
-// swap bits 2 and 3 (see the accumulator-layout note in the kernel).
-__device__ __forceinline__ int vt_pos(int kk) {
-  int w = kk & 15;
-  return (kk & ~15) | (w & 3) | ((w & 4) << 1) | ((w & 8) >> 1);
-}
 
 struct AttnArgs {
   const uint16_t* q;
@@ -63,19 +61,38 @@ struct AttnArgs {
   const int32_t* row_ptr;
   const int32_t* col_idx;
   int64_t sb, sh, sn;
-  int H, N, block, nb;
+  int B, H, N, block, nb;
   float scale_log2;  // scale * log2(e)
-  float scale;
 };
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 4 bf16 of one column from 4 consecutive rows of a row-major LDS tile.
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address of
+// 4 consecutive elements M[j][0..3]; lane i receives M[4e + i/4][i%4], e = 0..3.
+// With lane j pointing at row j/4, column 4*(j%4), lane i gets column i of rows 0..3.
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D, int BM>
-__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) attn_bf16_kernel(AttnArgs a) {
+__global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_kernel(AttnArgs a) {
   using C = AttnCfg<D>;
-  constexpr int NT = BM * 2;               // threads: BM / 32 waves of 64
-  constexpr int KCH = kBN * D / 8 / NT;    // 16-byte K chunks per thread per sub-tile
-  constexpr int VGT = (kBN / 4) * (D / 8);     // (4 keys x 8 d) V groups per sub-tile
-  constexpr int VG = (VGT + NT - 1) / NT;       // per thread (the last round may be partial)
-  static_assert(KCH >= 1 && KCH * NT * 8 == kBN * D, "tile/thread mismatch");
+  constexpr int NT = BM * 2;                 // BM / 32 waves of 64 lanes
+  constexpr int LCH = kBN * C::CH / NT;      // 16-byte chunks per thread per tile (K and V each)
+  static_assert(LCH >= 1 && LCH * NT == kBN * C::CH, "tile/thread mismatch");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2][C::K_ELEMS];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[2][C::V_ELEMS];
@@ -85,9 +102,17 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int wave = tid >> 6;
   const int l32 = lane & 31;
   const int hi = lane >> 5;
-  const int qblk = blockIdx.x;
-  const int h = blockIdx.y, b = blockIdx.z;
   const int N = a.N;
+
+  // Work item.  The hardware deals workgroups round-robin to the 8 XCDs; give
+  // each XCD a contiguous range of (batch, head, query block) so that the
+  // workgroups sharing one L2 walk neighbouring query blocks of one head.
+  int wid = blockIdx.x;
+  const int total = gridDim.x;
+  if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
+  const int qblk = wid % a.nb;
+  const int h = (wid / a.nb) % a.H;
+  const int b = wid / (a.nb * a.H);
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* __restrict__ Qh = a.q + head_off;
@@ -98,13 +123,9 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   const int qrow = qblk * a.block + wave * 32 + l32;
   bf16x8 qf[C::KT];
   {
-    const bool ok = qrow < N;
-    const uint16_t* src = Qh + (int64_t)(ok ? qrow : 0) * a.sn + hi * 8;
+    const uint16_t* src = Qh + (int64_t)min(qrow, N - 1) * a.sn + hi * 8;
 #pragma unroll
-    for (int t = 0; t < C::KT; ++t) {
-      u32x4 w = ok ? *(const u32x4*)(src + t * 16) : u32x4{0, 0, 0, 0};
-      qf[t] = __builtin_bit_cast(bf16x8, w);
-    }
+    for (int t = 0; t < C::KT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + t * 16));
   }
 
   const int rbeg = a.row_ptr[qblk], rend = a.row_ptr[qblk + 1];
@@ -115,55 +136,29 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
     const int last_real = N - (a.nb - 1) * a.block;
     nsub -= spb - (last_real + kBN - 1) / kBN;
   }
+  auto sub_key0 = [&](int u) -> int { return a.col_idx[rbeg + u / spb] * a.block + (u % spb) * kBN; };
 
-  auto sub_key0 = [&](int u) -> int {
-    return a.col_idx[rbeg + u / spb] * a.block + (u % spb) * kBN;
-  };
-
-  // ---- global -> register prefetch of one sub-tile
-  u32x4 kreg[KCH];
-  u32x4 vreg[VG][4];
+  // ---- global -> registers (one sub-tile ahead) -> LDS.  Rows past N are
+  // clamped to row N - 1: their logits are masked to -inf below, so they carry
+  // weight 0.
+  u32x4 kreg[LCH], vreg[LCH];
   auto fetch = [&](int key0) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < LCH; ++i) {
       const int c = tid + NT * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
-      const int key = key0 + row;
-      kreg[i] = key < N ? *(const u32x4*)(Kh + (int64_t)key * a.sn + col) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int g = 0; g < VG; ++g) {
-      const int grp = tid + NT * g;
-      if (VGT % NT != 0 && grp >= VGT) break;
-      const int kg = grp / (D / 8), dc = grp % (D / 8);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = key0 + kg * 4 + j;
-        vreg[g][j] = key < N ? *(const u32x4*)(Vh + (int64_t)key * a.sn + dc * 8) : u32x4{0, 0, 0, 0};
-      }
+      const int row = c / C::CH, col = (c % C::CH) * 8;
+      const int64_t off = (int64_t)min(key0 + row, N - 1) * a.sn + col;
+      kreg[i] = *(const u32x4*)(Kh + off);
+      vreg[i] = *(const u32x4*)(Vh + off);
     }
   };
   auto stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
+    for (int i = 0; i < LCH; ++i) {
       const int c = tid + NT * i;
-      const int row = c / (D / 8), col = (c % (D / 8)) * 8;
+      const int row = c / C::CH, col = (c % C::CH) * 8;
       *(u32x4*)&Ks[buf][row * C::KST + col] = kreg[i];
-    }
-#pragma unroll
-    for (int g = 0; g < VG; ++g) {
-      const int grp = tid + NT * g;
-      if (VGT % NT != 0 && grp >= VGT) break;
-      const int kg = grp / (D / 8), dc = grp % (D / 8);
-      const int pos = vt_pos(kg * 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {  // word e holds d = 2e (low half) and 2e+1 (high half)
-        const uint32_t w0 = vreg[g][0][e], w1 = vreg[g][1][e], w2 = vreg[g][2][e], w3 = vreg[g][3][e];
-        u32x2 lo = {(w0 & 0xffffu) | (w1 << 16), (w2 & 0xffffu) | (w3 << 16)};
-        u32x2 hi2 = {(w0 >> 16) | (w1 & 0xffff0000u), (w2 >> 16) | (w3 & 0xffff0000u)};
-        *(u32x2*)&Vs[buf][(dc * 8 + 2 * e) * C::VST + pos] = lo;
-        *(u32x2*)&Vs[buf][(dc * 8 + 2 * e + 1) * C::VST + pos] = hi2;
-      }
+      *(u32x4*)&Vs[buf][row * C::VST + col] = vreg[i];
     }
   };
 
@@ -171,9 +166,14 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   f32x16 o[C::DT];
 #pragma unroll
   for (int i = 0; i < C::DT; ++i) o[i] = f32x16{};
-  float m_run = -1e30f;  // finite start so that exp2(m_old - m_new) never sees inf - inf
+  float m_run = -1e30f;  // finite start: exp2(m_old - m_new) never sees inf - inf
   float l_run = 0.f;
   const float c2 = a.scale_log2;
+
+  // per-lane constants of the V^T operand reads (see lds_tr16)
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int v_row = 4 * hi + (j16 >> 2);
+  const int v_col = 16 * (g16 & 1) + 4 * (j16 & 3);
 
   if (nsub > 0) {
     fetch(sub_key0(0));
@@ -211,16 +211,22 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
         }
     }
 
-    // online softmax (log2 domain)
-    float mx = s[0][0];
+    // online softmax in the log2 domain; O and l are rescaled only when the
+    // running max of some lane moved
+    float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = fast_exp2((m_run - m_new) * c2);
-    const float mc = m_new * c2;
+    const float m_new = fmaxf(m_run, pair_max(mx));
+    if (__any(m_new > m_run)) {
+      const float alpha = fast_exp2((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < C::DT; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c2;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -230,12 +236,10 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
         s[kt][r] = p;
         psum += p;
       }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int i = 0; i < C::DT; ++i) o[i] *= alpha;
+    l_run += psum;
 
-    // P^T operands: k-step ks covers S^T registers 8*(ks%2) .. +8 of tile ks/2
+    // P^T operands: k-step ks covers S^T registers 8*(ks%2) .. +8 of tile ks/2,
+    // i.e. keys 16ks + 8*(e/4) + 4*hi + e%4 for element e.
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -246,14 +250,18 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
       pf[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T.  The A operand (row d = dt*32 + l32, the same 8 keys as
+    // P^T) is two transpose reads of 4 keys each from the row-major V stage.
     const uint16_t* Vb = Vs[buf];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt) {
-        const bf16x8 vf = *(const bf16x8*)&Vb[(dt * 32 + l32) * C::VST + ks * 16 + hi * 8];
-        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], o[dt], 0, 0, 0);
+        const uint16_t* p0 = &Vb[(ks * 16 + v_row) * C::VST + dt * 32 + v_col];
+        const u32x2 lo = lds_tr16(p0);
+        const u32x2 hi2 = lds_tr16(p0 + 8 * C::VST);
+        const u32x4 w = {lo[0], lo[1], hi2[0], hi2[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
       }
     }
 
@@ -262,7 +270,7 @@ __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 
   }
 
   // ---- epilogue: normalise and store. o[dt][r] = O^T[d dt*32 + 8*(r/4) + 4*hi + r%4][query l32]
-  const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+  const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     uint16_t* dst = a.o + head_off + (int64_t)qrow * a.sn;
@@ -379,9 +387,9 @@ bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v; a.o = (uint16_t*)o;
   a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx;
   a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
-  a.H = s.H; a.N = s.N; a.block = block; a.nb = (s.N + block - 1) / block;
-  a.scale = scale; a.scale_log2 = scale * kLog2e;
-  dim3 grid(a.nb, s.H, s.B);
+  a.B = s.B; a.H = s.H; a.N = s.N; a.block = block; a.nb = (s.N + block - 1) / block;
+  a.scale_log2 = scale * kLog2e;
+  dim3 grid((unsigned)((int64_t)a.nb * s.H * s.B));
   if (s.D == 128 && block == 128)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 128>), grid, dim3(256), 0, stream, a);
   else if (s.D == 128 && block == 64)

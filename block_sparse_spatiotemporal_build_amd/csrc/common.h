@@ -26,8 +26,11 @@ __device__ __forceinline__ uint32_t f2bf(float x) {
   __bf16 b = (__bf16)x;
   return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// two floats -> packed bf16 pair (RNE), one v_cvt_pk_bf16_f32 on gfx950
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f2bf(lo) | (f2bf(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

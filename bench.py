@@ -16,7 +16,9 @@ attention call; the attention kernel's roofline against the bf16 MFMA peak
 by rocprofv3 counters when a profile of the current kernel source exists; and
 the CPU oracle timed on a bounded sample of the same workload.
 
-Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens).
+Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens);
+linear_32k / linear_196k (elu+1 linear attention, HBM-bound: reported as
+algorithmic GB/s = (read Q, K, V + write O) / call time against 8 TB/s).
 """
 
 import argparse
@@ -41,7 +43,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="lvsa_32k", choices=["lvsa_32k", "radial_196k"])
+    ap.add_argument("--workload", default="lvsa_32k",
+                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -132,6 +135,57 @@ def copy_mode():
     print(json.dumps({"mode": "copy", "bytes_read_per_launch": n, "bytes_written_per_launch": n}))
 
 
+def bench_linear(args, wl):
+    """Linear attention: one step = one bsa_linear_attn_fwd call (state, reduce, apply)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_qkv(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    del d
+    out = torch.empty_like(q)
+    ws = torch.empty(bsa.linear_attn_workspace(q), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        bsa.linear_attn_fwd(q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        bsa.linear_attn_fwd(q, k, v, out=out, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    algo_bytes = 4 * wl.B * wl.H * wl.N * wl.D * 2
+    gbs = algo_bytes / (call_ms * 1e-3) / 1e9
+    return {
+        "metric": "algorithmic HBM GB/s of elu+1 linear attention",
+        "value": round(algo_bytes * args.steps / (t1 - t0) / 1e9, 1),
+        "unit": "GB/s (read Q, K, V + write O)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_per_call": round(call_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "algorithmic_bytes": algo_bytes},
+        "roofline": {"bound": "hbm", "kernel": "linear_attn_fwd (state + reduce + apply)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+    }
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -149,9 +203,12 @@ def main():
     import block_sparse_spatiotemporal_build_amd as bsa
     from synth import gen, get_workload
 
+    wl = get_workload(args.workload)
+    if wl.values == "iid":
+        print(json.dumps(bench_linear(args, wl)), flush=True)
+        return
     bsa.load()
     dev = torch.device("cuda:0")
-    wl = get_workload(args.workload)
     d = gen.make_qkv(wl)
 
     def up(a):

@@ -44,6 +44,9 @@ _SIGNATURES = {
     "bsa_block_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int,
                                                  ctypes.POINTER(Shape), _P, _P, ctypes.c_int32,
                                                  ctypes.c_float, _P]),
+    "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
+                                           _P, ctypes.c_size_t, _P]),
     "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bsa_last_error": (ctypes.c_char_p, []),
 }
@@ -159,3 +162,39 @@ def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out
                                          _ptr(col_idx), int(block), float(scale), _stream(q.device)),
            "bsa_block_sparse_attn_fwd")
     return out, lse
+
+
+def _check_qkv(q, k, v):
+    for t in (q, k, v):
+        if not t.is_cuda:
+            raise BsaError("q, k, v must be device tensors")
+    if k.shape != q.shape or v.shape != q.shape or k.stride() != q.stride() or v.stride() != q.stride():
+        raise BsaError("q, k, v must share one shape and one stride layout")
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise BsaError("q, k, v must share one dtype")
+
+
+def linear_attn_workspace(shape_like) -> int:
+    return int(load().bsa_linear_attn_workspace(ctypes.byref(_shape_of(shape_like))))
+
+
+def linear_attn_fwd(q, k, v, out=None, return_state: bool = False, workspace=None):
+    """elu+1 linear attention; returns out (bf16), plus S [B,H,D,D] and z [B,H,D] (fp32) if asked."""
+    lib = load()
+    _check_qkv(q, k, v)
+    shape = _shape_of(q)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if out.stride() != q.stride() or out.dtype != q.dtype:
+        raise BsaError("out must have the layout and dtype of q")
+    B, H, N, D = q.shape
+    S = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) if return_state else None
+    z = torch.empty((B, H, D), dtype=torch.float32, device=q.device) if return_state else None
+    need = int(lib.bsa_linear_attn_workspace(ctypes.byref(shape)))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_linear_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
+                                   ctypes.byref(shape), _ptr(S), _ptr(z), _ptr(workspace),
+                                   workspace.numel(), _stream(q.device)),
+           "bsa_linear_attn_fwd")
+    return (out, S, z) if return_state else out

@@ -38,6 +38,14 @@ bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o,
                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                            int block, float scale, hipStream_t stream);
 
+struct LinPlan {
+  int splits, chunk;
+  size_t off_part_s, off_part_z, off_st, off_z, total;
+};
+LinPlan linear_plan(const bsa_shape& s);
+bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
+                              float* S, float* z, void* ws, hipStream_t stream);
+
 static bsa_status fail(bsa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -135,6 +143,32 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (dtype == BSA_DT_BF16)
     return launch_attn_bf16(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
   return launch_attn_f32(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
+}
+
+size_t bsa_linear_attn_workspace(const bsa_shape* shape) {
+  if (check_shape(shape, 2, "bsa_linear_attn_workspace") != BSA_OK) return 0;
+  return linear_plan(*shape).total;
+}
+
+bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                               const bsa_shape* shape, float* S, float* z, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  const char* fn = "bsa_linear_attn_fwd";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (shape->D != 64 && shape->D != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, shape->D);
+  if (!q || !k || !v || !o) return fail(BSA_ERR_ARG, "%s: NULL tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  const size_t need = linear_plan(*shape).total;
+  if (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                workspace ? ws_bytes : (size_t)0);
+  g_err[0] = 0;
+  return launch_linear_attn(q, k, v, o, *shape, S, z, workspace, (hipStream_t)stream);
 }
 
 const char* bsa_status_string(bsa_status s) {

@@ -116,6 +116,29 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      const int32_t* row_ptr, const int32_t* col_idx,
                                      int32_t block, float scale, void* stream);
 
+/* Workspace bytes required by bsa_linear_attn_fwd for `shape` (0 if the shape
+ * is invalid).  The workspace holds per-chunk partial states (fp32), the
+ * reduced S^T in bf16 and z. */
+size_t bsa_linear_attn_workspace(const bsa_shape* shape);
+
+/* Non-causal linear attention with the elu+1 feature map.
+ * Operation (LinVideo page, technical summary sections 1-2: O(n) linear
+ * attention replacing quadratic softmax attention), with phi(x) = x + 1 for
+ * x > 0 and exp(x) otherwise:
+ *   S = sum_n phi(k_n) v_n^T,  z = sum_n phi(k_n),
+ *   o_n = phi(q_n)^T S / (phi(q_n)^T z)        (no softmax scale).
+ * q, k, v, o: bf16 device tensors with `shape`; D in {64, 128}.  phi is taken in
+ *   fp32; the MFMA operands phi(K), V, phi(Q) and S are bf16; S and z
+ *   accumulate in fp32; the denominator is fp32.
+ * S: nullable fp32 [B, H, D, D] device output (row d of S is phi-dimension d).
+ * z: nullable fp32 [B, H, D] device output.
+ * workspace: device buffer of at least bsa_linear_attn_workspace(shape) bytes,
+ *   256-byte aligned, owned by the caller; contents need not be initialised.
+ * Only dtype BSA_DT_BF16 is implemented (BSA_ERR_UNSUPPORTED otherwise). */
+bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                               const bsa_shape* shape, float* S, float* z, void* workspace,
+                               size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* bsa_status_string(bsa_status status);
 

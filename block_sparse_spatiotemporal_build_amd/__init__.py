@@ -47,6 +47,23 @@ _SIGNATURES = {
     "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                            _P, ctypes.c_size_t, _P]),
+    "bsa_cluster_centroids": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
+                                             ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]),
+    "bsa_route_scores_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
+    "bsa_route_scores": (ctypes.c_int, [_P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, ctypes.c_int32, _P,
+                                        ctypes.c_int32, _P, _P, _P, ctypes.c_float, _P, _P, ctypes.c_size_t,
+                                        _P]),
+    "bsa_route_select_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
+    "bsa_route_select": (ctypes.c_int, [_P, ctypes.POINTER(Shape), _P, ctypes.c_int32, _P, ctypes.c_int32,
+                                        ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_compensated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
+                                                ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P,
+                                                ctypes.c_float, _P]),
+    "bsa_centroid_compensate_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
+                                                            ctypes.c_int32]),
+    "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
+                                               ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bsa_last_error": (ctypes.c_char_p, []),
 }
@@ -198,3 +215,111 @@ def linear_attn_fwd(q, k, v, out=None, return_state: bool = False, workspace=Non
                                    workspace.numel(), _stream(q.device)),
            "bsa_linear_attn_fwd")
     return (out, S, z) if return_state else out
+
+
+# ---- clustered compensation ---------------------------------------------------
+
+def _check_offsets(q, q_off, k_off):
+    B, H = q.shape[0], q.shape[1]
+    for t in (q_off, k_off):
+        if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous() or t.dim() != 2 or t.shape[0] != B * H:
+            raise BsaError("offsets must be contiguous int32 device tensors [B*H, C+1]")
+    return q_off.shape[1] - 1, k_off.shape[1] - 1
+
+
+def cluster_centroids(q, k, v, q_off, k_off):
+    """fp32 centroids (q_cent [B*H, Cq, D], k_cent, v_cent [B*H, Ck, D])."""
+    lib = load()
+    _check_qkv(q, k, v)
+    Cq, Ck = _check_offsets(q, q_off, k_off)
+    B, H, N, D = q.shape
+    qc = torch.empty((B * H, Cq, D), dtype=torch.float32, device=q.device)
+    kc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device)
+    vc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device)
+    _check(lib.bsa_cluster_centroids(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(_shape_of(q)),
+                                     _ptr(q_off), Cq, _ptr(k_off), Ck, _ptr(qc), _ptr(kc), _ptr(vc),
+                                     _stream(q.device)), "bsa_cluster_centroids")
+    return qc, kc, vc
+
+
+def route_scores(k, v, q_off, k_off, q_cent, k_cent, v_cent, scale=None):
+    """fp32 routing scores [B*H, Cq, Ck]."""
+    lib = load()
+    _check_qkv(k, k, v)
+    Cq, Ck = _check_offsets(k, q_off, k_off)
+    B, H, N, D = k.shape
+    shape = _shape_of(k)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    score = torch.empty((B * H, Cq, Ck), dtype=torch.float32, device=k.device)
+    ws = torch.empty(int(lib.bsa_route_scores_workspace(ctypes.byref(shape), Cq, Ck)), dtype=torch.uint8,
+                     device=k.device)
+    _check(lib.bsa_route_scores(_ptr(k), _ptr(v), _dtype_code(k), ctypes.byref(shape), _ptr(q_off), Cq,
+                                _ptr(k_off), Ck, _ptr(q_cent.contiguous()), _ptr(k_cent.contiguous()),
+                                _ptr(v_cent.contiguous()), float(scale), _ptr(score), _ptr(ws), ws.numel(),
+                                _stream(k.device)), "bsa_route_scores")
+    return score
+
+
+def route_select(score, shape_like, q_off, k_off, density_ppm: int):
+    """Route CSR (row_ptr int32 [B*H, Cq+1], col int32 [B*H, Cq*Ck]) from a score array."""
+    lib = load()
+    Cq, Ck = _check_offsets(shape_like, q_off, k_off)
+    B, H = shape_like.shape[0], shape_like.shape[1]
+    shape = _shape_of(shape_like)
+    if score.dtype != torch.float32 or not score.is_contiguous() or score.numel() != B * H * Cq * Ck:
+        raise BsaError("score must be a contiguous float32 [B*H, Cq, Ck] tensor")
+    rrow = torch.empty((B * H, Cq + 1), dtype=torch.int32, device=score.device)
+    rcol = torch.empty((B * H, Cq * Ck), dtype=torch.int32, device=score.device)
+    ws = torch.empty(int(lib.bsa_route_select_workspace(ctypes.byref(shape), Cq, Ck)), dtype=torch.uint8,
+                     device=score.device)
+    _check(lib.bsa_route_select(_ptr(score), ctypes.byref(shape), _ptr(q_off), Cq, _ptr(k_off), Ck,
+                                int(density_ppm), _ptr(rrow), _ptr(rcol), _ptr(ws), ws.numel(),
+                                _stream(score.device)), "bsa_route_select")
+    return rrow, rcol
+
+
+def compensated_attn_fwd(q, k, v, q_off, k_off, rrow, rcol, k_cent, v_cent, scale=None, out=None,
+                         return_lse: bool = True):
+    """Compensated attention in cluster order; returns (out bf16, lse fp32 or None)."""
+    lib = load()
+    _check_qkv(q, k, v)
+    Cq, Ck = _check_offsets(q, q_off, k_off)
+    shape = _shape_of(q)
+    scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    _check(lib.bsa_compensated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                                        ctypes.byref(shape), _ptr(q_off), Cq, _ptr(k_off), Ck, _ptr(rrow),
+                                        _ptr(rcol), _ptr(k_cent.contiguous()), _ptr(v_cent.contiguous()),
+                                        float(scale), _stream(q.device)), "bsa_compensated_attn_fwd")
+    return out, lse
+
+
+def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out=None, lse=None,
+                        return_score: bool = False, workspace=None, rrow=None, rcol=None, score=None):
+    """All four steps; returns (out, lse, route_row_ptr, route_col[, score])."""
+    lib = load()
+    _check_qkv(q, k, v)
+    Cq, Ck = _check_offsets(q, q_off, k_off)
+    B, H, N, D = q.shape
+    shape = _shape_of(q)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if lse is None:
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if rrow is None:
+        rrow = torch.empty((B * H, Cq + 1), dtype=torch.int32, device=q.device)
+    if rcol is None:
+        rcol = torch.empty((B * H, Cq * Ck), dtype=torch.int32, device=q.device)
+    if score is None and return_score:
+        score = torch.empty((B * H, Cq, Ck), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib.bsa_centroid_compensate_workspace(ctypes.byref(shape), Cq, Ck)),
+                                dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_centroid_compensate(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
+                                       ctypes.byref(shape), _ptr(q_off), Cq, _ptr(k_off), Ck, int(density_ppm),
+                                       float(scale), _ptr(rrow), _ptr(rcol), _ptr(score), _ptr(workspace),
+                                       workspace.numel(), _stream(q.device)), "bsa_centroid_compensate")
+    return (out, lse, rrow, rcol, score) if return_score else (out, lse, rrow, rcol)

@@ -46,6 +46,25 @@ LinPlan linear_plan(const bsa_shape& s);
 bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
                               float* S, float* z, void* ws, hipStream_t stream);
 
+bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,
+                            int Cq, const int32_t* k_off, int Ck, float* qc, float* kc, float* vc,
+                            hipStream_t stream);
+struct ProbePlan {
+  int splits, cps;
+  size_t off_e, off_m, off_ms, off_zs, total;
+};
+ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck);
+bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s, const int32_t* q_off, int Cq,
+                               const int32_t* k_off, int Ck, const float* qc, const float* kc, const float* vc,
+                               float scale, float* score, void* ws, hipStream_t stream);
+bsa_status launch_route_select(const float* score, const bsa_shape& s, const int32_t* q_off, int Cq,
+                               const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
+                               uint8_t* flags, hipStream_t stream);
+bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
+                            const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
+                            const int32_t* rcol, const float* kc, const float* vc, float scale,
+                            hipStream_t stream);
+
 static bsa_status fail(bsa_status st, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -169,6 +188,162 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
                 workspace ? ws_bytes : (size_t)0);
   g_err[0] = 0;
   return launch_linear_attn(q, k, v, o, *shape, S, z, workspace, (hipStream_t)stream);
+}
+
+// ---- clustered compensation (SVG-EAR) -------------------------------------
+
+static constexpr int kMaxKeyClusters = 512;
+
+static size_t align256h(size_t x) { return (x + 255) & ~(size_t)255; }
+
+static bsa_status check_clusters(const bsa_shape* shape, const int32_t* q_off, int32_t Cq, const int32_t* k_off,
+                                 int32_t Ck, const char* fn) {
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (shape->D != 64 && shape->D != 128)
+    return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 64 or 128 (got %d)", fn, shape->D);
+  if (Cq < 1 || Ck < 1) return fail(BSA_ERR_ARG, "%s: Cq and Ck must be >= 1", fn);
+  if (Cq > 65535 || (int64_t)Cq * Ck > (1LL << 30))
+    return fail(BSA_ERR_ARG, "%s: Cq <= 65535 and Cq * Ck <= 2^30 required", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  if (!q_off || !k_off) return fail(BSA_ERR_ARG, "%s: NULL offsets", fn);
+  return BSA_OK;
+}
+
+static long long budget_of(int N, int32_t density_ppm) {
+  return (long long)N * (long long)N * (long long)density_ppm / 1000000LL;
+}
+
+bsa_status bsa_cluster_centroids(const void* q, const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
+                                 const int32_t* q_off, int32_t Cq, const int32_t* k_off, int32_t Ck, float* q_cent,
+                                 float* k_cent, float* v_cent, void* stream) {
+  const char* fn = "bsa_cluster_centroids";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
+  if (st != BSA_OK) return st;
+  if (!q || !k || !v || !q_cent || !k_cent || !v_cent) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(BSA_ERR_ARG, "%s: q, k, v must be 16-byte aligned", fn);
+  g_err[0] = 0;
+  return launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, q_cent, k_cent, v_cent, (hipStream_t)stream);
+}
+
+size_t bsa_route_scores_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
+  if (check_shape(shape, 2, "bsa_route_scores_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
+  return probe_plan(*shape, Cq, Ck).total;
+}
+
+bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
+                            const int32_t* q_off, int32_t Cq, const int32_t* k_off, int32_t Ck, const float* q_cent,
+                            const float* k_cent, const float* v_cent, float scale, float* score, void* workspace,
+                            size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_route_scores";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
+  if (st != BSA_OK) return st;
+  if (!k || !v || !q_cent || !k_cent || !v_cent || !score) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(v_cent)) return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
+  if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
+  const size_t need = probe_plan(*shape, Cq, Ck).total;
+  if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
+  g_err[0] = 0;
+  return launch_route_scores(k, v, *shape, q_off, Cq, k_off, Ck, q_cent, k_cent, v_cent, scale, score, workspace,
+                             (hipStream_t)stream);
+}
+
+size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
+  if (check_shape(shape, 2, "bsa_route_select_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
+  return align256h((size_t)shape->B * shape->H * Cq * Ck);
+}
+
+bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const int32_t* q_off, int32_t Cq,
+                            const int32_t* k_off, int32_t Ck, int32_t density_ppm, int32_t* route_row_ptr,
+                            int32_t* route_col, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_route_select";
+  bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
+  if (st != BSA_OK) return st;
+  if (!score || !route_row_ptr || !route_col) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (density_ppm < 0 || density_ppm > 1000000) return fail(BSA_ERR_ARG, "%s: density_ppm must be in [0, 1e6]", fn);
+  const size_t need = bsa_route_select_workspace(shape, Cq, Ck);
+  if (!workspace || ws_bytes < need) return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+  g_err[0] = 0;
+  return launch_route_select(score, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
+                             route_col, (uint8_t*)workspace, (hipStream_t)stream);
+}
+
+bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dtype,
+                                    const bsa_shape* shape, const int32_t* q_off, int32_t Cq, const int32_t* k_off,
+                                    int32_t Ck, const int32_t* route_row_ptr, const int32_t* route_col,
+                                    const float* k_cent, const float* v_cent, float scale, void* stream) {
+  const char* fn = "bsa_compensated_attn_fwd";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
+  if (st != BSA_OK) return st;
+  if (Ck > kMaxKeyClusters) return fail(BSA_ERR_UNSUPPORTED, "%s: Ck must be <= %d", fn, kMaxKeyClusters);
+  if (!q || !k || !v || !o || !route_row_ptr || !route_col || !k_cent || !v_cent)
+    return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cent) || !aligned16(v_cent))
+    return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
+  if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
+  g_err[0] = 0;
+  return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, k_cent, v_cent,
+                          scale, (hipStream_t)stream);
+}
+
+// fused call: workspace = centroids | scores | probe scratch | select flags
+struct CompPlan {
+  size_t qc, kc, vc, sc, probe, flags, total;
+};
+static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
+  CompPlan p;
+  const size_t bh = (size_t)s.B * s.H, D = s.D;
+  p.qc = 0;
+  p.kc = align256h(p.qc + bh * Cq * D * 4);
+  p.vc = align256h(p.kc + bh * Ck * D * 4);
+  p.sc = align256h(p.vc + bh * Ck * D * 4);
+  p.probe = align256h(p.sc + bh * Cq * Ck * 4);
+  p.flags = align256h(p.probe + probe_plan(s, Cq, Ck).total);
+  p.total = align256h(p.flags + bh * Cq * Ck);
+  return p;
+}
+
+size_t bsa_centroid_compensate_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
+  if (check_shape(shape, 2, "bsa_centroid_compensate_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
+  return comp_plan(*shape, Cq, Ck).total;
+}
+
+bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dtype,
+                                   const bsa_shape* shape, const int32_t* q_off, int32_t Cq, const int32_t* k_off,
+                                   int32_t Ck, int32_t density_ppm, float scale, int32_t* route_row_ptr,
+                                   int32_t* route_col, float* score, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_centroid_compensate";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
+  if (st != BSA_OK) return st;
+  if (Ck > kMaxKeyClusters) return fail(BSA_ERR_UNSUPPORTED, "%s: Ck must be <= %d", fn, kMaxKeyClusters);
+  if (!q || !k || !v || !o || !route_row_ptr || !route_col) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if (density_ppm < 0 || density_ppm > 1000000) return fail(BSA_ERR_ARG, "%s: density_ppm must be in [0, 1e6]", fn);
+  if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
+  const CompPlan pl = comp_plan(*shape, Cq, Ck);
+  if (!workspace || ws_bytes < pl.total || ((uintptr_t)workspace & 255u))
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, pl.total);
+  g_err[0] = 0;
+  char* w = (char*)workspace;
+  float* qc = (float*)(w + pl.qc);
+  float* kc = (float*)(w + pl.kc);
+  float* vc = (float*)(w + pl.vc);
+  float* sc = score ? score : (float*)(w + pl.sc);
+  hipStream_t sm = (hipStream_t)stream;
+  st = launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, sm);
+  if (st != BSA_OK) return st;
+  st = launch_route_scores(k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, scale, sc, w + pl.probe, sm);
+  if (st != BSA_OK) return st;
+  st = launch_route_select(sc, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
+                           route_col, (uint8_t*)(w + pl.flags), sm);
+  if (st != BSA_OK) return st;
+  return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale, sm);
 }
 
 const char* bsa_status_string(bsa_status s) {

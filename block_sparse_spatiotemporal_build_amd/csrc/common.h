@@ -35,6 +35,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// 4 bf16 of one column from 4 consecutive rows of a row-major LDS tile.
+// ds_read_b64_tr_b16: within each 16-lane group, lane j supplies the address of
+// 4 consecutive elements M[j][0..3]; lane i receives M[4e + i/4][i%4], e = 0..3.
+// With lane j pointing at row j/4, column 4*(j%4), lane i gets column i of rows 0..3.
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Combine a value of lane l with that of lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // Launch-error check used by every entry point after enqueueing kernels.
 bool launch_ok(const char* what);
 

@@ -28,13 +28,6 @@ namespace bsa {
 
 __device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
 
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
-__device__ __forceinline__ u32x2 lds_tr16_la(const uint16_t* p) {
-  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)(p));
-  return __builtin_bit_cast(u32x2, r);
-}
-
 constexpr int kLinTok = 64;      // tokens per state tile
 constexpr int kLinThreads = 256;
 
@@ -133,8 +126,8 @@ __global__ void __launch_bounds__(kLinThreads) lin_state_kernel(LinStateArgs a) 
         const int d1t = tile / C::NT32, d2t = tile % C::NT32;
         const uint16_t* pa = &Ks[buf][(ks * 16 + tr_row) * C::ST + d1t * 32 + tr_col];
         const uint16_t* pb = &Vs[buf][(ks * 16 + tr_row) * C::ST + d2t * 32 + tr_col];
-        const u32x2 a0 = lds_tr16_la(pa), a1 = lds_tr16_la(pa + 8 * C::ST);
-        const u32x2 b0 = lds_tr16_la(pb), b1 = lds_tr16_la(pb + 8 * C::ST);
+        const u32x2 a0 = lds_tr16(pa), a1 = lds_tr16(pa + 8 * C::ST);
+        const u32x2 b0 = lds_tr16(pb), b1 = lds_tr16(pb + 8 * C::ST);
         const u32x4 av = {a0[0], a0[1], a1[0], a1[1]};
         const u32x4 bv = {b0[0], b0[1], b1[0], b1[1]};
         acc[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, av),
@@ -259,8 +252,7 @@ __global__ void __launch_bounds__(256) lin_apply_kernel(LinApplyArgs a) {
       qf[t] = __builtin_bit_cast(bf16x8, w);
     }
     {
-      auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(den), __float_as_uint(den), false, false);
-      den = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+      den = pair_sum(den);
     }
     f32x16 o[DT];
 #pragma unroll

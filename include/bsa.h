@@ -139,6 +139,91 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
                                const bsa_shape* shape, float* S, float* z, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* ---- clustered sparse attention with centroid compensation ---------------
+ * Source: "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
+ * Generation via Error-aware Routing", technical summary section 2 Method.
+ * Inputs common to these calls:
+ *   q, k, v: bf16 [B, H, N, D] device tensors (D in {64, 128}) whose rows are
+ *     already ordered by cluster, per (batch, head): query cluster a is rows
+ *     [q_off[a], q_off[a+1]) of q, key cluster b is rows [k_off[b], k_off[b+1])
+ *     of k and v.
+ *   q_off: int32 [B*H][Cq + 1], k_off: int32 [B*H][Ck + 1] device arrays,
+ *     non-decreasing from 0 to N (not checked on the host: offsets outside
+ *     [0, N] are undefined behaviour).  Empty clusters are allowed.
+ *   A block is a (query cluster a, key cluster b) pair with cost n_a * n_b.
+ *   Centroid arrays are fp32 row-major: q_cent [B*H][Cq][D], k_cent and
+ *   v_cent [B*H][Ck][D].  Scores are fp32 [B*H][Cq][Ck]. */
+
+/* Step 1 (idea 1, cluster centroids): q_cent[a] = mean of the q rows of cluster
+ * a; k_cent[b], v_cent[b] = means of the k and v rows of key cluster b (fp32
+ * accumulation; an empty cluster gets zeros). */
+bsa_status bsa_cluster_centroids(const void* q, const void* k, const void* v, bsa_dtype dtype,
+                                 const bsa_shape* shape, const int32_t* q_off, int32_t Cq,
+                                 const int32_t* k_off, int32_t Ck, float* q_cent, float* k_cent,
+                                 float* v_cent, void* stream);
+
+/* Workspace bytes of bsa_route_scores (0 for an invalid shape). */
+size_t bsa_route_scores_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
+
+/* Step 2 (idea 2, error estimation by probing with query-cluster centroids as
+ * proxies, streamed without storing logits): with l_aj = scale * c^_a . k_j over
+ * all keys j, m_a = max_j l_aj, Z_a = sum_j exp(l_aj - m_a),
+ *   e_ab = (sum_{j in b} exp(l_aj - m_a) v_j - n_b exp(scale c^_a . c_b - m_a) vbar_b) / Z_a,
+ *   score[a][b] = |e_ab|^2 / n_b  (squared output error per unit cost),
+ * and 0 when cluster a or b is empty.  The sum is accumulated as
+ * sum_{j in b} (exp(l_aj - m_a) - exp(scale c^_a.c_b - m_a)) v_j (n_b vbar_b =
+ * sum_j v_j), with the proxies and the weight differences split into two bf16
+ * MFMA operands each (about 16 significant bits); everything else is fp32.
+ * workspace: at least
+ * bsa_route_scores_workspace bytes, 256-byte aligned. */
+bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
+                            const int32_t* q_off, int32_t Cq, const int32_t* k_off, int32_t Ck,
+                            const float* q_cent, const float* k_cent, const float* v_cent,
+                            float scale, float* score, void* workspace, size_t ws_bytes,
+                            void* stream);
+
+/* Workspace bytes of bsa_route_select (0 for an invalid shape). */
+size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
+
+/* Step 3 (idea 2, error-to-cost routing under a density budget): per (batch,
+ * head), order the non-empty blocks by (score descending, a * Ck + b
+ * ascending) and keep the longest prefix whose total cost is <=
+ * floor(N * N * density_ppm / 10^6) (integer arithmetic).  Bit-exact for a given
+ * score array.  Output CSR per (batch, head): route_row_ptr int32 [B*H][Cq + 1]
+ * (offsets relative to that head's route_col segment), route_col int32
+ * [B*H][Cq * Ck] with the kept key clusters of each query cluster ascending.
+ * density_ppm in [0, 10^6]. */
+bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const int32_t* q_off,
+                            int32_t Cq, const int32_t* k_off, int32_t Ck, int32_t density_ppm,
+                            int32_t* route_row_ptr, int32_t* route_col, void* workspace,
+                            size_t ws_bytes, void* stream);
+
+/* Step 4 (idea 1, parameter-free linear compensation): for a query q of
+ * cluster a, one softmax over the exact keys of the kept clusters of route row
+ * a and one virtual key per skipped non-empty cluster b (key k_cent[b], value
+ * v_cent[b], logit scale * q . k_cent[b] + ln n_b), i.e. the n_b keys of a
+ * skipped cluster are replaced by n_b copies of their centroid.  o (bf16) and
+ * lse (nullable fp32 [B, H, N]) are in the cluster order of q.  Ck <= 512. */
+bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                                    bsa_dtype dtype, const bsa_shape* shape, const int32_t* q_off,
+                                    int32_t Cq, const int32_t* k_off, int32_t Ck,
+                                    const int32_t* route_row_ptr, const int32_t* route_col,
+                                    const float* k_cent, const float* v_cent, float scale,
+                                    void* stream);
+
+/* Workspace bytes of bsa_centroid_compensate (0 for an invalid shape). */
+size_t bsa_centroid_compensate_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
+
+/* Steps 1-4 in one call: centroids, route scores, route selection at
+ * density_ppm, compensated attention.  route_row_ptr / route_col receive the
+ * route; score (nullable) receives the scores.  workspace: at least
+ * bsa_centroid_compensate_workspace bytes, 256-byte aligned. */
+bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   bsa_dtype dtype, const bsa_shape* shape, const int32_t* q_off,
+                                   int32_t Cq, const int32_t* k_off, int32_t Ck, int32_t density_ppm,
+                                   float scale, int32_t* route_row_ptr, int32_t* route_col,
+                                   float* score, void* workspace, size_t ws_bytes, void* stream);
+
 /* Text of a status code (static storage). */
 const char* bsa_status_string(bsa_status status);
 

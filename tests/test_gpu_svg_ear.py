@@ -1,0 +1,179 @@
+"""GPU centroid compensation with error-aware routing vs the oracle, step by step.
+
+Centroids and scores are compared with the float64 oracle; the selection is
+checked bit-exactly on a score array the oracle produced (rounded to fp32, the
+precision the device selects in); the compensated attention is checked on the
+oracle's route.  The fused call is checked against the step-by-step device
+path (bitwise) and its route overlap with the oracle's is reported.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import assert_parity, to_device, to_f64
+from oracle import attention as oa
+from oracle import svg_ear as oe
+from synth import gen, get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _small(seed=51, Cq=8, Ck=20, frames=2, fh=10, fw=30, H=2, D=128):
+    wl = gen.scaled(get_workload("svg_ear_32k"), H=H, D=D, frames=frames, frame_h=fh, frame_w=fw,
+                    n_q_clusters=Cq, n_k_clusters=Ck, kmeans_iters=3, seed=seed)
+    return wl, gen.make_clustered(wl)
+
+
+def _dev(d):
+    q, k, v = (to_device(d[n], "bf16") for n in ("q", "k", "v"))
+    qo = torch.from_numpy(d["q_off"]).cuda()
+    ko = torch.from_numpy(d["k_off"]).cuda()
+    return q, k, v, qo, ko
+
+
+def _head(d, r):
+    B_H = d["q"].shape[0] * d["q"].shape[1]
+    b, h = divmod(r, d["q"].shape[1])
+    q, k, v = (gen.to_f64(d[n][b, h], "bf16") for n in ("q", "k", "v"))
+    return q, k, v, d["q_off"][r], d["k_off"][r]
+
+
+def _check_steps(bsa, wl, d, ppm, attn_clusters=None):
+    q, k, v, qo, ko = _dev(d)
+    scale = 1.0 / math.sqrt(wl.D)
+    qc, kc, vc = bsa.cluster_centroids(q, k, v, qo, ko)
+    score = bsa.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+    torch.cuda.synchronize()
+    nh = wl.B * wl.H
+    oracle_scores32 = np.empty((nh, wl.n_q_clusters, wl.n_k_clusters), np.float32)
+    refs = []
+    for r in range(nh):
+        hq, hk, hv, hqo, hko = _head(d, r)
+        cents = oe.centroids(hq, hk, hv, hqo, hko)
+        for name, got in (("cq", qc[r]), ("ck", kc[r]), ("vk", vc[r])):
+            g = to_f64(got)
+            assert np.abs(g - cents[name]).max() <= 1e-5 * max(1.0, np.abs(cents[name]).max()), name
+        sc = oe.route_scores(hk, hv, hko, cents, scale)
+        gs = to_f64(score[r])
+        assert np.abs(gs - sc).max() <= 1e-3 * sc.max(), (r, np.abs(gs - sc).max(), sc.max())
+        oracle_scores32[r] = sc.astype(np.float32)
+        refs.append((hq, hk, hv, hqo, hko, cents))
+
+    # selection: bit-exact given the oracle's scores in fp32
+    s32 = torch.from_numpy(oracle_scores32).cuda()
+    rrow, rcol = bsa.route_select(s32, q, qo, ko, ppm)
+    torch.cuda.synchronize()
+    rrow_h, rcol_h = rrow.cpu().numpy(), rcol.cpu().numpy()
+    kept_all = []
+    for r in range(nh):
+        hq, hk, hv, hqo, hko, cents = refs[r]
+        want_rp, want_col, kept = oe.select_route(oracle_scores32[r].astype(np.float64), cents["nq"],
+                                                  cents["nk"], wl.N, ppm)
+        assert np.array_equal(rrow_h[r], want_rp), r
+        assert np.array_equal(rcol_h[r][: want_rp[-1]], want_col), r
+        kept_all.append(kept)
+
+    # attention on the oracle's route (the route the device just reproduced)
+    out, lse = bsa.compensated_attn_fwd(q, k, v, qo, ko, rrow, rcol, kc, vc, scale)
+    torch.cuda.synchronize()
+    got = to_f64(out)
+    glse = lse.cpu().numpy()
+    for r in range(nh):
+        hq, hk, hv, hqo, hko, cents = refs[r]
+        b, h = divmod(r, wl.H)
+        ref, rlse = oe.compensated_attention(hq, hk, hv, hqo, hko, kept_all[r], cents, scale, attn_clusters)
+        rows = ~np.isnan(ref[:, 0])
+        assert_parity(got[b, h][rows], ref[rows], "bf16", f"compensated attention head {r}")
+        assert np.abs(glse[b, h][rows] - rlse[rows]).max() < 2e-3
+    return dict(q=q, k=k, v=v, qo=qo, ko=ko, score=score, rrow=rrow, rcol=rcol, out=out, lse=lse,
+                kc=kc, vc=vc, s32=oracle_scores32)
+
+
+@pytest.mark.parametrize("ppm", [150000, 0, 1000000, 400000])
+def test_small_steps(gpu_lib, ppm):
+    wl, d = _small()
+    _check_steps(gpu_lib, wl, d, ppm)
+
+
+def test_small_d64_and_many_proxies(gpu_lib):
+    wl, d = _small(seed=52, Cq=150, Ck=40, frames=3, fh=10, fw=40, H=1, D=64)
+    _check_steps(gpu_lib, wl, d, 150000)
+
+
+def test_empty_clusters(gpu_lib):
+    wl, d = _small(seed=53)
+    # move every token of query cluster 3 and key cluster 5 into their neighbours
+    d = dict(d)
+    for key in ("q_off", "k_off"):
+        d[key] = d[key].copy()
+    d["q_off"][:, 4] = d["q_off"][:, 3]
+    d["k_off"][:, 6] = d["k_off"][:, 5]
+    _check_steps(gpu_lib, wl, d, 150000)
+
+
+def test_fused_call_matches_steps(gpu_lib):
+    wl, d = _small(seed=54)
+    q, k, v, qo, ko = _dev(d)
+    scale = 1.0 / math.sqrt(wl.D)
+    out, lse, rrow, rcol, score = gpu_lib.centroid_compensate(q, k, v, qo, ko, 150000, return_score=True)
+    qc, kc, vc = gpu_lib.cluster_centroids(q, k, v, qo, ko)
+    s2 = gpu_lib.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+    r2, c2 = gpu_lib.route_select(s2, q, qo, ko, 150000)
+    o2, l2 = gpu_lib.compensated_attn_fwd(q, k, v, qo, ko, r2, c2, kc, vc, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(score, s2) and torch.equal(rrow, r2)
+    assert torch.equal(out.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, l2)
+
+
+def test_equal_keys_make_compensation_exact(gpu_lib):
+    """Every key of a cluster equal to its centroid: output == dense attention at any budget."""
+    wl, d = _small(seed=55)
+    d = dict(d)
+    k = d["k"].copy()
+    for r in range(wl.B * wl.H):
+        b, h = divmod(r, wl.H)
+        ko = d["k_off"][r]
+        for c in range(len(ko) - 1):
+            if ko[c + 1] > ko[c]:
+                k[b, h, ko[c]:ko[c + 1]] = k[b, h, ko[c]]
+    d["k"] = k
+    q, kk, v, qo, ko_t = _dev(d)
+    for ppm in (0, 150000):
+        out, _, _, _ = gpu_lib.centroid_compensate(q, kk, v, qo, ko_t, ppm)
+        torch.cuda.synchronize()
+        ref, _ = oa.dense_attention(gen.to_f64(d["q"], "bf16"), gen.to_f64(k, "bf16"),
+                                    gen.to_f64(d["v"], "bf16"), 1.0 / math.sqrt(wl.D))
+        assert_parity(to_f64(out), ref, "bf16", f"equal keys ppm={ppm}")
+
+
+@pytest.fixture(scope="module")
+def svg_full():
+    wl = get_workload("svg_ear_32k")
+    return wl, gen.make_clustered(wl)
+
+
+def test_svg_ear_32k(gpu_lib, svg_full):
+    """Full workload: all centroids and scores, selection bit-exact on every head,
+    attention on sampled query clusters; then the fused call's route overlap."""
+    wl, d = svg_full
+    res = _check_steps(gpu_lib, wl, d, wl.density_ppm, attn_clusters=[0, 37, 99])
+    out, lse, rrow, rcol = gpu_lib.centroid_compensate(res["q"], res["k"], res["v"], res["qo"], res["ko"],
+                                                       wl.density_ppm)
+    torch.cuda.synchronize()
+    # the device's own route vs the oracle's route (reported; near-ties at the cut may differ)
+    rr, rc = rrow.cpu().numpy(), rcol.cpu().numpy()
+    jac = []
+    for r in range(wl.H):
+        hq, hk, hv, hqo, hko = _head(d, r)
+        mine = set()
+        for a in range(wl.n_q_clusters):
+            mine |= {(a, int(b)) for b in rc[r][rr[r][a]:rr[r][a + 1]]}
+        _, _, kept = oe.select_route(res["s32"][r].astype(np.float64),
+                                     np.diff(hqo), np.diff(hko), wl.N, wl.density_ppm)
+        ref = {(int(a), int(b)) for a, b in zip(*np.nonzero(kept))}
+        jac.append(len(mine & ref) / max(1, len(mine | ref)))
+    print("route Jaccard per head:", [round(j, 4) for j in jac])
+    assert min(jac) > 0.9

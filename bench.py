@@ -18,7 +18,11 @@ the CPU oracle timed on a bounded sample of the same workload.
 
 Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens);
 linear_32k / linear_196k (elu+1 linear attention, HBM-bound: reported as
-algorithmic GB/s = (read Q, K, V + write O) / call time against 8 TB/s).
+algorithmic GB/s = (read Q, K, V + write O) / call time against 8 TB/s);
+svg_ear_32k (clustered Q/K, centroid compensation at 15% density: one step is
+the fused call; routing = centroids + scores + selection reported as
+algorithmic GB/s of reading Q, K, V once; compensated attention as effective
+TFLOP/s over exact plus virtual keys).
 """
 
 import argparse
@@ -44,7 +48,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="lvsa_32k",
-                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k"])
+                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "svg_ear_32k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -186,6 +190,100 @@ def bench_linear(args, wl):
     }
 
 
+def bench_svg(args, wl):
+    """Centroid compensation: one step = one bsa_centroid_compensate call."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_clustered(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    qo = torch.from_numpy(d["q_off"]).to(dev)
+    ko = torch.from_numpy(d["k_off"]).to(dev)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    res = bsa.centroid_compensate(q, k, v, qo, ko, wl.density_ppm, out=out, lse=lse)
+    rrow, rcol = res[2], res[3]
+    scale = 1.0 / math.sqrt(wl.D)
+
+    def fused():
+        bsa.centroid_compensate(q, k, v, qo, ko, wl.density_ppm, out=out, lse=lse, rrow=rrow, rcol=rcol)
+
+    for _ in range(args.warmup):
+        fused()
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        fused()
+        e1.record()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    # per-step split through the step entry points (same kernels)
+    qc, kc, vc = bsa.cluster_centroids(q, k, v, qo, ko)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
+    split = []
+    for _ in range(max(3, args.steps // 4)):
+        marks[0].record()
+        bsa.cluster_centroids(q, k, v, qo, ko)
+        marks[1].record()
+        sc = bsa.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+        marks[2].record()
+        r2, c2 = bsa.route_select(sc, q, qo, ko, wl.density_ppm)
+        marks[3].record()
+        bsa.compensated_attn_fwd(q, k, v, qo, ko, r2, c2, kc, vc, scale, out=out, return_lse=False)
+        marks[4].record()
+        torch.cuda.synchronize(dev)
+        split.append([marks[i].elapsed_time(marks[i + 1]) for i in range(4)])
+    cent_ms, score_ms, sel_ms, attn_ms = (float(x) for x in np.median(np.array(split), axis=0))
+
+    # effective FLOP of the compensated attention: exact keys of kept clusters + virtual keys
+    rr, rc = rrow.cpu().numpy(), rcol.cpu().numpy()
+    qon, kon = d["q_off"], d["k_off"]
+    pairs = 0
+    for r in range(wl.B * wl.H):
+        nk = np.diff(kon[r]).astype(np.int64)
+        nq = np.diff(qon[r]).astype(np.int64)
+        for a in range(wl.n_q_clusters):
+            cols = rc[r][rr[r][a]:rr[r][a + 1]]
+            exact = int(nk[cols].sum())
+            virt = int((nk > 0).sum()) - len(cols)
+            pairs += int(nq[a]) * (exact + virt)
+    attn_flop = 4 * wl.D * pairs
+    route_bytes = 3 * wl.B * wl.H * wl.N * wl.D * 2
+    route_ms = cent_ms + score_ms + sel_ms
+    achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    return {
+        "metric": "ms per centroid-compensated attention call (routing + attention)",
+        "value": round(call_ms, 4), "unit": "ms", "higher_is_better": False,
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_split": {"centroids": round(cent_ms, 4), "route_scores": round(score_ms, 4),
+                     "route_select": round(sel_ms, 4), "compensated_attn": round(attn_ms, 4)},
+        "routing_gbs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
+        "routing_frac_of_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "Cq": wl.n_q_clusters, "Ck": wl.n_k_clusters, "density_ppm": wl.density_ppm,
+                   "attn_gflop": round(attn_flop / 1e9, 2), "routing_bytes": route_bytes},
+        "roofline": {"bound": "mfma", "kernel": "comp_attn_kernel<128>", "achieved": round(achieved, 2),
+                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": None},
+    }
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -206,6 +304,9 @@ def main():
     wl = get_workload(args.workload)
     if wl.values == "iid":
         print(json.dumps(bench_linear(args, wl)), flush=True)
+        return
+    if wl.values == "gmm":
+        print(json.dumps(bench_svg(args, wl)), flush=True)
         return
     bsa.load()
     dev = torch.device("cuda:0")

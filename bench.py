@@ -321,6 +321,7 @@ def main():
     nb = wl.nb
     rp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
     ci = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    ro = torch.empty(nb + 1, dtype=torch.int32, device=dev)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
 
@@ -336,10 +337,10 @@ def main():
         p = params[i % len(params)]
         if evs is not None:
             evs[0].record()
-        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci)
+        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci, row_order=ro)
         if evs is not None:
             evs[1].record()
-        bsa.block_sparse_attn_fwd(q, k, v, rp, ci, wl.block, out=out, lse=lse)
+        bsa.block_sparse_attn_fwd(q, k, v, rp, ci, wl.block, out=out, lse=lse, row_order=ro)
         if evs is not None:
             evs[2].record()
 
@@ -386,7 +387,7 @@ def main():
                    "mask": ("window +-3 frames, anchor every 8th frame rotated by step s=0..3, rows+cols"
                             if wl.mask_kind == 1 else f"radial W={wl.radial_w}"),
                    "gflop_per_call": [round(f / 1e9, 2) for f in flops]},
-        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel<128,128>",
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_d128_kernel",
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
     }

@@ -40,9 +40,9 @@ class Shape(ctypes.Structure):
 _P = ctypes.c_void_p
 _SIGNATURES = {
     "bsa_mask_num_blocks": (ctypes.c_int32, [ctypes.POINTER(MaskDesc)]),
-    "bsa_build_block_mask": (ctypes.c_int, [ctypes.POINTER(MaskDesc), _P, _P, ctypes.c_int64, _P]),
+    "bsa_build_block_mask": (ctypes.c_int, [ctypes.POINTER(MaskDesc), _P, _P, ctypes.c_int64, _P, _P]),
     "bsa_block_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int,
-                                                 ctypes.POINTER(Shape), _P, _P, ctypes.c_int32,
+                                                 ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_int32,
                                                  ctypes.c_float, _P]),
     "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
@@ -114,10 +114,15 @@ def num_blocks(params: dict) -> int:
     return nb
 
 
-def build_block_mask(params: dict, device="cuda", row_ptr=None, col_idx=None):
+def build_block_mask(params: dict, device="cuda", row_ptr=None, col_idx=None, row_order=None,
+                     with_order: bool = False):
     """CSR (row_ptr int32[nb+1], col_idx int32[nb*nb]) of the block mask, on the device.
 
-    Only the first row_ptr[nb] entries of col_idx are meaningful.
+    Only the first row_ptr[nb] entries of col_idx are meaningful.  With
+    ``with_order`` (or a given ``row_order`` buffer) also returns the rows sorted
+    schedule ``block_sparse_attn_fwd`` accepts: int32[nb + 1], rows with at least
+    1.5x the mean length first (longest first), then the others in index order,
+    and the number of those long rows last.
     """
     lib = load()
     desc = mask_desc(params)
@@ -126,11 +131,20 @@ def build_block_mask(params: dict, device="cuda", row_ptr=None, col_idx=None):
         row_ptr = torch.empty(nb + 1, dtype=torch.int32, device=device)
     if col_idx is None:
         col_idx = torch.empty(nb * nb, dtype=torch.int32, device=device)
-    assert row_ptr.dtype == torch.int32 and row_ptr.numel() >= nb + 1 and row_ptr.is_cuda
-    assert col_idx.dtype == torch.int32 and col_idx.is_cuda
+    if row_order is None and with_order:
+        row_order = torch.empty(nb + 1, dtype=torch.int32, device=device)
+    if row_ptr.dtype != torch.int32 or row_ptr.numel() < nb + 1 or not row_ptr.is_cuda:
+        raise BsaError("row_ptr must be an int32 device tensor of nb + 1 entries")
+    if col_idx.dtype != torch.int32 or not col_idx.is_cuda:
+        raise BsaError("col_idx must be an int32 device tensor")
+    if row_order is not None and (row_order.dtype != torch.int32 or row_order.numel() < nb + 1
+                                  or not row_order.is_cuda):
+        raise BsaError("row_order must be an int32 device tensor of nb + 1 entries")
     _check(lib.bsa_build_block_mask(ctypes.byref(desc), _ptr(row_ptr), _ptr(col_idx),
-                                    col_idx.numel(), _stream(row_ptr.device)),
+                                    col_idx.numel(), _ptr(row_order), _stream(row_ptr.device)),
            "bsa_build_block_mask")
+    if row_order is not None:
+        return row_ptr, col_idx, row_order
     return row_ptr, col_idx
 
 
@@ -152,7 +166,7 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out=None,
-                          return_lse: bool = True, lse=None):
+                          return_lse: bool = True, lse=None, row_order=None):
     """O (and LSE, fp32 [B, H, N]) of block-sparse softmax attention on the device."""
     lib = load()
     for t in (q, k, v):
@@ -172,11 +186,16 @@ def block_sparse_attn_fwd(q, k, v, row_ptr, col_idx, block: int, scale=None, out
     if lse is not None and (lse.dtype != torch.float32 or not lse.is_contiguous()
                             or tuple(lse.shape) != tuple(q.shape[:3])):
         raise BsaError("lse must be a contiguous float32 [B, H, N] tensor")
+    if row_order is not None:
+        nb = -(-q.shape[2] // int(block)) if int(block) > 0 else 0
+        if row_order.dtype != torch.int32 or not row_order.is_cuda or row_order.numel() < nb + 1:
+            raise BsaError("row_order must be an int32 device tensor of nb + 1 entries")
     if scale is None:
         scale = 1.0 / math.sqrt(q.shape[-1])
     _check(lib.bsa_block_sparse_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
                                          _dtype_code(q), ctypes.byref(shape), _ptr(row_ptr),
-                                         _ptr(col_idx), int(block), float(scale), _stream(q.device)),
+                                         _ptr(col_idx), _ptr(row_order), int(block), float(scale),
+                                         _stream(q.device)),
            "bsa_block_sparse_attn_fwd")
     return out, lse
 

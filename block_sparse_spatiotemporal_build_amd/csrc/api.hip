@@ -30,10 +30,10 @@ bool launch_ok(const char* what) {
 }
 
 bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
-                                   hipStream_t stream);
+                                   int32_t* row_order, hipStream_t stream);
 bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
-                            int block, float scale, hipStream_t stream);
+                            const int32_t* row_order, int block, float scale, hipStream_t stream);
 bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o, float* lse,
                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                            int block, float scale, hipStream_t stream);
@@ -118,7 +118,7 @@ int32_t bsa_mask_num_blocks(const bsa_mask_desc* desc) {
 }
 
 bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
-                                int64_t col_capacity, void* stream) {
+                                int64_t col_capacity, int32_t* row_order, void* stream) {
   const char* fn = "bsa_build_block_mask";
   bsa_status st = check_desc(desc, fn);
   if (st != BSA_OK) return st;
@@ -128,12 +128,13 @@ bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int
     return fail(BSA_ERR_CAPACITY, "%s: col_capacity %lld < nb*nb = %lld", fn, (long long)col_capacity,
                 (long long)(nb * nb));
   g_err[0] = 0;
-  return launch_build_block_mask(*desc, row_ptr, col_idx, (hipStream_t)stream);
+  return launch_build_block_mask(*desc, row_ptr, col_idx, row_order, (hipStream_t)stream);
 }
 
 bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                      bsa_dtype dtype, const bsa_shape* shape, const int32_t* row_ptr,
-                                     const int32_t* col_idx, int32_t block, float scale, void* stream) {
+                                     const int32_t* col_idx, const int32_t* row_order, int32_t block,
+                                     float scale, void* stream) {
   const char* fn = "bsa_block_sparse_attn_fwd";
   if (dtype != BSA_DT_BF16 && dtype != BSA_DT_F32) return fail(BSA_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
   const int eb = dtype == BSA_DT_BF16 ? 2 : 4;
@@ -160,7 +161,8 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
     return fail(BSA_ERR_ARG, "%s: B and H must be <= 65535", fn);
   g_err[0] = 0;
   if (dtype == BSA_DT_BF16)
-    return launch_attn_bf16(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
+    return launch_attn_bf16(q, k, v, o, lse, *shape, row_ptr, col_idx, row_order, block, scale,
+                            (hipStream_t)stream);
   return launch_attn_f32(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
 }
 

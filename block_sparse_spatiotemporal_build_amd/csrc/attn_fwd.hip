@@ -7,7 +7,9 @@
 // frames; SVG-EAR page, technical summary section 1: sparse attention computes
 // the kept blocks and skips the rest).  Skipped key blocks are never read.
 //
-// bf16 path (attn_bf16_kernel).  One workgroup per (query block, head, batch);
+// bf16 path (attn_bf16_kernel; attn_bf16_d128_kernel for head_dim 128 with
+// 128-token blocks, the same math with direct global->LDS staging, see below).
+// One workgroup per (query block, head, batch);
 // BM = block query rows, 32 rows per wave.  The loop walks the row's kept key
 // blocks in 64-key sub-tiles:
 //   * K (64 x D) and V (64 x D) are fetched with 16-byte coalesced loads into
@@ -60,10 +62,57 @@ struct AttnArgs {
   float* lse;
   const int32_t* row_ptr;
   const int32_t* col_idx;
+  const int32_t* row_order;  // nullable: schedule of query-block rows, int32[nb + 1]
   int64_t sb, sh, sn;
   int B, H, N, block, nb;
   float scale_log2;  // scale * log2(e)
 };
+
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+
+// Index, in a list of R items, of the item that workgroup S + j runs, chosen so
+// that the workgroups the hardware deals round-robin to one XCD (those with the
+// same pid mod 8) take one contiguous range of the list, in order.
+__device__ __forceinline__ int xcd_contiguous(int j, int S, int R) {
+  const int x = (S + j) & 7, off = S & 7;
+  int base = 0;
+  for (int y = 0; y < x; ++y) {
+    const int j0 = (y - off) & 7;
+    base += j0 < R ? (R - 1 - j0) / 8 + 1 : 0;
+  }
+  return base + (j - ((x - off) & 7)) / 8;
+}
+
+// Work item (query block, head, batch) of workgroup `pid`.
+//  * Rows not singled out below: each XCD gets a contiguous range of the
+//    (batch, head, query block) list, so the workgroups sharing an L2 walk
+//    neighbouring query blocks of one head and reuse their key blocks.
+//  * With a row order whose first nh = row_order[nb] rows are long ones (LVSA
+//    anchor rows are about twice the mean length): those rows, for every head,
+//    take the first nh * H * B workgroups, so they start in the first wave and
+//    do not stretch the tail of the launch; the other rows follow as above, in
+//    the order row_order lists them.
+struct WorkItem {
+  int qblk, h, b;
+};
+__device__ __forceinline__ WorkItem map_work(const AttnArgs& a) {
+  const int pid = blockIdx.x, total = gridDim.x, hb = a.H * a.B;
+  if (a.row_order != nullptr) {
+    const cint_ptr ord = (cint_ptr)a.row_order;
+    const int nh = ord[a.nb];
+    const int S = nh * hb;
+    if (pid < S) {
+      const int r = pid % hb;
+      return WorkItem{ord[pid / hb], r % a.H, r / a.H};
+    }
+    const int rest = a.nb - nh;
+    const int item = xcd_contiguous(pid - S, S, total - S);
+    const int r = item / rest;
+    return WorkItem{ord[nh + item % rest], r % a.H, r / a.H};
+  }
+  const int item = xcd_contiguous(pid, 0, total);
+  return WorkItem{item % a.nb, (item / a.nb) % a.H, item / (a.nb * a.H)};
+}
 
 template <int D, int BM>
 __global__ void __launch_bounds__(BM * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -83,15 +132,8 @@ attn_bf16_kernel(AttnArgs a) {
   const int hi = lane >> 5;
   const int N = a.N;
 
-  // Work item.  The hardware deals workgroups round-robin to the 8 XCDs; give
-  // each XCD a contiguous range of (batch, head, query block) so that the
-  // workgroups sharing one L2 walk neighbouring query blocks of one head.
-  int wid = blockIdx.x;
-  const int total = gridDim.x;
-  if ((total & 7) == 0) wid = (wid & 7) * (total >> 3) + (wid >> 3);
-  const int qblk = wid % a.nb;
-  const int h = (wid / a.nb) % a.H;
-  const int b = wid / (a.nb * a.H);
+  const WorkItem wi = map_work(a);
+  const int qblk = wi.qblk, h = wi.h, b = wi.b;
 
   const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
   const uint16_t* __restrict__ Qh = a.q + head_off;
@@ -106,16 +148,21 @@ attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < C::KT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + t * 16));
   }
+  retire_loads();
 
-  const int rbeg = a.row_ptr[qblk], rend = a.row_ptr[qblk + 1];
-  const int spb = a.block / kBN;  // sub-tiles per key block
+  // The CSR is read-only for the whole kernel: read it through the constant
+  // address space so that the uniform index loads are scalar (s_load).
+  const cint_ptr rowp = (cint_ptr)a.row_ptr;
+  const cint_ptr cols = (cint_ptr)a.col_idx;
+  const int rbeg = rowp[qblk], rend = rowp[qblk + 1];
+  constexpr int spb = BM / kBN;  // sub-tiles per key block (block == BM)
   int nsub = (rend - rbeg) * spb;
-  if (nsub > 0 && a.col_idx[rend - 1] == a.nb - 1) {
+  if (nsub > 0 && cols[rend - 1] == a.nb - 1) {
     // drop trailing sub-tiles of the last key block that hold no real key
-    const int last_real = N - (a.nb - 1) * a.block;
+    const int last_real = N - (a.nb - 1) * BM;
     nsub -= spb - (last_real + kBN - 1) / kBN;
   }
-  auto sub_key0 = [&](int u) -> int { return a.col_idx[rbeg + u / spb] * a.block + (u % spb) * kBN; };
+  auto sub_key0 = [&](int u) -> int { return cols[rbeg + u / spb] * BM + (u % spb) * kBN; };
 
   // ---- global -> registers (one sub-tile ahead) -> LDS.  Rows past N are
   // clamped to row N - 1: their logits are masked to -inf below, so they carry
@@ -154,16 +201,20 @@ attn_bf16_kernel(AttnArgs a) {
   const int v_row = 4 * hi + (j16 >> 2);
   const int v_col = 16 * (g16 & 1) + 4 * (j16 & 3);
 
+  // key offsets run two sub-tiles ahead of their use (scalar loads in flight)
+  int key_cur = nsub > 0 ? sub_key0(0) : 0;
+  int key_nxt = nsub > 1 ? sub_key0(1) : 0;
   if (nsub > 0) {
-    fetch(sub_key0(0));
+    fetch(key_cur);
     stage(0);
   }
   __syncthreads();
 
   for (int u = 0; u < nsub; ++u) {
     const int buf = u & 1;
-    const int key0 = sub_key0(u);
-    if (u + 1 < nsub) fetch(sub_key0(u + 1));
+    const int key0 = key_cur;
+    const int key_nn = u + 2 < nsub ? sub_key0(u + 2) : 0;
+    if (u + 1 < nsub) fetch(key_nxt);
 
     // S^T tile: 64 keys x 32 queries per wave as two 32x32 accumulators.
     // Accumulator layout: s[kt][r] = S^T[key kt*32 + 8*(r/4) + 4*hi + r%4][query l32].
@@ -245,6 +296,8 @@ attn_bf16_kernel(AttnArgs a) {
     }
 
     if (u + 1 < nsub) stage(buf ^ 1);
+    key_cur = key_nxt;
+    key_nxt = key_nn;
     __syncthreads();
   }
 
@@ -255,6 +308,230 @@ attn_bf16_kernel(AttnArgs a) {
     uint16_t* dst = a.o + head_off + (int64_t)qrow * a.sn;
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                   pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+        *(u32x2*)(dst + d0) = w;
+      }
+    if (a.lse != nullptr && hi == 0) {
+      const float v = l_tot > 0.f ? (m_run * c2 + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+      a.lse[((int64_t)b * a.H + h) * N + qrow] = v;
+    }
+  }
+}
+
+
+// ---------------------------------------------------------------------------
+// bf16 MFMA kernel, head_dim 128 and 128-token blocks: direct global->LDS loads
+// ---------------------------------------------------------------------------
+//
+// Same math and register layouts as attn_bf16_kernel, with the K/V staging done
+// by buffer_load_dwordx4 ... lds: each lane's 16 bytes land at (LDS base + 16 *
+// lane), so the tile layout is chosen by which global chunk each lane loads.
+// Rows are 256 bytes with an XOR swizzle of their 16 chunks instead of padding:
+//   K: physical chunk = logical ^ (row & 15): the 16 rows read by 16 lanes for
+//      one MFMA A operand hit 16 different chunks (all 64 banks);
+//   V: physical chunk = logical ^ (4 (row & 3) + ((row >> 2) & 3)): the 4 rows x
+//      4 chunks that 32 lanes touch in one ds_read_b64_tr_b16 are all distinct.
+// Two 32 KB stages; the loads for sub-tile u+1 are issued right after the
+// barrier that opens sub-tile u and overlap its compute; their completion is
+// waited for with an explicit vmcnt before the next barrier.  The stages are
+// separate LDS objects and the loop is unrolled by two, so that every LDS read
+// provably misses the stage being filled (otherwise the compiler makes the
+// first read wait for the copy in flight, which serialises copy and compute).
+
+typedef __attribute__((address_space(3))) void lds_void;
+// Buffer descriptor word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bf16_d128_kernel(AttnArgs a) {
+  constexpr int D = 128, BM = 128, KT = 8, DT = 4, TILE = kBN * D;
+  // two stages as four distinct LDS objects: the compiler can then tell that
+  // the copy into one stage never overlaps the reads of the other and does not
+  // make those reads wait for the copy
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+  const WorkItem wi = map_work(a);
+  const int qblk = wi.qblk, h = wi.h, b = wi.b;
+  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const uint16_t* __restrict__ Qh = a.q + head_off;
+  const uint16_t* __restrict__ Kh = a.k + head_off;
+  const uint16_t* __restrict__ Vh = a.v + head_off;
+
+  const int qrow = qblk * BM + wave * 32 + l32;
+  bf16x8 qf[KT];
+  {
+    const uint16_t* src = Qh + (int64_t)min(qrow, N - 1) * a.sn + hi * 8;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + t * 16));
+  }
+  retire_loads();
+
+  const cint_ptr rowp = (cint_ptr)a.row_ptr;
+  const cint_ptr cols = (cint_ptr)a.col_idx;
+  const int rbeg = rowp[qblk], rend = rowp[qblk + 1];
+  int nsub = (rend - rbeg) * 2;
+  if (nsub > 0 && cols[rend - 1] == a.nb - 1) {
+    const int last_real = N - (a.nb - 1) * BM;
+    nsub -= 2 - (last_real + kBN - 1) / kBN;
+  }
+  auto key0_of = [&](int u) -> int { return cols[rbeg + (u >> 1)] * BM + (u & 1) * kBN; };
+
+  // Copy roles: wave w, instruction j covers tile rows 16w + 4j + lane/16 at
+  // physical chunk lane%16 (i.e. logical chunk (lane%16) ^ swizzle(row)).  The
+  // copies are buffer loads straight to LDS: one descriptor per tensor and head,
+  // a 32-bit per-lane offset (row * row_bytes + 16 * chunk) and the sub-tile
+  // start in the scalar offset.  The host keeps (N + 64) * row_bytes < 2^31.
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, 0x7fffffff, kBufferWord3);
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int row = 16 * wv + 4 * j + (lane >> 4);
+    koff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16);
+    voff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+  }
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int key0) {
+    if (key0 + kBN <= N) {
+      const uint32_t so = (uint32_t)key0 * row_bytes;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, koff[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, voff[j], so, 0, 0);
+      }
+    } else {  // tail sub-tile: rows past N are clamped to row N - 1 (masked below)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * wv + 4 * j + (lane >> 4);
+        const uint32_t ro = (uint32_t)min(key0 + row, N - 1) * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+  const float c2 = a.scale_log2;
+  const int g16 = lane >> 4, j16 = lane & 15;
+
+  // One 64-key sub-tile u held in (Kb, Vb); the copy of sub-tile u + 1 goes to
+  // (Kn, Vn) as soon as every wave has passed the barrier (they have all
+  // finished reading that stage in step u - 1).
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
+    const int key0 = key0_of(u);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed, other stage drained
+    __builtin_amdgcn_s_barrier();
+    if (u + 1 < nsub) dma(Kn, Vn, key0_of(u + 1));
+
+    // S^T = K Q^T: read the 16 K fragments, then the MFMAs (reads run four ahead)
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 kfr[2][KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const int row = kt * 32 + l32;
+        kfr[kt][t] = *(const bf16x8*)&Kb[row * D + (((2 * t + hi) ^ swz_k(row)) << 3)];
+      }
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[kt][t], qf[t], s[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    if (key0 + kBN > N) {  // key row of s[kt][r]: key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4
+      const int lim = N - key0 - 4 * hi;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (kt * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -__builtin_inff();
+    }
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    const float m_new = fmaxf(m_run, pair_max(mx));
+    if (__any(m_new > m_run)) {
+      const float alpha = fast_exp2((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c2;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
+        s[kt][r] = p;
+        psum += p;
+      }
+    l_run += psum;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks >> 1, r0 = (ks & 1) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kt][r0 + 2 * e], s[kt][r0 + 2 * e + 1]);
+      pf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+
+    // O^T += V^T P^T with the transpose reads of the swizzled V stage
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
+        const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+        const int half = (j16 & 1) * 4;
+        const u32x2 lo = lds_tr16(&Vb[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
+        const u32x2 h2 = lds_tr16(&Vb[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+        const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
+      }
+  };
+
+  if (nsub > 0) dma(K0, V0, key0_of(0));
+  int u = 0;
+  for (; u + 2 <= nsub; u += 2) {
+    step(K0, V0, K1, V1, u);
+    step(K1, V1, K0, V0, u + 1);
+  }
+  if (u < nsub) step(K0, V0, K1, V1, u);
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    uint16_t* dst = a.o + head_off + (int64_t)qrow * a.sn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = dt * 32 + 8 * g + 4 * hi;
@@ -361,15 +638,19 @@ __global__ void __launch_bounds__(128) attn_f32_kernel(AttnF32Args a) {
 
 bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
                             const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
-                            int block, float scale, hipStream_t stream) {
+                            const int32_t* row_order, int block, float scale, hipStream_t stream) {
   AttnArgs a;
   a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v; a.o = (uint16_t*)o;
-  a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx;
+  a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx; a.row_order = row_order;
   a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
   a.B = s.B; a.H = s.H; a.N = s.N; a.block = block; a.nb = (s.N + block - 1) / block;
   a.scale_log2 = scale * kLog2e;
   dim3 grid((unsigned)((int64_t)a.nb * s.H * s.B));
-  if (s.D == 128 && block == 128)
+  // the buffer-load kernel addresses a head with 32-bit offsets
+  const bool offsets_fit = ((int64_t)s.N + 64) * a.sn * 2 < ((int64_t)1 << 31);
+  if (s.D == 128 && block == 128 && offsets_fit)
+    hipLaunchKernelGGL(attn_bf16_d128_kernel, grid, dim3(256), 0, stream, a);
+  else if (s.D == 128 && block == 128)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 128>), grid, dim3(256), 0, stream, a);
   else if (s.D == 128 && block == 64)
     hipLaunchKernelGGL((attn_bf16_kernel<128, 64>), grid, dim3(128), 0, stream, a);

@@ -57,6 +57,13 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Wait for every outstanding vector-memory load of this wave (s_waitcnt vmcnt(0)).
+// Used after loading registers that a loop then reuses: the loop's own prefetch
+// loads share the in-order vmcnt counter, so without a retire point before the
+// loop the compiler's waits for those registers would also wait for the
+// prefetch issued in each iteration.
+__device__ __forceinline__ void retire_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Launch-error check used by every entry point after enqueueing kernels.
 bool launch_ok(const char* what);
 

@@ -7,11 +7,13 @@
 // exponentially with temporal distance).  A block pair is kept when any real
 // token pair in it is kept.
 //
-// Three launches, all integer and deterministic:
+// Launches, all integer and deterministic:
 //   count: one workgroup per block row, row_ptr[i + 1] = number of kept columns
 //   scan : one workgroup, inclusive prefix sum of row_ptr[1..nb]
 //   fill : one workgroup per block row, kept columns written in ascending order
-//          using wave ballots for the in-row prefix.
+//          using wave ballots for the in-row prefix
+//   order: (optional) the row schedule for the attention launch (long rows
+//          first, see mask_order_kernel).
 
 #include "common.h"
 
@@ -131,8 +133,46 @@ __global__ void __launch_bounds__(kMaskThreads) mask_fill_kernel(MaskArgs m, con
   }
 }
 
+// Row schedule for the attention launch, int32[nb + 1].  Rows with at least 1.5x
+// the mean kept-block count are "long": they come first, by descending count
+// (ties by ascending index), and their number nh goes to row_order[nb]; the
+// other rows follow in ascending index order.  Every row of length >= a long
+// row's length is long too, so a long row's rank is #rows longer + #rows of
+// equal length before it; a short row's rank is nh + #short rows before it.
+// One thread per row, row lengths staged in LDS tiles.
+__device__ __forceinline__ bool long_row(int len, int nb, int total) {
+  return 2 * (int64_t)len * nb >= 3 * (int64_t)total && len > 0;
+}
+
+__global__ void __launch_bounds__(kMaskThreads) mask_order_kernel(const int32_t* row_ptr, int nb,
+                                                                  int32_t* row_order) {
+  __shared__ int len_tile[kMaskThreads];
+  const int i = blockIdx.x * kMaskThreads + threadIdx.x;
+  const int total = row_ptr[nb];
+  const int li = i < nb ? row_ptr[i + 1] - row_ptr[i] : 0;
+  const bool li_long = long_row(li, nb, total);
+  int longer = 0, equal_before = 0, n_long = 0, short_before = 0;
+  for (int j0 = 0; j0 < nb; j0 += kMaskThreads) {
+    const int j = j0 + threadIdx.x;
+    len_tile[threadIdx.x] = j < nb ? row_ptr[j + 1] - row_ptr[j] : -1;
+    __syncthreads();
+    const int cnt = min(kMaskThreads, nb - j0);
+    for (int t = 0; t < cnt; ++t) {
+      const int lj = len_tile[t];
+      const bool jl = long_row(lj, nb, total);
+      longer += lj > li ? 1 : 0;
+      equal_before += (lj == li && j0 + t < i) ? 1 : 0;
+      n_long += jl ? 1 : 0;
+      short_before += (!jl && j0 + t < i) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  if (i < nb) row_order[li_long ? longer + equal_before : n_long + short_before] = i;
+  if (i == 0) row_order[nb] = n_long;
+}
+
 bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
-                                   hipStream_t stream) {
+                                   int32_t* row_order, hipStream_t stream) {
   MaskArgs m;
   m.kind = d.kind; m.F = d.frames; m.P = d.frame_tokens; m.block = d.block;
   m.window = d.window; m.period = d.anchor_period; m.step = d.anchor_step;
@@ -142,6 +182,9 @@ bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int
   hipLaunchKernelGGL(mask_count_kernel, dim3(m.nb), dim3(kMaskThreads), 0, stream, m, row_ptr);
   hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_ptr, m.nb);
   hipLaunchKernelGGL(mask_fill_kernel, dim3(m.nb), dim3(kMaskThreads), 0, stream, m, row_ptr, col_idx);
+  if (row_order != nullptr)
+    hipLaunchKernelGGL(mask_order_kernel, dim3((m.nb + kMaskThreads - 1) / kMaskThreads), dim3(kMaskThreads), 0,
+                       stream, row_ptr, m.nb, row_order);
   return launch_ok("build_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 

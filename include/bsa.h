@@ -91,9 +91,15 @@ int32_t bsa_mask_num_blocks(const bsa_mask_desc* desc);
  * col_idx: int32[col_capacity] device, written with the kept key-block indices
  *          of each row in ascending order.  col_capacity must be >= nb * nb
  *          (the largest possible count), else BSA_ERR_CAPACITY.
+ * row_order: nullable int32[nb + 1] device output, a launch schedule for
+ *          bsa_block_sparse_attn_fwd: entries 0..nb-1 are a permutation of the
+ *          rows, entry nb is the number nh of "long" rows (kept-block count at
+ *          least 1.5 times the mean).  The nh long rows come first, by
+ *          descending count (ties by ascending index), then the other rows in
+ *          ascending index order.
  * The mask is shared by every batch and head. */
 bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int32_t* col_idx,
-                                int64_t col_capacity, void* stream);
+                                int64_t col_capacity, int32_t* row_order, void* stream);
 
 /* Block-sparse softmax attention forward.
  * Operation (LVSA review page section 1 Key Terms and section 3; SVG-EAR page,
@@ -110,11 +116,20 @@ bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int
  * lse: nullable fp32 [B, H, N] contiguous device array.
  * row_ptr, col_idx: the CSR from bsa_build_block_mask for the same N and block
  *   (nb = ceil(N / block) rows, ascending columns < nb).
+ * row_order: nullable int32[nb + 1]; the schedule written by
+ *   bsa_build_block_mask (any permutation of the nb rows followed by a count
+ *   nh in [0, nb] is valid).  The first nh listed rows run first, for every
+ *   batch and head, which keeps long rows out of the tail of the launch; the
+ *   rest run in list order with each XCD taking a contiguous range of (batch,
+ *   head, row).  Without it every row is in the second group, in index order.
+ *   Results are bitwise identical with or without it.  Ignored by the fp32
+ *   path.  Like col_idx, its device contents are trusted.
  * scale: the softmax scale (1/sqrt(D) for standard attention). */
 bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                      float* lse, bsa_dtype dtype, const bsa_shape* shape,
                                      const int32_t* row_ptr, const int32_t* col_idx,
-                                     int32_t block, float scale, void* stream);
+                                     const int32_t* row_order, int32_t block, float scale,
+                                     void* stream);
 
 /* Workspace bytes required by bsa_linear_attn_fwd for `shape` (0 if the shape
  * is invalid).  The workspace holds per-chunk partial states (fp32), the

@@ -57,16 +57,16 @@ def test_num_blocks(lib):
                                  dict(frames=100000, frame_tokens=100000)])
 def test_mask_rejects_bad_descriptions(lib, bad):
     st = lib.bsa_build_block_mask(ctypes.byref(_desc(**bad)), ctypes.c_void_p(16), ctypes.c_void_p(16),
-                                  1 << 40, None)
+                                  1 << 40, None, None)
     assert st == 1, lib.bsa_last_error()
     assert lib.bsa_last_error().decode()
 
 
 def test_mask_rejects_small_capacity_and_null(lib):
     d = _desc()
-    assert lib.bsa_build_block_mask(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), 15, None) == 3
+    assert lib.bsa_build_block_mask(ctypes.byref(d), ctypes.c_void_p(16), ctypes.c_void_p(16), 15, None, None) == 3
     assert b"col_capacity" in lib.bsa_last_error()
-    assert lib.bsa_build_block_mask(ctypes.byref(d), None, ctypes.c_void_p(16), 16, None) == 1
+    assert lib.bsa_build_block_mask(ctypes.byref(d), None, ctypes.c_void_p(16), 16, None, None) == 1
 
 
 def _shape(B=1, H=2, N=256, D=64, sn=None):
@@ -78,7 +78,7 @@ def _attn(lib, dtype=0, shape=None, block=64, scale=0.125, ptr=4096, rp=4096):
     shape = shape or _shape()
     p = ctypes.c_void_p(ptr)
     return lib.bsa_block_sparse_attn_fwd(p, p, p, p, None, dtype, ctypes.byref(shape),
-                                         ctypes.c_void_p(rp), ctypes.c_void_p(rp), block,
+                                         ctypes.c_void_p(rp), ctypes.c_void_p(rp), None, block,
                                          ctypes.c_float(scale), None)
 
 

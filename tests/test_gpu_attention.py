@@ -14,10 +14,12 @@ from synth import gen, get_workload
 pytestmark = pytest.mark.gpu
 
 
-def _run(bsa, d, wl, params, scale=None):
+def _run(bsa, d, wl, params, scale=None, order=True):
+    """Mask + attention as the benchmark launches them (with the mask builder's row schedule)."""
     q, k, v = (to_device(d[n], wl.dtype) for n in ("q", "k", "v"))
-    rp, ci = bsa.build_block_mask(params)
-    out, lse = bsa.block_sparse_attn_fwd(q, k, v, rp, ci, params["block"], scale)
+    rp, ci, ro = bsa.build_block_mask(params, with_order=True)
+    out, lse = bsa.block_sparse_attn_fwd(q, k, v, rp, ci, params["block"], scale,
+                                         row_order=ro if order else None)
     torch.cuda.synchronize()
     return out, lse
 
@@ -75,6 +77,36 @@ def test_bf16_reduced_full_compare(gpu_lib, D, block, kind):
     ref, rlse = _oracle(d, wl, p)
     assert_parity(to_f64(out), ref, "bf16", f"bf16 D={D} block={block} kind={kind}")
     assert np.abs(to_f64(lse) - rlse).max() < 1e-3
+
+
+@pytest.mark.parametrize("D,block", [(128, 128), (64, 64), (64, 128)])
+def test_row_order_only_schedules(gpu_lib, D, block):
+    """The row schedule changes which workgroup runs a row, never the result: the
+    builder's schedule, none, all rows "long", and a random permutation with a
+    random long count all give the same bits (outputs start as NaN, so a row
+    skipped or written twice by a wrong mapping would show)."""
+    wl = gen.scaled(get_workload("lvsa_32k"), H=3, D=D, frames=9, frame_h=10, frame_w=20, seed=23)
+    d = gen.make_qkv(wl)
+    p = dict(kind=1, frames=9, frame_tokens=200, block=block, window=1, anchor_period=4,
+             anchor_step=2, anchor_rows=1, radial_w=0)
+    q, k, v = (to_device(d[n], wl.dtype) for n in ("q", "k", "v"))
+    rp, ci, ro = gpu_lib.build_block_mask(p, with_order=True)
+    nb = rp.numel() - 1
+    assert 0 < int(ro[-1]) < nb
+    lens = np.diff(rp.cpu().numpy())
+    full = np.concatenate([np.argsort(-lens, kind="stable"), [nb]]).astype(np.int32)
+    r = np.random.default_rng(5)
+    rand = np.concatenate([r.permutation(nb), [r.integers(0, nb + 1)]]).astype(np.int32)
+    results = []
+    for sched in (ro, None, torch.from_numpy(full).cuda(), torch.from_numpy(rand).cuda()):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), device=q.device)
+        gpu_lib.block_sparse_attn_fwd(q, k, v, rp, ci, block, out=out, lse=lse, row_order=sched)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+        results.append((out.view(torch.int16).clone(), lse.clone()))
+    for o2, l2 in results[1:]:
+        assert torch.equal(results[0][0], o2) and torch.equal(results[0][1], l2)
 
 
 def test_bf16_tiny_sequence_shorter_than_a_block(gpu_lib):

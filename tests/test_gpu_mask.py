@@ -21,6 +21,18 @@ def _check(bsa, params):
     rp, ci = _gpu_csr(bsa, params)
     assert np.array_equal(rp, want_rp), params
     assert np.array_equal(ci, want_ci), params
+    # with the optional row order: same CSR, plus rows by descending length (stable)
+    rp2, ci2, ro = bsa.build_block_mask(params, with_order=True)
+    rp2 = rp2.cpu().numpy()
+    assert np.array_equal(rp2, want_rp), params
+    assert np.array_equal(ci2[: int(rp2[-1])].cpu().numpy(), want_ci), params
+    lens = np.diff(want_rp).astype(np.int64)
+    nb = len(lens)
+    is_long = (2 * lens * nb >= 3 * int(want_rp[-1])) & (lens > 0)
+    long_rows = np.nonzero(is_long)[0]
+    long_rows = long_rows[np.argsort(-lens[long_rows], kind="stable")]
+    want_order = np.concatenate([long_rows, np.nonzero(~is_long)[0], [len(long_rows)]])
+    assert np.array_equal(ro.cpu().numpy(), want_order), params
 
 
 def test_tiny_lvsa(gpu_lib):
@@ -63,6 +75,17 @@ def test_random_small_specs(gpu_lib):
 def test_single_block(gpu_lib):
     _check(gpu_lib, dict(kind=2, frames=1, frame_tokens=1, block=1, window=0, anchor_period=0,
                          anchor_step=0, anchor_rows=0, radial_w=0))
+
+
+def test_schedule_of_lvsa_32k(gpu_lib):
+    """The anchor-frame rows (all 256 blocks, about twice the mean) are the long rows."""
+    p = get_workload("lvsa_32k").mask_params(0)
+    rp, ci, ro = gpu_lib.build_block_mask(p, with_order=True)
+    ro = ro.cpu().numpy()
+    lens = np.diff(rp.cpu().numpy())
+    nh = int(ro[-1])
+    assert nh == int((lens == 256).sum()) > 0
+    assert (lens[ro[:nh]] == 256).all() and (lens[ro[nh:-1]] < 256).all()
 
 
 def test_repeatable(gpu_lib):

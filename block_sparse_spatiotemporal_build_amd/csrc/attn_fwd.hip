@@ -249,7 +249,7 @@ attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     const float m_new = fmaxf(m_run, pair_max(mx));
-    if (__any(m_new > m_run)) {
+    if (__any((m_new - m_run) * c2 > kLazyRescaleLog2)) {
       const float alpha = fast_exp2((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll
@@ -475,7 +475,7 @@ attn_bf16_d128_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
     const float m_new = fmaxf(m_run, pair_max(mx));
-    if (__any(m_new > m_run)) {
+    if (__any((m_new - m_run) * c2 > kLazyRescaleLog2)) {
       const float alpha = fast_exp2((m_run - m_new) * c2);
       l_run *= alpha;
 #pragma unroll

@@ -62,6 +62,13 @@ __device__ __forceinline__ float pair_sum(float x) {
 // loads share the in-order vmcnt counter, so without a retire point before the
 // loop the compiler's waits for those registers would also wait for the
 // prefetch issued in each iteration.
+// Online softmax with a lazily moved reference: the running maximum used as
+// the exponent reference is replaced only when a new score exceeds it by more
+// than this many powers of two, so weights stay below 2^8 and the O/l rescale
+// is skipped on most tiles.  O and l always share one reference, so the
+// normalised output and the LSE are unchanged up to rounding.
+constexpr float kLazyRescaleLog2 = 8.f;
+
 __device__ __forceinline__ void retire_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Launch-error check used by every entry point after enqueueing kernels.

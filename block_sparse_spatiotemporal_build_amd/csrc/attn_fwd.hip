@@ -342,11 +342,6 @@ attn_bf16_kernel(AttnArgs a) {
 // provably misses the stage being filled (otherwise the compiler makes the
 // first read wait for the copy in flight, which serialises copy and compute).
 
-typedef __attribute__((address_space(3))) void lds_void;
-// Buffer descriptor word 3 for raw (untyped, stride 0) buffer loads on gfx9-family parts.
-constexpr int kBufferWord3 = 0x00020000;
-__device__ __forceinline__ int swz_k(int row) { return row & 15; }
-__device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 attn_bf16_d128_kernel(AttnArgs a) {

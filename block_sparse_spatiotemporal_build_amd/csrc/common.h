@@ -62,6 +62,19 @@ __device__ __forceinline__ float pair_sum(float x) {
 // loads share the in-order vmcnt counter, so without a retire point before the
 // loop the compiler's waits for those registers would also wait for the
 // prefetch issued in each iteration.
+// Staging of 256-byte rows (head_dim 128, bf16) straight from global memory to
+// LDS with buffer_load ... lds: lane i of one instruction writes 16 bytes at
+// (LDS base + 16 i), so a tile's layout is chosen by which 16-byte chunk each
+// lane loads.  Rows keep their 16 chunks XOR-swizzled instead of padded:
+//   swz_k: chunk ^ (row & 15) -- the 16 rows that 16 lanes read for one MFMA A
+//          operand hit 16 different chunks (all 64 banks);
+//   swz_v: chunk ^ (4 (row & 3) + ((row >> 2) & 3)) -- the 4 rows x 4 chunks
+//          touched by one ds_read_b64_tr_b16 over 32 lanes are distinct.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int kBufferWord3 = 0x00020000;  // raw (untyped, stride 0) buffer loads, gfx9 family
+__device__ __forceinline__ int swz_k(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
+
 // Online softmax with a lazily moved reference: the running maximum used as
 // the exponent reference is replaced only when a new score exceeds it by more
 // than this many powers of two, so weights stay below 2^8 and the O/l rescale

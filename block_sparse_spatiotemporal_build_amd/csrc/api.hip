@@ -7,7 +7,7 @@
 #include <stdio.h>
 #include <string.h>
 
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 
@@ -28,42 +28,6 @@ bool launch_ok(const char* what) {
   }
   return true;
 }
-
-bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
-                                   int32_t* row_order, hipStream_t stream);
-bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
-                            const int32_t* row_order, int block, float scale, hipStream_t stream);
-bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o, float* lse,
-                           const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
-                           int block, float scale, hipStream_t stream);
-
-struct LinPlan {
-  int splits, chunk;
-  size_t off_part_s, off_part_z, off_st, off_z, total;
-};
-LinPlan linear_plan(const bsa_shape& s);
-bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
-                              float* S, float* z, void* ws, hipStream_t stream);
-
-bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,
-                            int Cq, const int32_t* k_off, int Ck, float* qc, float* kc, float* vc,
-                            hipStream_t stream);
-struct ProbePlan {
-  int splits, cps;
-  size_t off_e, off_m, off_ms, off_zs, total;
-};
-ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck);
-bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s, const int32_t* q_off, int Cq,
-                               const int32_t* k_off, int Ck, const float* qc, const float* kc, const float* vc,
-                               float scale, float* score, void* ws, hipStream_t stream);
-bsa_status launch_route_select(const float* score, const bsa_shape& s, const int32_t* q_off, int Cq,
-                               const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
-                               uint8_t* flags, hipStream_t stream);
-bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
-                            const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
-                            const int32_t* rcol, const float* kc, const float* vc, float scale,
-                            hipStream_t stream);
 
 static bsa_status fail(bsa_status st, const char* fmt, ...) {
   va_list ap;

@@ -29,7 +29,7 @@
 // fp32 path (attn_f32_kernel).  Straightforward: one thread per query row,
 // 32-key tiles of K and V staged in LDS, fp32 FMA dot products, expf.
 
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 

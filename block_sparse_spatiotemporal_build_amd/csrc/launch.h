@@ -1,0 +1,52 @@
+// Host-side launchers and workspace plans shared between the C-ABI layer
+// (api.hip) and the kernel files.  Every plan struct is defined here once: a
+// second copy with a stale layout in another translation unit would make the
+// C-ABI layer read the wrong fields (and overrun the returned struct).
+#pragma once
+
+#include "common.h"
+
+namespace bsa {
+
+// ---- block mask and block-sparse attention ---------------------------------
+bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
+                                   int32_t* row_order, hipStream_t stream);
+bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                            const int32_t* row_order, int block, float scale, hipStream_t stream);
+bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o, float* lse,
+                           const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                           int block, float scale, hipStream_t stream);
+
+// ---- linear attention ------------------------------------------------------
+struct LinPlan {
+  int splits, chunk;  // state: token splits per head and tokens per split
+  bool d128;          // head_dim 128 kernels (buffer-load staging, 32-bit offsets within a head)
+  int tph, tpw, apply_wgs;  // apply (head_dim 128): tiles per head, tiles per workgroup, workgroups
+  size_t off_part_s, off_part_z, off_st, off_z, total;  // workspace layout (bytes)
+};
+LinPlan linear_plan(const bsa_shape& s);
+bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
+                              float* S, float* z, void* ws, hipStream_t stream);
+
+// ---- centroid compensation with error-aware routing ------------------------
+struct ProbePlan {
+  int splits, cps;  // key-cluster splits per head and clusters per split
+  size_t off_e, off_m, off_ms, off_zs, total;  // workspace layout (bytes)
+};
+ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck);
+bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,
+                            int Cq, const int32_t* k_off, int Ck, float* qc, float* kc, float* vc,
+                            hipStream_t stream);
+bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s, const int32_t* q_off, int Cq,
+                               const int32_t* k_off, int Ck, const float* qc, const float* kc, const float* vc,
+                               float scale, float* score, void* ws, hipStream_t stream);
+bsa_status launch_route_select(const float* score, const bsa_shape& s, const int32_t* q_off, int Cq,
+                               const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
+                               uint8_t* flags, hipStream_t stream);
+bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
+                            const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
+                            const int32_t* rcol, const float* kc, const float* vc, float scale,
+                            hipStream_t stream);
+
+}  // namespace bsa

@@ -22,7 +22,7 @@
 //            as the B operand straight from global memory (phi in fp32, then
 //            bf16), and the denominator phi(q).z in fp32 per lane.
 
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 
@@ -165,6 +165,141 @@ __global__ void __launch_bounds__(kLinThreads) lin_state_kernel(LinStateArgs a) 
   }
 }
 
+// head_dim 128 state kernel.  K and V tiles of 32 tokens go straight from
+// global memory to LDS with buffer loads into a ring of four stages (eight
+// distinct LDS objects, the loop unrolled by four so no LDS read ever waits for
+// a copy in flight): three tiles are in flight while one is computed, which is
+// what it takes to cover the memory latency at two workgroups per CU.  Rows
+// are swizzled for the transpose read.  Wave w owns S rows d1 in
+// [32w, 32w + 32) and all four 32-column blocks of d2: its phi(K)^T fragment
+// (A operand) is read once per 16 tokens, phi is applied in fp32 (rows past
+// the split's end set to 0), the values are summed into the lane's z partial
+// for d1 = 32w + lane % 32 and rounded to bf16; the V fragments (B operand)
+// come from the same transpose read.  Element e of a fragment read for token
+// group ks is token 16 ks + 8 (e / 4) + 4 (lane / 32) + e % 4 of the tile.
+constexpr int kLinTok2 = 32;  // tokens per tile of the head_dim-128 state kernel
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+lin_state_d128_kernel(LinStateArgs a) {
+  constexpr int D = 128, TILE = kLinTok2 * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.H, h = bh % a.H;
+  const int64_t head_off = (int64_t)b * a.sb + (int64_t)h * a.sh;
+  const int n0 = split * a.chunk, n1 = min(n0 + a.chunk, a.N);
+  const int ntile = (n1 - n0 + kLinTok2 - 1) / kLinTok2;
+
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane/16
+  uint32_t off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wv + 4 * j + (lane >> 4);
+    off[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+  }
+  // each wave issues 4 copy instructions per tile
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int t0) {
+    if (t0 + kLinTok2 <= a.N) {
+      const uint32_t so = (uint32_t)t0 * row_bytes;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16, off[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16, off[j], so, 0, 0);
+      }
+    } else {  // last tile of the sequence: rows past N are clamped to row N - 1 (masked below)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 8 * wv + 4 * j + (lane >> 4);
+        const uint32_t o = (uint32_t)min(t0 + row, a.N - 1) * row_bytes +
+                           (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 acc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
+  float zl = 0.f;
+  // transpose-read addressing (rows of token group ks, 16-byte chunk of d block dt)
+  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> u32x4 {
+    const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
+    const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    const int half = (j16 & 1) * 4;
+    const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
+    const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+  };
+
+  // tile t sits in stage t % 4; at its step the copies of tiles t + 1 and t + 2
+  // may still be in flight (4 instructions each per wave), and the copy of
+  // tile t + 3 is issued into the stage that tile t - 1 used
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int t) {
+    const int t0 = n0 + t * kLinTok2;
+    const int ahead = ntile - 1 - t;  // tiles after t already issued: min(ahead, 2)
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
+    else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (t + 3 < ntile) dma(Kn, Vn, t0 + 3 * kLinTok2);
+    const int lim = n1 - t0 - 4 * hi;  // element e is a real token iff 16 ks + 8 (e / 4) + e % 4 < lim
+#pragma unroll
+    for (int ks = 0; ks < kLinTok2 / 16; ++ks) {
+      const u32x4 kr = tr_frag(Kb, ks, wave);
+      u32x4 kp;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int e0 = 2 * w, e1 = 2 * w + 1;
+        float f0 = phi(bf16_lo(kr[w])), f1 = phi(bf16_hi(kr[w]));
+        if (16 * ks + 8 * (e0 >> 2) + (e0 & 3) >= lim) f0 = 0.f;
+        if (16 * ks + 8 * (e1 >> 2) + (e1 & 3) >= lim) f1 = 0.f;
+        zl += f0 + f1;
+        kp[w] = pack_bf16x2(f0, f1);
+      }
+      const bf16x8 af = __builtin_bit_cast(bf16x8, kp);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, tr_frag(Vb, ks, dt)),
+                                                          acc[dt], 0, 0, 0);
+    }
+  };
+
+  if (ntile > 0) dma(K0, V0, n0);
+  if (ntile > 1) dma(K1, V1, n0 + kLinTok2);
+  if (ntile > 2) dma(K2, V2, n0 + 2 * kLinTok2);
+  int t = 0;
+  for (; t + 4 <= ntile; t += 4) {
+    step(K0, V0, K3, V3, t);
+    step(K1, V1, K0, V0, t + 1);
+    step(K2, V2, K1, V1, t + 2);
+    step(K3, V3, K2, V2, t + 3);
+  }
+  if (t < ntile) step(K0, V0, K3, V3, t);
+  if (t + 1 < ntile) step(K1, V1, K0, V0, t + 1);
+  if (t + 2 < ntile) step(K2, V2, K1, V1, t + 2);
+
+  // partial S: acc[dt][r] = S[32 w + 8 (r / 4) + 4 hi + r % 4][32 dt + lane % 32]
+  float* ps = a.part_s + ((int64_t)bh * a.splits + split) * D * D;
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int d1 = 32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3);
+      ps[d1 * D + 32 * dt + l32] = acc[dt][r];
+    }
+  const float z = pair_sum(zl);
+  if (hi == 0) a.part_z[((int64_t)bh * a.splits + split) * D + 32 * wave + l32] = z;
+}
+
 struct LinReduceArgs {
   const float* part_s;
   const float* part_z;
@@ -175,24 +310,50 @@ struct LinReduceArgs {
   int splits;
 };
 
+// 256 threads = 32 float4 columns of S x 8 groups of splits; each thread sums
+// its group's splits in order, then the 8 group sums are added in group order
+// (a fixed order: deterministic).  One workgroup per 128 elements of S.
+constexpr int kRedGroups = 8, kRedCols = 256 / kRedGroups;
+
 template <int D>
 __global__ void __launch_bounds__(256) lin_reduce_kernel(LinReduceArgs a) {
-  const int bh = blockIdx.y;
-  const int idx = blockIdx.x * 256 + threadIdx.x;  // element of S (row-major d1, d2)
-  const float* ps = a.part_s + (int64_t)bh * a.splits * D * D;
-  if (idx < D * D) {
-    float s = 0.f;
-    for (int p = 0; p < a.splits; ++p) s += ps[(int64_t)p * D * D + idx];
-    const int d1 = idx / D, d2 = idx % D;
-    if (a.S) a.S[(int64_t)bh * D * D + idx] = s;
-    a.st_bf[(int64_t)bh * D * D + d2 * D + d1] = (uint16_t)f2bf(s);
+  __shared__ float4 part[kRedGroups][kRedCols];
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  const int c4 = tid % kRedCols, g = tid / kRedCols;
+  const int idx4 = blockIdx.x * kRedCols + c4;  // float4 index into S (row-major d1, d2)
+  const float4* ps = reinterpret_cast<const float4*>(a.part_s + (int64_t)bh * a.splits * D * D);
+  const int per = (a.splits + kRedGroups - 1) / kRedGroups;
+  const int p0 = g * per, p1 = min(p0 + per, a.splits);
+  float4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int p = p0; p < p1; ++p) {
+    const float4 x = ps[(int64_t)p * (D * D / 4) + idx4];
+    acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
   }
-  if (blockIdx.x == 0 && threadIdx.x < D) {
+  part[g][c4] = acc;
+  __syncthreads();
+  if (g == 0) {
+    float4 t = part[0][c4];
+#pragma unroll
+    for (int q = 1; q < kRedGroups; ++q) {
+      const float4 x = part[q][c4];
+      t.x += x.x; t.y += x.y; t.z += x.z; t.w += x.w;
+    }
+    const int e = idx4 * 4, d1 = e / D, d2 = e % D;
+    if (a.S) reinterpret_cast<float4*>(a.S + (int64_t)bh * D * D)[idx4] = t;
+    uint16_t* st = a.st_bf + (int64_t)bh * D * D;
+    st[(d2 + 0) * D + d1] = (uint16_t)f2bf(t.x);
+    st[(d2 + 1) * D + d1] = (uint16_t)f2bf(t.y);
+    st[(d2 + 2) * D + d1] = (uint16_t)f2bf(t.z);
+    st[(d2 + 3) * D + d1] = (uint16_t)f2bf(t.w);
+  }
+  if (blockIdx.x == 0 && tid < D) {
     const float* pz = a.part_z + (int64_t)bh * a.splits * D;
-    float s = 0.f;
-    for (int p = 0; p < a.splits; ++p) s += pz[p * D + threadIdx.x];
-    a.z_ws[bh * D + threadIdx.x] = s;
-    if (a.z) a.z[bh * D + threadIdx.x] = s;
+    float z = 0.f;
+#pragma unroll 8
+    for (int p = 0; p < a.splits; ++p) z += pz[p * D + tid];
+    a.z_ws[bh * D + tid] = z;
+    if (a.z) a.z[bh * D + tid] = z;
   }
 }
 
@@ -206,6 +367,7 @@ struct LinApplyArgs {
   const float* z_ws;
   int64_t sb, sh, sn;
   int H, N;
+  int tph, total, tpw;  // head_dim 128 kernel: tiles per head, all tiles, tiles per workgroup
 };
 
 template <int D>
@@ -280,28 +442,135 @@ __global__ void __launch_bounds__(256) lin_apply_kernel(LinApplyArgs a) {
   }
 }
 
+// head_dim 128 apply.  The (batch, head, 128-query tile) items are dealt to
+// workgroups in equal contiguous runs of tpw items (one round of workgroups
+// covers the whole job).  S^T (bf16, rows d2 swizzled) and z are staged in
+// LDS with buffer loads whenever the run enters a new head; Q tiles come
+// straight from global memory into registers, the next tile's loads issued
+// before the current tile's compute so one tile of Q is always in flight.
+__global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
+  constexpr int D = 128, KT = 8, DT = 4;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ss[D * D];
+  __shared__ float zs[D];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hi = lane >> 5;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const int it0 = blockIdx.x * a.tpw, it1 = min(it0 + a.tpw, a.total);
+  if (it0 >= it1) return;
+
+  auto stage_head = [&](int bh) {
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.st_bf + (int64_t)bh * D * D), (short)0, D * D * 2, kBufferWord3);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 32 * wv + 4 * j + (lane >> 4);
+      const uint32_t o = (uint32_t)row * (D * 2) + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(srs, (lds_void*)&Ss[(32 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+    }
+    if (tid < D) zs[tid] = a.z_ws[bh * D + tid];
+  };
+  auto q_src = [&](int item) {
+    const int bh = item / a.tph, tile = item % a.tph;
+    const int qrow = min(tile * kApplyRows + wave * 32 + l32, a.N - 1);
+    return a.q + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)qrow * a.sn + hi * 8;
+  };
+  u32x4 qr[KT], qn[KT];
+  {
+    const uint16_t* src = q_src(it0);
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qr[t] = *(const u32x4*)(src + t * 16);
+  }
+  int cur_bh = -1;
+  for (int it = it0; it < it1; ++it) {
+    const int bh = it / a.tph, tile = it % a.tph;
+    if (bh != cur_bh) {
+      __syncthreads();  // every wave is done with the previous head's S^T
+      stage_head(bh);
+      __builtin_amdgcn_s_waitcnt(0x0070);
+      __syncthreads();
+      cur_bh = bh;
+    }
+    const bool more = it + 1 < it1;
+    if (more) {
+      const uint16_t* src = q_src(it + 1);
+#pragma unroll
+      for (int t = 0; t < KT; ++t) qn[t] = *(const u32x4*)(src + t * 16);
+    }
+    bf16x8 qf[KT];
+    float den = 0.f;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = t * 16 + hi * 8 + 2 * e;
+        const float f0 = phi(bf16_lo(qr[t][e])), f1 = phi(bf16_hi(qr[t][e]));
+        den = __builtin_fmaf(f0, zs[d], den);
+        den = __builtin_fmaf(f1, zs[d + 1], den);
+        w[e] = pack_bf16x2(f0, f1);
+      }
+      qf[t] = __builtin_bit_cast(bf16x8, w);
+    }
+    den = pair_sum(den);
+    f32x16 o[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      o[dt] = f32x16{};
+      const int row = dt * 32 + l32;
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        const bf16x8 sf = *(const bf16x8*)&Ss[row * D + (((2 * t + hi) ^ swz_k(row)) << 3)];
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[t], o[dt], 0, 0, 0);
+      }
+    }
+    const int qrow = tile * kApplyRows + wave * 32 + l32;
+    if (qrow < a.N) {
+      const float inv = 1.f / den;
+      uint16_t* dst = a.o + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)qrow * a.sn;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = dt * 32 + 8 * g + 4 * hi;
+          u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                     pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+          *(u32x2*)(dst + d0) = w;
+        }
+    }
+    if (more) {
+#pragma unroll
+      for (int t = 0; t < KT; ++t) qr[t] = qn[t];
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
-struct LinPlan {
-  int splits, chunk;
-  size_t off_part_s, off_part_z, off_st, off_z, total;
-};
 
 static size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 LinPlan linear_plan(const bsa_shape& s) {
   LinPlan p;
   const int64_t bh = (int64_t)s.B * s.H;
-  // about two workgroups per CU in total, at least one 64-token tile each
-  int64_t want = (512 + bh - 1) / bh;
-  const int64_t tiles = (s.N + kLinTok - 1) / kLinTok;
+  // the head_dim-128 kernels address a head with 32-bit offsets
+  p.d128 = s.D == 128 && ((int64_t)s.N + kLinTok) * s.stride_n * 2 < ((int64_t)1 << 31);
+  // state: at most two workgroups per CU in total, so the whole launch is one
+  // round (a few workgroups past 2 per CU would double the time)
+  const int tok = p.d128 ? kLinTok2 : kLinTok;
+  int64_t want = 512 / bh;
+  const int64_t tiles = (s.N + tok - 1) / tok;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
   const int64_t per = (tiles + want - 1) / want;
-  p.chunk = (int)(per * kLinTok);
+  p.chunk = (int)(per * tok);
   p.splits = (int)((s.N + p.chunk - 1) / p.chunk);
+  // apply (head_dim 128): (head, tile) items in equal runs over <= 512 workgroups
+  p.tph = (s.N + kApplyRows - 1) / kApplyRows;
+  const int64_t items = bh * p.tph;
+  p.tpw = (int)((items + 511) / 512);
+  p.apply_wgs = (int)((items + p.tpw - 1) / p.tpw);
   const size_t D = s.D;
   p.off_part_s = 0;
   p.off_part_z = align256(p.off_part_s + (size_t)bh * p.splits * D * D * 4);
@@ -321,15 +590,20 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
   LinReduceArgs ra{(const float*)(w + p.off_part_s), (const float*)(w + p.off_part_z), S, z,
                    (uint16_t*)(w + p.off_st), (float*)(w + p.off_z), p.splits};
   LinApplyArgs aa{(const uint16_t*)q, (uint16_t*)o, (const uint16_t*)(w + p.off_st),
-                  (const float*)(w + p.off_z), s.stride_b, s.stride_h, s.stride_n, s.H, s.N};
+                  (const float*)(w + p.off_z), s.stride_b, s.stride_h, s.stride_n, s.H, s.N,
+                  p.tph, bh * p.tph, p.tpw};
   const int row_groups = (s.N + kApplyRows * kApplyTiles - 1) / (kApplyRows * kApplyTiles);
-  if (s.D == 128) {
+  if (s.D == 128 && p.d128) {
+    hipLaunchKernelGGL(lin_state_d128_kernel, dim3(p.splits, bh), dim3(kLinThreads), 0, stream, sa);
+    hipLaunchKernelGGL(lin_reduce_kernel<128>, dim3(128 * 128 / (4 * kRedCols), bh), dim3(256), 0, stream, ra);
+    hipLaunchKernelGGL(lin_apply_d128_kernel, dim3(p.apply_wgs), dim3(256), 0, stream, aa);
+  } else if (s.D == 128) {
     hipLaunchKernelGGL(lin_state_kernel<128>, dim3(p.splits, bh), dim3(kLinThreads), 0, stream, sa);
-    hipLaunchKernelGGL(lin_reduce_kernel<128>, dim3(128 * 128 / 256, bh), dim3(256), 0, stream, ra);
+    hipLaunchKernelGGL(lin_reduce_kernel<128>, dim3(128 * 128 / (4 * kRedCols), bh), dim3(256), 0, stream, ra);
     hipLaunchKernelGGL(lin_apply_kernel<128>, dim3(row_groups, bh), dim3(256), 0, stream, aa);
   } else if (s.D == 64) {
     hipLaunchKernelGGL(lin_state_kernel<64>, dim3(p.splits, bh), dim3(kLinThreads), 0, stream, sa);
-    hipLaunchKernelGGL(lin_reduce_kernel<64>, dim3(64 * 64 / 256, bh), dim3(256), 0, stream, ra);
+    hipLaunchKernelGGL(lin_reduce_kernel<64>, dim3(64 * 64 / (4 * kRedCols), bh), dim3(256), 0, stream, ra);
     hipLaunchKernelGGL(lin_apply_kernel<64>, dim3(row_groups, bh), dim3(256), 0, stream, aa);
   } else {
     return BSA_ERR_UNSUPPORTED;

@@ -15,7 +15,7 @@
 //   order: (optional) the row schedule for the attention launch (long rows
 //          first, see mask_order_kernel).
 
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 

@@ -30,7 +30,7 @@
 //                        logit bias ln n_b).  Same MFMA core as the block-sparse
 //                        kernel, with a gathered key-row map.
 
-#include "common.h"
+#include "launch.h"
 
 namespace bsa {
 
@@ -791,10 +791,6 @@ bsa_status launch_centroids(const void* q, const void* k, const void* v, const b
   return launch_ok("cluster_centroids") ? BSA_OK : BSA_ERR_HIP;
 }
 
-struct ProbePlan {
-  int splits, cps;
-  size_t off_e, off_m, off_ms, off_zs, total;
-};
 
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 

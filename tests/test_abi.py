@@ -103,3 +103,31 @@ def test_status_strings(lib):
     for s in range(6):
         assert lib.bsa_status_string(s)
     assert lib.bsa_status_string(99) == b"unknown status"
+
+
+def test_workspace_queries_do_not_crash_and_are_aligned(lib):
+    """The host-side plans behind the workspace queries (a stale second copy of a
+    plan struct once made these overrun the caller's stack)."""
+    for N in (1, 7, 1000, 32760, 196560):
+        for H in (1, 2, 12):
+            sh = _shape(B=1, H=H, N=N, D=128)
+            lw = lib.bsa_linear_attn_workspace(ctypes.byref(sh))
+            assert lw > 0 and lw % 256 == 0
+            assert lw >= H * 128 * 128 * 2 + H * 128 * 4      # S^T (bf16) and z at least
+            for Cq, Ck in ((8, 20), (100, 500), (150, 40)):
+                rw = lib.bsa_route_scores_workspace(ctypes.byref(sh), Cq, Ck)
+                assert rw > 0 and rw % 256 == 0
+                assert rw >= 2 * H * Cq * Ck * 4                # e and m of every block at least
+                fw = lib.bsa_centroid_compensate_workspace(ctypes.byref(sh), Cq, Ck)
+                assert fw >= rw + H * Cq * Ck * (4 + 1)         # plus scores and select flags
+
+
+def test_each_struct_is_defined_once_in_the_native_sources():
+    """Host plan structs cross translation units by value: one definition only."""
+    csrc = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc")
+    seen = {}
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            for name in re.findall(r"^\s*struct\s+(\w+)\s*\{", open(os.path.join(csrc, f)).read(), flags=re.M):
+                assert name not in seen, f"struct {name} defined in {seen[name]} and {f}"
+                seen[name] = f

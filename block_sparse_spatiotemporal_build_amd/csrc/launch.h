@@ -32,7 +32,8 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
 // ---- centroid compensation with error-aware routing ------------------------
 struct ProbePlan {
   int splits, cps;  // key-cluster splits per head and clusters per split
-  size_t off_e, off_m, off_ms, off_zs, total;  // workspace layout (bytes)
+  bool d128;        // head_dim 128 probe (buffer-load staging, logits precomputed)
+  size_t off_e, off_m, off_ms, off_zs, off_lc, total;  // workspace layout (bytes)
 };
 ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck);
 bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,

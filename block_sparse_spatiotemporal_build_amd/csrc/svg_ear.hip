@@ -118,6 +118,7 @@ struct ProbeArgs {
   const float* q_cent;
   const float* k_cent;
   const float* v_cent;
+  const float* lc;  // [BH][Ck][Cq] proxy-centroid logits (log2 units), head_dim 128 path
   float* e_buf;     // [BH][Cq][Ck]  squared error norm at the recorded max
   float* m_buf;     // [BH][Cq][Ck]  the max (log2 units) it was taken at
   float* m_split;   // [BH][splits][Cq]
@@ -338,6 +339,261 @@ __global__ void __launch_bounds__(256) probe_kernel(ProbeArgs p) {
   }
 }
 
+// Proxy-centroid logits lc[b][a] = s log2(e) c^_a . c_b in fp32, with c^_a
+// taken as the same bf16 hi + lo pair the probe multiplies the keys with, so
+// that the centroid weight and the key weights of the difference form share
+// one proxy.  16 x 16 (a, b) pairs per workgroup.
+template <int D>
+__global__ void __launch_bounds__(256) proxy_logit_kernel(const float* q_cent, const float* k_cent, float* lc,
+                                                          int Cq, int Ck, float c2) {
+  __shared__ float qs[16][D + 1], ks[16][D + 1];
+  const int bh = blockIdx.z, a0 = blockIdx.y * 16, b0 = blockIdx.x * 16, tid = threadIdx.x;
+  for (int i = tid; i < 16 * D; i += 256) {
+    const int r = i / D, d = i % D;
+    const int a = a0 + r, b = b0 + r;
+    const float x = a < Cq ? q_cent[((int64_t)bh * Cq + a) * D + d] : 0.f;
+    const float h = bf16_lo(pack_bf16x2(x, 0.f));
+    qs[r][d] = h + bf16_lo(pack_bf16x2(x - h, 0.f));
+    ks[r][d] = b < Ck ? k_cent[((int64_t)bh * Ck + b) * D + d] : 0.f;
+  }
+  __syncthreads();
+  const int ty = tid >> 4, tx = tid & 15;
+  float dot = 0.f;
+#pragma unroll 8
+  for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qs[ty][d], ks[tx][d], dot);
+  const int a = a0 + ty, b = b0 + tx;
+  if (a < Cq && b < Ck) lc[((int64_t)bh * Ck + b) * Cq + a] = dot * c2;
+}
+
+// head_dim 128 probe: same computation as probe_kernel, with K/V staged by
+// buffer loads straight to LDS (two swizzled stages as separate LDS objects,
+// loop unrolled by two), the bf16 lo halves of the proxies in LDS instead of
+// registers, the split's cluster offsets and proxy-centroid logits in LDS.
+// This keeps two waves per SIMD, so one wave's softmax overlaps the other's
+// MFMAs and the copies overlap both.
+constexpr int kPrMaxCps = 16;  // clusters per split (the plan keeps cps <= this)
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) probe_d128_kernel(ProbeArgs p) {
+  constexpr int D = 128, KT = 8, DT = 4, TILE = kPrBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t CL[128 * D];  // proxy lo halves, rows swizzled (swz_k)
+  __shared__ float lcs[kPrMaxCps][128];
+  __shared__ int koffs[kPrMaxCps + 1];
+
+  const SvgArgs& a = p.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int prow = wave * 32 + l32;
+  const int prox = blockIdx.z * 128 + prow;  // proxy (query cluster) of this lane
+  const bool pvalid = prox < a.Cq;
+  const int32_t* koff_g = a.k_off + (int64_t)bh * (a.Ck + 1);
+  const uint16_t* Kh = head_ptr(a.k, a, bh);
+  const uint16_t* Vh = head_ptr(a.v, a, bh);
+  const int b0 = split * p.cps, b1 = min(b0 + p.cps, a.Ck), nclu = b1 - b0;
+
+  // proxy fragments: c^ = hi + lo (bf16 each); hi is the MFMA B operand in
+  // registers, lo is read from LDS per tile
+  bf16x8 cf[KT];
+  {
+    const float* src = p.q_cent + ((int64_t)bh * a.Cq + (pvalid ? prox : 0)) * D + hi * 8;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      u32x4 wh, wl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = pvalid ? src[t * 16 + 2 * e] : 0.f, x1 = pvalid ? src[t * 16 + 2 * e + 1] : 0.f;
+        wh[e] = pack_bf16x2(x0, x1);
+        wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+      }
+      cf[t] = __builtin_bit_cast(bf16x8, wh);
+      *(u32x4*)&CL[prow * D + (((2 * t + hi) ^ swz_k(prow)) << 3)] = wl;
+    }
+  }
+  for (int i = tid; i <= nclu; i += 256) koffs[i] = koff_g[b0 + i];
+  for (int i = wave; i < nclu; i += 4)
+    for (int j = lane; j < 128; j += 64) {
+      const int px = blockIdx.z * 128 + j;
+      lcs[i][j] = px < a.Cq ? p.lc[((int64_t)bh * a.Ck + b0 + i) * a.Cq + px] : 0.f;
+    }
+  __syncthreads();
+  retire_loads();
+
+  auto ntiles_of = [&](int i) { return (koffs[i + 1] - koffs[i] + kPrBN - 1) / kPrBN; };
+  int total = 0;
+  for (int i = 0; i < nclu; ++i) total += ntiles_of(i);
+
+  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane/16
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, 0x7fffffff, kBufferWord3);
+  uint32_t koff[2], voff[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wv + 4 * j + (lane >> 4);
+    koff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16);
+    voff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+  }
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int key0, int kend) {
+    if (key0 + kPrBN <= kend) {
+      const uint32_t so = (uint32_t)key0 * row_bytes;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16, koff[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16, voff[j], so, 0, 0);
+      }
+    } else {  // last tile of a cluster: rows past its end are clamped to its last key (masked below)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 8 * wv + 4 * j + (lane >> 4);
+        const uint32_t ro = (uint32_t)min(key0 + row, kend - 1) * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16,
+                                                 ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16,
+                                                 ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 U[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) U[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f, lc2 = 0.f;
+  const int g16 = lane >> 4, j16 = lane & 15;
+
+  // walk state: cluster (local index) and sub-tile of the tile being computed,
+  // and the prefetch cursor one tile ahead
+  int cb = 0, cst = 0;
+  while (cb < nclu && ntiles_of(cb) == 0) ++cb;
+  int fb = cb, fst = 0;
+  auto advance = [&](int& bb, int& st) {
+    ++st;
+    if (st >= ntiles_of(bb)) {
+      st = 0;
+      ++bb;
+      while (bb < nclu && ntiles_of(bb) == 0) ++bb;
+    }
+  };
+
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): tile u landed, other stage drained
+    __builtin_amdgcn_s_barrier();
+    if (u + 1 < total) {
+      dma(Kn, Vn, koffs[fb] + fst * kPrBN, koffs[fb + 1]);
+      advance(fb, fst);
+    }
+    const int kend = koffs[cb + 1];
+    const int key0 = koffs[cb] + cst * kPrBN;
+    if (cst == 0) {
+#pragma unroll
+      for (int i = 0; i < DT; ++i) U[i] = f32x16{};
+      lc2 = lcs[cb][prow];
+    }
+    // S^T (32 keys x 32 proxies) = K (c_hi + c_lo)^T
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      const bf16x8 kf = *(const bf16x8*)&Kb[l32 * D + (((2 * t + hi) ^ swz_k(l32)) << 3)];
+      const bf16x8 cl = *(const bf16x8*)&CL[prow * D + (((2 * t + hi) ^ swz_k(prow)) << 3)];
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, cf[t], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, cl, s, 0, 0, 0);
+    }
+    if (key0 + kPrBN > kend) {  // key of s[r]: key0 + 8 (r / 4) + 4 hi + r % 4
+      const int lim = kend - key0 - 4 * hi;
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -__builtin_inff();
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    const float m_new = fmaxf(m_run, pair_max(mx) * p.c2);
+    if (__any(m_new - m_run > kLazyRescaleLog2)) {
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) U[i] *= alpha;
+      m_run = m_new;
+    }
+    // U accumulates sum_j (p_j - p_c) v_j (the difference form)
+    const float pc = fast_exp2(lc2 - m_run);
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pr = fast_exp2(__builtin_fmaf(s[r], p.c2, -m_run));
+      psum += pr;
+      s[r] = (s[r] == -__builtin_inff()) ? 0.f : pr - pc;
+    }
+    l_run += psum;
+    // P' = hi + lo (bf16 each)
+    bf16x8 pf[2], pl[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 wh, wl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x0 = s[8 * ks + 2 * e], x1 = s[8 * ks + 2 * e + 1];
+        wh[e] = pack_bf16x2(x0, x1);
+        wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+      }
+      pf[ks] = __builtin_bit_cast(bf16x8, wh);
+      pl[ks] = __builtin_bit_cast(bf16x8, wl);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
+        const int lcn = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+        const int half = (j16 & 1) * 4;
+        const u32x2 lo = lds_tr16(&Vb[r0 * D + ((lcn ^ swz_v(r0)) << 3) + half]);
+        const u32x2 h2 = lds_tr16(&Vb[r1 * D + ((lcn ^ swz_v(r1)) << 3) + half]);
+        const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+        U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], U[dt], 0, 0, 0);
+        U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[ks], U[dt], 0, 0, 0);
+      }
+
+    if (cst + 1 == ntiles_of(cb)) {
+      // cluster finished: squared norm of the accumulated error (at reference m_run)
+      float e2 = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e2 = __builtin_fmaf(U[dt][r], U[dt][r], e2);
+      e2 = pair_sum(e2);
+      if (pvalid && hi == 0) {
+        const int64_t o = ((int64_t)bh * a.Cq + prox) * a.Ck + b0 + cb;
+        p.e_buf[o] = e2;
+        p.m_buf[o] = m_run;
+      }
+      cst = 0;
+      ++cb;
+      while (cb < nclu && ntiles_of(cb) == 0) ++cb;
+    } else {
+      ++cst;
+    }
+  };
+
+  if (total > 0) {
+    dma(K0, V0, koffs[fb] + fst * kPrBN, koffs[fb + 1]);
+    advance(fb, fst);
+  }
+  int u = 0;
+  for (; u + 2 <= total; u += 2) {
+    step(K0, V0, K1, V1, u);
+    step(K1, V1, K0, V0, u + 1);
+  }
+  if (u < total) step(K0, V0, K1, V1, u);
+
+  const float z = pair_sum(l_run);
+  if (pvalid && hi == 0) {
+    p.m_split[((int64_t)bh * p.splits + split) * a.Cq + prox] = m_run;
+    p.z_split[((int64_t)bh * p.splits + split) * a.Cq + prox] = z;
+  }
+}
+
 struct FinalizeArgs {
   const int32_t* q_off;
   const int32_t* k_off;
@@ -350,18 +606,23 @@ struct FinalizeArgs {
 };
 
 __global__ void __launch_bounds__(256) probe_finalize_kernel(FinalizeArgs f) {
-  const int a = blockIdx.x, bh = blockIdx.y;
+  const int a = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   __shared__ float mz[2];
-  if (threadIdx.x == 0) {
+  if (tid < 64) {
+    // combine the splits' (max, normaliser) pairs of proxy a, one wave
     float m = -1e30f;
-    for (int s = 0; s < f.splits; ++s) m = fmaxf(m, f.m_split[((int64_t)bh * f.splits + s) * f.Cq + a]);
+    for (int s = lane; s < f.splits; s += 64) m = fmaxf(m, f.m_split[((int64_t)bh * f.splits + s) * f.Cq + a]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     float z = 0.f;
-    for (int s = 0; s < f.splits; ++s) {
+    for (int s = lane; s < f.splits; s += 64) {
       const int64_t o = ((int64_t)bh * f.splits + s) * f.Cq + a;
       z += f.z_split[o] * fast_exp2(f.m_split[o] - m);
     }
-    mz[0] = m;
-    mz[1] = z;
+    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+    if (lane == 0) {
+      mz[0] = m;
+      mz[1] = z;
+    }
   }
   __syncthreads();
   const float m = mz[0], z = mz[1];
@@ -369,7 +630,7 @@ __global__ void __launch_bounds__(256) probe_finalize_kernel(FinalizeArgs f) {
   const int32_t* ko = f.k_off + (int64_t)bh * (f.Ck + 1);
   const int na = qo[a + 1] - qo[a];
   const float inv_z2 = z > 0.f ? 1.f / (z * z) : 0.f;
-  for (int b = threadIdx.x; b < f.Ck; b += 256) {
+  for (int b = tid; b < f.Ck; b += 256) {
     const int nb = ko[b + 1] - ko[b];
     const int64_t o = ((int64_t)bh * f.Cq + a) * f.Ck + b;
     float sc = 0.f;
@@ -382,29 +643,18 @@ __global__ void __launch_bounds__(256) probe_finalize_kernel(FinalizeArgs f) {
 // route select
 // ---------------------------------------------------------------------------
 
-constexpr int kSelThreads = 1024;
+constexpr int kSelThreads = 1024, kSelWaves = kSelThreads / 64, kSelMaxCk = 4096;
 
-// Inclusive scan of an int64 over the workgroup (wave shuffles + LDS).
-__device__ long long block_scan_incl(long long x, long long* wsum) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ __forceinline__ long long wave_sum64(long long x) {
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+__device__ __forceinline__ long long wave_incl_scan64(long long x, int lane) {
   for (int off = 1; off < 64; off <<= 1) {
     const long long y = __shfl_up(x, off, 64);
     if (lane >= off) x += y;
   }
-  if (lane == 63) wsum[wave] = x;
-  __syncthreads();
-  if (wave == 0) {
-    long long t = lane < kSelThreads / 64 ? wsum[lane] : 0;
-    for (int off = 1; off < 64; off <<= 1) {
-      const long long y = __shfl_up(t, off, 64);
-      if (lane >= off) t += y;
-    }
-    if (lane < kSelThreads / 64) wsum[lane] = t;
-  }
-  __syncthreads();
-  const long long r = x + (wave > 0 ? wsum[wave - 1] : 0);
-  __syncthreads();
-  return r;
+  return x;
 }
 
 struct SelectArgs {
@@ -418,113 +668,167 @@ struct SelectArgs {
   long long budget;
 };
 
+// One workgroup per (batch, head).  Blocks are ranked by (score descending,
+// index a * Ck + b ascending); the kept set is the longest prefix of that order
+// whose total cost n_a n_b fits the budget.  Non-negative floats order like
+// their bit patterns, so the cut is a threshold pattern T found by a
+// cost-weighted radix select (4 passes of 8 bits, one histogram per wave):
+// every block above T is kept, and blocks equal to T are kept in index order
+// while the remaining budget lasts.  Wave w owns the contiguous rows
+// [w * rpw, (w + 1) * rpw), so index order is wave order, then row order, then
+// column order.
 __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
-  __shared__ unsigned long long hist[256];
-  __shared__ long long wsum[64];
+  __shared__ unsigned long long hist[kSelWaves][256];
+  __shared__ unsigned long long htot[256];
+  __shared__ long long wred[kSelWaves];
+  __shared__ int nbk[kSelMaxCk];
+  __shared__ int wcnt[kSelWaves];
   __shared__ long long sh_R;
-  __shared__ unsigned int sh_prefix, sh_mask;
-  __shared__ int sh_all;
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int M = s.Cq * s.Ck;
-  const float* sc = s.score + (int64_t)bh * M;
-  const int32_t* qo = s.q_off + (int64_t)bh * (s.Cq + 1);
-  const int32_t* ko = s.k_off + (int64_t)bh * (s.Ck + 1);
+  __shared__ unsigned int sh_prefix;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = s.Cq, Ck = s.Ck;
+  const int64_t M = (int64_t)Cq * Ck;
+  const unsigned* sc = (const unsigned*)(s.score + (int64_t)bh * M);
+  const int32_t* qo = s.q_off + (int64_t)bh * (Cq + 1);
+  const int32_t* ko = s.k_off + (int64_t)bh * (Ck + 1);
   uint8_t* fl = s.flags + (int64_t)bh * M;
-  auto cost_of = [&](int e) -> long long {
-    const int a = e / s.Ck, b = e % s.Ck;
-    return (long long)(qo[a + 1] - qo[a]) * (long long)(ko[b + 1] - ko[b]);
-  };
+  int32_t* rr = s.rrow + (int64_t)bh * (Cq + 1);
+  int32_t* rc = s.rcol + (int64_t)bh * M;
+
+  const bool nb_lds = Ck <= kSelMaxCk;
+  if (nb_lds)
+    for (int b = tid; b < Ck; b += kSelThreads) nbk[b] = ko[b + 1] - ko[b];
+  __syncthreads();
+  auto nb_of = [&](int b) -> int { return nb_lds ? nbk[b] : ko[b + 1] - ko[b]; };
+  const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
+  const int ra0 = min(wave * rpw, Cq), ra1 = min(ra0 + rpw, Cq);
 
   // total cost of all non-empty blocks
   long long part = 0;
-  for (int e = tid; e < M; e += kSelThreads) part += cost_of(e);
-  const long long total = block_scan_incl(part, wsum);
-  if (tid == kSelThreads - 1) {
-    sh_all = total <= s.budget;
-    sh_R = s.budget;
-    sh_prefix = 0;
-    sh_mask = 0;
+  for (int a = ra0; a < ra1; ++a) {
+    const long long na = qo[a + 1] - qo[a];
+    if (na == 0) continue;
+    for (int b = lane; b < Ck; b += 64) part += na * nb_of(b);
   }
+  part = wave_sum64(part);
+  if (lane == 0) wred[wave] = part;
   __syncthreads();
-  const bool take_all = sh_all;
+  long long total = 0;
+  for (int w = 0; w < kSelWaves; ++w) total += wred[w];
+  const bool take_all = total <= s.budget;
 
+  unsigned T = 0;
+  long long R = s.budget;
   if (!take_all) {
-    // radix select of the threshold bit pattern T, 8 bits at a time
+    unsigned pre = 0, msk = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int i = tid; i < 256; i += kSelThreads) hist[i] = 0;
-      __syncthreads();
-      const unsigned pre = sh_prefix, msk = sh_mask;
-      for (int e = tid; e < M; e += kSelThreads) {
-        const long long c = cost_of(e);
-        const unsigned bits = __float_as_uint(sc[e]);
-        if (c > 0 && (bits & msk) == pre) atomicAdd(&hist[(bits >> shift) & 255u], (unsigned long long)c);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        long long acc = 0, R = sh_R;
-        int d = 255;
-        for (; d > 0; --d) {
-          if (acc + (long long)hist[d] > R) break;
-          acc += (long long)hist[d];
+      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+      __builtin_amdgcn_wave_barrier();
+      for (int a = ra0; a < ra1; ++a) {
+        const long long na = qo[a + 1] - qo[a];
+        if (na == 0) continue;
+        const unsigned* row = sc + (int64_t)a * Ck;
+        for (int b = lane; b < Ck; b += 64) {
+          const int nbv = nb_of(b);
+          const unsigned bits = row[b];
+          if (nbv > 0 && (bits & msk) == pre)
+            atomicAdd(&hist[wave][(bits >> shift) & 255u], (unsigned long long)(na * nbv));
         }
-        sh_R = R - acc;
-        sh_prefix = pre | ((unsigned)d << shift);
-        sh_mask = msk | (255u << shift);
       }
       __syncthreads();
+      if (tid < 256) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kSelWaves; ++w) t += hist[w][tid];
+        htot[tid] = t;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds digits 4l .. 4l+3; the cut digit d is the first one from
+        // the top where the cost of the digits above stays within R but adding
+        // d's own cost exceeds it (digit 0 if none does)
+        unsigned long long h[4], own = 0;
+        for (int i = 0; i < 4; ++i) {
+          h[i] = htot[4 * lane + i];
+          own += h[i];
+        }
+        long long above = (long long)own;  // becomes: cost of all digits held by higher lanes
+        for (int off = 1; off < 64; off <<= 1) {
+          const long long y = __shfl_down(above, off, 64);
+          if (lane + off < 64) above += y;
+        }
+        above -= (long long)own;
+        for (int i = 3; i >= 0; --i) {
+          const int d = 4 * lane + i;
+          const bool cut = (above + (long long)h[i] > R) || d == 0;
+          if (cut && above <= R) {
+            sh_R = R - above;
+            sh_prefix = pre | ((unsigned)d << shift);
+            break;
+          }
+          above += (long long)h[i];
+        }
+      }
+      __syncthreads();
+      R = sh_R;
+      pre = sh_prefix;
+      msk |= 255u << shift;
+      __syncthreads();
     }
+    T = pre;
   }
-  const unsigned T = sh_prefix;
-  const long long R = sh_R;
 
-  // flags: above the threshold, or in the tie group within the remaining budget (index order)
-  long long carry = 0;
-  for (int base = 0; base < M; base += kSelThreads) {
-    const int e = base + tid;
-    long long c = 0;
-    unsigned bits = 0;
-    if (e < M) {
-      c = cost_of(e);
-      bits = __float_as_uint(sc[e]);
+  // keep flags; ties at T in index order within the remaining budget
+  long long tc = 0;
+  if (!take_all)
+    for (int a = ra0; a < ra1; ++a) {
+      const long long na = qo[a + 1] - qo[a];
+      if (na == 0) continue;
+      const unsigned* row = sc + (int64_t)a * Ck;
+      for (int b = lane; b < Ck; b += 64) {
+        const int nbv = nb_of(b);
+        if (nbv > 0 && row[b] == T) tc += na * nbv;
+      }
     }
-    const bool tie = !take_all && e < M && c > 0 && bits == T;
-    const long long incl = block_scan_incl(tie ? c : 0, wsum);
-    if (e < M) {
-      bool keep;
-      if (take_all) keep = c > 0;
-      else keep = c > 0 && (bits > T || (tie && carry + incl <= R));
-      fl[e] = keep ? 1 : 0;
-    }
-    if (tid == kSelThreads - 1) wsum[63] = incl;
-    __syncthreads();
-    carry += wsum[63];
-    __syncthreads();
-  }
+  tc = wave_sum64(tc);
+  if (lane == 0) wred[wave] = tc;
   __syncthreads();
-
-  // CSR of the kept blocks, columns ascending
-  int32_t* rr = s.rrow + (int64_t)bh * (s.Cq + 1);
-  int32_t* rc = s.rcol + (int64_t)bh * M;
-  long long rowbase = 0;
-  for (int a0 = 0; a0 < s.Cq; a0 += kSelThreads) {
-    const int a = a0 + tid;
-    int cnt = 0;
-    if (a < s.Cq)
-      for (int b = 0; b < s.Ck; ++b) cnt += fl[a * s.Ck + b];
-    const long long incl = block_scan_incl(cnt, wsum);
-    const long long start = rowbase + incl - cnt;
-    if (a < s.Cq) {
-      rr[a] = (int32_t)start;
-      int w = (int)start;
-      for (int b = 0; b < s.Ck; ++b)
-        if (fl[a * s.Ck + b]) rc[w++] = b;
+  long long carry = 0;
+  for (int w = 0; w < wave; ++w) carry += wred[w];
+  int wave_kept = 0;
+  for (int a = ra0; a < ra1; ++a) {
+    const long long na = qo[a + 1] - qo[a];
+    const unsigned* row = sc + (int64_t)a * Ck;
+    for (int b0 = 0; b0 < Ck; b0 += 64) {
+      const int b = b0 + lane;
+      const bool valid = b < Ck;
+      const long long c = valid ? na * nb_of(b) : 0;
+      const unsigned bits = valid ? row[b] : 0u;
+      const bool tie = !take_all && c > 0 && bits == T;
+      long long incl = 0;
+      if (__any(tie)) incl = wave_incl_scan64(tie ? c : 0, lane);
+      const bool keep = take_all ? c > 0 : (c > 0 && (bits > T || (tie && carry + incl <= R)));
+      carry += __shfl(incl, 63, 64);
+      if (valid) fl[(int64_t)a * Ck + b] = keep ? 1 : 0;
+      wave_kept += __popcll(__ballot(keep));
     }
-    if (tid == kSelThreads - 1) wsum[63] = incl;
-    __syncthreads();
-    rowbase += wsum[63];
-    __syncthreads();
   }
-  if (tid == 0) rr[s.Cq] = (int32_t)rowbase;
+  if (lane == 0) wcnt[wave] = wave_kept;
+  __syncthreads();
+  // CSR: wave w's rows start after the blocks kept by waves < w; columns
+  // ascending, 64 at a time with ballots (each lane re-reads only flags it wrote)
+  int start = 0;
+  for (int w = 0; w < wave; ++w) start += wcnt[w];
+  if (tid == 0) rr[0] = 0;
+  for (int a = ra0; a < ra1; ++a) {
+    for (int b0 = 0; b0 < Ck; b0 += 64) {
+      const int b = b0 + lane;
+      const bool keep = b < Ck && fl[(int64_t)a * Ck + b] != 0;
+      const unsigned long long bal = __ballot(keep);
+      if (keep) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = b;
+      start += __popcll(bal);
+    }
+    if (lane == 0) rr[a + 1] = start;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -798,17 +1102,21 @@ ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck) {
   ProbePlan p;
   const int bh = s.B * s.H;
   const int groups = (Cq + 127) / 128;
+  // the head_dim-128 kernel addresses a head with 32-bit offsets
+  p.d128 = s.D == 128 && ((int64_t)s.N + kPrBN) * s.stride_n * 2 < ((int64_t)1 << 31);
   int want = (512 + bh * groups - 1) / (bh * groups);
   if (want > Ck) want = Ck;
   if (want < 1) want = 1;
   p.cps = (Ck + want - 1) / want;
+  if (p.d128 && p.cps > kPrMaxCps) p.cps = kPrMaxCps;
   p.splits = (Ck + p.cps - 1) / p.cps;
   const size_t blocks = (size_t)bh * Cq * Ck;
   p.off_e = 0;
   p.off_m = al256(p.off_e + blocks * 4);
   p.off_ms = al256(p.off_m + blocks * 4);
   p.off_zs = al256(p.off_ms + (size_t)bh * p.splits * Cq * 4);
-  p.total = al256(p.off_zs + (size_t)bh * p.splits * Cq * 4);
+  p.off_lc = al256(p.off_zs + (size_t)bh * p.splits * Cq * 4);
+  p.total = al256(p.off_lc + (p.d128 ? blocks * 4 : 0));
   return p;
 }
 
@@ -820,13 +1128,22 @@ bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s,
   ProbeArgs p;
   p.s = svg_args(nullptr, k, v, s, q_off, Cq, k_off, Ck);
   p.q_cent = qc; p.k_cent = kc; p.v_cent = vc;
+  p.lc = pl.d128 ? (const float*)(w + pl.off_lc) : nullptr;
   p.e_buf = (float*)(w + pl.off_e); p.m_buf = (float*)(w + pl.off_m);
   p.m_split = (float*)(w + pl.off_ms); p.z_split = (float*)(w + pl.off_zs);
   p.splits = pl.splits; p.cps = pl.cps; p.c2 = scale * kLog2e;
   dim3 grid(pl.splits, s.B * s.H, (Cq + 127) / 128);
-  if (s.D == 128) hipLaunchKernelGGL(probe_kernel<128>, grid, dim3(256), 0, stream, p);
-  else if (s.D == 64) hipLaunchKernelGGL(probe_kernel<64>, grid, dim3(256), 0, stream, p);
-  else return BSA_ERR_UNSUPPORTED;
+  if (pl.d128) {
+    hipLaunchKernelGGL(proxy_logit_kernel<128>, dim3((Ck + 15) / 16, (Cq + 15) / 16, s.B * s.H), dim3(256), 0,
+                       stream, qc, kc, (float*)(w + pl.off_lc), Cq, Ck, p.c2);
+    hipLaunchKernelGGL(probe_d128_kernel, grid, dim3(256), 0, stream, p);
+  } else if (s.D == 128) {
+    hipLaunchKernelGGL(probe_kernel<128>, grid, dim3(256), 0, stream, p);
+  } else if (s.D == 64) {
+    hipLaunchKernelGGL(probe_kernel<64>, grid, dim3(256), 0, stream, p);
+  } else {
+    return BSA_ERR_UNSUPPORTED;
+  }
   FinalizeArgs f{q_off, k_off, p.e_buf, p.m_buf, p.m_split, p.z_split, score, Cq, Ck, pl.splits};
   hipLaunchKernelGGL(probe_finalize_kernel, dim3(Cq, s.B * s.H), dim3(256), 0, stream, f);
   return launch_ok("route_scores") ? BSA_OK : BSA_ERR_HIP;

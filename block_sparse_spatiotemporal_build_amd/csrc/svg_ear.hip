@@ -342,27 +342,59 @@ __global__ void __launch_bounds__(256) probe_kernel(ProbeArgs p) {
 // Proxy-centroid logits lc[b][a] = s log2(e) c^_a . c_b in fp32, with c^_a
 // taken as the same bf16 hi + lo pair the probe multiplies the keys with, so
 // that the centroid weight and the key weights of the difference form share
-// one proxy.  16 x 16 (a, b) pairs per workgroup.
+// one proxy.  A workgroup covers 16 proxies x 64 key clusters; thread
+// (a = tid / 16, tx = tid % 16) computes the clusters tx, tx + 16, tx + 32,
+// tx + 48 with float4 reads (row stride D + 4 floats: conflict-free).
 template <int D>
 __global__ void __launch_bounds__(256) proxy_logit_kernel(const float* q_cent, const float* k_cent, float* lc,
                                                           int Cq, int Ck, float c2) {
-  __shared__ float qs[16][D + 1], ks[16][D + 1];
-  const int bh = blockIdx.z, a0 = blockIdx.y * 16, b0 = blockIdx.x * 16, tid = threadIdx.x;
-  for (int i = tid; i < 16 * D; i += 256) {
-    const int r = i / D, d = i % D;
-    const int a = a0 + r, b = b0 + r;
-    const float x = a < Cq ? q_cent[((int64_t)bh * Cq + a) * D + d] : 0.f;
-    const float h = bf16_lo(pack_bf16x2(x, 0.f));
-    qs[r][d] = h + bf16_lo(pack_bf16x2(x - h, 0.f));
-    ks[r][d] = b < Ck ? k_cent[((int64_t)bh * Ck + b) * D + d] : 0.f;
+  constexpr int ST = D + 4;
+  __shared__ __attribute__((aligned(16))) float qs[16][ST];
+  __shared__ __attribute__((aligned(16))) float ks[64][ST];
+  const int bh = blockIdx.z, a0 = blockIdx.y * 16, b0 = blockIdx.x * 64, tid = threadIdx.x;
+  for (int i = tid; i < 16 * D / 4; i += 256) {
+    const int r = i / (D / 4), d = (i % (D / 4)) * 4;
+    const int a = a0 + r;
+    float4 x = {0.f, 0.f, 0.f, 0.f};
+    if (a < Cq) x = *(const float4*)&q_cent[((int64_t)bh * Cq + a) * D + d];
+    float4 y;
+    float* xs = &x.x;
+    float* ys = &y.x;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float h = bf16_lo(pack_bf16x2(xs[e], 0.f));
+      ys[e] = h + bf16_lo(pack_bf16x2(xs[e] - h, 0.f));
+    }
+    *(float4*)&qs[r][d] = y;
+  }
+  for (int i = tid; i < 64 * D / 4; i += 256) {
+    const int r = i / (D / 4), d = (i % (D / 4)) * 4;
+    const int bb = b0 + r;
+    float4 x = {0.f, 0.f, 0.f, 0.f};
+    if (bb < Ck) x = *(const float4*)&k_cent[((int64_t)bh * Ck + bb) * D + d];
+    *(float4*)&ks[r][d] = x;
   }
   __syncthreads();
   const int ty = tid >> 4, tx = tid & 15;
-  float dot = 0.f;
-#pragma unroll 8
-  for (int d = 0; d < D; ++d) dot = __builtin_fmaf(qs[ty][d], ks[tx][d], dot);
-  const int a = a0 + ty, b = b0 + tx;
-  if (a < Cq && b < Ck) lc[((int64_t)bh * Ck + b) * Cq + a] = dot * c2;
+  float dot[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int d = 0; d < D; d += 4) {
+    const float4 q = *(const float4*)&qs[ty][d];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 k = *(const float4*)&ks[tx + 16 * j][d];
+      dot[j] = __builtin_fmaf(q.x, k.x, dot[j]);
+      dot[j] = __builtin_fmaf(q.y, k.y, dot[j]);
+      dot[j] = __builtin_fmaf(q.z, k.z, dot[j]);
+      dot[j] = __builtin_fmaf(q.w, k.w, dot[j]);
+    }
+  }
+  const int a = a0 + ty;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int bb = b0 + tx + 16 * j;
+    if (a < Cq && bb < Ck) lc[((int64_t)bh * Ck + bb) * Cq + a] = dot[j] * c2;
+  }
 }
 
 // head_dim 128 probe: same computation as probe_kernel, with K/V staged by
@@ -644,6 +676,7 @@ __global__ void __launch_bounds__(256) probe_finalize_kernel(FinalizeArgs f) {
 // ---------------------------------------------------------------------------
 
 constexpr int kSelThreads = 1024, kSelWaves = kSelThreads / 64, kSelMaxCk = 4096;
+constexpr int kSelBatch = 8;  // 64-column chunks whose loads are issued together
 
 __device__ __forceinline__ long long wave_sum64(long long x) {
   for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -683,6 +716,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
   __shared__ long long wred[kSelWaves];
   __shared__ int nbk[kSelMaxCk];
   __shared__ int wcnt[kSelWaves];
+  __shared__ unsigned wmin[kSelWaves], wmax[kSelWaves];
   __shared__ long long sh_R;
   __shared__ unsigned int sh_prefix;
   const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -703,36 +737,98 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
   const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
   const int ra0 = min(wave * rpw, Cq), ra1 = min(ra0 + rpw, Cq);
 
-  // total cost of all non-empty blocks
+  // total cost of all non-empty blocks, and the range of their score bits
   long long part = 0;
+  unsigned bmin = 0xffffffffu, bmax = 0u;
   for (int a = ra0; a < ra1; ++a) {
     const long long na = qo[a + 1] - qo[a];
     if (na == 0) continue;
-    for (int b = lane; b < Ck; b += 64) part += na * nb_of(b);
+    const unsigned* row = sc + (int64_t)a * Ck;
+    for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
+      unsigned bits[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const int b = b0 + 64 * j + lane;
+        bits[j] = b < Ck ? row[b] : 0u;
+      }
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const int b = b0 + 64 * j + lane;
+        const int nbv = b < Ck ? nb_of(b) : 0;
+        if (nbv > 0) {
+          part += na * nbv;
+          bmin = min(bmin, bits[j]);
+          bmax = max(bmax, bits[j]);
+        }
+      }
+    }
   }
   part = wave_sum64(part);
-  if (lane == 0) wred[wave] = part;
+  for (int off = 32; off > 0; off >>= 1) {
+    bmin = min(bmin, (unsigned)__shfl_xor((int)bmin, off, 64));
+    bmax = max(bmax, (unsigned)__shfl_xor((int)bmax, off, 64));
+  }
+  if (lane == 0) {
+    wred[wave] = part;
+    wmin[wave] = bmin;
+    wmax[wave] = bmax;
+  }
   __syncthreads();
   long long total = 0;
-  for (int w = 0; w < kSelWaves; ++w) total += wred[w];
+  unsigned gmin = 0xffffffffu, gmax = 0u;
+  for (int w = 0; w < kSelWaves; ++w) {
+    total += wred[w];
+    gmin = min(gmin, wmin[w]);
+    gmax = max(gmax, wmax[w]);
+  }
   const bool take_all = total <= s.budget;
 
   unsigned T = 0;
   long long R = s.budget;
   if (!take_all) {
-    unsigned pre = 0, msk = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    // every counted block shares the leading bits where gmin and gmax agree,
+    // so the digits start right below them (the first digit is then spread
+    // over many bins instead of piling onto one)
+    const int lead = gmin == gmax ? 32 : __clz((int)(gmin ^ gmax));
+    unsigned msk = lead == 0 ? 0u : (lead == 32 ? 0xffffffffu : ~0u << (32 - lead));
+    unsigned pre = gmin & msk;
+    for (int low = 32 - lead; low > 0;) {
+      const int width = min(8, low);
+      const int shift = low - width;
+      const unsigned dmask = (1u << width) - 1u;
+      low = shift;
       for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
       __builtin_amdgcn_wave_barrier();
       for (int a = ra0; a < ra1; ++a) {
         const long long na = qo[a + 1] - qo[a];
         if (na == 0) continue;
         const unsigned* row = sc + (int64_t)a * Ck;
-        for (int b = lane; b < Ck; b += 64) {
-          const int nbv = nb_of(b);
-          const unsigned bits = row[b];
-          if (nbv > 0 && (bits & msk) == pre)
-            atomicAdd(&hist[wave][(bits >> shift) & 255u], (unsigned long long)(na * nbv));
+        for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
+          // the batch's loads are independent of the atomics below, so they are
+          // all in flight together instead of one memory latency per element
+          unsigned bits[kSelBatch];
+#pragma unroll
+          for (int j = 0; j < kSelBatch; ++j) {
+            const int b = b0 + 64 * j + lane;
+            bits[j] = b < Ck ? row[b] : 0u;
+          }
+#pragma unroll
+          for (int j = 0; j < kSelBatch; ++j) {
+            const int b = b0 + 64 * j + lane;
+            const int nbv = b < Ck ? nb_of(b) : 0;
+            const bool in = nbv > 0 && (bits[j] & msk) == pre;
+            const unsigned dig = (bits[j] >> shift) & dmask;
+            const unsigned long long inb = __ballot(in);
+            if (inb == 0) continue;
+            const unsigned d0 = (unsigned)__shfl((int)dig, __ffsll((long long)inb) - 1, 64);
+            if (__ballot(in && dig == d0) == inb) {
+              // the whole batch element falls into one bin: one atomic for the wave
+              const long long c = wave_sum64(in ? na * nbv : 0);
+              if (lane == 0) atomicAdd(&hist[wave][d0], (unsigned long long)c);
+            } else if (in) {
+              atomicAdd(&hist[wave][dig], (unsigned long long)(na * nbv));
+            }
+          }
         }
       }
       __syncthreads();
@@ -771,7 +867,7 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
       __syncthreads();
       R = sh_R;
       pre = sh_prefix;
-      msk |= 255u << shift;
+      msk |= dmask << shift;
       __syncthreads();
     }
     T = pre;
@@ -784,9 +880,19 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
       const long long na = qo[a + 1] - qo[a];
       if (na == 0) continue;
       const unsigned* row = sc + (int64_t)a * Ck;
-      for (int b = lane; b < Ck; b += 64) {
-        const int nbv = nb_of(b);
-        if (nbv > 0 && row[b] == T) tc += na * nbv;
+      for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
+        unsigned bits[kSelBatch];
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const int b = b0 + 64 * j + lane;
+          bits[j] = b < Ck ? row[b] : 0u;
+        }
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const int b = b0 + 64 * j + lane;
+          const int nbv = b < Ck ? nb_of(b) : 0;
+          if (nbv > 0 && bits[j] == T) tc += na * nbv;
+        }
       }
     }
   tc = wave_sum64(tc);
@@ -798,11 +904,23 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
   for (int a = ra0; a < ra1; ++a) {
     const long long na = qo[a + 1] - qo[a];
     const unsigned* row = sc + (int64_t)a * Ck;
+    unsigned bits_b[kSelBatch];
     for (int b0 = 0; b0 < Ck; b0 += 64) {
+      const int jb = (b0 / 64) % kSelBatch;
+      if (jb == 0) {
+#pragma unroll
+        for (int j = 0; j < kSelBatch; ++j) {
+          const int bb = b0 + 64 * j + lane;
+          bits_b[j] = bb < Ck ? row[bb] : 0u;
+        }
+      }
       const int b = b0 + lane;
       const bool valid = b < Ck;
       const long long c = valid ? na * nb_of(b) : 0;
-      const unsigned bits = valid ? row[b] : 0u;
+      unsigned bits = 0u;
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j)
+        if (j == jb) bits = bits_b[j];
       const bool tie = !take_all && c > 0 && bits == T;
       long long incl = 0;
       if (__any(tie)) incl = wave_incl_scan64(tie ? c : 0, lane);
@@ -820,12 +938,20 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
   for (int w = 0; w < wave; ++w) start += wcnt[w];
   if (tid == 0) rr[0] = 0;
   for (int a = ra0; a < ra1; ++a) {
-    for (int b0 = 0; b0 < Ck; b0 += 64) {
-      const int b = b0 + lane;
-      const bool keep = b < Ck && fl[(int64_t)a * Ck + b] != 0;
-      const unsigned long long bal = __ballot(keep);
-      if (keep) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = b;
-      start += __popcll(bal);
+    for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
+      bool keep[kSelBatch];
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const int b = b0 + 64 * j + lane;
+        keep[j] = b < Ck && fl[(int64_t)a * Ck + b] != 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kSelBatch; ++j) {
+        const int b = b0 + 64 * j + lane;
+        const unsigned long long bal = __ballot(keep[j]);
+        if (keep[j]) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = b;
+        start += __popcll(bal);
+      }
     }
     if (lane == 0) rr[a + 1] = start;
   }
@@ -1134,7 +1260,7 @@ bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s,
   p.splits = pl.splits; p.cps = pl.cps; p.c2 = scale * kLog2e;
   dim3 grid(pl.splits, s.B * s.H, (Cq + 127) / 128);
   if (pl.d128) {
-    hipLaunchKernelGGL(proxy_logit_kernel<128>, dim3((Ck + 15) / 16, (Cq + 15) / 16, s.B * s.H), dim3(256), 0,
+    hipLaunchKernelGGL(proxy_logit_kernel<128>, dim3((Ck + 63) / 64, (Cq + 15) / 16, s.B * s.H), dim3(256), 0,
                        stream, qc, kc, (float*)(w + pl.off_lc), Cq, Ck, p.c2);
     hipLaunchKernelGGL(probe_d128_kernel, grid, dim3(256), 0, stream, p);
   } else if (s.D == 128) {

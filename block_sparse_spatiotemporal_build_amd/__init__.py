@@ -58,7 +58,8 @@ _SIGNATURES = {
                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_compensated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                 ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P,
-                                                ctypes.c_float, _P]),
+                                                ctypes.c_float, _P, ctypes.c_size_t, _P]),
+    "bsa_compensated_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
     "bsa_centroid_compensate_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
                                                             ctypes.c_int32]),
     "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
@@ -308,10 +309,13 @@ def compensated_attn_fwd(q, k, v, q_off, k_off, rrow, rcol, k_cent, v_cent, scal
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device) if return_lse else None
+    need = int(lib.bsa_compensated_attn_workspace(ctypes.byref(shape), Cq, Ck))
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need > 0 else None
     _check(lib.bsa_compensated_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                         ctypes.byref(shape), _ptr(q_off), Cq, _ptr(k_off), Ck, _ptr(rrow),
                                         _ptr(rcol), _ptr(k_cent.contiguous()), _ptr(v_cent.contiguous()),
-                                        float(scale), _stream(q.device)), "bsa_compensated_attn_fwd")
+                                        float(scale), _ptr(ws), need, _stream(q.device)),
+           "bsa_compensated_attn_fwd")
     return out, lse
 
 

@@ -237,10 +237,16 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
                              route_col, (uint8_t*)workspace, (hipStream_t)stream);
 }
 
+size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
+  if (check_shape(shape, 2, "bsa_compensated_attn_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
+  return comp_attn_workspace(*shape, Ck);
+}
+
 bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dtype,
                                     const bsa_shape* shape, const int32_t* q_off, int32_t Cq, const int32_t* k_off,
                                     int32_t Ck, const int32_t* route_row_ptr, const int32_t* route_col,
-                                    const float* k_cent, const float* v_cent, float scale, void* stream) {
+                                    const float* k_cent, const float* v_cent, float scale, void* workspace,
+                                    size_t ws_bytes, void* stream) {
   const char* fn = "bsa_compensated_attn_fwd";
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
@@ -251,14 +257,17 @@ bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cent) || !aligned16(v_cent))
     return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
   if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
+  const size_t need = comp_attn_workspace(*shape, Ck);
+  if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
   g_err[0] = 0;
   return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, k_cent, v_cent,
-                          scale, (hipStream_t)stream);
+                          scale, workspace, (hipStream_t)stream);
 }
 
 // fused call: workspace = centroids | scores | probe scratch | select flags
 struct CompPlan {
-  size_t qc, kc, vc, sc, probe, flags, total;
+  size_t qc, kc, vc, sc, probe, flags, attn, total;
 };
 static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
   CompPlan p;
@@ -269,7 +278,8 @@ static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
   p.sc = align256h(p.vc + bh * Ck * D * 4);
   p.probe = align256h(p.sc + bh * Cq * Ck * 4);
   p.flags = align256h(p.probe + probe_plan(s, Cq, Ck).total);
-  p.total = align256h(p.flags + bh * Cq * Ck);
+  p.attn = align256h(p.flags + bh * Cq * Ck);
+  p.total = align256h(p.attn + comp_attn_workspace(s, Ck));
   return p;
 }
 
@@ -309,7 +319,8 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
   st = launch_route_select(sc, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
                            route_col, (uint8_t*)(w + pl.flags), sm);
   if (st != BSA_OK) return st;
-  return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale, sm);
+  return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale,
+                          w + pl.attn, sm);
 }
 
 const char* bsa_status_string(bsa_status s) {

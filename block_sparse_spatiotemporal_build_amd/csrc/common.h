@@ -75,6 +75,22 @@ constexpr int kBufferWord3 = 0x00020000;  // raw (untyped, stride 0) buffer load
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
+// Valid-row mask of the S^T accumulators of a 64-key sub-tile when only its
+// first n rows are real keys: bit 16 kt + r covers s[kt][r], whose key row is
+// 32 kt + 8 (r / 4) + 4 hi + r % 4 (hi = lane / 32).  Built from n with
+// immediates only, so that the per-element tests need no per-element registers.
+__device__ __forceinline__ uint32_t tile_row_mask(int n, int hi) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = min(max(n - (32 * kt + 8 * g + 4 * hi), 0), 4);
+      m |= ((1u << c) - 1u) << (16 * kt + 4 * g);
+    }
+  return m;
+}
+
 // Online softmax with a lazily moved reference: the running maximum used as
 // the exponent reference is replaced only when a new score exceeds it by more
 // than this many powers of two, so weights stay below 2^8 and the O/l rescale

@@ -972,6 +972,8 @@ struct CompArgs {
   const float* k_cent;
   const float* v_cent;
   float scale, c2;
+  const uint16_t* kc_bf;  // head_dim 128 path: bf16 copies of k_cent / v_cent, [BH][Ck][D]
+  const uint16_t* vc_bf;
 };
 
 template <int D>
@@ -1196,6 +1198,314 @@ comp_attn_kernel(CompArgs p) {
   }
 }
 
+// bf16 copies of the key / value centroids (the virtual keys and values of the
+// head_dim-128 compensated attention are staged from them like real rows).
+__global__ void __launch_bounds__(256) centroid_bf16_kernel(const float* k_cent, const float* v_cent,
+                                                            uint16_t* kc_bf, uint16_t* vc_bf, int64_t n2) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // pair of elements
+  if (i < n2) {
+    const float2 k = reinterpret_cast<const float2*>(k_cent)[i];
+    const float2 v = reinterpret_cast<const float2*>(v_cent)[i];
+    reinterpret_cast<uint32_t*>(kc_bf)[i] = pack_bf16x2(k.x, k.y);
+    reinterpret_cast<uint32_t*>(vc_bf)[i] = pack_bf16x2(v.x, v.y);
+  }
+}
+
+// head_dim 128 compensated attention.  Same online-softmax core and staging
+// as attn_bf16_d128_kernel: 64-key sub-tiles copied straight to two swizzled
+// LDS stages (separate objects, loop unrolled by two).  Sub-tile u < ne holds
+// the concatenated keys of the kept clusters of the row's query cluster (each
+// staged row is gathered: slot -> kept cluster through a per-lane cursor over
+// the kept-size prefix cum[], -> key row); sub-tiles u >= ne hold the virtual
+// keys, one per key cluster b (bf16 centroid rows), whose logit gets the bias
+// ln(n_b) / scale, or -inf when b is kept or empty.
+constexpr int kCaMaxCk = 512;
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+comp_attn_d128_kernel(CompArgs p) {
+  constexpr int D = 128, KT = 8, DT = 4, TILE = kCaBN * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
+  __shared__ int cum[kCaMaxCk + 1];    // prefix of kept cluster sizes
+  __shared__ int kstart[kCaMaxCk];     // first key row of each kept cluster
+  __shared__ float bias[kCaMaxCk];     // virtual-key logit bias (raw units) or -inf
+  __shared__ int scan[256];
+  __shared__ int sh_tile[3];
+
+  const SvgArgs& a = p.s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int bh = blockIdx.y;
+  const int32_t* qo = a.q_off + (int64_t)bh * (a.Cq + 1);
+  const int32_t* ko = a.k_off + (int64_t)bh * (a.Ck + 1);
+
+  // ---- which query cluster and rows this workgroup covers: tiles of 128 rows
+  // per cluster, numbered cluster by cluster (parallel count + scan)
+  if (tid == 0) sh_tile[0] = -1;
+  const int per = (a.Cq + 255) / 256;
+  const int c0 = min(tid * per, a.Cq), c1 = min(c0 + per, a.Cq);
+  int cnt = 0;
+  for (int c = c0; c < c1; ++c) cnt += (qo[c + 1] - qo[c] + 127) / 128;
+  scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  {
+    const int x = blockIdx.x;
+    int t0 = scan[tid] - cnt;
+    if (x >= t0 && x < t0 + cnt) {
+      for (int c = c0; c < c1; ++c) {
+        const int nt = (qo[c + 1] - qo[c] + 127) / 128;
+        if (x < t0 + nt) {
+          sh_tile[0] = c;
+          sh_tile[1] = qo[c] + 128 * (x - t0);
+          sh_tile[2] = qo[c + 1];
+          break;
+        }
+        t0 += nt;
+      }
+    }
+  }
+  __syncthreads();
+  // workgroup-uniform values read from LDS are moved to scalar registers
+  const int ca = __builtin_amdgcn_readfirstlane(sh_tile[0]);
+  if (ca < 0) return;  // beyond the last query tile of this head (uniform)
+  const int r0 = __builtin_amdgcn_readfirstlane(sh_tile[1]), r1 = __builtin_amdgcn_readfirstlane(sh_tile[2]);
+
+  // ---- kept clusters of row ca (a caller-given route is clamped into range so
+  // every table index and every staged row stays in bounds)
+  const int rb = __builtin_amdgcn_readfirstlane(max(0, min(p.rrow[(int64_t)bh * (a.Cq + 1) + ca], a.Cq * a.Ck)));
+  const int nk = __builtin_amdgcn_readfirstlane(
+      max(0, min(p.rrow[(int64_t)bh * (a.Cq + 1) + ca + 1] - rb, min(a.Ck, a.Cq * a.Ck - rb))));
+  const int32_t* cl = p.rcol + (int64_t)bh * a.Cq * a.Ck + rb;
+  for (int b = tid; b < a.Ck; b += 256) {
+    const int n = ko[b + 1] - ko[b];
+    bias[b] = n > 0 ? __logf((float)n) / p.scale : -__builtin_inff();
+  }
+  // prefix of kept sizes: thread t holds entries 2t, 2t + 1 (nk <= 512)
+  int sz[2] = {0, 0};
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int i = 2 * tid + e;
+    if (i < nk) {
+      const int b = max(0, min(cl[i], a.Ck - 1));
+      sz[e] = ko[b + 1] - ko[b];
+      kstart[i] = ko[b];
+    }
+  }
+  scan[tid] = sz[0] + sz[1];
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  {
+    const int ex = scan[tid] - sz[0] - sz[1];
+    if (2 * tid < nk) cum[2 * tid] = ex;
+    if (2 * tid + 1 < nk) cum[2 * tid + 1] = ex + sz[0];
+    if (tid == 255) cum[nk] = scan[255];
+  }
+  __syncthreads();
+  for (int i = tid; i < nk; i += 256) bias[max(0, min(cl[i], a.Ck - 1))] = -__builtin_inff();
+  const int E = __builtin_amdgcn_readfirstlane(cum[nk]);
+  const int ne = (E + kCaBN - 1) / kCaBN;
+  const int nv = (a.Ck + kCaBN - 1) / kCaBN;
+  const int nsub = ne + nv;
+
+  // ---- query fragments (rows past the cluster end are computed, not stored)
+  const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
+  const int qrow = r0 + wave * 32 + l32;
+  bf16x8 qf[KT];
+  {
+    const uint16_t* src = a.q + head_off + (int64_t)min(qrow, a.N - 1) * a.sn + hi * 8;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + t * 16));
+  }
+  retire_loads();
+  __syncthreads();  // cum, kstart and bias complete
+
+  // ---- copy roles: wave w, instruction j covers tile rows 16w + 4j + lane/16
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t kcs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.kc_bf + (int64_t)bh * a.Ck * D), (short)0, a.Ck * D * 2, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vcs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(p.vc_bf + (int64_t)bh * a.Ck * D), (short)0, a.Ck * D * 2, kBufferWord3);
+  // a lane stages rows 16w + 4j + lane/16 (j = 0..3): increasing slots, so one
+  // cursor (kept-list index of the cluster holding the slot) serves all four.
+  // For those rows swz_k(row) = 4j + lane/16 and swz_v(row) = 4 (lane/16) + j,
+  // so the swizzled chunk offsets are one per-lane base XOR an immediate.
+  int cur = 0;
+  const uint32_t kbase = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
+  const uint32_t vbase = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int u) {
+    if (u < ne) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * wv + 4 * j + (lane >> 4);
+        const int slot = min(u * kCaBN + row, E - 1);  // slots past E are masked below
+        while (cur + 1 < nk && cum[cur + 1] <= slot) ++cur;
+        const uint32_t ro = (uint32_t)(kstart[cur] + slot - cum[cur]) * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (kbase ^ (64u * j)), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (vbase ^ (16u * j)), 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * wv + 4 * j + (lane >> 4);
+        const int b = min((u - ne) * kCaBN + row, a.Ck - 1);  // clusters past Ck are masked below
+        const uint32_t ro = (uint32_t)b * (D * 2);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kcs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (kbase ^ (64u * j)), 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vcs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (vbase ^ (16u * j)), 0, 0, 0);
+      }
+    }
+  };
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) o[i] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+  const float c2 = p.c2;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  // LDS element offsets of the swizzled stage reads, as one per-lane base and
+  // an XOR / add of immediates (keeps a handful of address registers live):
+  //   K fragment (kt, t):        4096 kt + (kaddr ^ 16 t)
+  //   V transpose read (ks, dt): 2048 ks + (vaddr ^ 32 dt)  (+ vdelta for rows + 8)
+  const int kaddr = l32 * 128 + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1));
+  const int vq = j16 >> 2, vc1 = (2 * (g16 & 1) + ((j16 >> 1) & 1)) ^ hi;
+  const int vaddr = (4 * hi + vq) * 128 + 32 * vq + 8 * vc1 + (j16 & 1) * 4;
+  const int vdelta = 1024 + 8 * ((vc1 ^ 2) - vc1);
+
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed, other stage drained
+    __builtin_amdgcn_s_barrier();
+    if (u + 1 < nsub) dma(Kn, Vn, u + 1);
+
+    f32x16 s[2];
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+    bf16x8 kfr[2][KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) kfr[kt][t] = *(const bf16x8*)&Kb[4096 * kt + (kaddr ^ (16 * t))];
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kfr[kt][t], qf[t], s[kt], 0, 0, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+
+    // key of s[kt][r]: tile row kt 32 + 8 (r / 4) + 4 hi + r % 4
+    if (u < ne) {
+      if ((u + 1) * kCaBN > E) {
+        const uint32_t vm = tile_row_mask(E - u * kCaBN, hi);
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (!((vm >> (16 * kt + r)) & 1u)) s[kt][r] = -__builtin_inff();
+      }
+    } else {
+      const int bb = (u - ne) * kCaBN + 4 * hi;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int b = bb + kt * 32 + 8 * (r >> 2) + (r & 3);
+          s[kt][r] = b < a.Ck ? s[kt][r] + bias[b] : -__builtin_inff();
+        }
+    }
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int r = 2; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+    const float m_new = fmaxf(m_run, pair_max(mx));
+    if (__any((m_new - m_run) * c2 > kLazyRescaleLog2)) {
+      const float alpha = fast_exp2((m_run - m_new) * c2);
+      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < DT; ++i) o[i] *= alpha;
+      m_run = m_new;
+    }
+    const float mc = m_run * c2;
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pr = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
+        s[kt][r] = pr;
+        psum += pr;
+      }
+    l_run += psum;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks >> 1, q0 = (ks & 1) * 8;
+      u32x4 w;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kt][q0 + 2 * e], s[kt][q0 + 2 * e + 1]);
+      pf[ks] = __builtin_bit_cast(bf16x8, w);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const int va = 2048 * ks + (vaddr ^ (32 * dt));
+        const u32x2 lo = lds_tr16(&Vb[va]);
+        const u32x2 h2 = lds_tr16(&Vb[va + vdelta]);
+        const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
+        o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
+      }
+  };
+
+  dma(K0, V0, 0);  // nsub >= 1 (Ck >= 1)
+  int u = 0;
+  for (; u + 2 <= nsub; u += 2) {
+    step(K0, V0, K1, V1, u);
+    step(K1, V1, K0, V0, u + 1);
+  }
+  if (u < nsub) step(K0, V0, K1, V1, u);
+
+  const float l_tot = pair_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < r1) {
+    uint16_t* dst = p.o + head_off + (int64_t)qrow * a.sn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = dt * 32 + 8 * g + 4 * hi;
+        u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                   pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+        *(u32x2*)(dst + d0) = w;
+      }
+    if (p.lse != nullptr && hi == 0)
+      p.lse[(int64_t)bh * a.N + qrow] =
+          l_tot > 0.f ? (m_run * c2 + __builtin_log2f(l_tot)) * kLn2 : -__builtin_inff();
+  }
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
@@ -1283,19 +1593,42 @@ bsa_status launch_route_select(const float* score, const bsa_shape& s, const int
   return launch_ok("route_select") ? BSA_OK : BSA_ERR_HIP;
 }
 
+static bool comp_d128(const bsa_shape& s) {
+  return s.D == 128 && ((int64_t)s.N + kCaBN) * s.stride_n * 2 < ((int64_t)1 << 31);
+}
+
+size_t comp_attn_workspace(const bsa_shape& s, int Ck) {
+  if (!comp_d128(s)) return 0;
+  return 2 * al256((size_t)s.B * s.H * Ck * s.D * 2);
+}
+
 bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
                             const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
-                            const int32_t* rcol, const float* kc, const float* vc, float scale,
+                            const int32_t* rcol, const float* kc, const float* vc, float scale, void* ws,
                             hipStream_t stream) {
   CompArgs p;
   p.s = svg_args(q, k, v, s, q_off, Cq, k_off, Ck);
   p.o = (uint16_t*)o; p.lse = lse; p.rrow = rrow; p.rcol = rcol; p.k_cent = kc; p.v_cent = vc;
   p.scale = scale; p.c2 = scale * kLog2e;
+  p.kc_bf = nullptr; p.vc_bf = nullptr;
   const int max_tiles = (s.N + 127) / 128 + Cq;
   dim3 grid(max_tiles, s.B * s.H);
-  if (s.D == 128) hipLaunchKernelGGL(comp_attn_kernel<128>, grid, dim3(256), 0, stream, p);
-  else if (s.D == 64) hipLaunchKernelGGL(comp_attn_kernel<64>, grid, dim3(256), 0, stream, p);
-  else return BSA_ERR_UNSUPPORTED;
+  if (comp_d128(s)) {
+    const size_t half = al256((size_t)s.B * s.H * Ck * s.D * 2);
+    uint16_t* kb = (uint16_t*)ws;
+    uint16_t* vb = (uint16_t*)((char*)ws + half);
+    const int64_t n2 = (int64_t)s.B * s.H * Ck * s.D / 2;
+    hipLaunchKernelGGL(centroid_bf16_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, kc, vc, kb,
+                       vb, n2);
+    p.kc_bf = kb; p.vc_bf = vb;
+    hipLaunchKernelGGL(comp_attn_d128_kernel, grid, dim3(256), 0, stream, p);
+  } else if (s.D == 128) {
+    hipLaunchKernelGGL(comp_attn_kernel<128>, grid, dim3(256), 0, stream, p);
+  } else if (s.D == 64) {
+    hipLaunchKernelGGL(comp_attn_kernel<64>, grid, dim3(256), 0, stream, p);
+  } else {
+    return BSA_ERR_UNSUPPORTED;
+  }
   return launch_ok("compensated_attn_fwd") ? BSA_OK : BSA_ERR_HIP;
 }
 

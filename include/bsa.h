@@ -218,13 +218,21 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
  * a and one virtual key per skipped non-empty cluster b (key k_cent[b], value
  * v_cent[b], logit scale * q . k_cent[b] + ln n_b), i.e. the n_b keys of a
  * skipped cluster are replaced by n_b copies of their centroid.  o (bf16) and
- * lse (nullable fp32 [B, H, N]) are in the cluster order of q.  Ck <= 512. */
+ * lse (nullable fp32 [B, H, N]) are in the cluster order of q.  Ck <= 512.
+ * The centroids enter the dot products rounded to bf16, like any key.
+ * workspace: at least bsa_compensated_attn_workspace bytes, 256-byte aligned
+ * (may be NULL when that is 0). */
 bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                                     bsa_dtype dtype, const bsa_shape* shape, const int32_t* q_off,
                                     int32_t Cq, const int32_t* k_off, int32_t Ck,
                                     const int32_t* route_row_ptr, const int32_t* route_col,
                                     const float* k_cent, const float* v_cent, float scale,
-                                    void* stream);
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of bsa_compensated_attn_fwd: bf16 copies of the key and value
+ * centroids (the virtual keys and values) for head_dim 128; 0 otherwise (then
+ * workspace may be NULL).  0 for an invalid shape as well. */
+size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
 
 /* Workspace bytes of bsa_centroid_compensate (0 for an invalid shape). */
 size_t bsa_centroid_compensate_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);

@@ -388,20 +388,23 @@ attn_bf16_d128_kernel(AttnArgs a) {
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, 0x7fffffff, kBufferWord3);
-  uint32_t koff[4], voff[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int row = 16 * wv + 4 * j + (lane >> 4);
-    koff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16);
-    voff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
-  }
+  // For rows 16w + 4j + lane/16: swz_k(row) = 4j + lane/16 and swz_v(row) =
+  // 4 (lane/16) + j, so the swizzled 16-byte chunk offsets are one per-lane
+  // base XOR an immediate, and the row offsets one per-lane base plus a
+  // uniform multiple of 4 rows (few registers live across the loop).
+  const uint32_t rbase = (uint32_t)(16 * wv + (lane >> 4)) * row_bytes;
+  const uint32_t kbase = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
+  const uint32_t vbase = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
   auto dma = [&](uint16_t* kst, uint16_t* vst, int key0) {
     if (key0 + kBN <= N) {
       const uint32_t so = (uint32_t)key0 * row_bytes;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, koff[j], so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, voff[j], so, 0, 0);
+        const uint32_t ro = rbase + (uint32_t)(4 * j) * row_bytes;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (kbase ^ (64u * j)), so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                 ro + (vbase ^ (16u * j)), so, 0, 0);
       }
     } else {  // tail sub-tile: rows past N are clamped to row N - 1 (masked below)
 #pragma unroll
@@ -409,9 +412,9 @@ attn_bf16_d128_kernel(AttnArgs a) {
         const int row = 16 * wv + 4 * j + (lane >> 4);
         const uint32_t ro = (uint32_t)min(key0 + row, N - 1) * row_bytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
-                                                 ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
+                                                 ro + (kbase ^ (64u * j)), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
-                                                 ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
+                                                 ro + (vbase ^ (16u * j)), 0, 0, 0);
       }
     }
   };
@@ -422,6 +425,14 @@ attn_bf16_d128_kernel(AttnArgs a) {
   float m_run = -1e30f, l_run = 0.f;
   const float c2 = a.scale_log2;
   const int g16 = lane >> 4, j16 = lane & 15;
+  // LDS element offsets of the swizzled stage reads, as one per-lane base and
+  // an XOR / add of immediates:
+  //   K fragment (kt, t):        4096 kt + (kaddr ^ 16 t)
+  //   V transpose read (ks, dt): 2048 ks + (vaddr ^ 32 dt)  (+ vdelta for rows + 8)
+  const int kaddr = l32 * 128 + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1));
+  const int vq = j16 >> 2, vc1 = (2 * (g16 & 1) + ((j16 >> 1) & 1)) ^ hi;
+  const int vaddr = (4 * hi + vq) * 128 + 32 * vq + 8 * vc1 + (j16 & 1) * 4;
+  const int vdelta = 1024 + 8 * ((vc1 ^ 2) - vc1);
 
   // One 64-key sub-tile u held in (Kb, Vb); the copy of sub-tile u + 1 goes to
   // (Kn, Vn) as soon as every wave has passed the barrier (they have all
@@ -440,10 +451,7 @@ attn_bf16_d128_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int row = kt * 32 + l32;
-        kfr[kt][t] = *(const bf16x8*)&Kb[row * D + (((2 * t + hi) ^ swz_k(row)) << 3)];
-      }
+      for (int kt = 0; kt < 2; ++kt) kfr[kt][t] = *(const bf16x8*)&Kb[4096 * kt + (kaddr ^ (16 * t))];
 #pragma unroll
     for (int t = 0; t < KT; ++t)
 #pragma unroll
@@ -457,12 +465,12 @@ attn_bf16_d128_kernel(AttnArgs a) {
     __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
 
     if (key0 + kBN > N) {  // key row of s[kt][r]: key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4
-      const int lim = N - key0 - 4 * hi;
+      const uint32_t vm = tile_row_mask(N - key0, hi);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (kt * 32 + 8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -__builtin_inff();
+          if (!((vm >> (16 * kt + r)) & 1u)) s[kt][r] = -__builtin_inff();
     }
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
@@ -503,11 +511,9 @@ attn_bf16_d128_kernel(AttnArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
-        const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-        const int half = (j16 & 1) * 4;
-        const u32x2 lo = lds_tr16(&Vb[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
-        const u32x2 h2 = lds_tr16(&Vb[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+        const int va = 2048 * ks + (vaddr ^ (32 * dt));
+        const u32x2 lo = lds_tr16(&Vb[va]);
+        const u32x2 h2 = lds_tr16(&Vb[va + vdelta]);
         const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
       }

@@ -506,7 +506,11 @@ attn_bf16_d128_kernel(AttnArgs a) {
       pf[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
-    // O^T += V^T P^T with the transpose reads of the swizzled V stage
+    // O^T += V^T P^T with the transpose reads of the swizzled V stage.  The
+    // wave raises its issue priority for this block: the two waves sharing a
+    // SIMD (from different workgroups) then drift out of phase, one wave's
+    // softmax running under the other's matrix work.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -517,6 +521,7 @@ attn_bf16_d128_kernel(AttnArgs a) {
         const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   if (nsub > 0) dma(K0, V0, key0_of(0));

@@ -65,6 +65,7 @@ struct AttnArgs {
   const int32_t* row_order;  // nullable: schedule of query-block rows, int32[nb + 1]
   int64_t sb, sh, sn;
   int B, H, N, block, nb;
+  int head_major;    // 1: rows of one head are dealt round-robin over the XCDs (see map_work)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -84,9 +85,14 @@ __device__ __forceinline__ int xcd_contiguous(int j, int S, int R) {
 }
 
 // Work item (query block, head, batch) of workgroup `pid`.
-//  * Rows not singled out below: each XCD gets a contiguous range of the
-//    (batch, head, query block) list, so the workgroups sharing an L2 walk
-//    neighbouring query blocks of one head and reuse their key blocks.
+//  * Rows not singled out below, default: each XCD gets a contiguous range of
+//    the (batch, head, query block) list, so the workgroups sharing an L2 walk
+//    neighbouring query blocks of one head and reuse their key blocks.  The
+//    eight XCDs then work on eight different heads at a time.
+//  * head_major: the list is taken in launch order, so at any time all XCDs
+//    work on neighbouring query blocks of the same head.  The launcher picks
+//    this when eight heads of K and V would not fit the last-level cache: the
+//    key blocks that miss in one XCD's L2 are then found in that cache.
 //  * With a row order whose first nh = row_order[nb] rows are long ones (LVSA
 //    anchor rows are about twice the mean length): those rows, for every head,
 //    take the first nh * H * B workgroups, so they start in the first wave and
@@ -106,12 +112,20 @@ __device__ __forceinline__ WorkItem map_work(const AttnArgs& a) {
       return WorkItem{ord[pid / hb], r % a.H, r / a.H};
     }
     const int rest = a.nb - nh;
-    const int item = xcd_contiguous(pid - S, S, total - S);
+    const int item = a.head_major ? pid - S : xcd_contiguous(pid - S, S, total - S);
     const int r = item / rest;
     return WorkItem{ord[nh + item % rest], r % a.H, r / a.H};
   }
-  const int item = xcd_contiguous(pid, 0, total);
+  const int item = a.head_major ? pid : xcd_contiguous(pid, 0, total);
   return WorkItem{item % a.nb, (item / a.nb) % a.H, item / (a.nb * a.H)};
+}
+
+// Last-level cache (Infinity Cache) capacity used by the mapping choice above.
+constexpr int64_t kLastLevelCacheBytes = 256ll << 20;
+// Eight heads of K and V in flight (one per XCD) would not fit that cache.
+inline int choose_head_major(const bsa_shape& s, int elem_bytes) {
+  const int64_t kv_per_head = 2 * (int64_t)s.N * s.D * elem_bytes;
+  return 8 * kv_per_head > kLastLevelCacheBytes ? 1 : 0;
 }
 
 template <int D, int BM>
@@ -650,6 +664,7 @@ bsa_status launch_attn_bf16(const void* q, const void* k, const void* v, void* o
   a.lse = lse; a.row_ptr = row_ptr; a.col_idx = col_idx; a.row_order = row_order;
   a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
   a.B = s.B; a.H = s.H; a.N = s.N; a.block = block; a.nb = (s.N + block - 1) / block;
+  a.head_major = choose_head_major(s, 2);
   a.scale_log2 = scale * kLog2e;
   dim3 grid((unsigned)((int64_t)a.nb * s.H * s.B));
   // the buffer-load kernel addresses a head with 32-bit offsets

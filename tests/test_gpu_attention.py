@@ -109,6 +109,38 @@ def test_row_order_only_schedules(gpu_lib, D, block):
         assert torch.equal(results[0][0], o2) and torch.equal(results[0][1], l2)
 
 
+def test_head_major_mapping_covers_every_row(gpu_lib):
+    """Past 8 heads of K and V above the 256 MiB last-level cache (here N = 70000,
+    D = 128) the launcher deals the rows of one head over the XCDs in launch
+    order.  Every row must still be written exactly once with the same bits under
+    any row schedule, and sampled rows must match the oracle."""
+    wl = gen.scaled(get_workload("lvsa_32k"), H=2, D=128, frames=70, frame_h=25, frame_w=40, seed=41)
+    assert 8 * 2 * wl.N * wl.D * 2 > 256 << 20
+    d = gen.make_qkv(wl)
+    p = dict(kind=1, frames=70, frame_tokens=1000, block=128, window=1, anchor_period=16,
+             anchor_step=3, anchor_rows=1, radial_w=0)
+    q, k, v = (to_device(d[n], wl.dtype) for n in ("q", "k", "v"))
+    rp, ci, ro = gpu_lib.build_block_mask(p, with_order=True)
+    nb = rp.numel() - 1
+    r = np.random.default_rng(9)
+    rand = np.concatenate([r.permutation(nb), [r.integers(0, nb + 1)]]).astype(np.int32)
+    results = []
+    for sched in (ro, None, torch.from_numpy(rand).cuda()):
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full(q.shape[:3], float("nan"), device=q.device)
+        gpu_lib.block_sparse_attn_fwd(q, k, v, rp, ci, 128, out=out, lse=lse, row_order=sched)
+        torch.cuda.synchronize()
+        assert not torch.isnan(out).any() and not torch.isnan(lse).any()
+        results.append((out.view(torch.int16).clone(), lse.clone()))
+    for o2, l2 in results[1:]:
+        assert torch.equal(results[0][0], o2) and torch.equal(results[0][1], l2)
+    blocks = [0, nb // 2, nb - 1]
+    ref, _ = _oracle(d, wl, p, query_blocks=blocks)
+    rows = _rows(blocks, 128, wl.N)
+    got = results[0][0].view(torch.bfloat16).float().cpu().numpy()
+    assert_parity(got[:, :, rows], ref[:, :, rows], "bf16", "head-major mapping")
+
+
 def test_bf16_tiny_sequence_shorter_than_a_block(gpu_lib):
     wl = gen.scaled(get_workload("lvsa_32k"), H=1, frames=1, frame_h=3, frame_w=7, seed=22)
     d = gen.make_qkv(wl)

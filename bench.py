@@ -53,6 +53,10 @@ def parse_args():
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
                     help="copy: run a plain device copy of known size (HBM counter calibration)")
+    ap.add_argument("--no-refs", action="store_true",
+                    help="skip the measured references (sustained bf16 GEMM, 1 GiB copy)")
+    ap.add_argument("--cold-calls", type=int, default=10,
+                    help="attention calls timed after a 512 MiB scratch write each (cold caches)")
     return ap.parse_args()
 
 
@@ -73,9 +77,10 @@ def kept_flops_from_csr(row_ptr, col_idx, N, block, D, B, H) -> int:
     return 4 * D * pairs * B * H
 
 
-def read_traffic(workload: str):
-    """HBM bytes per attention launch from a committed counter profile of this kernel source."""
-    path = os.path.join(PROFILES, f"attn_bf16_{workload}.hbm_counters.txt")
+def read_traffic(workload: str, profile: str = "attn_bf16", src: str = KERNEL_SRC):
+    """HBM bytes per launch from a committed counter profile taken with this kernel
+    source (None when there is none, or the source changed since)."""
+    path = os.path.join(PROFILES, f"{profile}_{workload}.hbm_counters.txt")
     if not os.path.exists(path):
         return None
     fields = {}
@@ -83,12 +88,49 @@ def read_traffic(workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("kernel_source_sha256") != source_hash():
+    if fields.get("kernel_source_sha256") != source_hash(src):
         return None
     try:
         return int(float(fields["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def _events_ms(fn, calls, warm):
+    import torch
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(calls):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / calls
+
+
+def measure_gemm_tflops():
+    """Sustained dense bf16 matrix rate of this GPU as the vendor GEMM reaches it:
+    torch.matmul of two contiguous 8192 x 8192 bf16 matrices, about 0.5 s of
+    back-to-back calls after as long a warm-up (the clock settles under load)."""
+    import torch
+    n = 8192
+    a = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, device="cuda").to(torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    ms = _events_ms(lambda: torch.matmul(a, b, out=c), 600, 600)
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
+def measure_copy_gbs():
+    """Read + write GB/s of a plain 1 GiB device copy (the measured HBM ceiling)."""
+    import torch
+    n = 1 << 30
+    src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _events_ms(lambda: dst.copy_(src), 10, 3)
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def cpu_baseline(wl, d, params, budget_s: float):
@@ -182,6 +224,9 @@ def bench_linear(args, wl):
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
     algo_bytes = 4 * wl.B * wl.H * wl.N * wl.D * 2
     gbs = algo_bytes / (call_ms * 1e-3) / 1e9
+    copy = None if args.no_refs else measure_copy_gbs()
+    src = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "linear_attn.hip")
+    traffic = read_traffic(wl.name, "linear_attn", src)
     return {
         "metric": "algorithmic HBM GB/s of elu+1 linear attention",
         "value": round(algo_bytes * args.steps / (t1 - t0) / 1e9, 1),
@@ -195,7 +240,10 @@ def bench_linear(args, wl):
                    "algorithmic_bytes": algo_bytes},
         "roofline": {"bound": "hbm", "kernel": "linear_attn_fwd (state + reduce + apply)",
                      "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "measured_copy": None if copy is None else {
+            "kernel": "1 GiB device copy, read + write", "gbs": round(copy, 1),
+            "frac_of_copy": round(gbs / copy, 4)},
     }
 
 
@@ -274,6 +322,10 @@ def bench_svg(args, wl):
     route_bytes = 3 * wl.B * wl.H * wl.N * wl.D * 2
     route_ms = cent_ms + score_ms + sel_ms
     achieved = attn_flop / (attn_ms * 1e-3) / 1e12
+    route_gbs = route_bytes / (route_ms * 1e-3) / 1e9
+    copy = None if args.no_refs else measure_copy_gbs()
+    gemm = None if args.no_refs else measure_gemm_tflops()
+    src = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "svg_ear.hip")
     return {
         "metric": "ms per centroid-compensated attention call (routing + attention)",
         "value": round(call_ms, 4), "unit": "ms", "higher_is_better": False,
@@ -281,15 +333,21 @@ def bench_svg(args, wl):
         "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
         "ms_split": {"centroids": round(cent_ms, 4), "route_scores": round(score_ms, 4),
                      "route_select": round(sel_ms, 4), "compensated_attn": round(attn_ms, 4)},
-        "routing_gbs": round(route_bytes / (route_ms * 1e-3) / 1e9, 1),
-        "routing_frac_of_hbm": round(route_bytes / (route_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "routing_gbs": round(route_gbs, 1),
+        "routing_frac_of_hbm": round(route_gbs / HBM_PEAK_GBS, 4),
+        "routing_frac_of_copy": None if copy is None else round(route_gbs / copy, 4),
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
                    "Cq": wl.n_q_clusters, "Ck": wl.n_k_clusters, "density_ppm": wl.density_ppm,
                    "attn_gflop": round(attn_flop / 1e9, 2), "routing_bytes": route_bytes},
-        "roofline": {"bound": "mfma", "kernel": "comp_attn_kernel<128>", "achieved": round(achieved, 2),
+        "roofline": {"bound": "mfma", "kernel": "comp_attn_d128_kernel", "achieved": round(achieved, 2),
                      "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": None},
+                     "traffic": read_traffic(wl.name, "comp_attn", src)},
+        "measured_copy": None if copy is None else {"kernel": "1 GiB device copy, read + write",
+                                                    "gbs": round(copy, 1)},
+        "measured_peak": None if gemm is None else {
+            "kernel": "sustained bf16 GEMM 8192^3 (torch.matmul)", "tflops": round(gemm, 1),
+            "attn_frac_of_measured": round(achieved / gemm, 4)},
     }
 
 
@@ -373,6 +431,23 @@ def main():
     achieved = float(np.mean(step_flops)) / (attn_avg_ms * 1e-3) / 1e12
     traffic = read_traffic(wl.name)
 
+    # cold caches: a 512 MiB scratch write before each timed attention call
+    cold_ms = []
+    if args.cold_calls > 0:
+        scratch = torch.empty(128 << 20, dtype=torch.float32, device=dev)
+        for i in range(args.cold_calls):
+            p = params[i % len(params)]
+            bsa.build_block_mask(p, row_ptr=rp, col_idx=ci, row_order=ro)
+            scratch.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            bsa.block_sparse_attn_fwd(q, k, v, rp, ci, wl.block, out=out, lse=lse, row_order=ro)
+            e1.record()
+            torch.cuda.synchronize(dev)
+            cold_ms.append(e0.elapsed_time(e1))
+        del scratch
+    gemm = None if args.no_refs else measure_gemm_tflops()
+
     result = {
         "metric": "ms/attn call and effective TFLOP/s at 32K video tokens; % of bf16 MFMA peak",
         "value": round(sum(step_flops) / total_s / 1e12, 3),
@@ -382,8 +457,10 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(total_s * 1e3 / args.steps, 4),
         "ms_per_attn_call": round(attn_avg_ms, 4),
+        "ms_per_attn_call_median": round(float(np.median(attn_ms)), 4),
         "ms_per_attn_call_p10_p90": [round(float(np.percentile(attn_ms, 10)), 4),
                                      round(float(np.percentile(attn_ms, 90)), 4)],
+        "ms_per_attn_call_cold_median": round(float(np.median(cold_ms)), 4) if cold_ms else None,
         "ms_per_mask_build": round(float(np.mean(mask_ms)), 4),
         "pct_of_bf16_mfma_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
         "higher_is_better": True,
@@ -400,6 +477,10 @@ def main():
                      "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": traffic},
     }
+    if gemm is not None:
+        result["measured_peak"] = {"kernel": "sustained bf16 GEMM 8192^3 (torch.matmul)",
+                                   "tflops": round(gemm, 1),
+                                   "attn_frac_of_measured": round(achieved / gemm, 4)}
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, d, params[0], args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -1389,10 +1389,15 @@ comp_attn_d128_kernel(CompArgs p) {
   const int vaddr = (4 * hi + vq) * 128 + 32 * vq + 8 * vc1 + (j16 & 1) * 4;
   const int vdelta = 1024 + 8 * ((vc1 ^ 2) - vc1);
 
+  // a wave whose 32 rows all lie past the cluster end (the ragged last tile of
+  // a cluster) only takes its share of the copies: its SIMD is left to the
+  // co-resident wave of another workgroup
+  const bool wave_live = r0 + 32 * wv < r1;
   auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed, other stage drained
     __builtin_amdgcn_s_barrier();
     if (u + 1 < nsub) dma(Kn, Vn, u + 1);
+    if (!wave_live) return;
 
     f32x16 s[2];
     s[0] = f32x16{};
@@ -1467,6 +1472,9 @@ comp_attn_d128_kernel(CompArgs p) {
       for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kt][q0 + 2 * e], s[kt][q0 + 2 * e + 1]);
       pf[ks] = __builtin_bit_cast(bf16x8, w);
     }
+    // raised issue priority over the PV block (co-resident waves drift out of
+    // phase, softmax under matrix work)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
@@ -1477,6 +1485,7 @@ comp_attn_d128_kernel(CompArgs p) {
         const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
       }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   dma(K0, V0, 0);  // nsub >= 1 (Ck >= 1)

@@ -1,0 +1,94 @@
+"""Host check of the LDS / copy addressing used by the head_dim-128 kernels
+(`csrc/attn_fwd.hip`, `csrc/svg_ear.hip`, `csrc/common.h`).
+
+The kernels stage 64-row tiles of K and V (row = 128 bf16 = 16 chunks of 16 B)
+with a per-row chunk permutation, and compute every per-lane address as one
+lane base XOR / plus a compile-time immediate.  These tests restate the direct
+definitions (swizzle of a row, MFMA operand layouts, accumulator rows) and check
+the closed forms against them for every lane, exhaustively.  No GPU involved.
+"""
+
+import itertools
+
+
+def swz_k(row):
+    return row & 15
+
+
+def swz_v(row):
+    return 4 * (row & 3) + ((row >> 2) & 3)
+
+
+def phys(row, col, swz):
+    """Element offset of logical (row, col) in a swizzled 64 x 128 bf16 stage."""
+    return row * 128 + 8 * ((col // 8) ^ swz(row)) + col % 8
+
+
+def test_swizzles_are_permutations_of_the_chunks():
+    for row in range(64):
+        assert sorted(c ^ swz_k(row) for c in range(16)) == list(range(16))
+        assert sorted(c ^ swz_v(row) for c in range(16)) == list(range(16))
+
+
+def test_copy_offsets_xor_form():
+    """Copy role: wave w, instruction j, lane l stages tile row 16w + 4j + l/16 at
+    physical chunk l % 16, i.e. logical chunk (l % 16) ^ swizzle(row); the byte
+    offset in the source row is base ^ immediate(j)."""
+    for w, j, lane in itertools.product(range(4), range(4), range(64)):
+        row = 16 * w + 4 * j + lane // 16
+        p = lane % 16
+        kbase = ((lane & 15) ^ (lane >> 4)) * 16
+        vbase = ((lane & 15) ^ (4 * (lane >> 4))) * 16
+        assert 16 * (p ^ swz_k(row)) == kbase ^ (64 * j)
+        assert 16 * (p ^ swz_v(row)) == vbase ^ (16 * j)
+
+
+def test_k_fragment_reads_xor_form():
+    """A operand of S^T = K Q^T (32x32x16): lane l holds key row 32 kt + l % 32,
+    head dims 16 t + 8 (l / 32) + 0..7, i.e. logical chunk 2t + l / 32."""
+    for kt, t, lane in itertools.product(range(2), range(8), range(64)):
+        l32, hi = lane % 32, lane // 32
+        row = 32 * kt + l32
+        direct = phys(row, 16 * t + 8 * hi, swz_k)
+        kaddr = l32 * 128 + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1))
+        assert direct == 4096 * kt + (kaddr ^ (16 * t))
+
+
+def test_v_transpose_read_xor_form():
+    """ds_read_b64_tr_b16 of the PV operand: in each 16-lane group, lane j16 points
+    at 4 consecutive elements of row 16 ks + 4 (l / 32) + j16 / 4 (+ 8 for the
+    second read), columns 32 dt + 16 ((l / 16) & 1) + 4 (j16 & 3)."""
+    for ks, dt, lane in itertools.product(range(4), range(4), range(64)):
+        hi, g16, j16 = lane // 32, lane // 16, lane % 16
+        row = 16 * ks + 4 * hi + j16 // 4
+        col = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)
+        vq = j16 >> 2
+        vc1 = (2 * (g16 & 1) + ((j16 >> 1) & 1)) ^ hi
+        vaddr = (4 * hi + vq) * 128 + 32 * vq + 8 * vc1 + (j16 & 1) * 4
+        vdelta = 1024 + 8 * ((vc1 ^ 2) - vc1)
+        va = 2048 * ks + (vaddr ^ (32 * dt))
+        assert phys(row, col, swz_v) == va
+        assert phys(row + 8, col, swz_v) == va + vdelta
+        # the 4 elements a lane names stay inside one 16-byte chunk
+        assert col % 8 in (0, 4)
+
+
+def tile_row_mask(n, hi):
+    m = 0
+    for kt in range(2):
+        for g in range(4):
+            c = min(max(n - (32 * kt + 8 * g + 4 * hi), 0), 4)
+            m |= ((1 << c) - 1) << (16 * kt + 4 * g)
+    return m
+
+
+def test_tail_row_mask_matches_accumulator_rows():
+    """Bit 16 kt + r of the mask covers s[kt][r], whose key row in the sub-tile is
+    32 kt + 8 (r / 4) + 4 hi + r % 4; it is set exactly when that row is < n."""
+    for n in range(0, 65):
+        for hi in range(2):
+            m = tile_row_mask(n, hi)
+            for kt in range(2):
+                for r in range(16):
+                    key = 32 * kt + 8 * (r // 4) + 4 * hi + r % 4
+                    assert bool((m >> (16 * kt + r)) & 1) == (key < n)

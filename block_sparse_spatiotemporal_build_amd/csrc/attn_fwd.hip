@@ -71,19 +71,6 @@ struct AttnArgs {
 
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 
-// Index, in a list of R items, of the item that workgroup S + j runs, chosen so
-// that the workgroups the hardware deals round-robin to one XCD (those with the
-// same pid mod 8) take one contiguous range of the list, in order.
-__device__ __forceinline__ int xcd_contiguous(int j, int S, int R) {
-  const int x = (S + j) & 7, off = S & 7;
-  int base = 0;
-  for (int y = 0; y < x; ++y) {
-    const int j0 = (y - off) & 7;
-    base += j0 < R ? (R - 1 - j0) / 8 + 1 : 0;
-  }
-  return base + (j - ((x - off) & 7)) / 8;
-}
-
 // Work item (query block, head, batch) of workgroup `pid`.
 //  * Rows not singled out below, default: each XCD gets a contiguous range of
 //    the (batch, head, query block) list, so the workgroups sharing an L2 walk

@@ -106,4 +106,17 @@ bool launch_ok(const char* what);
 // Records a failure message for bsa_last_error() (host, thread-local).
 void set_error(const char* fmt, ...);
 
+// Index, in a list of R items, of the item that workgroup S + j runs, chosen so
+// that the workgroups the hardware deals round-robin to one XCD (those with the
+// same pid mod 8) take one contiguous range of the list, in order.
+__device__ __forceinline__ int xcd_contiguous(int j, int S, int R) {
+  const int x = (S + j) & 7, off = S & 7;
+  int base = 0;
+  for (int y = 0; y < x; ++y) {
+    const int j0 = (y - off) & 7;
+    base += j0 < R ? (R - 1 - j0) / 8 + 1 : 0;
+  }
+  return base + (j - ((x - off) & 7)) / 8;
+}
+
 }  // namespace bsa

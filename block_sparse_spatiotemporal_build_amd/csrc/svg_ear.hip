@@ -1234,7 +1234,11 @@ comp_attn_d128_kernel(CompArgs p) {
 
   const SvgArgs& a = p.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int bh = blockIdx.y;
+  // (head, tile) of this workgroup: the grid's (x = tile, y = head) list is
+  // dealt XCD-contiguously, so the tiles of one query cluster (which stage the
+  // same kept keys) run on one XCD and share its L2
+  const int item = xcd_contiguous(blockIdx.x + blockIdx.y * gridDim.x, 0, gridDim.x * gridDim.y);
+  const int bh = item / gridDim.x, tile = item % gridDim.x;
   const int32_t* qo = a.q_off + (int64_t)bh * (a.Cq + 1);
   const int32_t* ko = a.k_off + (int64_t)bh * (a.Ck + 1);
 
@@ -1254,7 +1258,7 @@ comp_attn_d128_kernel(CompArgs p) {
     __syncthreads();
   }
   {
-    const int x = blockIdx.x;
+    const int x = tile;
     int t0 = scan[tid] - cnt;
     if (x >= t0 && x < t0 + cnt) {
       for (int c = c0; c < c1; ++c) {

@@ -445,18 +445,27 @@ __global__ void __launch_bounds__(256) lin_apply_kernel(LinApplyArgs a) {
 // head_dim 128 apply.  The (batch, head, 128-query tile) items are dealt to
 // workgroups in equal contiguous runs of tpw items (one round of workgroups
 // covers the whole job).  S^T (bf16, rows d2 swizzled) and z are staged in
-// LDS with buffer loads whenever the run enters a new head; Q tiles come
-// straight from global memory into registers, the next tile's loads issued
-// before the current tile's compute so one tile of Q is always in flight.
+// LDS with buffer loads whenever the run enters a new head.  Global traffic is
+// row-contiguous: a wave loads its 32 Q rows of the next tile with 16-byte
+// loads that cover 4 whole rows per instruction (issued before the current
+// tile's compute, so one tile is always in flight), writes them into its own
+// 8 KiB LDS region (rows swizzled like the K stages), reads the MFMA operand
+// fragments back from there, and sends O the same way in reverse: the
+// accumulators go to the region, whole rows come back and are stored with
+// 16-byte stores.  The region is private to the wave, so no barrier is needed.
 __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
-  constexpr int D = 128, KT = 8, DT = 4;
+  constexpr int D = 128, KT = 8, DT = 4, RW = 32;  // rows per wave
   __shared__ __attribute__((aligned(1024))) uint16_t Ss[D * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Xs[4 * RW * D];
   __shared__ float zs[D];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hi = lane >> 5;
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const int it0 = blockIdx.x * a.tpw, it1 = min(it0 + a.tpw, a.total);
   if (it0 >= it1) return;
+  uint16_t* X = Xs + wv * RW * D;
+  // element offset of 16-byte chunk c of wave row r in the region
+  auto xoff = [](int r, int c) { return r * D + 8 * (c ^ (r & 15)); };
 
   auto stage_head = [&](int bh) {
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
@@ -469,17 +478,20 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
     }
     if (tid < D) zs[tid] = a.z_ws[bh * D + tid];
   };
-  auto q_src = [&](int item) {
+  auto head_off = [&](int bh) { return (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh; };
+  // instruction i covers wave rows 4 i + lane / 16, chunk lane % 16
+  auto q_load = [&](int item, u32x4 (&buf)[8]) {
     const int bh = item / a.tph, tile = item % a.tph;
-    const int qrow = min(tile * kApplyRows + wave * 32 + l32, a.N - 1);
-    return a.q + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)qrow * a.sn + hi * 8;
-  };
-  u32x4 qr[KT], qn[KT];
-  {
-    const uint16_t* src = q_src(it0);
+    const uint16_t* base = a.q + head_off(bh) + 8 * (lane & 15);
 #pragma unroll
-    for (int t = 0; t < KT; ++t) qr[t] = *(const u32x4*)(src + t * 16);
-  }
+    for (int i = 0; i < 8; ++i) {
+      const int row = min(tile * kApplyRows + RW * wv + 4 * i + (lane >> 4), a.N - 1);
+      buf[i] = *(const u32x4*)(base + (int64_t)row * a.sn);
+    }
+  };
+
+  u32x4 qb[8];
+  q_load(it0, qb);
   int cur_bh = -1;
   for (int it = it0; it < it1; ++it) {
     const int bh = it / a.tph, tile = it % a.tph;
@@ -490,21 +502,21 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
       __syncthreads();
       cur_bh = bh;
     }
-    const bool more = it + 1 < it1;
-    if (more) {
-      const uint16_t* src = q_src(it + 1);
+    // this tile's Q rows into the region, then the next tile's loads
 #pragma unroll
-      for (int t = 0; t < KT; ++t) qn[t] = *(const u32x4*)(src + t * 16);
-    }
+    for (int i = 0; i < 8; ++i) *(u32x4*)&X[xoff(4 * i + (lane >> 4), lane & 15)] = qb[i];
+    if (it + 1 < it1) q_load(it + 1, qb);
+    // B operand: lane (l32, hi) takes row l32, head dims 16 t + 8 hi .. + 7
     bf16x8 qf[KT];
     float den = 0.f;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
+      const u32x4 raw = *(const u32x4*)&X[xoff(l32, 2 * t + hi)];
       u32x4 w;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int d = t * 16 + hi * 8 + 2 * e;
-        const float f0 = phi(bf16_lo(qr[t][e])), f1 = phi(bf16_hi(qr[t][e]));
+        const float f0 = phi(bf16_lo(raw[e])), f1 = phi(bf16_hi(raw[e]));
         den = __builtin_fmaf(f0, zs[d], den);
         den = __builtin_fmaf(f1, zs[d + 1], den);
         w[e] = pack_bf16x2(f0, f1);
@@ -523,23 +535,24 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[t], o[dt], 0, 0, 0);
       }
     }
-    const int qrow = tile * kApplyRows + wave * 32 + l32;
-    if (qrow < a.N) {
-      const float inv = 1.f / den;
-      uint16_t* dst = a.o + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)qrow * a.sn;
+    // O^T accumulators -> region (row l32, head dims 32 dt + 8 g + 4 hi .. + 3)
+    const float inv = 1.f / den;
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+    for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = dt * 32 + 8 * g + 4 * hi;
-          u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
-                     pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
-          *(u32x2*)(dst + d0) = w;
-        }
-    }
-    if (more) {
+      for (int g = 0; g < 4; ++g) {
+        u32x2 w = {pack_bf16x2(o[dt][4 * g] * inv, o[dt][4 * g + 1] * inv),
+                   pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
+        *(u32x2*)&X[xoff(l32, 4 * dt + g) + 4 * hi] = w;
+      }
+    // whole rows back out, 16-byte stores (rows past N are not stored)
+    uint16_t* obase = a.o + head_off(bh) + 8 * (lane & 15);
 #pragma unroll
-      for (int t = 0; t < KT; ++t) qr[t] = qn[t];
+    for (int i = 0; i < 8; ++i) {
+      const int r = 4 * i + (lane >> 4);
+      const u32x4 v = *(const u32x4*)&X[xoff(r, lane & 15)];
+      const int row = tile * kApplyRows + RW * wv + r;
+      if (row < a.N) *(u32x4*)(obase + (int64_t)row * a.sn) = v;
     }
   }
 }

@@ -166,10 +166,10 @@ __global__ void __launch_bounds__(kLinThreads) lin_state_kernel(LinStateArgs a) 
 }
 
 // head_dim 128 state kernel.  K and V tiles of 32 tokens go straight from
-// global memory to LDS with buffer loads into a ring of four stages (eight
-// distinct LDS objects, the loop unrolled by four so no LDS read ever waits for
-// a copy in flight): three tiles are in flight while one is computed, which is
-// what it takes to cover the memory latency at two workgroups per CU.  Rows
+// global memory to LDS with buffer loads into a ring of five stages (ten
+// distinct LDS objects, 80 KiB, the loop unrolled by five so no LDS read ever
+// waits for a copy in flight): four tiles are in flight while one is computed,
+// 128 KiB per CU at two workgroups per CU, to cover the memory latency.  Rows
 // are swizzled for the transpose read.  Wave w owns S rows d1 in
 // [32w, 32w + 32) and all four 32-column blocks of d2: its phi(K)^T fragment
 // (A operand) is read once per 16 tokens, phi is applied in fp32 (rows past
@@ -182,8 +182,8 @@ constexpr int kLinTok2 = 32;  // tokens per tile of the head_dim-128 state kerne
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 lin_state_d128_kernel(LinStateArgs a) {
   constexpr int D = 128, TILE = kLinTok2 * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[TILE], K4[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[TILE], V4[TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
   const int g16 = lane >> 4, j16 = lane & 15;
   const int split = blockIdx.x, bh = blockIdx.y;
@@ -240,17 +240,18 @@ lin_state_d128_kernel(LinStateArgs a) {
     return u32x4{x0[0], x0[1], x1[0], x1[1]};
   };
 
-  // tile t sits in stage t % 4; at its step the copies of tiles t + 1 and t + 2
+  // tile t sits in stage t % 5; at its step the copies of tiles t + 1 .. t + 3
   // may still be in flight (4 instructions each per wave), and the copy of
-  // tile t + 3 is issued into the stage that tile t - 1 used
+  // tile t + 4 is issued into the stage that tile t - 1 used
   auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int t) {
     const int t0 = n0 + t * kLinTok2;
-    const int ahead = ntile - 1 - t;  // tiles after t already issued: min(ahead, 2)
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(0x0078);       // vmcnt(8) lgkmcnt(0)
+    const int ahead = ntile - 1 - t;  // tiles after t already issued: min(ahead, 3)
+    if (ahead >= 3) __builtin_amdgcn_s_waitcnt(0x007C);       // vmcnt(12) lgkmcnt(0)
+    else if (ahead == 2) __builtin_amdgcn_s_waitcnt(0x0078);  // vmcnt(8) lgkmcnt(0)
     else if (ahead == 1) __builtin_amdgcn_s_waitcnt(0x0074);  // vmcnt(4) lgkmcnt(0)
     else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (t + 3 < ntile) dma(Kn, Vn, t0 + 3 * kLinTok2);
+    if (t + 4 < ntile) dma(Kn, Vn, t0 + 4 * kLinTok2);
     const int lim = n1 - t0 - 4 * hi;  // element e is a real token iff 16 ks + 8 (e / 4) + e % 4 < lim
 #pragma unroll
     for (int ks = 0; ks < kLinTok2 / 16; ++ks) {
@@ -276,16 +277,19 @@ lin_state_d128_kernel(LinStateArgs a) {
   if (ntile > 0) dma(K0, V0, n0);
   if (ntile > 1) dma(K1, V1, n0 + kLinTok2);
   if (ntile > 2) dma(K2, V2, n0 + 2 * kLinTok2);
+  if (ntile > 3) dma(K3, V3, n0 + 3 * kLinTok2);
   int t = 0;
-  for (; t + 4 <= ntile; t += 4) {
-    step(K0, V0, K3, V3, t);
+  for (; t + 5 <= ntile; t += 5) {
+    step(K0, V0, K4, V4, t);
     step(K1, V1, K0, V0, t + 1);
     step(K2, V2, K1, V1, t + 2);
     step(K3, V3, K2, V2, t + 3);
+    step(K4, V4, K3, V3, t + 4);
   }
-  if (t < ntile) step(K0, V0, K3, V3, t);
+  if (t < ntile) step(K0, V0, K4, V4, t);
   if (t + 1 < ntile) step(K1, V1, K0, V0, t + 1);
   if (t + 2 < ntile) step(K2, V2, K1, V1, t + 2);
+  if (t + 3 < ntile) step(K3, V3, K2, V2, t + 3);
 
   // partial S: acc[dt][r] = S[32 w + 8 (r / 4) + 4 hi + r % 4][32 dt + lane % 32]
   float* ps = a.part_s + ((int64_t)bh * a.splits + split) * D * D;

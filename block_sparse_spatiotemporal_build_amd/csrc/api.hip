@@ -239,7 +239,7 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
 
 size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
   if (check_shape(shape, 2, "bsa_compensated_attn_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
-  return comp_attn_workspace(*shape, Ck);
+  return comp_attn_workspace(*shape, Cq, Ck);
 }
 
 bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dtype,
@@ -257,7 +257,7 @@ bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v,
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(k_cent) || !aligned16(v_cent))
     return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
   if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
-  const size_t need = comp_attn_workspace(*shape, Ck);
+  const size_t need = comp_attn_workspace(*shape, Cq, Ck);
   if (need > 0 && (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u)))
     return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
   g_err[0] = 0;
@@ -279,7 +279,7 @@ static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
   p.probe = align256h(p.sc + bh * Cq * Ck * 4);
   p.flags = align256h(p.probe + probe_plan(s, Cq, Ck).total);
   p.attn = align256h(p.flags + bh * Cq * Ck);
-  p.total = align256h(p.attn + comp_attn_workspace(s, Ck));
+  p.total = align256h(p.attn + comp_attn_workspace(s, Cq, Ck));
   return p;
 }
 

@@ -47,7 +47,7 @@ bsa_status launch_route_select(const float* score, const bsa_shape& s, const int
                                uint8_t* flags, hipStream_t stream);
 // compensated attention workspace: bf16 copies of the key / value centroids
 // for the head_dim-128 kernel (0 bytes otherwise)
-size_t comp_attn_workspace(const bsa_shape& s, int Ck);
+size_t comp_attn_workspace(const bsa_shape& s, int Cq, int Ck);
 bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
                             const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
                             const int32_t* rcol, const float* kc, const float* vc, float scale, void* ws,

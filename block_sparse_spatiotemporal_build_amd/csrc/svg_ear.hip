@@ -974,6 +974,9 @@ struct CompArgs {
   float scale, c2;
   const uint16_t* kc_bf;  // head_dim 128 path: bf16 copies of k_cent / v_cent, [BH][Ck][D]
   const uint16_t* vc_bf;
+  const int32_t* tile_item;   // head_dim 128 path: tile schedule, longest first: item bh * Cq + a,
+  const int32_t* tile_x;      // tile x of that cluster (rows q_off[a] + 128 x ...),
+  const int32_t* tile_count;  // and the number of tiles
 };
 
 template <int D>
@@ -1211,6 +1214,94 @@ __global__ void __launch_bounds__(256) centroid_bf16_kernel(const float* k_cent,
   }
 }
 
+// Tile schedule of the head_dim-128 compensated attention, longest first.  A
+// tile is 128 query rows of one cluster; its work is its number of 64-key
+// sub-tiles, ceil(E_a / 64) + ceil(Ck / 64), E_a = the exact keys of the kept
+// clusters of row a.  Launching the longest tiles first keeps the launch's
+// tail short (the lengths vary by a factor of about 4 on the clustered
+// workload).  The schedule only decides which workgroup runs a tile and when;
+// no result depends on it.
+constexpr int kOrdBuckets = 4096;  // work is bucketed by min(sub-tiles, 4095)
+
+struct CompOrderArgs {
+  const int32_t* q_off;
+  const int32_t* k_off;
+  const int32_t* rrow;
+  const int32_t* rcol;
+  int Cq, Ck, BH, cap;  // cap: capacity of the schedule arrays
+  int32_t* work;   // [BH * Cq] sub-tiles of a tile of cluster (bh, a)
+  int32_t* ntile;  // [BH * Cq] tiles of cluster (bh, a)
+  int32_t* tile_item;
+  int32_t* tile_x;
+  int32_t* tile_count;
+};
+
+// one wave per (head, cluster): E_a from the route row (indices clamped like the
+// attention kernel clamps them)
+__global__ void __launch_bounds__(256) comp_steps_kernel(CompOrderArgs o) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bh = blockIdx.y, ca = blockIdx.x * 4 + wave;
+  if (ca >= o.Cq) return;
+  const int32_t* qo = o.q_off + (int64_t)bh * (o.Cq + 1);
+  const int32_t* ko = o.k_off + (int64_t)bh * (o.Ck + 1);
+  const int rb = max(0, min(o.rrow[(int64_t)bh * (o.Cq + 1) + ca], o.Cq * o.Ck));
+  const int nk = max(0, min(o.rrow[(int64_t)bh * (o.Cq + 1) + ca + 1] - rb, min(o.Ck, o.Cq * o.Ck - rb)));
+  const int32_t* cl = o.rcol + (int64_t)bh * o.Cq * o.Ck + rb;
+  int e = 0;
+  for (int i = lane; i < nk; i += 64) {
+    const int b = max(0, min(cl[i], o.Ck - 1));
+    e += ko[b + 1] - ko[b];
+  }
+  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
+  if (lane == 0) {
+    const int i = bh * o.Cq + ca;
+    o.work[i] = (e + kCaBN - 1) / kCaBN + (o.Ck + kCaBN - 1) / kCaBN;
+    o.ntile[i] = max(0, (qo[ca + 1] - qo[ca] + 127) / 128);
+  }
+}
+
+// one workgroup: histogram of tiles by work, bucket starts in descending work
+// order, then every cluster's tiles are placed at its bucket's cursor
+__global__ void __launch_bounds__(1024) comp_order_kernel(CompOrderArgs o) {
+  __shared__ int hist[kOrdBuckets];
+  __shared__ int part[1024];
+  const int tid = threadIdx.x, n = o.BH * o.Cq;
+  for (int b = tid; b < kOrdBuckets; b += 1024) hist[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) atomicAdd(&hist[min(o.work[i], kOrdBuckets - 1)], o.ntile[i]);
+  __syncthreads();
+  // exclusive prefix from the top bucket down: thread t owns buckets
+  // kOrdBuckets - 4 (t + 1) .. kOrdBuckets - 4 t - 1, taken from the top
+  constexpr int per = kOrdBuckets / 1024;
+  const int top = kOrdBuckets - per * tid;
+  int sum = 0;
+  for (int q = 1; q <= per; ++q) sum += hist[top - q];
+  part[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int add = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += add;
+    __syncthreads();
+  }
+  int run = part[tid] - sum;
+  for (int q = 1; q <= per; ++q) {
+    const int c = hist[top - q];
+    hist[top - q] = run;  // now the cursor of the bucket
+    run += c;
+  }
+  if (tid == 1023) *o.tile_count = min(part[1023], o.cap);
+  __syncthreads();
+  for (int i = tid; i < n; i += 1024) {
+    const int nt = o.ntile[i];
+    const int base = atomicAdd(&hist[min(o.work[i], kOrdBuckets - 1)], nt);
+    for (int x = 0; x < nt && base + x < o.cap; ++x) {  // (cap holds for offsets within [0, N])
+      o.tile_item[base + x] = i;
+      o.tile_x[base + x] = x;
+    }
+  }
+}
+
 // head_dim 128 compensated attention.  Same online-softmax core and staging
 // as attn_bf16_d128_kernel: 64-key sub-tiles copied straight to two swizzled
 // LDS stages (separate objects, loop unrolled by two).  Sub-tile u < ne holds
@@ -1230,54 +1321,24 @@ comp_attn_d128_kernel(CompArgs p) {
   __shared__ int kstart[kCaMaxCk];     // first key row of each kept cluster
   __shared__ float bias[kCaMaxCk];     // virtual-key logit bias (raw units) or -inf
   __shared__ int scan[256];
-  __shared__ int sh_tile[3];
 
   const SvgArgs& a = p.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  // (head, tile) of this workgroup: the grid's (x = tile, y = head) list is
-  // dealt XCD-contiguously, so the tiles of one query cluster (which stage the
-  // same kept keys) run on one XCD and share its L2
-  const int item = xcd_contiguous(blockIdx.x + blockIdx.y * gridDim.x, 0, gridDim.x * gridDim.y);
-  const int bh = item / gridDim.x, tile = item % gridDim.x;
+  // Tile of this workgroup from the longest-first schedule.  Three consecutive
+  // schedule entries (usually the tiles of one query cluster, which stage the
+  // same kept keys) go to workgroups that the hardware deals to one XCD, so
+  // they share its L2: within each run of 24 workgroups, workgroup r takes
+  // entry 3 (r % 8) + r / 8.
+  const int pid = blockIdx.x, r24 = pid % 24;
+  const int j = pid - r24 + 3 * (r24 % 8) + r24 / 8;
+  if (j >= *p.tile_count) return;  // uniform
+  const int item = __builtin_amdgcn_readfirstlane(p.tile_item[j]);
+  const int tx = __builtin_amdgcn_readfirstlane(p.tile_x[j]);
+  const int bh = item / a.Cq, ca = item % a.Cq;
   const int32_t* qo = a.q_off + (int64_t)bh * (a.Cq + 1);
   const int32_t* ko = a.k_off + (int64_t)bh * (a.Ck + 1);
-
-  // ---- which query cluster and rows this workgroup covers: tiles of 128 rows
-  // per cluster, numbered cluster by cluster (parallel count + scan)
-  if (tid == 0) sh_tile[0] = -1;
-  const int per = (a.Cq + 255) / 256;
-  const int c0 = min(tid * per, a.Cq), c1 = min(c0 + per, a.Cq);
-  int cnt = 0;
-  for (int c = c0; c < c1; ++c) cnt += (qo[c + 1] - qo[c] + 127) / 128;
-  scan[tid] = cnt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  {
-    const int x = tile;
-    int t0 = scan[tid] - cnt;
-    if (x >= t0 && x < t0 + cnt) {
-      for (int c = c0; c < c1; ++c) {
-        const int nt = (qo[c + 1] - qo[c] + 127) / 128;
-        if (x < t0 + nt) {
-          sh_tile[0] = c;
-          sh_tile[1] = qo[c] + 128 * (x - t0);
-          sh_tile[2] = qo[c + 1];
-          break;
-        }
-        t0 += nt;
-      }
-    }
-  }
-  __syncthreads();
-  // workgroup-uniform values read from LDS are moved to scalar registers
-  const int ca = __builtin_amdgcn_readfirstlane(sh_tile[0]);
-  if (ca < 0) return;  // beyond the last query tile of this head (uniform)
-  const int r0 = __builtin_amdgcn_readfirstlane(sh_tile[1]), r1 = __builtin_amdgcn_readfirstlane(sh_tile[2]);
+  const int r0 = __builtin_amdgcn_readfirstlane(qo[ca] + 128 * tx);
+  const int r1 = __builtin_amdgcn_readfirstlane(qo[ca + 1]);
 
   // ---- kept clusters of row ca (a caller-given route is clamped into range so
   // every table index and every staged row stays in bounds)
@@ -1610,9 +1671,29 @@ static bool comp_d128(const bsa_shape& s) {
   return s.D == 128 && ((int64_t)s.N + kCaBN) * s.stride_n * 2 < ((int64_t)1 << 31);
 }
 
-size_t comp_attn_workspace(const bsa_shape& s, int Ck) {
+// head_dim-128 workspace: bf16 k_cent, bf16 v_cent, per-cluster work and tile
+// counts, the tile schedule (item, x) and its length
+struct CompWs {
+  size_t kb, vb, work, ntile, item, x, count, total;
+  int cap;  // upper bound of the tiles of all heads
+};
+static CompWs comp_ws(const bsa_shape& s, int Cq, int Ck) {
+  CompWs w;
+  const size_t bh = (size_t)s.B * s.H;
+  w.cap = (int)(bh * ((s.N + 127) / 128 + Cq));
+  w.kb = 0;
+  w.vb = al256(bh * Ck * s.D * 2);
+  w.work = w.vb + al256(bh * Ck * s.D * 2);
+  w.ntile = w.work + al256(bh * Cq * 4);
+  w.item = w.ntile + al256(bh * Cq * 4);
+  w.x = w.item + al256((size_t)w.cap * 4);
+  w.count = w.x + al256((size_t)w.cap * 4);
+  w.total = w.count + 256;
+  return w;
+}
+size_t comp_attn_workspace(const bsa_shape& s, int Cq, int Ck) {
   if (!comp_d128(s)) return 0;
-  return 2 * al256((size_t)s.B * s.H * Ck * s.D * 2);
+  return comp_ws(s, Cq, Ck).total;
 }
 
 bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
@@ -1627,14 +1708,23 @@ bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o
   const int max_tiles = (s.N + 127) / 128 + Cq;
   dim3 grid(max_tiles, s.B * s.H);
   if (comp_d128(s)) {
-    const size_t half = al256((size_t)s.B * s.H * Ck * s.D * 2);
-    uint16_t* kb = (uint16_t*)ws;
-    uint16_t* vb = (uint16_t*)((char*)ws + half);
+    const CompWs w = comp_ws(s, Cq, Ck);
+    char* base = (char*)ws;
+    uint16_t* kb = (uint16_t*)(base + w.kb);
+    uint16_t* vb = (uint16_t*)(base + w.vb);
     const int64_t n2 = (int64_t)s.B * s.H * Ck * s.D / 2;
     hipLaunchKernelGGL(centroid_bf16_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, kc, vc, kb,
                        vb, n2);
+    CompOrderArgs oa{q_off, k_off, rrow, rcol, Cq, Ck, s.B * s.H, w.cap, (int32_t*)(base + w.work),
+                     (int32_t*)(base + w.ntile), (int32_t*)(base + w.item), (int32_t*)(base + w.x),
+                     (int32_t*)(base + w.count)};
+    hipLaunchKernelGGL(comp_steps_kernel, dim3((Cq + 3) / 4, s.B * s.H), dim3(256), 0, stream, oa);
+    hipLaunchKernelGGL(comp_order_kernel, dim3(1), dim3(1024), 0, stream, oa);
     p.kc_bf = kb; p.vc_bf = vb;
-    hipLaunchKernelGGL(comp_attn_d128_kernel, grid, dim3(256), 0, stream, p);
+    p.tile_item = oa.tile_item; p.tile_x = oa.tile_x; p.tile_count = oa.tile_count;
+    // 1-D grid, a multiple of 24 covering every schedule entry (see the kernel)
+    const int wgs = (w.cap + 23) / 24 * 24;
+    hipLaunchKernelGGL(comp_attn_d128_kernel, dim3(wgs), dim3(256), 0, stream, p);
   } else if (s.D == 128) {
     hipLaunchKernelGGL(comp_attn_kernel<128>, grid, dim3(256), 0, stream, p);
   } else if (s.D == 64) {

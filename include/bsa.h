@@ -229,9 +229,11 @@ bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v,
                                     const float* k_cent, const float* v_cent, float scale,
                                     void* workspace, size_t ws_bytes, void* stream);
 
-/* Workspace bytes of bsa_compensated_attn_fwd: bf16 copies of the key and value
- * centroids (the virtual keys and values) for head_dim 128; 0 otherwise (then
- * workspace may be NULL).  0 for an invalid shape as well. */
+/* Workspace bytes of bsa_compensated_attn_fwd: for head_dim 128, bf16 copies of
+ * the key and value centroids (the virtual keys and values) and the launch's
+ * tile schedule (per-cluster work, and the 128-row query tiles ordered longest
+ * first); 0 otherwise (then workspace may be NULL).  0 for an invalid shape as
+ * well. */
 size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
 
 /* Workspace bytes of bsa_centroid_compensate (0 for an invalid shape). */

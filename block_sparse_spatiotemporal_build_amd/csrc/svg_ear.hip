@@ -957,6 +957,207 @@ __global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
   }
 }
 
+// Register-resident form of select_kernel for Cq <= 16 * kSrRows and
+// Ck <= 64 * kSrCpl: the same selection and the same CSR, with every score of
+// the head loaded once into registers (lane l of wave w holds the columns
+// 64 c + l of its rows ra0 + r) and every pass run from there, instead of
+// re-reading the scores from memory in each radix pass.
+constexpr int kSrRows = 8, kSrCpl = 8;
+
+__global__ void __launch_bounds__(kSelThreads) select_reg_kernel(SelectArgs s) {
+  __shared__ unsigned long long hist[kSelWaves][256];
+  __shared__ unsigned long long htot[256];
+  __shared__ long long wred[kSelWaves];
+  __shared__ int wcnt[kSelWaves];
+  __shared__ unsigned wmin[kSelWaves], wmax[kSelWaves];
+  __shared__ long long sh_R;
+  __shared__ unsigned int sh_prefix;
+  __shared__ int nbk[64 * kSrCpl];
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int Cq = s.Cq, Ck = s.Ck;
+  const int64_t M = (int64_t)Cq * Ck;
+  const unsigned* sc = (const unsigned*)(s.score + (int64_t)bh * M);
+  const int32_t* qo = s.q_off + (int64_t)bh * (Cq + 1);
+  const int32_t* ko = s.k_off + (int64_t)bh * (Ck + 1);
+  int32_t* rr = s.rrow + (int64_t)bh * (Cq + 1);
+  int32_t* rc = s.rcol + (int64_t)bh * M;
+  const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
+  const int ra0 = min(wave * rpw, Cq), nrow = min(ra0 + rpw, Cq) - ra0;
+
+  // scores in registers; key-cluster sizes in LDS (read at each use, so the
+  // compiler does not keep 64 per-lane costs live across the passes)
+  unsigned sb[kSrRows][kSrCpl];
+  int nar[kSrRows];
+  for (int b = tid; b < 64 * kSrCpl; b += kSelThreads) nbk[b] = b < Ck ? ko[b + 1] - ko[b] : 0;
+#pragma unroll
+  for (int r = 0; r < kSrRows; ++r) nar[r] = r < nrow ? qo[ra0 + r + 1] - qo[ra0 + r] : 0;
+#pragma unroll
+  for (int r = 0; r < kSrRows; ++r)
+#pragma unroll
+    for (int c = 0; c < kSrCpl; ++c) {
+      const int b = 64 * c + lane;
+      sb[r][c] = (r < nrow && b < Ck) ? sc[(int64_t)(ra0 + r) * Ck + b] : 0u;
+    }
+  __syncthreads();
+  auto cost = [&](int r, int c) -> long long { return (long long)nar[r] * nbk[64 * c + lane]; };
+
+  // total cost of the non-empty blocks and the range of their score bits
+  long long part = 0;
+  unsigned bmin = 0xffffffffu, bmax = 0u;
+#pragma unroll
+  for (int r = 0; r < kSrRows; ++r)
+#pragma unroll
+    for (int c = 0; c < kSrCpl; ++c) {
+      const long long w = cost(r, c);
+      if (w > 0) {
+        part += w;
+        bmin = min(bmin, sb[r][c]);
+        bmax = max(bmax, sb[r][c]);
+      }
+    }
+  part = wave_sum64(part);
+  for (int off = 32; off > 0; off >>= 1) {
+    bmin = min(bmin, (unsigned)__shfl_xor((int)bmin, off, 64));
+    bmax = max(bmax, (unsigned)__shfl_xor((int)bmax, off, 64));
+  }
+  if (lane == 0) {
+    wred[wave] = part;
+    wmin[wave] = bmin;
+    wmax[wave] = bmax;
+  }
+  __syncthreads();
+  long long total = 0;
+  unsigned gmin = 0xffffffffu, gmax = 0u;
+  for (int w = 0; w < kSelWaves; ++w) {
+    total += wred[w];
+    gmin = min(gmin, wmin[w]);
+    gmax = max(gmax, wmax[w]);
+  }
+  const bool take_all = total <= s.budget;
+
+  unsigned T = 0;
+  long long R = s.budget;
+  if (!take_all) {
+    // digits start below the leading bits shared by every counted score
+    const int lead = gmin == gmax ? 32 : __clz((int)(gmin ^ gmax));
+    unsigned msk = lead == 0 ? 0u : (lead == 32 ? 0xffffffffu : ~0u << (32 - lead));
+    unsigned pre = gmin & msk;
+    for (int low = 32 - lead; low > 0;) {
+      const int width = min(8, low);
+      const int shift = low - width;
+      const unsigned dmask = (1u << width) - 1u;
+      low = shift;
+      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int r = 0; r < kSrRows; ++r)
+#pragma unroll
+        for (int c = 0; c < kSrCpl; ++c) {
+          const long long w = cost(r, c);
+          const bool in = w > 0 && (sb[r][c] & msk) == pre;
+          const unsigned dig = (sb[r][c] >> shift) & dmask;
+          const unsigned long long inb = __ballot(in);
+          if (inb == 0) continue;
+          const unsigned d0 = (unsigned)__shfl((int)dig, __ffsll((long long)inb) - 1, 64);
+          if (__ballot(in && dig == d0) == inb) {
+            const long long cw = wave_sum64(in ? w : 0);
+            if (lane == 0) atomicAdd(&hist[wave][d0], (unsigned long long)cw);
+          } else if (in) {
+            atomicAdd(&hist[wave][dig], (unsigned long long)w);
+          }
+        }
+      __syncthreads();
+      if (tid < 256) {
+        unsigned long long t = 0;
+        for (int w = 0; w < kSelWaves; ++w) t += hist[w][tid];
+        htot[tid] = t;
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l holds digits 4l .. 4l+3; the cut digit is the first from the
+        // top whose own cost takes the cost above it past R (digit 0 if none)
+        unsigned long long h[4], own = 0;
+        for (int i = 0; i < 4; ++i) {
+          h[i] = htot[4 * lane + i];
+          own += h[i];
+        }
+        long long above = (long long)own;
+        for (int off = 1; off < 64; off <<= 1) {
+          const long long y = __shfl_down(above, off, 64);
+          if (lane + off < 64) above += y;
+        }
+        above -= (long long)own;
+        for (int i = 3; i >= 0; --i) {
+          const int d = 4 * lane + i;
+          const bool cut = (above + (long long)h[i] > R) || d == 0;
+          if (cut && above <= R) {
+            sh_R = R - above;
+            sh_prefix = pre | ((unsigned)d << shift);
+            break;
+          }
+          above += (long long)h[i];
+        }
+      }
+      __syncthreads();
+      R = sh_R;
+      pre = sh_prefix;
+      msk |= dmask << shift;
+      __syncthreads();
+    }
+    T = pre;
+  }
+
+  // cost of the ties at T held by each wave, for the index-order carry
+  long long tc = 0;
+  if (!take_all)
+#pragma unroll
+    for (int r = 0; r < kSrRows; ++r)
+#pragma unroll
+      for (int c = 0; c < kSrCpl; ++c) {
+        const long long w = cost(r, c);
+        if (w > 0 && sb[r][c] == T) tc += w;
+      }
+  tc = wave_sum64(tc);
+  if (lane == 0) wred[wave] = tc;
+  __syncthreads();
+  long long carry = 0;
+  for (int w = 0; w < wave; ++w) carry += wred[w];
+  // keep decisions in index order (row, then column), packed one bit each
+  unsigned long long keepm = 0;
+  int wave_kept = 0;
+#pragma unroll
+  for (int r = 0; r < kSrRows; ++r)
+#pragma unroll
+    for (int c = 0; c < kSrCpl; ++c) {
+      const long long w = cost(r, c);
+      const bool tie = !take_all && w > 0 && sb[r][c] == T;
+      long long incl = 0;
+      if (__any(tie)) incl = wave_incl_scan64(tie ? w : 0, lane);
+      const bool keep = take_all ? w > 0 : (w > 0 && (sb[r][c] > T || (tie && carry + incl <= R)));
+      carry += __shfl(incl, 63, 64);
+      if (keep) keepm |= 1ull << (r * kSrCpl + c);
+      wave_kept += __popcll(__ballot(keep));
+    }
+  if (lane == 0) wcnt[wave] = wave_kept;
+  __syncthreads();
+  // CSR: wave w's rows start after the blocks kept by waves < w
+  int start = 0;
+  for (int w = 0; w < wave; ++w) start += wcnt[w];
+  if (tid == 0) rr[0] = 0;
+#pragma unroll
+  for (int r = 0; r < kSrRows; ++r) {
+    if (r >= nrow) break;
+#pragma unroll
+    for (int c = 0; c < kSrCpl; ++c) {
+      const bool keep = (keepm >> (r * kSrCpl + c)) & 1ull;
+      const unsigned long long bal = __ballot(keep);
+      if (keep) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = 64 * c + lane;
+      start += __popcll(bal);
+    }
+    if (lane == 0) rr[ra0 + r + 1] = start;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // compensated attention
 // ---------------------------------------------------------------------------
@@ -1663,7 +1864,10 @@ bsa_status launch_route_select(const float* score, const bsa_shape& s, const int
                                const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
                                uint8_t* flags, hipStream_t stream) {
   SelectArgs a{score, q_off, k_off, rrow, rcol, flags, Cq, Ck, s.N, budget};
-  hipLaunchKernelGGL(select_kernel, dim3(s.B * s.H), dim3(kSelThreads), 0, stream, a);
+  if (Cq <= kSelWaves * kSrRows && Ck <= 64 * kSrCpl)
+    hipLaunchKernelGGL(select_reg_kernel, dim3(s.B * s.H), dim3(kSelThreads), 0, stream, a);
+  else
+    hipLaunchKernelGGL(select_kernel, dim3(s.B * s.H), dim3(kSelThreads), 0, stream, a);
   return launch_ok("route_select") ? BSA_OK : BSA_ERR_HIP;
 }
 

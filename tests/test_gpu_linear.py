@@ -32,6 +32,22 @@ def test_small_full_compare(gpu_lib, D, N):
     assert rel_z < 1e-5, rel_z                      # z accumulates phi in fp32
 
 
+@pytest.mark.parametrize("k", [2, 3, 4, 6, 8, 9])
+def test_every_copy_ring_remainder(gpu_lib, k):
+    """64 heads split the state pass into 8 chunks of k 32-token tiles each
+    (N = 256 k - 13, so the last tile is ragged): the state kernel's ring of
+    copy stages then runs every loop remainder (k mod 5) and its tail path."""
+    N = 256 * k - 13
+    wl = gen.scaled(get_workload("linear_32k"), H=64, D=128, frames=1, frame_h=1, frame_w=N, seed=60 + k)
+    d = gen.make_qkv(wl)
+    out, S, z = _run(gpu_lib, d)
+    q, kk, v = inputs_f64(d, "bf16")
+    ref, rS, rz = ol.linear_attention(q, kk, v)
+    assert_parity(to_f64(out), ref, "bf16", f"linear ring k={k}")
+    _, rel_z = parity(to_f64(z), rz)
+    assert rel_z < 1e-5, rel_z
+
+
 def test_single_token_gives_its_value(gpu_lib):
     wl = gen.scaled(get_workload("linear_32k"), H=2, frames=1, frame_h=1, frame_w=1, seed=42)
     d = gen.make_qkv(wl)

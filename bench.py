@@ -140,11 +140,7 @@ def cpu_baseline(wl, d, params, budget_s: float):
     from oracle import attention as oa
     from oracle import mask as om
     from synth import gen
-    try:
-        import threadpoolctl
-        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: report the affinity size
-        threads = len(os.sched_getaffinity(0))
+    threads = _oracle_threads()
     m = om.block_mask(om.spec_from_params(params))
     scale = 1.0 / math.sqrt(wl.D)
     sizes = np.minimum(wl.block, wl.N - np.arange(wl.nb) * wl.block)
@@ -167,6 +163,57 @@ def cpu_baseline(wl, d, params, budget_s: float):
             "cores": int(threads), "kind": "oracle",
             "sample": f"{done} of {wl.nb * wl.H} query-block rows (heads 0..{heads - 1} in order), "
                       f"mask step 0: {flops / 1e9:.1f} GFLOP in {dt:.1f} s, float64 numpy"}
+
+
+def _oracle_threads():
+    try:
+        import threadpoolctl
+        return max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: report the affinity size
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline_linear(wl, d, budget_s: float):
+    """The linear-attention oracle on whole heads in order until the budget is spent,
+    as algorithmic GB/s (read Q, K, V + write O of the heads done)."""
+    from oracle import linear as ol
+    from synth import gen
+    heads, dt = 0, 0.0
+    for h in range(wl.H):
+        q, k, v = (gen.to_f64(d[n][:, h:h + 1], wl.dtype) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        ol.linear_attention(q, k, v)
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= budget_s:
+            break
+    nbytes = 4 * heads * wl.N * wl.D * 2
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s (read Q, K, V + write O)",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"heads 0..{heads - 1} of {wl.H} in order: {dt:.1f} s, float64 numpy"}
+
+
+def cpu_baseline_svg(wl, d, budget_s: float):
+    """The SVG-EAR oracle (centroids, scores, selection, compensated attention of every
+    query cluster) on whole heads in order until the budget is spent; ms per call
+    extrapolated to all B * H heads."""
+    from oracle import svg_ear as oe
+    from synth import gen
+    scale = 1.0 / math.sqrt(wl.D)
+    heads, dt = 0, 0.0
+    for r in range(wl.B * wl.H):
+        b, h = divmod(r, wl.H)
+        q, k, v = (gen.to_f64(d[n][b, h], wl.dtype) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        oe.svg_ear_head(q, k, v, d["q_off"][r], d["k_off"][r], scale, wl.density_ppm)
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= budget_s:
+            break
+    ms = dt / heads * wl.B * wl.H * 1e3
+    return {"value": round(ms, 1), "unit": "ms per call (extrapolated from the heads done)",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"heads 0..{heads - 1} of {wl.B * wl.H} in order, all five steps: {dt:.1f} s, float64 numpy"}
 
 
 def copy_mode():
@@ -206,6 +253,7 @@ def bench_linear(args, wl):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    d_host = d if args.cpu_seconds > 0 else None
     del d
     out = torch.empty_like(q)
     ws = torch.empty(bsa.linear_attn_workspace(q), dtype=torch.uint8, device=dev)
@@ -227,7 +275,7 @@ def bench_linear(args, wl):
     copy = None if args.no_refs else measure_copy_gbs()
     src = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "linear_attn.hip")
     traffic = read_traffic(wl.name, "linear_attn", src)
-    return {
+    result = {
         "metric": "algorithmic HBM GB/s of elu+1 linear attention",
         "value": round(algo_bytes * args.steps / (t1 - t0) / 1e9, 1),
         "unit": "GB/s (read Q, K, V + write O)",
@@ -245,6 +293,9 @@ def bench_linear(args, wl):
             "kernel": "1 GiB device copy, read + write", "gbs": round(copy, 1),
             "frac_of_copy": round(gbs / copy, 4)},
     }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_linear(wl, d_host, args.cpu_seconds)
+    return result
 
 
 def bench_svg(args, wl):
@@ -326,7 +377,7 @@ def bench_svg(args, wl):
     copy = None if args.no_refs else measure_copy_gbs()
     gemm = None if args.no_refs else measure_gemm_tflops()
     src = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "svg_ear.hip")
-    return {
+    result = {
         "metric": "ms per centroid-compensated attention call (routing + attention)",
         "value": round(call_ms, 4), "unit": "ms", "higher_is_better": False,
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -349,6 +400,9 @@ def bench_svg(args, wl):
             "kernel": "sustained bf16 GEMM 8192^3 (torch.matmul)", "tflops": round(gemm, 1),
             "attn_frac_of_measured": round(achieved / gemm, 4)},
     }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_svg(wl, d, args.cpu_seconds)
+    return result
 
 
 def main():

@@ -26,6 +26,7 @@ TFLOP/s over exact plus virtual keys).
 """
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -48,7 +49,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="lvsa_32k",
-                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "svg_ear_32k"])
+                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "svg_ear_32k", "lipar_32k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -298,6 +299,88 @@ def bench_linear(args, wl):
     return result
 
 
+def bench_lipar(args, wl):
+    """Latent inter-frame pruning + restoration: one step = bsa_lipar_prune of the
+    sequence, then bsa_lipar_restore of the pruned rows back to full length."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    xb = gen.make_video(wl)
+    x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
+    out = torch.empty_like(x)
+    keep, cpos, kidx, nk, xp = bsa.lipar_prune(x, wl.frames, wl.lipar_tau)
+    ws = torch.empty(int(bsa.load().bsa_lipar_workspace(ctypes.byref(bsa._shape_of(x)))), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau, workspace=ws)
+        bsa.lipar_restore(p2, k2, c2, wl.frames, out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau, workspace=ws)
+        e[1].record()
+        bsa.lipar_restore(p2, k2, c2, wl.frames, out)
+        e[2].record()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    prune_ms = float(np.median([a[0].elapsed_time(a[1]) for a in evs]))
+    restore_ms = float(np.median([a[1].elapsed_time(a[2]) for a in evs]))
+    n_kept = int(nk.sum().item())
+    rows = wl.B * wl.H * wl.N
+    row_b = wl.D * 2
+    prune_bytes = rows * row_b + n_kept * row_b + rows * (1 + 4) + n_kept * 4
+    restore_bytes = n_kept * row_b + rows * row_b + rows * (1 + 4)
+    algo = prune_bytes + restore_bytes
+    gbs = algo / ((prune_ms + restore_ms) * 1e-3) / 1e9
+    copy = None if args.no_refs else measure_copy_gbs()
+    result = {
+        "metric": "algorithmic HBM GB/s of latent inter-frame pruning + restoration",
+        "value": round(algo * args.steps / (t1 - t0) / 1e9, 1),
+        "unit": "GB/s (read tokens, write kept rows, read kept rows, write tokens, flags and positions)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_split": {"prune": round(prune_ms, 4), "restore": round(restore_ms, 4)},
+        "kept_fraction": round(n_kept / rows, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "frames": wl.frames,
+                   "tau": wl.lipar_tau, "algorithmic_bytes": algo},
+        "roofline": {"bound": "hbm", "kernel": "lipar prune (flag, count, scan, compact) + restore",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "measured_copy": None if copy is None else {
+            "kernel": "1 GiB device copy, read + write", "gbs": round(copy, 1),
+            "frac_of_copy": round(gbs / copy, 4)},
+    }
+    if args.cpu_seconds > 0:
+        from oracle import lipar as olp
+        t = time.perf_counter()
+        done = 0
+        while True:
+            xf = gen.to_f64(xb[0, 0], "bf16")
+            kk, idx, y = olp.prune(xf, wl.frames, wl.lipar_tau)
+            olp.restore(y, kk, wl.frames)
+            done += 1
+            if time.perf_counter() - t >= min(args.cpu_seconds, 5.0):
+                break
+        dt = time.perf_counter() - t
+        result["cpu_baseline"] = {"value": round(done * algo / (wl.B * wl.H) / dt / 1e9, 4),
+                                  "unit": result["unit"], "cores": int(_oracle_threads()), "kind": "oracle",
+                                  "sample": f"{done} full sequence(s) (prune + restore): {dt:.1f} s, float64 numpy"}
+    return result
+
+
 def bench_svg(args, wl):
     """Centroid compensation: one step = one bsa_centroid_compensate call."""
     import numpy as np
@@ -428,6 +511,9 @@ def main():
         return
     if wl.values == "gmm":
         print(json.dumps(bench_svg(args, wl)), flush=True)
+        return
+    if wl.values == "video":
+        print(json.dumps(bench_lipar(args, wl)), flush=True)
         return
     bsa.load()
     dev = torch.device("cuda:0")

@@ -65,6 +65,11 @@ _SIGNATURES = {
     "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_lipar_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "bsa_lipar_prune": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_float,
+                                       _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_lipar_restore": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P,
+                                         _P]),
     "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "bsa_last_error": (ctypes.c_char_p, []),
 }
@@ -346,3 +351,35 @@ def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out
                                        float(scale), _ptr(rrow), _ptr(rcol), _ptr(score), _ptr(workspace),
                                        workspace.numel(), _stream(q.device)), "bsa_centroid_compensate")
     return (out, lse, rrow, rcol, score) if return_score else (out, lse, rrow, rcol)
+
+
+def lipar_prune(x, frames: int, tau: float, workspace=None):
+    """Latent inter-frame pruning of x [B, H, N, D] (bf16); returns
+    (keep uint8 [B*H, N], cpos int32 [B*H, N], kept_idx int32 [B*H, N],
+    n_kept int32 [B*H], x_pruned bf16 [B*H, N, D] with rows < n_kept valid)."""
+    lib = load()
+    shape = _shape_of(x)
+    B, H, N, D = x.shape
+    dev = x.device
+    keep = torch.empty((B * H, N), dtype=torch.uint8, device=dev)
+    cpos = torch.empty((B * H, N), dtype=torch.int32, device=dev)
+    kidx = torch.empty((B * H, N), dtype=torch.int32, device=dev)
+    nk = torch.empty((B * H,), dtype=torch.int32, device=dev)
+    xp = torch.empty((B * H, N, D), dtype=x.dtype, device=dev)
+    if workspace is None:
+        workspace = torch.empty(int(lib.bsa_lipar_workspace(ctypes.byref(shape))), dtype=torch.uint8, device=dev)
+    _check(lib.bsa_lipar_prune(_ptr(x), _dtype_code(x), ctypes.byref(shape), int(frames), float(tau), _ptr(keep),
+                               _ptr(cpos), _ptr(kidx), _ptr(nk), _ptr(xp), _ptr(workspace), workspace.numel(),
+                               _stream(dev)), "bsa_lipar_prune")
+    return keep, cpos, kidx, nk, xp
+
+
+def lipar_restore(y_pruned, keep, cpos, frames: int, out):
+    """Restoration into out [B, H, N, D] (bf16) from dense pruned rows y_pruned [B*H, N, D]."""
+    lib = load()
+    shape = _shape_of(out)
+    if y_pruned.shape != (shape.B * shape.H, shape.N, shape.D) or not y_pruned.is_contiguous():
+        raise BsaError("y_pruned must be a contiguous [B*H, N, D] tensor")
+    _check(lib.bsa_lipar_restore(_ptr(y_pruned), _dtype_code(out), ctypes.byref(shape), int(frames), _ptr(keep),
+                                 _ptr(cpos), _ptr(out), _stream(out.device)), "bsa_lipar_restore")
+    return out

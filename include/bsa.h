@@ -249,6 +249,49 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
                                    float scale, int32_t* route_row_ptr, int32_t* route_col,
                                    float* score, void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- latent inter-frame pruning and restoration --------------------------
+ * Source: "LIPAR: 비디오 생성 AI 를 위한 '스마트 스킵' 기술" (summary of the
+ * LIPAR paper), section 2 Methodology, B. LIPAR pipeline: latent inter-frame
+ * pruning (patches whose difference to the adjacent frame is at most tau are
+ * dropped) and restoration (the pruned sequence is expanded back by copying the
+ * previous frame's patches).
+ * Each (batch, head) slice of x [B, H, N, D] (bf16, D a multiple of 8, at most
+ * 4096) is one token sequence of `frames` frames of P = N / frames patches,
+ * token n = f * P + p.  Token (f, p), f >= 1, is kept iff
+ *   sum_c |x[f, p, c] - x[f - 1, p, c]| > tau * D
+ * (mean absolute difference to the same patch of the previous input frame
+ * above tau), the sum taken in float64 from the bf16 values (exact for values
+ * within a normal exponent range); frame 0 is always kept.  tau may be
+ * negative (keep all) or +inf (keep frame 0 only); NaN is rejected.
+ * The motion-detection refinement the page mentions is not specified there and
+ * is not applied. */
+
+/* Workspace bytes of bsa_lipar_prune (0 for an invalid shape). */
+size_t bsa_lipar_workspace(const bsa_shape* shape);
+
+/* Outputs, all caller-owned device arrays, per sequence r = b * H + h:
+ *   keep     uint8 [B*H][N]  1 if kept
+ *   cpos     int32 [B*H][N]  number of kept tokens before token n (the position
+ *                            of a kept token in the pruned sequence)
+ *   kept_idx int32 [B*H][N]  entries 0 .. n_kept[r] - 1: the kept tokens, ascending
+ *   n_kept   int32 [B*H]
+ *   x_pruned bf16 dense [B*H][N][D]: rows 0 .. n_kept[r] - 1 are the kept rows in
+ *            token order (row j of sequence r at ((r * N) + j) * D); the other
+ *            rows are left untouched.
+ * workspace: at least bsa_lipar_workspace bytes, 256-byte aligned. */
+bsa_status bsa_lipar_prune(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t frames,
+                           float tau, uint8_t* keep, int32_t* cpos, int32_t* kept_idx,
+                           int32_t* n_kept, void* x_pruned, void* workspace, size_t ws_bytes,
+                           void* stream);
+
+/* Restoration: out [B, H, N, D] (bf16, strides of shape) gets, for a kept token
+ * n, row cpos[n] of y_pruned (dense [B*H][N][D] like x_pruned above), and for a
+ * pruned token (f, p) the restored row of (f - 1, p): the row of the latest kept
+ * frame of patch p.  keep and cpos as written by bsa_lipar_prune. */
+bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_shape* shape,
+                             int32_t frames, const uint8_t* keep, const int32_t* cpos, void* out,
+                             void* stream);
+
 /* Text of a status code (static storage). */
 const char* bsa_status_string(bsa_status status);
 

@@ -44,6 +44,8 @@ class Workload:
     gmm_sigma: float = 0.3
     kmeans_iters: int = 10
     ar_rho: float = 0.9
+    # latent inter-frame pruning (LIPAR): threshold on the mean |difference|
+    lipar_tau: float = 0.0
     notes: str = field(default="", compare=False)
 
     @property
@@ -95,6 +97,12 @@ WORKLOADS = {
     "linear_196k": Workload(
         name="linear_196k", seed=5, B=1, H=12, D=128, frames=126, frame_h=30, frame_w=52,
         dtype="bf16", values="iid"),
+    # LIPAR: one latent token sequence of 21 frames x 30x52 patches, 1536 values
+    # per token (a DiT hidden width); a static scene with per-frame jitter, a
+    # moving object and a region that changes every frame (the "video" recipe).
+    "lipar_32k": Workload(
+        name="lipar_32k", seed=6, B=1, H=1, D=1536, frames=21, frame_h=30, frame_w=52,
+        dtype="bf16", values="video", lipar_tau=0.05),
 }
 
 

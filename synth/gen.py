@@ -191,6 +191,37 @@ def make_clustered(wl: Workload, heads=None):
     return dict(q=q, k=k, v=v, q_off=q_off, k_off=k_off, perm_q=perm_q, perm_k=perm_k)
 
 
+def make_video(wl: Workload):
+    """Latent token sequences [B, H, N, D] (bf16 bits) of the "video" recipe.
+
+    Per (batch, head): a static background N(0, 1) per patch, plus per frame
+    0.02 N(0, 1) jitter on every value; a rectangle of frame_h/4 x frame_w/5
+    patches carrying its own N(0, 1) texture that moves one patch to the right
+    per frame (wrapping); and the bottom eighth of the frame redrawn N(0, 1)
+    every frame.  Jitter alone keeps the mean |difference| between frames near
+    0.023, the object and the changing region near 1.1.
+    """
+    F, fh, fw, D = wl.frames, wl.frame_h, wl.frame_w, wl.D
+    dt = np.uint16 if wl.dtype == "bf16" else np.float32
+    out = np.empty((wl.B, wl.H, wl.N, D), dt)
+    oh, ow = max(1, fh // 4), max(1, fw // 5)
+    h0 = fh // 3
+    ch = max(1, fh // 8)
+    for b in range(wl.B):
+        for h in range(wl.H):
+            bg = normal_f32((wl.seed, 0, b, h, _PURPOSE_NOISE), (fh, fw, D))
+            tex = normal_f32((wl.seed, 1, b, h, _PURPOSE_NOISE), (oh, ow, D))
+            x = np.empty((F, fh, fw, D), np.float32)
+            for f in range(F):
+                fr = bg + np.float32(0.02) * normal_f32((wl.seed, 2, b, h, f), (fh, fw, D))
+                cols = (np.arange(ow) + f) % fw
+                fr[h0:h0 + oh][:, cols] = tex
+                fr[fh - ch:] = normal_f32((wl.seed, 3, b, h, f), (ch, fw, D))
+                x[f] = fr
+            out[b, h] = store(x.reshape(wl.N, D), wl.dtype)
+    return out
+
+
 def scaled(wl: Workload, **changes) -> Workload:
     """A smaller (or otherwise changed) copy of a workload with the same recipe."""
     return dataclasses.replace(wl, **changes)

@@ -26,7 +26,6 @@ TFLOP/s over exact plus virtual keys).
 """
 
 import argparse
-import ctypes
 import hashlib
 import json
 import math
@@ -314,11 +313,9 @@ def bench_lipar(args, wl):
     x = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).to(dev)
     out = torch.empty_like(x)
     keep, cpos, kidx, nk, xp = bsa.lipar_prune(x, wl.frames, wl.lipar_tau)
-    ws = torch.empty(int(bsa.load().bsa_lipar_workspace(ctypes.byref(bsa._shape_of(x)))), dtype=torch.uint8,
-                     device=dev)
 
     def step():
-        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau, workspace=ws)
+        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau)
         bsa.lipar_restore(p2, k2, c2, wl.frames, out)
 
     for _ in range(args.warmup):
@@ -328,7 +325,7 @@ def bench_lipar(args, wl):
     t0 = time.perf_counter()
     for e in evs:
         e[0].record()
-        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau, workspace=ws)
+        k2, c2, _, _, p2 = bsa.lipar_prune(x, wl.frames, wl.lipar_tau)
         e[1].record()
         bsa.lipar_restore(p2, k2, c2, wl.frames, out)
         e[2].record()

@@ -65,9 +65,8 @@ _SIGNATURES = {
     "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "bsa_lipar_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_lipar_prune": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_float,
-                                       _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+                                       _P, _P, _P, _P, _P, _P]),
     "bsa_lipar_restore": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P,
                                          _P]),
     "bsa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -353,7 +352,7 @@ def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out
     return (out, lse, rrow, rcol, score) if return_score else (out, lse, rrow, rcol)
 
 
-def lipar_prune(x, frames: int, tau: float, workspace=None):
+def lipar_prune(x, frames: int, tau: float):
     """Latent inter-frame pruning of x [B, H, N, D] (bf16); returns
     (keep uint8 [B*H, N], cpos int32 [B*H, N], kept_idx int32 [B*H, N],
     n_kept int32 [B*H], x_pruned bf16 [B*H, N, D] with rows < n_kept valid)."""
@@ -366,11 +365,8 @@ def lipar_prune(x, frames: int, tau: float, workspace=None):
     kidx = torch.empty((B * H, N), dtype=torch.int32, device=dev)
     nk = torch.empty((B * H,), dtype=torch.int32, device=dev)
     xp = torch.empty((B * H, N, D), dtype=x.dtype, device=dev)
-    if workspace is None:
-        workspace = torch.empty(int(lib.bsa_lipar_workspace(ctypes.byref(shape))), dtype=torch.uint8, device=dev)
     _check(lib.bsa_lipar_prune(_ptr(x), _dtype_code(x), ctypes.byref(shape), int(frames), float(tau), _ptr(keep),
-                               _ptr(cpos), _ptr(kidx), _ptr(nk), _ptr(xp), _ptr(workspace), workspace.numel(),
-                               _stream(dev)), "bsa_lipar_prune")
+                               _ptr(cpos), _ptr(kidx), _ptr(nk), _ptr(xp), _stream(dev)), "bsa_lipar_prune")
     return keep, cpos, kidx, nk, xp
 
 

@@ -336,14 +336,9 @@ static bsa_status check_lipar(const bsa_shape* shape, int32_t frames, const char
   return BSA_OK;
 }
 
-size_t bsa_lipar_workspace(const bsa_shape* shape) {
-  if (check_shape(shape, 2, "bsa_lipar_workspace") != BSA_OK) return 0;
-  return lipar_workspace(*shape);
-}
-
 bsa_status bsa_lipar_prune(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t frames, float tau,
                            uint8_t* keep, int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned,
-                           void* workspace, size_t ws_bytes, void* stream) {
+                           void* stream) {
   const char* fn = "bsa_lipar_prune";
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_lipar(shape, frames, fn);
@@ -351,12 +346,8 @@ bsa_status bsa_lipar_prune(const void* x, bsa_dtype dtype, const bsa_shape* shap
   if (!x || !keep || !cpos || !kept_idx || !n_kept || !x_pruned) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
   if (!aligned16(x) || !aligned16(x_pruned)) return fail(BSA_ERR_ARG, "%s: x, x_pruned must be 16-byte aligned", fn);
   if (__builtin_isnan(tau)) return fail(BSA_ERR_ARG, "%s: tau is NaN", fn);
-  const size_t need = lipar_workspace(*shape);
-  if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u))
-    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
   g_err[0] = 0;
-  return launch_lipar_prune(x, *shape, frames, tau, keep, cpos, kept_idx, n_kept, x_pruned, workspace,
-                            (hipStream_t)stream);
+  return launch_lipar_prune(x, *shape, frames, tau, keep, cpos, kept_idx, n_kept, x_pruned, (hipStream_t)stream);
 }
 
 bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_shape* shape, int32_t frames,

@@ -53,9 +53,8 @@ bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o
                             const int32_t* rcol, const float* kc, const float* vc, float scale, void* ws,
                             hipStream_t stream);
 
-size_t lipar_workspace(const bsa_shape& s);
 bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, float tau, uint8_t* keep,
-                              int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned, void* ws,
+                              int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned,
                               hipStream_t stream);
 bsa_status launch_lipar_restore(const void* y_pruned, const bsa_shape& s, int frames, const uint8_t* keep,
                                 const int32_t* cpos, void* out, hipStream_t stream);

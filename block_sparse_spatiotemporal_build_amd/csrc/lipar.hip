@@ -16,10 +16,9 @@
 //   flag    : one wave per patch walks its frames in order, holding the previous
 //             frame's row in registers (each row is read once; the next two
 //             frames' loads are in flight while a frame is reduced).
-//   count   : kept tokens per 1024-token block.
-//   scan    : one workgroup per sequence: block offsets and the kept count.
-//   compact : per block, the position of every token among the kept ones
-//             (ballots, in token order) and the kept-token list.
+//   positions : one workgroup per frame: the position of every token among
+//             the kept ones (in token order), the kept-token list and the
+//             kept count.
 //   gather  : one wave per pruned row copies its token's row.
 //   restore : one wave per output row finds its source frame (the latest kept
 //             frame of its patch, from the flags) and copies that pruned row.
@@ -28,20 +27,17 @@
 
 namespace bsa {
 
-constexpr int kLpBlock = 1024;      // tokens per count / compact block
 
 struct LiparArgs {
   const uint16_t* x;   // [B, H, N, D] with strides
   int64_t sb, sh, sn;
-  int H, N, D, F, P, nblk;
+  int H, N, D, F, P;
   double thr;          // tau * D
   uint8_t* keep;       // [BH][N]
   int32_t* cpos;       // [BH][N]: kept tokens before n
   int32_t* kidx;       // [BH][N]: token of pruned row j
   int32_t* nkept;      // [BH]
   uint16_t* xp;        // [BH][N][D] pruned rows (dense)
-  int32_t* bcount;     // [BH][nblk] workspace
-  int32_t* boff;       // [BH][nblk] workspace
 };
 
 __device__ __forceinline__ const uint16_t* lp_row(const LiparArgs& a, int bh, int n) {
@@ -92,74 +88,43 @@ __global__ void __launch_bounds__(256) lipar_flag_kernel(LiparArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(256) lipar_count_kernel(LiparArgs a) {
-  __shared__ int wsum[4];
-  const int bh = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x;
+// positions, one workgroup per (frame, sequence): the kept tokens of the
+// earlier frames give the frame's first position (coalesced byte reads, summed
+// over the workgroup), then the frame's P flags are scanned 1024 at a time in
+// token order, writing cpos, the kept-token list and, for the last frame, the
+// kept count
+__global__ void __launch_bounds__(1024) lipar_positions_kernel(LiparArgs a) {
+  __shared__ int wsum[16];
+  const int f = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint8_t* keep = a.keep + (int64_t)bh * a.N;
-  int c = 0;
-  for (int n = blk * kLpBlock + tid; n < min((blk + 1) * kLpBlock, a.N); n += 256) c += keep[n];
-  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
-  if ((tid & 63) == 0) wsum[tid >> 6] = c;
-  __syncthreads();
-  if (tid == 0) a.bcount[bh * a.nblk + blk] = wsum[0] + wsum[1] + wsum[2] + wsum[3];
-}
-
-// exclusive prefix of the block counts of one sequence (1024 threads, nblk <= 1024 * 64)
-__global__ void __launch_bounds__(1024) lipar_scan_kernel(LiparArgs a) {
-  __shared__ int part[1024];
-  const int bh = blockIdx.x, tid = threadIdx.x;
-  const int per = (a.nblk + 1023) / 1024;
-  const int b0 = min(tid * per, a.nblk), b1 = min(b0 + per, a.nblk);
-  const int32_t* cnt = a.bcount + (int64_t)bh * a.nblk;
-  int s = 0;
-  for (int b = b0; b < b1; ++b) s += cnt[b];
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int add = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
-  }
-  int run = part[tid] - s;
-  for (int b = b0; b < b1; ++b) {
-    a.boff[(int64_t)bh * a.nblk + b] = run;
-    run += cnt[b];
-  }
-  if (tid == 1023) a.nkept[bh] = part[1023];
-}
-
-// positions in token order and the copy of kept rows (4 waves; wave w takes the
-// 64-token chunks w, w + 4, ... of the block, offsets from a per-chunk prefix)
-__global__ void __launch_bounds__(256) lipar_compact_kernel(LiparArgs a) {
-  __shared__ int chunk_cnt[kLpBlock / 64];
-  const int bh = blockIdx.y, blk = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint8_t* keep = a.keep + (int64_t)bh * a.N;
-  const int n0 = blk * kLpBlock;
-  constexpr int NCH = kLpBlock / 64;
-  bool kc[NCH / 4];
-  unsigned long long bal[NCH / 4];
-#pragma unroll
-  for (int i = 0; i < NCH / 4; ++i) {
-    const int n = n0 + (i * 4 + wave) * 64 + lane;
-    kc[i] = n < a.N && keep[n] != 0;
-    bal[i] = __ballot(kc[i]);
-    if (lane == 0) chunk_cnt[i * 4 + wave] = __popcll(bal[i]);
-  }
-  __syncthreads();
-  const int base = a.boff[(int64_t)bh * a.nblk + blk];
   int32_t* cpos = a.cpos + (int64_t)bh * a.N;
   int32_t* kidx = a.kidx + (int64_t)bh * a.N;
-#pragma unroll
-  for (int i = 0; i < NCH / 4; ++i) {
-    const int ch = i * 4 + wave;
-    int before = 0;
-    for (int c = 0; c < ch; ++c) before += chunk_cnt[c];
-    const int n = n0 + ch * 64 + lane;
-    const int r = before + __popcll(bal[i] & ((1ull << lane) - 1ull));
-    if (n < a.N) cpos[n] = base + r;
-    if (kc[i]) kidx[base + r] = n;
+  const int f0 = f * a.P;
+  int c = 0;
+  for (int n = tid; n < f0; n += 1024) c += keep[n];
+  for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
+  if (lane == 0) wsum[wave] = c;
+  __syncthreads();
+  int run = 0;
+  for (int w = 0; w < 16; ++w) run += wsum[w];
+  __syncthreads();
+  for (int p0 = 0; p0 < a.P; p0 += 1024) {
+    const int n = f0 + p0 + tid;
+    const bool k = p0 + tid < a.P && keep[n] != 0;
+    const unsigned long long bal = __ballot(k);
+    if (lane == 0) wsum[wave] = __popcll(bal);
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    int total = 0;
+    for (int w = 0; w < 16; ++w) total += wsum[w];
+    const int r = before + __popcll(bal & ((1ull << lane) - 1ull));
+    if (p0 + tid < a.P) cpos[n] = r;
+    if (k) kidx[r] = n;
+    run += total;
+    __syncthreads();
   }
+  if (f == a.F - 1 && tid == 0) a.nkept[bh] = run;
 }
 
 // the kept rows into the pruned sequence: one wave per pruned row slot
@@ -203,24 +168,14 @@ __global__ void __launch_bounds__(256) lipar_restore_kernel(LiparRestoreArgs a) 
 // host side
 // ---------------------------------------------------------------------------
 
-size_t lipar_workspace(const bsa_shape& s) {
-  const size_t nblk = (size_t)(s.N + kLpBlock - 1) / kLpBlock;
-  const size_t one = ((size_t)s.B * s.H * nblk * 4 + 255) / 256 * 256;  // block counts, then offsets
-  return 2 * one;
-}
-
 bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, float tau, uint8_t* keep,
-                              int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned, void* ws,
+                              int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned,
                               hipStream_t stream) {
   LiparArgs a;
   a.x = (const uint16_t*)x; a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
   a.H = s.H; a.N = s.N; a.D = s.D; a.F = frames; a.P = s.N / frames;
-  a.nblk = (s.N + kLpBlock - 1) / kLpBlock;
   a.thr = (double)tau * (double)s.D;
   a.keep = keep; a.cpos = cpos; a.kidx = kept_idx; a.nkept = n_kept; a.xp = (uint16_t*)x_pruned;
-  const size_t half = lipar_workspace(s) / 2;
-  a.bcount = (int32_t*)ws;
-  a.boff = (int32_t*)((char*)ws + half);
   const int bh = s.B * s.H;
   const dim3 pg((a.P + 3) / 4, bh);
   const int cpl = (s.D / 8 + 63) / 64;
@@ -228,9 +183,7 @@ bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, flo
   else if (cpl <= 2) hipLaunchKernelGGL(lipar_flag_kernel<2>, pg, dim3(256), 0, stream, a);
   else if (cpl <= 4) hipLaunchKernelGGL(lipar_flag_kernel<4>, pg, dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(lipar_flag_kernel<8>, pg, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(lipar_count_kernel, dim3(a.nblk, bh), dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(lipar_scan_kernel, dim3(bh), dim3(1024), 0, stream, a);
-  hipLaunchKernelGGL(lipar_compact_kernel, dim3(a.nblk, bh), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(lipar_positions_kernel, dim3(frames, bh), dim3(1024), 0, stream, a);
   hipLaunchKernelGGL(lipar_gather_kernel, dim3((s.N + 3) / 4, bh), dim3(256), 0, stream, a);
   return launch_ok("lipar_prune") ? BSA_OK : BSA_ERR_HIP;
 }

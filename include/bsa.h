@@ -266,9 +266,6 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
  * The motion-detection refinement the page mentions is not specified there and
  * is not applied. */
 
-/* Workspace bytes of bsa_lipar_prune (0 for an invalid shape). */
-size_t bsa_lipar_workspace(const bsa_shape* shape);
-
 /* Outputs, all caller-owned device arrays, per sequence r = b * H + h:
  *   keep     uint8 [B*H][N]  1 if kept
  *   cpos     int32 [B*H][N]  number of kept tokens before token n (the position
@@ -277,12 +274,10 @@ size_t bsa_lipar_workspace(const bsa_shape* shape);
  *   n_kept   int32 [B*H]
  *   x_pruned bf16 dense [B*H][N][D]: rows 0 .. n_kept[r] - 1 are the kept rows in
  *            token order (row j of sequence r at ((r * N) + j) * D); the other
- *            rows are left untouched.
- * workspace: at least bsa_lipar_workspace bytes, 256-byte aligned. */
+ *            rows are left untouched. */
 bsa_status bsa_lipar_prune(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t frames,
                            float tau, uint8_t* keep, int32_t* cpos, int32_t* kept_idx,
-                           int32_t* n_kept, void* x_pruned, void* workspace, size_t ws_bytes,
-                           void* stream);
+                           int32_t* n_kept, void* x_pruned, void* stream);
 
 /* Restoration: out [B, H, N, D] (bf16, strides of shape) gets, for a kept token
  * n, row cpos[n] of y_pruned (dense [B*H][N][D] like x_pruned above), and for a

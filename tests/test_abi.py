@@ -133,24 +133,19 @@ def test_each_struct_is_defined_once_in_the_native_sources():
                 seen[name] = f
 
 
-def _lipar(lib, shape, frames=4, tau=0.1, ptr=4096, ws=4096, ws_bytes=1 << 20):
+def _lipar(lib, shape, frames=4, tau=0.1, ptr=4096):
     p = ctypes.c_void_p(ptr)
-    return lib.bsa_lipar_prune(p, 0, ctypes.byref(shape), frames, ctypes.c_float(tau), p, p, p, p, p,
-                               ctypes.c_void_p(ws), ws_bytes, None)
+    return lib.bsa_lipar_prune(p, 0, ctypes.byref(shape), frames, ctypes.c_float(tau), p, p, p, p, p, None)
 
 
 def test_lipar_argument_checks(lib):
     ok = _shape(B=1, H=2, N=256, D=64)
-    assert lib.bsa_lipar_workspace(ctypes.byref(ok)) % 256 == 0
-    assert lib.bsa_lipar_workspace(ctypes.byref(ok)) > 0
     assert _lipar(lib, _shape(D=60)) == 1                        # 120-byte rows: not 16-byte multiple
     assert _lipar(lib, _shape(D=68, sn=72)) == 2                 # D not a multiple of 8
     assert _lipar(lib, _shape(D=4104)) == 2                      # D > 4096
     assert _lipar(lib, ok, frames=3) == 1                        # 3 does not divide 256
     assert _lipar(lib, ok, frames=0) == 1
     assert _lipar(lib, ok, tau=float("nan")) == 1
-    assert _lipar(lib, ok, ws_bytes=16) == 4                     # workspace too small
-    assert _lipar(lib, ok, ws=4097) == 4                         # misaligned workspace
     assert _lipar(lib, ok, ptr=4098) == 1                        # misaligned tensor
     assert b"bsa_lipar_prune" in lib.bsa_last_error()
     p = ctypes.c_void_p(4096)

@@ -36,3 +36,31 @@ def linear_attention_rows(q_rows, S, z):
     """Apply a given state (S, z) to some query rows (float64 [..., D])."""
     fq = phi(q_rows)
     return (fq @ S) / (fq @ z)[..., None]
+
+
+def causal_linear_attention(q, k, v, rows=None):
+    """Causal elu+1 linear attention, float64 [B, H, N, D] inputs.
+
+    Each query sees only itself and the tokens before it:
+        out_n = sum_{m <= n} (phi(q_n) . phi(k_m)) v_m / sum_{m <= n} phi(q_n) . phi(k_m)
+    which is phi(q_n)^T S_n / phi(q_n)^T z_n with prefix states S_n, z_n (the
+    causal form used by autoregressive video models such as the Self-Forcing
+    setting of the LIPAR page).  Written out as that quadratic form, one query
+    row at a time; ``rows`` restricts the computation to some query rows (the
+    others are NaN).
+    """
+    fq, fk = phi(q), phi(k)
+    v = np.asarray(v, np.float64)
+    B, H, N, D = fq.shape
+    out = np.full((B, H, N, v.shape[-1]), np.nan)
+    for n in (range(N) if rows is None else rows):
+        w = np.einsum("bhd,bhmd->bhm", fq[:, :, n], fk[:, :, : n + 1])
+        out[:, :, n] = np.einsum("bhm,bhme->bhe", w, v[:, :, : n + 1]) / w.sum(axis=2)[..., None]
+    return out
+
+
+def mixed_attention(soft_out, lin_out, r: float):
+    """LinVideo mixed attention (technical summary, section 2 A. Selective
+    Transfer): a per-layer scalar r in [0, 1] blends quadratic attention
+    (r = 1) and linear attention (r = 0): r * soft_out + (1 - r) * lin_out."""
+    return r * np.asarray(soft_out, np.float64) + (1.0 - r) * np.asarray(lin_out, np.float64)

@@ -65,6 +65,9 @@ _SIGNATURES = {
     "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_mixed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P, _P,
+                                          ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t,
+                                          _P]),
     "bsa_lipar_prune": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_float,
                                        _P, _P, _P, _P, _P, _P]),
     "bsa_lipar_restore": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, _P, _P, _P,
@@ -378,4 +381,23 @@ def lipar_restore(y_pruned, keep, cpos, frames: int, out):
         raise BsaError("y_pruned must be a contiguous [B*H, N, D] tensor")
     _check(lib.bsa_lipar_restore(_ptr(y_pruned), _dtype_code(out), ctypes.byref(shape), int(frames), _ptr(keep),
                                  _ptr(cpos), _ptr(out), _stream(out.device)), "bsa_lipar_restore")
+    return out
+
+
+def mixed_attn_fwd(q, k, v, r: float, row_ptr=None, col_idx=None, block: int = 128, scale=None, out=None,
+                   row_order=None, workspace=None):
+    """r * block-sparse softmax attention + (1 - r) * elu+1 linear attention (bf16, D = 128)."""
+    lib = load()
+    _check_qkv(q, k, v)
+    shape = _shape_of(q)
+    D = q.shape[3]
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if workspace is None and r < 1.0:
+        workspace = torch.empty(linear_attn_workspace(q), dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_mixed_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q), ctypes.byref(shape),
+                                  _ptr(row_ptr), _ptr(col_idx), _ptr(row_order), int(block), float(scale),
+                                  float(r), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                                  _stream(q.device)), "bsa_mixed_attn_fwd")
     return out

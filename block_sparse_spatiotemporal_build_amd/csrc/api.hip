@@ -156,6 +156,38 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
   return launch_linear_attn(q, k, v, o, *shape, S, z, workspace, (hipStream_t)stream);
 }
 
+bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                              const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                              const int32_t* row_order, int32_t block, float scale, float r, void* workspace,
+                              size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_mixed_attn_fwd";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (!(r >= 0.f && r <= 1.f)) return fail(BSA_ERR_ARG, "%s: r must be in [0, 1]", fn);
+  if (shape->D != 128 || !linear_plan(*shape).d128)
+    return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 128 (and a head within 32-bit offsets)", fn);
+  if (!q || !k || !v || !o || (r > 0.f && (!row_ptr || !col_idx)))
+    return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if (r > 0.f) {
+    if (!__builtin_isfinite(scale) || scale == 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+    if (block != 64 && block != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: block must be 64 or 128", fn);
+  }
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  const size_t need = linear_plan(*shape).total;
+  if (r < 1.f && (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0))
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
+  g_err[0] = 0;
+  hipStream_t sm = (hipStream_t)stream;
+  if (r > 0.f) {
+    st = launch_attn_bf16(q, k, v, o, nullptr, *shape, row_ptr, col_idx, row_order, block, scale, sm);
+    if (st != BSA_OK || r == 1.f) return st;
+  }
+  return launch_linear_attn(q, k, v, o, *shape, nullptr, nullptr, workspace, sm, r > 0.f ? r : -1.f);
+}
+
 // ---- clustered compensation (SVG-EAR) -------------------------------------
 
 static constexpr int kMaxKeyClusters = 512;

@@ -26,8 +26,9 @@ struct LinPlan {
   size_t off_part_s, off_part_z, off_st, off_z, total;  // workspace layout (bytes)
 };
 LinPlan linear_plan(const bsa_shape& s);
+// mix_r >= 0 (head_dim-128 plan only): o = mix_r * o + (1 - mix_r) * linear attention
 bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
-                              float* S, float* z, void* ws, hipStream_t stream);
+                              float* S, float* z, void* ws, hipStream_t stream, float mix_r = -1.f);
 
 // ---- centroid compensation with error-aware routing ------------------------
 struct ProbePlan {

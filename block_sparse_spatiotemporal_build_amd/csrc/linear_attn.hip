@@ -372,6 +372,7 @@ struct LinApplyArgs {
   int64_t sb, sh, sn;
   int H, N;
   int tph, total, tpw;  // head_dim 128 kernel: tiles per head, all tiles, tiles per workgroup
+  float mix_r;          // head_dim 128 kernel: < 0 plain; else o = mix_r * o + (1 - mix_r) * linear
 };
 
 template <int D>
@@ -549,14 +550,25 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
                    pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv)};
         *(u32x2*)&X[xoff(l32, 4 * dt + g) + 4 * hi] = w;
       }
-    // whole rows back out, 16-byte stores (rows past N are not stored)
+    // whole rows back out, 16-byte stores (rows past N are not stored); in the
+    // mixed form each row is first blended with the row already in o
     uint16_t* obase = a.o + head_off(bh) + 8 * (lane & 15);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int r = 4 * i + (lane >> 4);
-      const u32x4 v = *(const u32x4*)&X[xoff(r, lane & 15)];
+      u32x4 v = *(const u32x4*)&X[xoff(r, lane & 15)];
       const int row = tile * kApplyRows + RW * wv + r;
-      if (row < a.N) *(u32x4*)(obase + (int64_t)row * a.sn) = v;
+      if (row < a.N) {
+        if (a.mix_r >= 0.f) {
+          const u32x4 sft = *(const u32x4*)(obase + (int64_t)row * a.sn);
+          const float wl = 1.f - a.mix_r;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            v[e] = pack_bf16x2(__builtin_fmaf(a.mix_r, bf16_lo(sft[e]), wl * bf16_lo(v[e])),
+                               __builtin_fmaf(a.mix_r, bf16_hi(sft[e]), wl * bf16_hi(v[e])));
+        }
+        *(u32x4*)(obase + (int64_t)row * a.sn) = v;
+      }
     }
   }
 }
@@ -598,7 +610,7 @@ LinPlan linear_plan(const bsa_shape& s) {
 }
 
 bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
-                              float* S, float* z, void* ws, hipStream_t stream) {
+                              float* S, float* z, void* ws, hipStream_t stream, float mix_r) {
   const LinPlan p = linear_plan(s);
   char* w = (char*)ws;
   const int bh = s.B * s.H;
@@ -608,7 +620,7 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
                    (uint16_t*)(w + p.off_st), (float*)(w + p.off_z), p.splits};
   LinApplyArgs aa{(const uint16_t*)q, (uint16_t*)o, (const uint16_t*)(w + p.off_st),
                   (const float*)(w + p.off_z), s.stride_b, s.stride_h, s.stride_n, s.H, s.N,
-                  p.tph, bh * p.tph, p.tpw};
+                  p.tph, bh * p.tph, p.tpw, mix_r};
   const int row_groups = (s.N + kApplyRows * kApplyTiles - 1) / (kApplyRows * kApplyTiles);
   if (s.D == 128 && p.d128) {
     hipLaunchKernelGGL(lin_state_d128_kernel, dim3(p.splits, bh), dim3(kLinThreads), 0, stream, sa);

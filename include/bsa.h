@@ -154,6 +154,25 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
                                const bsa_shape* shape, float* S, float* z, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Mixed attention.  Source: "LinVideo: A Post-Training Framework towards O(n)
+ * Attention in Efficient Video Generation", technical summary section 2 A.
+ * Selective Transfer: a per-layer scalar r in [0, 1] blends quadratic
+ * attention (r = 1) and linear attention (r = 0):
+ *   o = r * block_sparse_attn(q, k, v; row_ptr, col_idx, block, scale)
+ *       + (1 - r) * linear_attn(q, k, v)
+ * (the quadratic branch is the block-sparse call above; an all-blocks mask is
+ * dense attention).  bf16, D = 128.  With r = 1 only the quadratic branch runs
+ * (workspace may be NULL), with r = 0 only the linear one (row_ptr, col_idx may
+ * be NULL).  Otherwise the quadratic output is written to o first and the
+ * linear pass blends into it row by row: each branch is rounded to bf16 once
+ * before the blend (two roundings in all).
+ * workspace: at least bsa_linear_attn_workspace bytes, 256-byte aligned.
+ * r outside [0, 1] or NaN is rejected. */
+bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                              const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
+                              const int32_t* row_order, int32_t block, float scale, float r,
+                              void* workspace, size_t ws_bytes, void* stream);
+
 /* ---- clustered sparse attention with centroid compensation ---------------
  * Source: "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
  * Generation via Error-aware Routing", technical summary section 2 Method.

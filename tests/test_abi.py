@@ -151,3 +151,22 @@ def test_lipar_argument_checks(lib):
     p = ctypes.c_void_p(4096)
     assert lib.bsa_lipar_restore(p, 0, ctypes.byref(ok), 3, p, p, p, None) == 1
     assert lib.bsa_lipar_restore(p, 1, ctypes.byref(ok), 4, p, p, p, None) == 2   # fp32 not implemented
+
+
+def _mixed(lib, shape, r=0.5, block=128, ws=1 << 30, ptr=4096, mask=4096):
+    p, m = ctypes.c_void_p(ptr), ctypes.c_void_p(mask)
+    return lib.bsa_mixed_attn_fwd(p, p, p, p, 0, ctypes.byref(shape), m, m, None, block, ctypes.c_float(0.1),
+                                  ctypes.c_float(r), ctypes.c_void_p(1 << 20), ws, None)
+
+
+def test_mixed_attention_argument_checks(lib):
+    ok = _shape(B=1, H=2, N=1000, D=128)
+    assert _mixed(lib, ok, r=-0.1) == 1
+    assert _mixed(lib, ok, r=1.5) == 1
+    assert _mixed(lib, ok, r=float("nan")) == 1
+    assert _mixed(lib, _shape(B=1, H=2, N=1000, D=64)) == 2      # D = 128 only
+    assert _mixed(lib, ok, block=32) == 2
+    assert _mixed(lib, ok, mask=0) == 1                           # softmax term needs the mask
+    assert _mixed(lib, ok, ws=16) == 4                            # linear term needs the workspace
+    assert _mixed(lib, ok, ptr=4098) == 1
+    assert b"bsa_mixed_attn_fwd" in lib.bsa_last_error()

@@ -38,7 +38,7 @@ def linear_attention_rows(q_rows, S, z):
     return (fq @ S) / (fq @ z)[..., None]
 
 
-def causal_linear_attention(q, k, v, rows=None):
+def causal_linear_attention(q, k, v, rows=None, S0=None, z0=None):
     """Causal elu+1 linear attention, float64 [B, H, N, D] inputs.
 
     Each query sees only itself and the tokens before it:
@@ -48,14 +48,26 @@ def causal_linear_attention(q, k, v, rows=None):
     setting of the LIPAR page).  Written out as that quadratic form, one query
     row at a time; ``rows`` restricts the computation to some query rows (the
     others are NaN).
+
+    Chunked use carries the state of the tokens before this sequence: with
+    S0 [B, H, D, D] and z0 [B, H, D] (sums of phi(k) v^T and phi(k) over the
+    earlier tokens) every row also sees them:
+        out_n = (phi(q_n)^T S0 + sum_{m <= n} w_nm v_m) / (phi(q_n)^T z0 + sum_{m <= n} w_nm).
+    The state after the sequence is S0 + S, z0 + z with S, z of
+    ``linear_attention``.
     """
     fq, fk = phi(q), phi(k)
     v = np.asarray(v, np.float64)
     B, H, N, D = fq.shape
-    out = np.full((B, H, N, v.shape[-1]), np.nan)
+    E = v.shape[-1]
+    S0 = np.zeros((B, H, D, E)) if S0 is None else np.asarray(S0, np.float64)
+    z0 = np.zeros((B, H, D)) if z0 is None else np.asarray(z0, np.float64)
+    out = np.full((B, H, N, E), np.nan)
     for n in (range(N) if rows is None else rows):
         w = np.einsum("bhd,bhmd->bhm", fq[:, :, n], fk[:, :, : n + 1])
-        out[:, :, n] = np.einsum("bhm,bhme->bhe", w, v[:, :, : n + 1]) / w.sum(axis=2)[..., None]
+        num = np.einsum("bhm,bhme->bhe", w, v[:, :, : n + 1]) + np.einsum("bhd,bhde->bhe", fq[:, :, n], S0)
+        den = w.sum(axis=2) + np.einsum("bhd,bhd->bh", fq[:, :, n], z0)
+        out[:, :, n] = num / den[..., None]
     return out
 
 

@@ -77,3 +77,37 @@ def test_mixed_endpoints_and_affinity(r):
         assert np.array_equal(mixed, soft)
     if r == 0.0:
         assert np.array_equal(mixed, lin)
+
+
+@pytest.mark.parametrize("cut", [1, 5, 12])
+def test_carried_state_continues_the_sequence(cut):
+    """Running the tokens after ``cut`` with the state of the tokens before it
+    (taken from the pinned non-causal oracle) gives the causal output of the
+    whole sequence on those rows."""
+    q, k, v = _qkv(2, 2, 17, 4, 7)
+    whole = ol.causal_linear_attention(q, k, v)
+    _, S0, z0 = ol.linear_attention(q[:, :, :cut], k[:, :, :cut], v[:, :, :cut])
+    tail = ol.causal_linear_attention(q[:, :, cut:], k[:, :, cut:], v[:, :, cut:], S0=S0, z0=z0)
+    assert np.allclose(tail, whole[:, :, cut:], rtol=1e-12, atol=1e-12)
+
+
+def test_carried_state_brute_force():
+    """A given (S0, z0) enters numerator and denominator as phi(q).S0 and phi(q).z0."""
+    q, k, v = _qkv(1, 1, 4, 3, 8)
+    r = np.random.default_rng(9)
+    S0 = r.random((1, 1, 3, 3)) * 5
+    z0 = r.random((1, 1, 3)) * 5 + 0.5
+
+    def phi(x):
+        return x + 1.0 if x > 0 else np.exp(x)
+
+    out = ol.causal_linear_attention(q, k, v, S0=S0, z0=z0)
+    for n in range(4):
+        fq = [phi(q[0, 0, n, d]) for d in range(3)]
+        num = np.array([sum(fq[d] * S0[0, 0, d, e] for d in range(3)) for e in range(3)])
+        den = sum(fq[d] * z0[0, 0, d] for d in range(3))
+        for m in range(n + 1):
+            w = sum(fq[d] * phi(k[0, 0, m, d]) for d in range(3))
+            num = num + w * v[0, 0, m]
+            den += w
+        assert np.allclose(out[0, 0, n], num / den, rtol=1e-12)

@@ -47,6 +47,9 @@ _SIGNATURES = {
     "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                            _P, ctypes.c_size_t, _P]),
+    "bsa_causal_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "bsa_causal_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
+                                                  _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_cluster_centroids": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                              ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "bsa_route_scores_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
@@ -242,6 +245,54 @@ def linear_attn_fwd(q, k, v, out=None, return_state: bool = False, workspace=Non
                                    workspace.numel(), _stream(q.device)),
            "bsa_linear_attn_fwd")
     return (out, S, z) if return_state else out
+
+
+def causal_linear_attn_workspace(shape_like) -> int:
+    return int(load().bsa_causal_linear_attn_workspace(ctypes.byref(_shape_of(shape_like))))
+
+
+def _state_tensor(t, shape, name):
+    if t is None:
+        return None
+    if t.dtype != torch.float32 or not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+        raise BsaError(f"{name} must be a contiguous fp32 device tensor of shape {shape}")
+    return t
+
+
+def causal_linear_attn_fwd(q, k, v, out=None, state=None, return_state: bool = False, state_out=None,
+                           workspace=None):
+    """Causal elu+1 linear attention (bf16, D = 128).
+
+    ``state`` = (S, z) carried in from earlier tokens (fp32 [B,H,D,D], [B,H,D]);
+    with ``return_state`` (or a given ``state_out`` pair, which may be ``state``
+    itself) the state after the last token is returned as well."""
+    lib = load()
+    _check_qkv(q, k, v)
+    shape = _shape_of(q)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if out.stride() != q.stride() or out.dtype != q.dtype:
+        raise BsaError("out must have the layout and dtype of q")
+    B, H, N, D = q.shape
+    S_in = z_in = None
+    if state is not None:
+        S_in = _state_tensor(state[0], (B, H, D, D), "S")
+        z_in = _state_tensor(state[1], (B, H, D), "z")
+    S_out = z_out = None
+    if state_out is not None:
+        S_out = _state_tensor(state_out[0], (B, H, D, D), "S_out")
+        z_out = _state_tensor(state_out[1], (B, H, D), "z_out")
+    elif return_state:
+        S_out = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device)
+        z_out = torch.empty((B, H, D), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        need = int(lib.bsa_causal_linear_attn_workspace(ctypes.byref(shape)))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_causal_linear_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
+                                          ctypes.byref(shape), _ptr(S_in), _ptr(z_in), _ptr(S_out), _ptr(z_out),
+                                          _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "bsa_causal_linear_attn_fwd")
+    return (out, S_out, z_out) if (return_state or state_out is not None) else out
 
 
 # ---- clustered compensation ---------------------------------------------------

@@ -156,6 +156,37 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
   return launch_linear_attn(q, k, v, o, *shape, S, z, workspace, (hipStream_t)stream);
 }
 
+size_t bsa_causal_linear_attn_workspace(const bsa_shape* shape) {
+  if (check_shape(shape, 2, "bsa_causal_linear_attn_workspace") != BSA_OK) return 0;
+  if (shape->D != 128 || !linear_plan(*shape).d128) return 0;
+  return causal_plan(*shape).total;
+}
+
+bsa_status bsa_causal_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                                      const bsa_shape* shape, const float* S_in, const float* z_in,
+                                      float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                                      void* stream) {
+  const char* fn = "bsa_causal_linear_attn_fwd";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (shape->D != 128 || !linear_plan(*shape).d128)
+    return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 128 (and a head within 32-bit offsets)", fn);
+  if (!q || !k || !v || !o) return fail(BSA_ERR_ARG, "%s: NULL tensor pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
+    return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
+  if ((S_in == nullptr) != (z_in == nullptr)) return fail(BSA_ERR_ARG, "%s: give both S_in and z_in or neither", fn);
+  if (!aligned16(S_in) || !aligned16(z_in) || !aligned16(S_out) || !aligned16(z_out))
+    return fail(BSA_ERR_ARG, "%s: S_in, z_in, S_out, z_out must be 16-byte aligned", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  const size_t need = causal_plan(*shape).total;
+  if (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                workspace ? ws_bytes : (size_t)0);
+  g_err[0] = 0;
+  return launch_causal_linear_attn(q, k, v, o, *shape, S_in, z_in, S_out, z_out, workspace, (hipStream_t)stream);
+}
+
 bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
                               const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
                               const int32_t* row_order, int32_t block, float scale, float r, void* workspace,

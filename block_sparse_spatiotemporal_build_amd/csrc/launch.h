@@ -30,6 +30,18 @@ LinPlan linear_plan(const bsa_shape& s);
 bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
                               float* S, float* z, void* ws, hipStream_t stream, float mix_r = -1.f);
 
+// causal (chunked) linear attention, head_dim 128: state partials over splits
+// of chunk_s tokens, an exclusive prefix at every f-th split, and the causal
+// walk over apply splits of chunk_a = f * chunk_s tokens
+struct CausalPlan {
+  int chunk_s, splits_s, chunk_a, splits_a, f;
+  size_t off_part_s, off_part_z, total;  // workspace layout (bytes)
+};
+CausalPlan causal_plan(const bsa_shape& s);
+bsa_status launch_causal_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
+                                     const float* s_in, const float* z_in, float* s_out, float* z_out, void* ws,
+                                     hipStream_t stream);
+
 // ---- centroid compensation with error-aware routing ------------------------
 struct ProbePlan {
   int splits, cps;  // key-cluster splits per head and clusters per split

@@ -574,6 +574,326 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Causal (chunked) linear attention, head_dim 128.
+//
+//   out_n = phi(q_n)^T S_n / phi(q_n)^T z_n,  S_n = S0 + sum_{m <= n} phi(k_m) v_m^T,
+//   z_n = z0 + sum_{m <= n} phi(k_m),
+// with (S0, z0) the state carried in from earlier tokens (zero if none).
+//
+// Three launches:
+//   state  : lin_state_d128_kernel over token splits of chunk_s tokens.
+//   prefix : per head, the split partials are summed in order; every f-th split
+//            is overwritten with the state before it (exclusive prefix, starting
+//            from the carried state), and the state after the last token is the
+//            optional output.
+//   causal : grid (apply splits, B*H), an apply split being f state splits.  A
+//            workgroup walks its split in steps of 32 tokens, holding the running
+//            state in MFMA accumulators (wave w owns S rows d1 in [32w, 32w+32))
+//            and a bf16 copy of S^T plus z in LDS.  Per step:
+//              - Q, K, V tiles arrive by buffer loads into a ring of three stages
+//                (rows swizzled for the transpose read), two steps ahead;
+//              - phi is applied in place to the K and Q tiles (fp32, rounded to
+//                bf16; K rows past the split are zeroed), the fp32 phi(k) column
+//                sums go to z and phi(q_n) . z_prev to a per-row LDS slot;
+//              - every wave computes the 32 x 32 score tile A^T = phi(K) phi(Q)^T
+//                of the step (keys x queries) and masks keys after the query;
+//              - wave w produces output columns d2 in [32w, 32w+32):
+//                O^T = S_prev^T phi(Q)^T + V^T A^T (the P operand of the second
+//                product is the masked score accumulator, as in the softmax
+//                kernel's O^T += V^T P^T);
+//              - the denominator is phi(q_n) . z_prev plus the masked score row
+//                sum;
+//              - the state takes the step: S += phi(K)^T V, and the bf16 S^T copy
+//                for the next step goes to the other half of a double buffer.
+// ---------------------------------------------------------------------------
+
+struct LinPrefixArgs {
+  float* part_s;       // [BH][splits][D][D]: partials in; exclusive prefix at every f-th split out
+  float* part_z;       // [BH][splits][D]
+  const float* s_in;   // nullable [BH][D][D] carried state
+  const float* z_in;   // nullable [BH][D]
+  float* s_out;        // nullable [BH][D][D] state after the sequence (may alias s_in)
+  float* z_out;        // nullable [BH][D]
+  int splits, f;
+};
+
+// one thread per float4 column of a head's S (or z); reads every partial once,
+// in split order (deterministic)
+template <int C4>
+__device__ __forceinline__ void prefix_column(float4* __restrict__ p, const float4* in, float4* out, int idx,
+                                              int splits, int f) {
+  float4 run = in ? in[idx] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+  for (int s = 0; s < splits; ++s) {
+    const float4 x = p[(int64_t)s * C4 + idx];
+    if (s % f == 0) p[(int64_t)s * C4 + idx] = run;
+    run.x += x.x; run.y += x.y; run.z += x.z; run.w += x.w;
+  }
+  if (out) out[idx] = run;
+}
+
+// grid (17, BH): blocks 0..15 scan S (4096 float4 columns), block 16 scans z
+__global__ void __launch_bounds__(256) lin_prefix_d128_kernel(LinPrefixArgs a) {
+  constexpr int D = 128;
+  const int bh = blockIdx.y, tid = threadIdx.x;
+  if (blockIdx.x < 16) {
+    const int64_t h = (int64_t)bh * D * D;
+    prefix_column<D * D / 4>((float4*)(a.part_s + h * a.splits), a.s_in ? (const float4*)(a.s_in + h) : nullptr,
+                             a.s_out ? (float4*)(a.s_out + h) : nullptr, blockIdx.x * 256 + tid, a.splits, a.f);
+  } else if (tid < D / 4) {
+    const int64_t h = (int64_t)bh * D;
+    prefix_column<D / 4>((float4*)(a.part_z + h * a.splits), a.z_in ? (const float4*)(a.z_in + h) : nullptr,
+                         a.z_out ? (float4*)(a.z_out + h) : nullptr, tid, a.splits, a.f);
+  }
+}
+
+struct CausalArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  const float* pre_s;  // [BH][splits_s][D][D]: state before state split j (j a multiple of f)
+  const float* pre_z;  // [BH][splits_s][D]
+  int64_t sb, sh, sn;
+  int H, N, chunk, splits_s, f;
+};
+
+constexpr int kCT = 32;  // tokens per step of the causal kernel
+
+// compiler-only ordering point next to a hardware barrier (emits nothing)
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
+  constexpr int D = 128, TILE = kCT * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE], Q2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t Ss[2][D * D];  // S^T bf16, rows d2 (swz_k)
+  __shared__ __attribute__((aligned(16))) float zs[2][D];
+  __shared__ __attribute__((aligned(16))) float zred[4][D];
+  __shared__ float dq[kCT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int g16 = lane >> 4, j16 = lane & 15;
+  const int split = blockIdx.x, bh = blockIdx.y;
+  const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
+  const int n0 = split * a.chunk, n1 = min(n0 + a.chunk, a.N);
+  const int nch = (n1 - n0 + kCT - 1) / kCT;
+
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane/16
+  uint32_t off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = 8 * wv + 4 * j + (lane >> 4);
+    off[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+  }
+  // six copy instructions per wave and step
+  auto dma = [&](uint16_t* qs, uint16_t* ks, uint16_t* vs, int t0) {
+    if (t0 + kCT <= a.N) {
+      const uint32_t so = (uint32_t)t0 * row_bytes;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int r = (8 * wv + 4 * j) * D;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, off[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, off[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, off[j], so, 0, 0);
+      }
+    } else {  // the sequence's last tile: rows past N repeat row N - 1 (zeroed or not stored)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int row = 8 * wv + 4 * j + (lane >> 4);
+        const uint32_t o = (uint32_t)min(t0 + row, a.N - 1) * row_bytes +
+                           (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+        const int r = (8 * wv + 4 * j) * D;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, o, 0, 0, 0);
+      }
+    }
+  };
+  // transpose read: lane (l32, hi) gets column 32 dt + l32 at the tile rows
+  // 16 ks + 8 (e / 4) + 4 hi + e % 4, e = 0..7 (the accumulator row order)
+  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> u32x4 {
+    const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
+    const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+    const int half = (j16 & 1) * 4;
+    const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
+    const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+  };
+  // row fragment: tile row r, head dims 16 t + 8 hi .. + 7
+  auto row_frag = [&](const uint16_t* st, int r, int t) -> bf16x8 {
+    return *(const bf16x8*)&st[r * D + (((2 * t + hi) ^ swz_v(r)) << 3)];
+  };
+  // the bf16 S^T copy: acc[dt][r] = S[32 w + 8 (r / 4) + 4 hi + r % 4][32 dt + l32]
+  f32x16 acc[4];
+  auto write_state = [&](uint16_t* dst) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int row = 32 * dt + l32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(acc[dt][4 * g], acc[dt][4 * g + 1]),
+                         pack_bf16x2(acc[dt][4 * g + 2], acc[dt][4 * g + 3])};
+        *(u32x2*)&dst[row * D + (((4 * wave + g) ^ swz_k(row)) << 3) + 4 * hi] = w;
+      }
+    }
+  };
+
+  // state at the split's first token
+  {
+    const int64_t j = (int64_t)bh * a.splits_s + (int64_t)split * a.f;
+    const float* ps = a.pre_s + j * D * D;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        acc[dt][r] = ps[(32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3)) * D + 32 * dt + l32];
+    write_state(Ss[0]);
+    if (tid < D) zs[0][tid] = a.pre_z[j * D + tid];
+  }
+  if (nch > 0) dma(Q0, K0, V0, n0);
+  if (nch > 1) dma(Q1, K1, V1, n0 + kCT);
+
+  const int cc = tid & 15;            // phi pass: logical 16-byte chunk
+  const int prow = tid >> 4;          // phi pass: tile rows prow and prow + 16
+  uint16_t* obase = a.o + head_off + 32 * wave + 4 * hi;
+
+  auto step = [&](uint16_t* Qb, uint16_t* Kb, uint16_t* Vb, uint16_t* Qn, uint16_t* Kn, uint16_t* Vn, int c) {
+    const int t0 = n0 + c * kCT;
+    const float* zp = zs[c & 1];
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0): the next tile may be in flight
+    else __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
+    lds_barrier();
+
+    // phi in place on the K and Q tiles; z and phi(q) . z_prev partials in fp32
+    {
+      float zk[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) zk[e] = 0.f;
+      const f32x4 z0 = *(const f32x4*)&zp[8 * cc], z1 = *(const f32x4*)&zp[8 * cc + 4];
+      const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = prow + 16 * i;
+        const int po = row * D + ((cc ^ swz_v(row)) << 3);
+        const bool live = t0 + row < n1;
+        const u32x4 kr = *(const u32x4*)&Kb[po];
+        const u32x4 qr = *(const u32x4*)&Qb[po];
+        u32x4 kp, qp;
+        float d = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float k0 = live ? phi(bf16_lo(kr[w])) : 0.f, k1 = live ? phi(bf16_hi(kr[w])) : 0.f;
+          zk[2 * w] += k0;
+          zk[2 * w + 1] += k1;
+          kp[w] = pack_bf16x2(k0, k1);
+          const float q0 = phi(bf16_lo(qr[w])), q1 = phi(bf16_hi(qr[w]));
+          d = __builtin_fmaf(q0, zz[2 * w], d);
+          d = __builtin_fmaf(q1, zz[2 * w + 1], d);
+          qp[w] = pack_bf16x2(q0, q1);
+        }
+        *(u32x4*)&Kb[po] = kp;
+        *(u32x4*)&Qb[po] = qp;
+        // the 16 lanes of this row hold its 16 chunks
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) d += __shfl_xor(d, m, 64);
+        if (cc == 0) dq[row] = d;
+      }
+      // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same chunk
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        zk[e] += __shfl_xor(zk[e], 16, 64);
+        zk[e] += __shfl_xor(zk[e], 32, 64);
+      }
+      if (lane < 16) {
+        *(f32x4*)&zred[wave][8 * cc] = f32x4{zk[0], zk[1], zk[2], zk[3]};
+        *(f32x4*)&zred[wave][8 * cc + 4] = f32x4{zk[4], zk[5], zk[6], zk[7]};
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    lds_barrier();
+    if (tid < D) zs[(c + 1) & 1][tid] = zp[tid] + zred[0][tid] + zred[1][tid] + zred[2][tid] + zred[3][tid];
+
+    // phi(Q) B operand: query row l32, head dims 16 t + 8 hi .. + 7
+    bf16x8 qf[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) qf[t] = row_frag(Qb, l32, t);
+    // A^T = phi(K) phi(Q)^T and the inter-step term O^T = S_prev^T phi(Q)^T
+    f32x16 s = f32x16{}, o = f32x16{};
+    const uint16_t* Sp = Ss[c & 1];
+    const int srow = 32 * wave + l32;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Kb, l32, t), qf[t], s, 0, 0, 0);
+      const bf16x8 sf = *(const bf16x8*)&Sp[srow * D + (((2 * t + hi) ^ swz_k(srow)) << 3)];
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[t], o, 0, 0, 0);
+    }
+    // the step's state: S[d1 = 32 w + .., d2] += phi(K)^T V
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8 af = __builtin_bit_cast(bf16x8, tr_frag(Kb, ks, wave));
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, tr_frag(Vb, ks, dt)),
+                                                          acc[dt], 0, 0, 0);
+    }
+    // causal mask: s[r] is key 8 (r / 4) + 4 hi + r % 4 of the step, query l32
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      if (8 * (r >> 2) + 4 * hi + (r & 3) > l32) s[r] = 0.f;
+      rs += s[r];
+    }
+    const float den = pair_sum(rs) + dq[l32];
+    // intra-step term O^T += V^T A^T over the step's keys
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pw = {pack_bf16x2(s[8 * ks], s[8 * ks + 1]), pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]),
+                        pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]), pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7])};
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, tr_frag(Vb, ks, wave)),
+                                                  __builtin_bit_cast(bf16x8, pw), o, 0, 0, 0);
+    }
+    write_state(Ss[(c + 1) & 1]);
+    // o[r] = O^T[32 w + 8 (r / 4) + 4 hi + r % 4][query l32]
+    const int row = t0 + l32;
+    if (row < n1) {
+      const float inv = 1.f / den;
+      uint16_t* dst = obase + (int64_t)row * a.sn;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(o[4 * g] * inv, o[4 * g + 1] * inv),
+                         pack_bf16x2(o[4 * g + 2] * inv, o[4 * g + 3] * inv)};
+        *(u32x2*)(dst + 8 * g) = w;
+      }
+    }
+    // the tile two steps ahead goes into the stage of step c - 1 (every wave
+    // has passed this step's first barrier, so none still reads it)
+    if (c + 2 < nch) dma(Qn, Kn, Vn, t0 + 2 * kCT);
+  };
+
+  int c = 0;
+  for (; c + 3 <= nch; c += 3) {
+    step(Q0, K0, V0, Q2, K2, V2, c);
+    step(Q1, K1, V1, Q0, K0, V0, c + 1);
+    step(Q2, K2, V2, Q1, K1, V1, c + 2);
+  }
+  if (c < nch) step(Q0, K0, V0, Q2, K2, V2, c);
+  if (c + 1 < nch) step(Q1, K1, V1, Q0, K0, V0, c + 1);
+}
+
+// ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 
@@ -638,6 +958,49 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
     return BSA_ERR_UNSUPPORTED;
   }
   return launch_ok("linear_attn_fwd") ? BSA_OK : BSA_ERR_HIP;
+}
+
+CausalPlan causal_plan(const bsa_shape& s) {
+  CausalPlan p;
+  const int64_t bh = (int64_t)s.B * s.H;
+  // apply: one workgroup per CU (its LDS holds three tile stages and two S^T
+  // copies), so at most 256 workgroups in total; the state pass runs twice as
+  // many splits of half the length (its kernel fits two workgroups per CU)
+  const int64_t tiles = (s.N + kCT - 1) / kCT;
+  int64_t want = 256 / bh;
+  if (want > tiles) want = tiles;
+  if (want < 1) want = 1;
+  int64_t per = (tiles + want - 1) / want;
+  if (per > 1 && (per & 1)) ++per;
+  p.f = per > 1 ? 2 : 1;
+  p.chunk_a = (int)(per * kCT);
+  p.chunk_s = p.chunk_a / p.f;
+  p.splits_a = (int)((s.N + p.chunk_a - 1) / p.chunk_a);
+  p.splits_s = (int)((s.N + p.chunk_s - 1) / p.chunk_s);
+  const size_t D = s.D;
+  p.off_part_s = 0;
+  p.off_part_z = align256((size_t)bh * p.splits_s * D * D * 4);
+  p.total = align256(p.off_part_z + (size_t)bh * p.splits_s * D * 4);
+  return p;
+}
+
+bsa_status launch_causal_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
+                                     const float* s_in, const float* z_in, float* s_out, float* z_out, void* ws,
+                                     hipStream_t stream) {
+  const CausalPlan p = causal_plan(s);
+  char* w = (char*)ws;
+  const int bh = s.B * s.H;
+  float* part_s = (float*)(w + p.off_part_s);
+  float* part_z = (float*)(w + p.off_part_z);
+  LinStateArgs sa{(const uint16_t*)k, (const uint16_t*)v, part_s, part_z, s.stride_b, s.stride_h, s.stride_n,
+                  s.H, s.N, p.splits_s, p.chunk_s};
+  LinPrefixArgs pa{part_s, part_z, s_in, z_in, s_out, z_out, p.splits_s, p.f};
+  CausalArgs ca{(const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, part_s, part_z,
+                s.stride_b, s.stride_h, s.stride_n, s.H, s.N, p.chunk_a, p.splits_s, p.f};
+  hipLaunchKernelGGL(lin_state_d128_kernel, dim3(p.splits_s, bh), dim3(kLinThreads), 0, stream, sa);
+  hipLaunchKernelGGL(lin_prefix_d128_kernel, dim3(17, bh), dim3(256), 0, stream, pa);
+  hipLaunchKernelGGL(causal_lin_d128_kernel, dim3(p.splits_a, bh), dim3(256), 0, stream, ca);
+  return launch_ok("causal_linear_attn_fwd") ? BSA_OK : BSA_ERR_HIP;
 }
 
 }  // namespace bsa

@@ -154,6 +154,39 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
                                const bsa_shape* shape, float* S, float* z, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* Workspace bytes required by bsa_causal_linear_attn_fwd for `shape` (0 if
+ * the shape is invalid or not supported): the fp32 state partials of every
+ * token split, B * H * splits * (D * D + D) * 4 bytes, splits being about
+ * 512 / (B * H) (at least 1, at most the number of 32-token tiles). */
+size_t bsa_causal_linear_attn_workspace(const bsa_shape* shape);
+
+/* Causal (chunked) linear attention with the elu+1 feature map.
+ * Operation: the linear attention of the LinVideo page (technical summary
+ * sections 1-2) restricted to earlier tokens, the form used by causal
+ * (autoregressive) video generators such as the Self-Forcing model of the
+ * LIPAR page (sections 3 Key Contributions and 4 Results: causal as well as
+ * bidirectional attention):
+ *   S_n = S0 + sum_{m <= n} phi(k_m) v_m^T,  z_n = z0 + sum_{m <= n} phi(k_m),
+ *   o_n = phi(q_n)^T S_n / (phi(q_n)^T z_n).
+ * (S0, z0) is the state carried in from earlier tokens, so a long sequence can
+ * be processed in pieces: passing the S_out, z_out of one call as S_in, z_in of
+ * the next gives the same result as one call over the concatenation (up to
+ * fp32 rounding of the carried state).
+ * q, k, v, o: bf16 device tensors with `shape`, D = 128, 16-byte aligned rows.
+ * S_in, z_in: nullable fp32 device inputs [B, H, D, D] (row d = phi dimension
+ *   d) and [B, H, D]; both NULL (zero state) or both given.
+ * S_out, z_out: nullable fp32 device outputs, the state after the last token;
+ *   may be the same buffers as S_in, z_in.  All four 16-byte aligned.
+ * Precision: phi is taken in fp32; phi(Q), phi(K), V, the step scores and S^T
+ *   enter the MFMA as bf16; S, z, the scores and the denominator are fp32.
+ * workspace: at least bsa_causal_linear_attn_workspace(shape) bytes, 256-byte
+ *   aligned, owned by the caller; contents need not be initialised.
+ * Only dtype BSA_DT_BF16 is implemented (BSA_ERR_UNSUPPORTED otherwise). */
+bsa_status bsa_causal_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                                      const bsa_shape* shape, const float* S_in, const float* z_in,
+                                      float* S_out, float* z_out, void* workspace, size_t ws_bytes,
+                                      void* stream);
+
 /* Mixed attention.  Source: "LinVideo: A Post-Training Framework towards O(n)
  * Attention in Efficient Video Generation", technical summary section 2 A.
  * Selective Transfer: a per-layer scalar r in [0, 1] blends quadratic

@@ -170,3 +170,34 @@ def test_mixed_attention_argument_checks(lib):
     assert _mixed(lib, ok, ws=16) == 4                            # linear term needs the workspace
     assert _mixed(lib, ok, ptr=4098) == 1
     assert b"bsa_mixed_attn_fwd" in lib.bsa_last_error()
+
+
+def _causal(lib, shape, ws=1 << 30, ptr=4096, s_in=None, z_in=None, s_out=None):
+    p = ctypes.c_void_p(ptr)
+    return lib.bsa_causal_linear_attn_fwd(p, p, p, p, 0, ctypes.byref(shape), s_in, z_in, s_out, None,
+                                          ctypes.c_void_p(1 << 20), ws, None)
+
+
+def test_causal_linear_argument_checks(lib):
+    ok = _shape(B=1, H=2, N=1000, D=128)
+    assert _causal(lib, _shape(B=1, H=2, N=1000, D=64)) == 2      # D = 128 only
+    assert lib.bsa_causal_linear_attn_workspace(ctypes.byref(_shape(D=64))) == 0
+    assert _causal(lib, ok, ws=16) == 4
+    assert _causal(lib, ok, ptr=4098) == 1
+    assert _causal(lib, ok, s_in=ctypes.c_void_p(4096)) == 1        # S_in without z_in
+    assert _causal(lib, ok, s_in=ctypes.c_void_p(4096), z_in=ctypes.c_void_p(4100)) == 1   # misaligned z_in
+    assert _causal(lib, ok, s_out=ctypes.c_void_p(4104)) == 1
+    assert b"bsa_causal_linear_attn_fwd" in lib.bsa_last_error()
+    p = ctypes.c_void_p(4096)
+    assert lib.bsa_causal_linear_attn_fwd(p, p, p, p, 1, ctypes.byref(ok), None, None, None, None, p,
+                                          1 << 30, None) == 2       # fp32 not implemented
+
+
+def test_causal_workspace_plan(lib):
+    for N, H in ((1, 1), (7, 2), (1000, 3), (32760, 12), (196560, 12), (4100, 1)):
+        sh = _shape(B=1, H=H, N=N, D=128)
+        w = lib.bsa_causal_linear_attn_workspace(ctypes.byref(sh))
+        assert w > 0 and w % 256 == 0
+        tiles = -(-N // 32)
+        splits = w // (H * (128 * 128 + 128) * 4)              # about 512 / H state splits
+        assert 1 <= splits <= max(2 * 256 // H, 1) + 1 and splits <= tiles

@@ -19,10 +19,15 @@ the CPU oracle timed on a bounded sample of the same workload.
 Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens);
 linear_32k / linear_196k (elu+1 linear attention, HBM-bound: reported as
 algorithmic GB/s = (read Q, K, V + write O) / call time against 8 TB/s);
-svg_ear_32k (clustered Q/K, centroid compensation at 15% density: one step is
-the fused call; routing = centroids + scores + selection reported as
-algorithmic GB/s of reading Q, K, V once; compensated attention as effective
-TFLOP/s over exact plus virtual keys).
+causal_linear_32k (causal elu+1 linear attention: state partials, split
+prefix and the causal walk, as algorithmic GB/s like the non-causal one);
+mixed_32k (LinVideo mixed attention r = 0.5: the LVSA mask of the step, then
+one mixed call; effective TFLOP/s over kept blocks plus the linear branch's
+4 N D^2 per head); svg_ear_32k (clustered Q/K, centroid compensation at 15%
+density: one step is the fused call; routing = centroids + scores + selection
+reported as algorithmic GB/s of reading Q, K, V once; compensated attention as
+effective TFLOP/s over exact plus virtual keys); lipar_32k (latent inter-frame
+pruning and restoration as algorithmic GB/s).
 """
 
 import argparse
@@ -48,7 +53,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="lvsa_32k",
-                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "svg_ear_32k", "lipar_32k"])
+                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "causal_linear_32k",
+                             "mixed_32k", "svg_ear_32k", "lipar_32k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -298,6 +304,204 @@ def bench_linear(args, wl):
     return result
 
 
+def cpu_baseline_causal(wl, d, budget_s: float):
+    """The causal oracle (one quadratic form per query row, every head at once) on
+    uniformly drawn rows, 64 per call, until the budget is spent; the mean time
+    per row, times N, gives the whole call's time and so an algorithmic GB/s."""
+    import numpy as np
+    from oracle import linear as ol
+    from synth import gen
+    q, k, v = (gen.to_f64(d[n], wl.dtype) for n in ("q", "k", "v"))
+    rows = np.random.default_rng(0).permutation(wl.N)
+    done, dt = 0, 0.0
+    for i in range(0, wl.N, 64):
+        t0 = time.perf_counter()
+        ol.causal_linear_attention(q, k, v, rows=rows[i:i + 64].tolist())
+        dt += time.perf_counter() - t0
+        done += len(rows[i:i + 64])
+        if dt >= budget_s:
+            break
+    est_s = dt / done * wl.N
+    nbytes = 4 * wl.B * wl.H * wl.N * wl.D * 2
+    return {"value": round(nbytes / est_s / 1e9, 4), "unit": "GB/s (read Q, K, V + write O)",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"{done} uniformly drawn query rows of {wl.N} (all {wl.B * wl.H} heads each): "
+                      f"{dt:.1f} s, extrapolated by N / rows, float64 numpy"}
+
+
+def bench_causal(args, wl):
+    """Causal linear attention: one step = one bsa_causal_linear_attn_fwd call
+    (state partials, split prefix, causal walk)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_qkv(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    d_host = d if args.cpu_seconds > 0 else None
+    del d
+    out = torch.empty_like(q)
+    ws = torch.empty(bsa.causal_linear_attn_workspace(q), dtype=torch.uint8, device=dev)
+    for _ in range(args.warmup):
+        bsa.causal_linear_attn_fwd(q, k, v, out=out, workspace=ws)
+    torch.cuda.synchronize(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in evs:
+        e0.record()
+        bsa.causal_linear_attn_fwd(q, k, v, out=out, workspace=ws)
+        e1.record()
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    algo_bytes = 4 * wl.B * wl.H * wl.N * wl.D * 2
+    gbs = algo_bytes / (call_ms * 1e-3) / 1e9
+    copy = None if args.no_refs else measure_copy_gbs()
+    src = os.path.join(ROOT, "block_sparse_spatiotemporal_build_amd", "csrc", "linear_attn.hip")
+    traffic = read_traffic(wl.name, "causal_linear", src)
+    result = {
+        "metric": "algorithmic HBM GB/s of causal elu+1 linear attention",
+        "value": round(algo_bytes * args.steps / (t1 - t0) / 1e9, 1),
+        "unit": "GB/s (read Q, K, V + write O)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_per_call": round(call_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D,
+                   "algorithmic_bytes": algo_bytes},
+        "roofline": {"bound": "hbm", "kernel": "causal_linear_attn_fwd (state + prefix + causal walk)",
+                     "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "measured_copy": None if copy is None else {
+            "kernel": "1 GiB device copy, read + write", "gbs": round(copy, 1),
+            "frac_of_copy": round(gbs / copy, 4)},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_causal(wl, d_host, args.cpu_seconds)
+    return result
+
+
+def cpu_baseline_mixed(wl, d, params, budget_s: float):
+    """The oracles of both branches on whole heads in order (the linear branch of a
+    head, then its block-sparse branch block row by block row, each blended)
+    until the budget is spent, as effective TFLOP/s counted like the GPU line."""
+    import numpy as np
+    from oracle import attention as oa
+    from oracle import linear as ol
+    from oracle import mask as om
+    from synth import gen
+    m = om.block_mask(om.spec_from_params(params))
+    scale = 1.0 / math.sqrt(wl.D)
+    sizes = np.minimum(wl.block, wl.N - np.arange(wl.nb) * wl.block)
+    flops, rows_done, dt, heads = 0, 0, 0.0, 0
+    for h in range(wl.H):
+        q, k, v = (gen.to_f64(d[n][:, h:h + 1], wl.dtype) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        lin, _, _ = ol.linear_attention(q, k, v)
+        flops += 4 * wl.N * wl.D * wl.D
+        for i in range(wl.nb):
+            soft, _ = oa.block_sparse_attention(q, k, v, m, wl.block, scale, query_blocks=[i])
+            r0, r1 = i * wl.block, min((i + 1) * wl.block, wl.N)
+            ol.mixed_attention(soft[:, :, r0:r1], lin[:, :, r0:r1], wl.mix_r)
+            flops += 4 * wl.D * int(sizes[i]) * int(sizes[m[i]].sum())
+            rows_done += 1
+            if dt + time.perf_counter() - t0 >= budget_s:
+                break
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= budget_s:
+            break
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s (effective, kept blocks + linear branch)",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"{rows_done} of {wl.nb * wl.H} query-block rows (heads 0..{heads - 1} in order, "
+                      f"each head's linear branch included), mask step 0: {flops / 1e9:.1f} GFLOP in {dt:.1f} s, "
+                      "float64 numpy"}
+
+
+def bench_mixed(args, wl):
+    """LinVideo mixed attention: one step = the LVSA mask of the step, then one
+    bsa_mixed_attn_fwd call (block-sparse branch into o, linear pass blending)."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_qkv(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    params = [wl.mask_params(s) for s in wl.anchor_steps]
+    nb = wl.nb
+    rp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    ro = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(bsa.linear_attn_workspace(q), dtype=torch.uint8, device=dev)
+    lin_flops = 4 * wl.B * wl.H * wl.N * wl.D * wl.D     # S = phi(K)^T V and phi(Q) S
+    flops = []
+    for p in params:
+        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci)
+        r = rp.cpu().numpy()
+        c = ci[: int(r[-1])].cpu().numpy()
+        flops.append(kept_flops_from_csr(r, c, wl.N, wl.block, wl.D, wl.B, wl.H) + lin_flops)
+
+    def step(i, evs=None):
+        bsa.build_block_mask(params[i % len(params)], row_ptr=rp, col_idx=ci, row_order=ro)
+        if evs is not None:
+            evs[0].record()
+        bsa.mixed_attn_fwd(q, k, v, wl.mix_r, rp, ci, wl.block, out=out, row_order=ro, workspace=ws)
+        if evs is not None:
+            evs[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    call_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    step_flops = [flops[i % len(flops)] for i in range(args.steps)]
+    achieved = float(np.mean(step_flops)) / (float(np.mean(call_ms)) * 1e-3) / 1e12
+    d_host = d if args.cpu_seconds > 0 else None
+    result = {
+        "metric": "effective TFLOP/s of LinVideo mixed attention (r = 0.5) at 32K video tokens",
+        "value": round(sum(step_flops) / (t1 - t0) / 1e12, 3),
+        "unit": "TFLOP/s (kept blocks + linear branch; mask build + mixed call per step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_per_call": round(float(np.mean(call_ms)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "r": wl.mix_r,
+                   "mask": "window +-3 frames, anchor every 8th frame rotated by step s=0..3, rows+cols",
+                   "gflop_per_call": [round(f / 1e9, 2) for f in flops]},
+        "roofline": {"bound": "mfma", "kernel": "mixed_attn_fwd (block-sparse + linear with blend)",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if d_host is not None:
+        result["cpu_baseline"] = cpu_baseline_mixed(wl, d_host, params[0], args.cpu_seconds)
+    return result
+
+
 def bench_lipar(args, wl):
     """Latent inter-frame pruning + restoration: one step = bsa_lipar_prune of the
     sequence, then bsa_lipar_restore of the pruned rows back to full length."""
@@ -503,6 +707,12 @@ def main():
     from synth import gen, get_workload
 
     wl = get_workload(args.workload)
+    if wl.op == "causal":
+        print(json.dumps(bench_causal(args, wl)), flush=True)
+        return
+    if wl.op == "mixed":
+        print(json.dumps(bench_mixed(args, wl)), flush=True)
+        return
     if wl.values == "iid":
         print(json.dumps(bench_linear(args, wl)), flush=True)
         return

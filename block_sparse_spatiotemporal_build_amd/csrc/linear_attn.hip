@@ -588,8 +588,8 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
 //            optional output.
 //   causal : grid (apply splits, B*H), an apply split being f state splits.  A
 //            workgroup walks its split in steps of 32 tokens, holding the running
-//            state in MFMA accumulators (wave w owns S rows d1 in [32w, 32w+32))
-//            and a bf16 copy of S^T plus z in LDS.  Per step:
+//            state in MFMA accumulators (wave w owns S columns d2 in
+//            [32w, 32w+32)) and z in LDS.  Per step:
 //              - Q, K, V tiles arrive by buffer loads into a ring of three stages
 //                (rows swizzled for the transpose read), two steps ahead;
 //              - phi is applied in place to the K and Q tiles (fp32, rounded to
@@ -603,8 +603,9 @@ __global__ void __launch_bounds__(256) lin_apply_d128_kernel(LinApplyArgs a) {
 //                kernel's O^T += V^T P^T);
 //              - the denominator is phi(q_n) . z_prev plus the masked score row
 //                sum;
-//              - the state takes the step: S += phi(K)^T V, and the bf16 S^T copy
-//                for the next step goes to the other half of a double buffer.
+//              - the state takes the step: S += phi(K)^T V (its bf16 rounding
+//                for the inter-step product is taken from the accumulators
+//                before the update).
 // ---------------------------------------------------------------------------
 
 struct LinPrefixArgs {
@@ -667,12 +668,44 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
+template <bool B>
+struct BoolTag {
+  static constexpr bool value = B;
+};
+
+// sum over the 16 lanes of a DPP row (every lane gets the sum)
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float row16_sum(float x) {
+  x += dpp_f<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+  x += dpp_f<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+  x += dpp_f<0x141>(x);  // row_half_mirror
+  x += dpp_f<0x140>(x);  // row_mirror
+  return x;
+}
+
+// x + x of lane ^ 16
+__device__ __forceinline__ float xor16_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Wave w owns the state columns d2 in [32w, 32w + 32): acc[t][r] =
+// S[32 t + 8 (r / 4) + 4 hi + r % 4][32 w + l32].  That block, rounded to bf16,
+// is the A operand of the inter-step product O^T[d2 in the wave's block] =
+// S^T phi(Q)^T: for k-step f (d1 in [16 f, 16 f + 16)) the two halves of the
+// wave swap the 4-value groups they do not hold, after which lane (l32, hi)
+// has d1 = 16 f + 8 hi .. + 7 like the phi(Q) row fragment (one 16-byte read).
+// No copy of S goes through LDS; LDS holds the tile ring (72 KiB) and z, so
+// two workgroups fit a CU.
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+causal_lin_d128_kernel(CausalArgs a) {
   constexpr int D = 128, TILE = kCT * D;
   __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE], Q2[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t Ss[2][D * D];  // S^T bf16, rows d2 (swz_k)
   __shared__ __attribute__((aligned(16))) float zs[2][D];
   __shared__ __attribute__((aligned(16))) float zred[4][D];
   __shared__ float dq[kCT];
@@ -724,43 +757,28 @@ __global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
   };
   // transpose read: lane (l32, hi) gets column 32 dt + l32 at the tile rows
   // 16 ks + 8 (e / 4) + 4 hi + e % 4, e = 0..7 (the accumulator row order)
-  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> u32x4 {
+  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> bf16x8 {
     const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
     const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
     const int half = (j16 & 1) * 4;
     const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
     const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
-    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+    return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
   };
-  // row fragment: tile row r, head dims 16 t + 8 hi .. + 7
-  auto row_frag = [&](const uint16_t* st, int r, int t) -> bf16x8 {
-    return *(const bf16x8*)&st[r * D + (((2 * t + hi) ^ swz_v(r)) << 3)];
-  };
-  // the bf16 S^T copy: acc[dt][r] = S[32 w + 8 (r / 4) + 4 hi + r % 4][32 dt + l32]
-  f32x16 acc[4];
-  auto write_state = [&](uint16_t* dst) {
-#pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const int row = 32 * dt + l32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const u32x2 w = {pack_bf16x2(acc[dt][4 * g], acc[dt][4 * g + 1]),
-                         pack_bf16x2(acc[dt][4 * g + 2], acc[dt][4 * g + 3])};
-        *(u32x2*)&dst[row * D + (((4 * wave + g) ^ swz_k(row)) << 3) + 4 * hi] = w;
-      }
-    }
+  // row fragment f of tile row r: head dims 16 f + 8 hi .. + 7 (one 16-byte chunk)
+  auto row_frag = [&](const uint16_t* st, int r, int f) -> bf16x8 {
+    return *(const bf16x8*)&st[r * D + (((2 * f + hi) ^ swz_v(r)) << 3)];
   };
 
   // state at the split's first token
+  f32x16 acc[4];
   {
     const int64_t j = (int64_t)bh * a.splits_s + (int64_t)split * a.f;
-    const float* ps = a.pre_s + j * D * D;
+    const float* ps = a.pre_s + j * D * D + 32 * wave + l32;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt)
+    for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        acc[dt][r] = ps[(32 * wave + 8 * (r >> 2) + 4 * hi + (r & 3)) * D + 32 * dt + l32];
-    write_state(Ss[0]);
+      for (int r = 0; r < 16; ++r) acc[t][r] = ps[(32 * t + 8 * (r >> 2) + 4 * hi + (r & 3)) * D];
     if (tid < D) zs[0][tid] = a.pre_z[j * D + tid];
   }
   if (nch > 0) dma(Q0, K0, V0, n0);
@@ -778,7 +796,8 @@ __global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
     lds_barrier();
 
     // phi in place on the K and Q tiles; z and phi(q) . z_prev partials in fp32
-    {
+    // (K rows past the split are zeroed; only a sequence's last tile has any)
+    auto convert = [&](auto full) {
       float zk[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) zk[e] = 0.f;
@@ -788,7 +807,7 @@ __global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
       for (int i = 0; i < 2; ++i) {
         const int row = prow + 16 * i;
         const int po = row * D + ((cc ^ swz_v(row)) << 3);
-        const bool live = t0 + row < n1;
+        const bool live = decltype(full)::value || t0 + row < n1;
         const u32x4 kr = *(const u32x4*)&Kb[po];
         const u32x4 qr = *(const u32x4*)&Qb[po];
         u32x4 kp, qp;
@@ -806,48 +825,59 @@ __global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
         }
         *(u32x4*)&Kb[po] = kp;
         *(u32x4*)&Qb[po] = qp;
-        // the 16 lanes of this row hold its 16 chunks
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) d += __shfl_xor(d, m, 64);
+        d = row16_sum(d);  // the 16 lanes of this row hold its 16 chunks
         if (cc == 0) dq[row] = d;
       }
       // lanes l, l ^ 16, l ^ 32, l ^ 48 hold the same chunk
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        zk[e] += __shfl_xor(zk[e], 16, 64);
-        zk[e] += __shfl_xor(zk[e], 32, 64);
-      }
+      for (int e = 0; e < 8; ++e) zk[e] = pair_sum(xor16_sum(zk[e]));
       if (lane < 16) {
         *(f32x4*)&zred[wave][8 * cc] = f32x4{zk[0], zk[1], zk[2], zk[3]};
         *(f32x4*)&zred[wave][8 * cc + 4] = f32x4{zk[4], zk[5], zk[6], zk[7]};
       }
-    }
+    };
+    if (t0 + kCT <= n1) convert(BoolTag<true>{});
+    else convert(BoolTag<false>{});
+    // S_prev^T for the inter-step product, rounded before this step's update.
+    // k-step f = 2 t + ks covers d1 = 16 f + 8 hi + e: the lane of half hi
+    // holds d1 = 32 t + 8 g + 4 hi + 0..3 (g = 2 ks, 2 ks + 1), so the halves
+    // trade the 4-value groups they lack (one swap of lanes l and l + 32)
+    bf16x8 sf[8];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int g0 = 2 * ks, g1 = g0 + 1;
+        const uint32_t x0 = pack_bf16x2(acc[t][4 * g0], acc[t][4 * g0 + 1]);
+        const uint32_t x1 = pack_bf16x2(acc[t][4 * g0 + 2], acc[t][4 * g0 + 3]);
+        const uint32_t y0 = pack_bf16x2(acc[t][4 * g1], acc[t][4 * g1 + 1]);
+        const uint32_t y1 = pack_bf16x2(acc[t][4 * g1 + 2], acc[t][4 * g1 + 3]);
+        // lanes < 32 keep x and take the upper lanes' x; lanes >= 32 take the
+        // lower lanes' y and keep y
+        const auto p0 = __builtin_amdgcn_permlane32_swap(x0, y0, false, false);
+        const auto p1 = __builtin_amdgcn_permlane32_swap(x1, y1, false, false);
+        sf[2 * t + ks] = __builtin_bit_cast(bf16x8, u32x4{p0[0], p1[0], p0[1], p1[1]});
+      }
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     lds_barrier();
     if (tid < D) zs[(c + 1) & 1][tid] = zp[tid] + zred[0][tid] + zred[1][tid] + zred[2][tid] + zred[3][tid];
 
-    // phi(Q) B operand: query row l32, head dims 16 t + 8 hi .. + 7
-    bf16x8 qf[8];
-#pragma unroll
-    for (int t = 0; t < 8; ++t) qf[t] = row_frag(Qb, l32, t);
-    // A^T = phi(K) phi(Q)^T and the inter-step term O^T = S_prev^T phi(Q)^T
+    // scores A^T = phi(K) phi(Q)^T (keys x queries) and O^T = S_prev^T phi(Q)^T
     f32x16 s = f32x16{}, o = f32x16{};
-    const uint16_t* Sp = Ss[c & 1];
-    const int srow = 32 * wave + l32;
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Kb, l32, t), qf[t], s, 0, 0, 0);
-      const bf16x8 sf = *(const bf16x8*)&Sp[srow * D + (((2 * t + hi) ^ swz_k(srow)) << 3)];
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf, qf[t], o, 0, 0, 0);
+    for (int f = 0; f < 8; ++f) {
+      const bf16x8 qf = row_frag(Qb, l32, f);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Kb, l32, f), qf, s, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(sf[f], qf, o, 0, 0, 0);
     }
-    // the step's state: S[d1 = 32 w + .., d2] += phi(K)^T V
+    // the step's state: S[d1, d2 = 32 w + ..] += phi(K)^T V
+    bf16x8 vf[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const bf16x8 af = __builtin_bit_cast(bf16x8, tr_frag(Kb, ks, wave));
+      vf[ks] = tr_frag(Vb, ks, wave);
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, tr_frag(Vb, ks, dt)),
-                                                          acc[dt], 0, 0, 0);
+      for (int t = 0; t < 4; ++t)
+        acc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kb, ks, t), vf[ks], acc[t], 0, 0, 0);
     }
     // causal mask: s[r] is key 8 (r / 4) + 4 hi + r % 4 of the step, query l32
     float rs = 0.f;
@@ -862,10 +892,8 @@ __global__ void __launch_bounds__(256) causal_lin_d128_kernel(CausalArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 pw = {pack_bf16x2(s[8 * ks], s[8 * ks + 1]), pack_bf16x2(s[8 * ks + 2], s[8 * ks + 3]),
                         pack_bf16x2(s[8 * ks + 4], s[8 * ks + 5]), pack_bf16x2(s[8 * ks + 6], s[8 * ks + 7])};
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, tr_frag(Vb, ks, wave)),
-                                                  __builtin_bit_cast(bf16x8, pw), o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[ks], __builtin_bit_cast(bf16x8, pw), o, 0, 0, 0);
     }
-    write_state(Ss[(c + 1) & 1]);
     // o[r] = O^T[32 w + 8 (r / 4) + 4 hi + r % 4][query l32]
     const int row = t0 + l32;
     if (row < n1) {
@@ -963,16 +991,14 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
 CausalPlan causal_plan(const bsa_shape& s) {
   CausalPlan p;
   const int64_t bh = (int64_t)s.B * s.H;
-  // apply: one workgroup per CU (its LDS holds three tile stages and two S^T
-  // copies), so at most 256 workgroups in total; the state pass runs twice as
-  // many splits of half the length (its kernel fits two workgroups per CU)
+  // two workgroups per CU for both the state and the causal kernel (at most
+  // 512 in all, one round); the prefix starts every state split (f = 1)
   const int64_t tiles = (s.N + kCT - 1) / kCT;
-  int64_t want = 256 / bh;
+  int64_t want = 512 / bh;
   if (want > tiles) want = tiles;
   if (want < 1) want = 1;
-  int64_t per = (tiles + want - 1) / want;
-  if (per > 1 && (per & 1)) ++per;
-  p.f = per > 1 ? 2 : 1;
+  const int64_t per = (tiles + want - 1) / want;
+  p.f = 1;
   p.chunk_a = (int)(per * kCT);
   p.chunk_s = p.chunk_a / p.f;
   p.splits_a = (int)((s.N + p.chunk_a - 1) / p.chunk_a);

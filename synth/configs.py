@@ -46,6 +46,10 @@ class Workload:
     ar_rho: float = 0.9
     # latent inter-frame pruning (LIPAR): threshold on the mean |difference|
     lipar_tau: float = 0.0
+    # which call a linear-attention workload runs: "" non-causal, "causal", or
+    # "mixed" (LinVideo blend with weight mix_r on the block-sparse branch)
+    op: str = ""
+    mix_r: float = 0.0
     notes: str = field(default="", compare=False)
 
     @property
@@ -94,6 +98,16 @@ WORKLOADS = {
     "linear_32k": Workload(
         name="linear_32k", seed=4, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
         dtype="bf16", values="iid"),
+    # Causal (chunked) elu+1 linear attention, the 32,760-token latent.
+    "causal_linear_32k": Workload(
+        name="causal_linear_32k", seed=7, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
+        dtype="bf16", values="iid", op="causal"),
+    # LinVideo mixed attention: r = 0.5 of the LVSA block-sparse branch (mask as
+    # lvsa_32k) plus 0.5 of elu+1 linear attention.
+    "mixed_32k": Workload(
+        name="mixed_32k", seed=8, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
+        dtype="bf16", values="ar1", block=128, mask_kind=MASK_WINDOW_ANCHOR,
+        window=3, anchor_period=8, anchor_steps=(0, 1, 2, 3), anchor_rows=1, op="mixed", mix_r=0.5),
     "linear_196k": Workload(
         name="linear_196k", seed=5, B=1, H=12, D=128, frames=126, frame_h=30, frame_w=52,
         dtype="bf16", values="iid"),

@@ -92,3 +92,26 @@ def test_tail_row_mask_matches_accumulator_rows():
                 for r in range(16):
                     key = 32 * kt + 8 * (r // 4) + 4 * hi + r % 4
                     assert bool((m >> (16 * kt + r)) & 1) == (key < n)
+
+
+def test_causal_state_fragment_swap():
+    """Causal linear kernel (`csrc/linear_attn.hip`): wave w keeps
+    acc[t][r] = S[32 t + 8 (r / 4) + 4 hi + r % 4][32 w + l32].  For k-step
+    f = 2 t + ks the lane packs x = group g0 = 2 ks and y = group g1 = g0 + 1 of
+    acc[t] and swaps x of the upper 32 lanes with y of the lower 32 (a
+    permlane32 swap).  Then the operand of lane (l32, hi), {x'[0], x'[1],
+    y'[0], y'[1]}, holds d1 = 16 f + 8 hi + 0..7 in order, as the row fragment
+    of phi(Q) does."""
+    def held(t, g, hi):        # the 4 d1 values of group g of acc[t] in a lane of half hi
+        return [32 * t + 8 * g + 4 * hi + j for j in range(4)]
+
+    for f in range(8):
+        t, ks = divmod(f, 2)
+        g0, g1 = 2 * ks, 2 * ks + 1
+        x = {hi: held(t, g0, hi) for hi in range(2)}
+        y = {hi: held(t, g1, hi) for hi in range(2)}
+        # swap(vdst = x, vsrc = y): vdst' = [x_lo, y_lo], vsrc' = [x_hi, y_hi]
+        x_new = {0: x[0], 1: y[0]}
+        y_new = {0: x[1], 1: y[1]}
+        for hi in range(2):
+            assert x_new[hi] + y_new[hi] == [16 * f + 8 * hi + e for e in range(8)]

@@ -17,12 +17,17 @@ descriptions on the five pages:
   compensation of skipped blocks, error estimation with query-cluster
   centroids as proxies, error-to-cost routing under a density budget.
 * "LinVideo: A Post-Training Framework towards O(n) Attention in Efficient
-  Video Generation", technical summary sections 1-2: O(n) linear attention.
+  Video Generation", technical summary sections 1-2: O(n) linear attention,
+  and section 2 A: the mixed (r-weighted) form.
+* "LIPAR: 비디오 생성 AI 를 위한 '스마트 스킵' 기술" (gist.science summary),
+  section 2 B: latent inter-frame pruning and restoration.
 
 Modules: ``mask`` (block rule and CSR), ``attention`` (block-sparse softmax
 attention), ``svg_ear`` (centroids, routing scores, budget selection,
 compensated attention; the score formula is "parity unpinned" as far as the
-pages go, see that module), ``linear`` (elu+1 linear attention).
+pages go, see that module), ``linear`` (elu+1 linear attention, causal and
+mixed forms), ``lipar`` (pruning and restoration), ``kmeans`` (the token
+clustering and cluster order in front of the SVG-EAR calls).
 """
 
-from . import mask, attention, linear, svg_ear  # noqa: F401
+from . import mask, attention, linear, svg_ear, lipar, kmeans  # noqa: F401

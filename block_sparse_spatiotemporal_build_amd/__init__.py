@@ -50,6 +50,11 @@ _SIGNATURES = {
     "bsa_causal_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_causal_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                                   _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_kmeans_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32]),
+    "bsa_kmeans": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32, _P, _P,
+                                  _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_gather_rows": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P, _P]),
+    "bsa_scatter_rows": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P, _P]),
     "bsa_cluster_centroids": (ctypes.c_int, [_P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                              ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]),
     "bsa_route_scores_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
@@ -293,6 +298,63 @@ def causal_linear_attn_fwd(q, k, v, out=None, state=None, return_state: bool = F
                                           _ptr(workspace), workspace.numel(), _stream(q.device)),
            "bsa_causal_linear_attn_fwd")
     return (out, S_out, z_out) if (return_state or state_out is not None) else out
+
+
+# ---- token clustering -----------------------------------------------------------
+
+def kmeans_workspace(shape_like, C: int) -> int:
+    return int(load().bsa_kmeans_workspace(ctypes.byref(_shape_of(shape_like)), int(C)))
+
+
+def kmeans(x, C: int, iters: int, init, workspace=None):
+    """k-means of the token rows of every (batch, head) of x (bf16 [B, H, N, 128]).
+
+    ``init``: fp32 [B*H, C, D] initial centres (copied).  Returns (labels int32
+    [B*H, N], centres fp32 [B*H, C, D], perm int32 [B*H, N], offsets int32
+    [B*H, C + 1]); perm / offsets are the stable cluster order of the labels."""
+    lib = load()
+    if x.dtype != torch.bfloat16 or not x.is_cuda or x.dim() != 4:
+        raise BsaError("x must be a bf16 device tensor [B, H, N, D]")
+    B, H, N, D = x.shape
+    shape = _shape_of(x)
+    cent = init.to(device=x.device, dtype=torch.float32).contiguous().clone()
+    if tuple(cent.shape) != (B * H, C, D):
+        raise BsaError(f"init must have shape {(B * H, C, D)}")
+    labels = torch.empty((B * H, N), dtype=torch.int32, device=x.device)
+    perm = torch.empty((B * H, N), dtype=torch.int32, device=x.device)
+    off = torch.empty((B * H, C + 1), dtype=torch.int32, device=x.device)
+    if workspace is None:
+        workspace = torch.empty(max(kmeans_workspace(x, C), 1), dtype=torch.uint8, device=x.device)
+    _check(lib.bsa_kmeans(_ptr(x), _dtype_code(x), ctypes.byref(shape), int(C), int(iters), _ptr(cent),
+                          _ptr(labels), _ptr(perm), _ptr(off), _ptr(workspace), workspace.numel(),
+                          _stream(x.device)), "bsa_kmeans")
+    return labels, cent, perm, off
+
+
+def _rows_permute(fn, x, perm, out):
+    lib = load()
+    if not x.is_cuda or x.dim() != 4:
+        raise BsaError("x must be a device tensor [B, H, N, D]")
+    if perm.dtype != torch.int32 or not perm.is_cuda or not perm.is_contiguous() or \
+            tuple(perm.shape) != (x.shape[0] * x.shape[1], x.shape[2]):
+        raise BsaError("perm must be a contiguous int32 device tensor [B*H, N]")
+    if out is None:
+        out = torch.empty_strided(x.shape, x.stride(), dtype=x.dtype, device=x.device)
+    if out.stride() != x.stride() or out.dtype != x.dtype:
+        raise BsaError("out must have the layout and dtype of x")
+    _check(getattr(lib, fn)(_ptr(x), _dtype_code(x), ctypes.byref(_shape_of(x)), _ptr(perm), _ptr(out),
+                            _stream(x.device)), fn)
+    return out
+
+
+def gather_rows(x, perm, out=None):
+    """out[b, h, i] = x[b, h, perm[b*H + h, i]] (rows into cluster order)."""
+    return _rows_permute("bsa_gather_rows", x, perm, out)
+
+
+def scatter_rows(y, perm, out=None):
+    """out[b, h, perm[b*H + h, i]] = y[b, h, i] (rows back to token order)."""
+    return _rows_permute("bsa_scatter_rows", y, perm, out)
 
 
 # ---- clustered compensation ---------------------------------------------------

@@ -219,6 +219,65 @@ bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void*
   return launch_linear_attn(q, k, v, o, *shape, nullptr, nullptr, workspace, sm, r > 0.f ? r : -1.f);
 }
 
+// ---- token clustering --------------------------------------------------------
+
+size_t bsa_kmeans_workspace(const bsa_shape* shape, int32_t C) {
+  if (check_shape(shape, 2, "bsa_kmeans_workspace") != BSA_OK) return 0;
+  if (shape->D != 128 || C < 1 || C > kMaxKmClusters) return 0;
+  return kmeans_plan(*shape, C).total;
+}
+
+bsa_status bsa_kmeans(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t C, int32_t iters,
+                      float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_kmeans";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (shape->D != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 128 (got %d)", fn, shape->D);
+  if (C < 1 || C > kMaxKmClusters) return fail(BSA_ERR_ARG, "%s: C must be in [1, %d]", fn, kMaxKmClusters);
+  if (iters < 0 || iters > 100000) return fail(BSA_ERR_ARG, "%s: iters must be in [0, 100000]", fn);
+  if (!x || !centroids || !labels) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(x) || !aligned16(centroids) || !aligned16(labels) || !aligned16(perm) || !aligned16(offsets))
+    return fail(BSA_ERR_ARG, "%s: x, centroids, labels, perm, offsets must be 16-byte aligned", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  if ((int64_t)(shape->N + 255) / 256 > 65535) return fail(BSA_ERR_ARG, "%s: N too large", fn);
+  const size_t need = kmeans_plan(*shape, C).total;
+  if (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                workspace ? ws_bytes : (size_t)0);
+  g_err[0] = 0;
+  return launch_kmeans(x, *shape, C, iters, centroids, labels, perm, offsets, workspace, (hipStream_t)stream);
+}
+
+static bsa_status rows_permute(const void* src, bsa_dtype dtype, const bsa_shape* shape, const int32_t* perm,
+                               void* dst, void* stream, bool scatter) {
+  const char* fn = scatter ? "bsa_scatter_rows" : "bsa_gather_rows";
+  if (dtype != BSA_DT_BF16 && dtype != BSA_DT_F32) return fail(BSA_ERR_ARG, "%s: unknown dtype %d", fn, dtype);
+  const int eb = dtype == BSA_DT_BF16 ? 2 : 4;
+  bsa_status st = check_shape(shape, eb, fn);
+  if (st != BSA_OK) return st;
+  if ((shape->D * eb) % 16 != 0) return fail(BSA_ERR_ARG, "%s: rows must be a multiple of 16 bytes", fn);
+  if (shape->D * eb > 16 * 1024) return fail(BSA_ERR_UNSUPPORTED, "%s: rows above 16 KiB", fn);
+  if (!src || !dst || !perm) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (src == dst) return fail(BSA_ERR_ARG, "%s: in place is not supported", fn);
+  if (!aligned16(src) || !aligned16(dst)) return fail(BSA_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  if ((int64_t)(shape->N + 3) / 4 > 0x7fffffffLL) return fail(BSA_ERR_ARG, "%s: N too large", fn);
+  g_err[0] = 0;
+  return launch_rows_permute(src, *shape, eb, perm, dst, scatter, (hipStream_t)stream);
+}
+
+bsa_status bsa_gather_rows(const void* x, bsa_dtype dtype, const bsa_shape* shape, const int32_t* perm, void* out,
+                           void* stream) {
+  return rows_permute(x, dtype, shape, perm, out, stream, false);
+}
+
+bsa_status bsa_scatter_rows(const void* y, bsa_dtype dtype, const bsa_shape* shape, const int32_t* perm, void* out,
+                            void* stream) {
+  return rows_permute(y, dtype, shape, perm, out, stream, true);
+}
+
 // ---- clustered compensation (SVG-EAR) -------------------------------------
 
 static constexpr int kMaxKeyClusters = 512;

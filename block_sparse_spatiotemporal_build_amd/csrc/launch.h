@@ -42,6 +42,18 @@ bsa_status launch_causal_linear_attn(const void* q, const void* k, const void* v
                                      const float* s_in, const float* z_in, float* s_out, float* z_out, void* ws,
                                      hipStream_t stream);
 
+// ---- token clustering (k-means, cluster order, row permutation) -------------
+constexpr int kMaxKmClusters = 1024;
+struct KmPlan {
+  int Cp, tiles;  // centres padded to a multiple of 32; 256-token tiles per sequence
+  size_t off_cb, off_cn, off_hist, off_perm, off_off, total;  // workspace layout (bytes)
+};
+KmPlan kmeans_plan(const bsa_shape& s, int C);
+bsa_status launch_kmeans(const void* x, const bsa_shape& s, int C, int iters, float* cent, int32_t* labels,
+                         int32_t* perm, int32_t* offsets, void* ws, hipStream_t stream);
+bsa_status launch_rows_permute(const void* src, const bsa_shape& s, int elem_bytes, const int32_t* perm, void* dst,
+                               bool scatter, hipStream_t stream);
+
 // ---- centroid compensation with error-aware routing ------------------------
 struct ProbePlan {
   int splits, cps;  // key-cluster splits per head and clusters per split

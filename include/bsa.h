@@ -206,6 +206,52 @@ bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void*
                               const int32_t* row_order, int32_t block, float scale, float r,
                               void* workspace, size_t ws_bytes, void* stream);
 
+/* ---- token clustering ------------------------------------------------------
+ * Source: "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
+ * Generation via Error-aware Routing", technical summary section 2 Method:
+ * query and key tokens are grouped by similarity into clusters before the
+ * cluster-block calls below, which take their rows in cluster order. */
+
+/* Workspace bytes required by bsa_kmeans for `shape` and C clusters (0 if the
+ * shape or C is invalid or not supported). */
+size_t bsa_kmeans_workspace(const bsa_shape* shape, int32_t C);
+
+/* k-means of the N token rows of every (batch, head): from the given centres,
+ * `iters` Lloyd steps (assign each row to its nearest centre, move each centre
+ * to the mean of its rows; a centre without rows stays), then a final
+ * assignment to the final centres.  Ties go to the lowest centre index.
+ * x: bf16 [B, H, N, D] device tensor with `shape`, D = 128.
+ * C: clusters per (batch, head), 1 <= C <= 1024.
+ * centroids: fp32 [B*H][C][D] device buffer; in: the initial centres, out: the
+ *   final ones (the centres the returned labels refer to).
+ * labels: int32 [B*H][N] device output, the cluster of every row.
+ * perm, offsets: nullable int32 device outputs [B*H][N] and [B*H][C + 1]: the
+ *   stable cluster order of the final labels (cluster a is rows
+ *   [offsets[a], offsets[a+1]) of the permuted sequence, tokens in their
+ *   original order; perm[i] is the original row of permuted row i), the
+ *   q_off / k_off form the calls below take.
+ * Precision: the assignment compares |c_b|^2 - 2 x.c_b with c_b the centre
+ *   rounded to bf16 (fp32 MFMA accumulation of exact bf16 products); means are
+ *   fp32 sums in cluster order divided by the count.  Deterministic.
+ * workspace: at least bsa_kmeans_workspace(shape, C) bytes, 256-byte aligned.
+ * All pointers 16-byte aligned.  Only BSA_DT_BF16 (BSA_ERR_UNSUPPORTED). */
+bsa_status bsa_kmeans(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t C, int32_t iters,
+                      float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* workspace,
+                      size_t ws_bytes, void* stream);
+
+/* Rows into cluster order: out[b, h, i] = x[b, h, perm[b*H + h][i]] for every
+ * i < N.  x and out: device tensors of `dtype` (bf16 or fp32) with the layout
+ * of `shape` (rows of a multiple of 16 bytes), distinct buffers.  perm: int32
+ * [B*H][N] device array; an entry outside [0, N) leaves that output row
+ * untouched.  Bit-exact copies. */
+bsa_status bsa_gather_rows(const void* x, bsa_dtype dtype, const bsa_shape* shape, const int32_t* perm, void* out,
+                           void* stream);
+
+/* Rows back to token order: out[b, h, perm[b*H + h][i]] = y[b, h, i] (the
+ * inverse of bsa_gather_rows for a permutation).  Same conventions. */
+bsa_status bsa_scatter_rows(const void* y, bsa_dtype dtype, const bsa_shape* shape, const int32_t* perm, void* out,
+                            void* stream);
+
 /* ---- clustered sparse attention with centroid compensation ---------------
  * Source: "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
  * Generation via Error-aware Routing", technical summary section 2 Method.

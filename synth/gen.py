@@ -124,6 +124,29 @@ def _mixture(wl: Workload, t: int, b: int, h: int, C: int):
     return x, centres
 
 
+def make_gmm_tokens(wl: Workload, heads=None):
+    """Q, K, V of the Gaussian-mixture recipe in token order (not clustered), and
+    the generating centres (float32 [B*H', C, D]) that serve as the initial
+    k-means centres."""
+    hs = list(range(wl.H)) if heads is None else list(heads)
+    Cq, Ck = wl.n_q_clusters, wl.n_k_clusters
+    dt = np.uint16 if wl.dtype == "bf16" else np.float32
+    q = np.empty((wl.B, len(hs), wl.N, wl.D), dt)
+    k = np.empty_like(q)
+    v = np.empty_like(q)
+    cq = np.empty((wl.B * len(hs), Cq, wl.D), np.float32)
+    ck = np.empty((wl.B * len(hs), Ck, wl.D), np.float32)
+    for b in range(wl.B):
+        for i, h in enumerate(hs):
+            r = b * len(hs) + i
+            xq, gq = _mixture(wl, TENSOR_ID["q"], b, h, Cq)
+            xk, gk = _mixture(wl, TENSOR_ID["k"], b, h, Ck)
+            xv = normal_f32((wl.seed, TENSOR_ID["v"], b, h, _PURPOSE_NOISE), (wl.N, wl.D))
+            q[b, i], k[b, i], v[b, i] = store(xq, wl.dtype), store(xk, wl.dtype), store(xv, wl.dtype)
+            cq[r], ck[r] = gq, gk
+    return dict(q=q, k=k, v=v, centres_q=cq, centres_k=ck)
+
+
 def kmeans_labels(x: np.ndarray, init: np.ndarray, iters: int) -> np.ndarray:
     """Lloyd iterations in float64 from the given centres; ties go to the lowest index.
 

@@ -201,3 +201,25 @@ def test_causal_workspace_plan(lib):
         tiles = -(-N // 32)
         splits = w // (H * (128 * 128 + 128) * 4)              # about 512 / H state splits
         assert 1 <= splits <= max(2 * 256 // H, 1) + 1 and splits <= tiles
+
+
+def test_kmeans_and_row_permute_argument_checks(lib):
+    p = ctypes.c_void_p(4096)
+    ok_ = _shape(B=1, H=2, N=1000, D=128)
+
+    def km(shape=ok_, C=10, iters=3, dtype=0, ws=1 << 30, ptr=p):
+        return lib.bsa_kmeans(ptr, dtype, ctypes.byref(shape), C, iters, p, p, None, None,
+                              ctypes.c_void_p(1 << 20), ws, None)
+
+    assert km(shape=_shape(D=64)) == 2
+    assert km(C=0) == 1 and km(C=1025) == 1
+    assert km(iters=-1) == 1
+    assert km(dtype=1) == 2
+    assert km(ws=16) == 4
+    assert km(ptr=ctypes.c_void_p(4098)) == 1
+    assert lib.bsa_kmeans_workspace(ctypes.byref(ok_), 0) == 0
+    assert lib.bsa_kmeans_workspace(ctypes.byref(ok_), 500) > 0
+    assert lib.bsa_gather_rows(p, 0, ctypes.byref(_shape(D=4, sn=8)), p, ctypes.c_void_p(8192), None) == 1
+    assert lib.bsa_gather_rows(p, 0, ctypes.byref(ok_), p, p, None) == 1          # in place
+    assert lib.bsa_scatter_rows(p, 7, ctypes.byref(ok_), p, ctypes.c_void_p(8192), None) == 1
+    assert b"bsa_scatter_rows" in lib.bsa_last_error()

@@ -1,0 +1,163 @@
+"""GPU token clustering (k-means, cluster order, row gather / scatter) vs the oracle.
+
+Labels are integers decided by float distances: where the nearest centre is
+unique by a margin well above fp32 accumulation error they must equal the
+oracle's (which takes the decision in the kernel's precision: centres rounded
+to bf16); everywhere they must be a valid nearest centre within that error.
+The cluster order and the row copies are bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+from helpers import to_device
+from oracle import kmeans as ok
+from synth import gen, get_workload
+
+pytestmark = pytest.mark.gpu
+
+
+def _dist(x, cent):
+    cb = ok.round_bf16(cent)
+    return (cb * cb).sum(1)[None, :] - 2.0 * (x @ cb.T)
+
+
+def _check_valid(x, labels, cent):
+    """labels are nearest centres within the fp32 error bound; returns the share
+    of tokens whose nearest centre is unique by more than that bound."""
+    d = _dist(x, cent)
+    cb = ok.round_bf16(cent)
+    eps = 1e-5 * ((cb * cb).sum(1)[None, :] + 2.0 * (np.abs(x) @ np.abs(cb).T)).max()
+    dmin = d.min(axis=1)
+    assert (d[np.arange(len(x)), labels] <= dmin + eps).all()
+    srt = np.sort(d, axis=1)
+    clear = srt[:, 1] - srt[:, 0] > 2 * eps if d.shape[1] > 1 else np.ones(len(x), bool)
+    assert np.array_equal(labels[clear], d.argmin(axis=1)[clear])
+    return clear.mean()
+
+
+def _tokens(B, H, N, C, sigma, seed):
+    r = np.random.default_rng(seed)
+    cen = r.standard_normal((B * H, C, 128))
+    cen /= np.linalg.norm(cen, axis=2, keepdims=True)
+    lab = r.integers(0, C, (B * H, N))
+    x = np.stack([cen[i][lab[i]] for i in range(B * H)]) + sigma * r.standard_normal((B * H, N, 128))
+    bits = gen.store(x.reshape(B, H, N, 128).astype(np.float32), "bf16")
+    init = (cen + 0.05 * r.standard_normal(cen.shape) / np.sqrt(128)).astype(np.float32)
+    return bits, init
+
+
+@pytest.mark.parametrize("N,C,iters", [(3000, 37, 5), (257, 32, 3), (700, 100, 0), (1000, 500, 4)])
+def test_well_separated_matches_oracle(gpu_lib, N, C, iters):
+    B, H = 1, 3
+    bits, init = _tokens(B, H, N, C, 0.05, N + C)
+    x = to_device(bits, "bf16")
+    labels, cent, perm, off = gpu_lib.kmeans(x, C, iters, torch.from_numpy(init))
+    torch.cuda.synchronize()
+    lab_h, cent_h, perm_h, off_h = (t.cpu().numpy() for t in (labels, cent, perm, off))
+    for r in range(B * H):
+        xf = gen.to_f64(bits[0, r], "bf16")
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), iters)
+        assert np.array_equal(lab_h[r], rl), r
+        assert np.abs(cent_h[r] - rc).max() < 1e-5
+        p, o = ok.cluster_order(lab_h[r], C)
+        assert np.array_equal(perm_h[r], p) and np.array_equal(off_h[r], o)
+
+
+def test_empty_and_single_clusters(gpu_lib):
+    N = 900
+    bits, init = _tokens(1, 2, N, 4, 0.05, 5)
+    far = np.full((2, 3, 128), 50.0, np.float32)
+    init6 = np.concatenate([init, far], axis=1)                   # clusters 4..6 never win
+    x = to_device(bits, "bf16")
+    labels, cent, perm, off = gpu_lib.kmeans(x, 7, 3, torch.from_numpy(init6))
+    torch.cuda.synchronize()
+    c = cent.cpu().numpy()
+    assert np.array_equal(c[:, 4:], init6[:, 4:])
+    o = off.cpu().numpy()
+    assert (o[:, 4] == N).all() and (o[:, 7] == N).all()
+    labels1, cent1, _, off1 = gpu_lib.kmeans(x, 1, 2, torch.from_numpy(init[:, :1].copy()))
+    torch.cuda.synchronize()
+    assert (labels1.cpu().numpy() == 0).all()
+    for r in range(2):
+        mean = gen.to_f64(bits[0, r], "bf16").mean(axis=0)
+        assert np.abs(cent1.cpu().numpy()[r, 0] - mean).max() < 1e-5
+
+
+def test_assignment_and_update_steps_on_overlapping_clusters(gpu_lib):
+    """The SVG-EAR mixture (sigma 0.3 around unit centres, 32,760 tokens, 500 key
+    clusters): zero steps = one assignment to the initial centres; one step's
+    centres = the means of that assignment."""
+    wl = gen.scaled(get_workload("svg_ear_32k"), H=2)
+    d = gen.make_gmm_tokens(wl)
+    x = to_device(d["k"], "bf16")
+    init = torch.from_numpy(d["centres_k"])
+    lab0, cent0, _, _ = gpu_lib.kmeans(x, wl.n_k_clusters, 0, init)
+    lab1, cent1, perm1, off1 = gpu_lib.kmeans(x, wl.n_k_clusters, 1, init)
+    torch.cuda.synchronize()
+    for r in range(2):
+        xf = gen.to_f64(d["k"][0, r], "bf16")
+        l0 = lab0.cpu().numpy()[r]
+        assert np.array_equal(cent0.cpu().numpy()[r], d["centres_k"][r])
+        assert _check_valid(xf, l0, d["centres_k"][r].astype(np.float64)) > 0.999
+        want = ok.update(xf, l0, d["centres_k"][r].astype(np.float64))
+        assert np.abs(cent1.cpu().numpy()[r] - want).max() < 1e-5
+        l1 = lab1.cpu().numpy()[r]
+        _check_valid(xf, l1, cent1.cpu().numpy()[r].astype(np.float64))
+        p, o = ok.cluster_order(l1, wl.n_k_clusters)
+        assert np.array_equal(perm1.cpu().numpy()[r], p) and np.array_equal(off1.cpu().numpy()[r], o)
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_svg_ear_32k_ten_steps(gpu_lib, which):
+    """Ten Lloyd steps on the 32,760-token workload (queries: 100 clusters, keys:
+    500), two heads: valid final labels for the final centres, the exact cluster
+    order, and agreement with the oracle run from the same centres."""
+    wl = gen.scaled(get_workload("svg_ear_32k"), H=2)
+    d = gen.make_gmm_tokens(wl)
+    C = wl.n_q_clusters if which == "q" else wl.n_k_clusters
+    x = to_device(d[which], "bf16")
+    init = d["centres_" + which]
+    labels, cent, perm, off = gpu_lib.kmeans(x, C, wl.kmeans_iters, torch.from_numpy(init))
+    torch.cuda.synchronize()
+    for r in range(2):
+        xf = gen.to_f64(d[which][0, r], "bf16")
+        lab = labels.cpu().numpy()[r]
+        cen = cent.cpu().numpy()[r].astype(np.float64)
+        _check_valid(xf, lab, cen)
+        p, o = ok.cluster_order(lab, C)
+        assert np.array_equal(perm.cpu().numpy()[r], p) and np.array_equal(off.cpu().numpy()[r], o)
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), wl.kmeans_iters)
+        assert (rl == lab).mean() > 0.999
+        assert np.abs(rc - cen).max() < 1e-3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_gather_scatter_roundtrip(gpu_lib, dtype):
+    B, H, N, D = 2, 3, 1001, 128 if dtype == "bf16" else 64
+    r = np.random.default_rng(20)
+    x = r.standard_normal((B, N, H, D)).astype(np.float32)          # stored [B, N, H, D]
+    stored = gen.store(x, dtype)
+    dev = to_device(stored, dtype).permute(0, 2, 1, 3)              # a strided [B, H, N, D] view
+    perm = np.stack([r.permutation(N) for _ in range(B * H)]).astype(np.int32)
+    pt = torch.from_numpy(perm).cuda()
+    g = gpu_lib.gather_rows(dev, pt)
+    back = gpu_lib.scatter_rows(g, pt)
+    torch.cuda.synchronize()
+    ref = gen.to_f64(np.ascontiguousarray(stored.transpose(0, 2, 1, 3)), dtype).reshape(B * H, N, D)
+    gh = g.float().cpu().numpy().reshape(B * H, N, D)
+    for i in range(B * H):
+        assert np.array_equal(gh[i], ok.gather_rows(ref[i], perm[i]))
+    assert torch.equal(back.view(torch.int16 if dtype == "bf16" else torch.int32),
+                       dev.view(torch.int16 if dtype == "bf16" else torch.int32))
+
+
+def test_gather_skips_out_of_range_entries(gpu_lib):
+    x = torch.randn(1, 1, 10, 128, device="cuda").to(torch.bfloat16)
+    perm = torch.tensor([[3, -1, 10, 0, 1, 2, 4, 5, 6, 7]], dtype=torch.int32, device="cuda")
+    out = torch.full_like(x, 7.0)
+    gpu_lib.gather_rows(x, perm, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out[0, 0, 0], x[0, 0, 3])
+    assert (out[0, 0, 1:3].float() == 7.0).all()
+    assert torch.equal(out[0, 0, 3:], x[0, 0, [0, 1, 2, 4, 5, 6, 7]])

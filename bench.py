@@ -26,8 +26,11 @@ one mixed call; effective TFLOP/s over kept blocks plus the linear branch's
 4 N D^2 per head); svg_ear_32k (clustered Q/K, centroid compensation at 15%
 density: one step is the fused call; routing = centroids + scores + selection
 reported as algorithmic GB/s of reading Q, K, V once; compensated attention as
-effective TFLOP/s over exact plus virtual keys); lipar_32k (latent inter-frame
-pruning and restoration as algorithmic GB/s).
+effective TFLOP/s over exact plus virtual keys); kmeans_32k (the token
+clustering in front of it: k-means of queries and keys, 10 Lloyd steps each,
+rows into cluster order and one tensor back, as effective TFLOP/s of the
+distance products); lipar_32k (latent inter-frame pruning and restoration as
+algorithmic GB/s).
 """
 
 import argparse
@@ -54,7 +57,7 @@ def parse_args():
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="lvsa_32k",
                     choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "causal_linear_32k",
-                             "mixed_32k", "svg_ear_32k", "lipar_32k"])
+                             "mixed_32k", "svg_ear_32k", "kmeans_32k", "lipar_32k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
     ap.add_argument("--mode", default="bench", choices=["bench", "copy"],
@@ -502,6 +505,112 @@ def bench_mixed(args, wl):
     return result
 
 
+def cpu_baseline_kmeans(wl, d, budget_s: float):
+    """The k-means oracle (keys, then queries, of whole heads in order, all Lloyd
+    steps) until the budget is spent, as TFLOP/s of the distance products."""
+    from oracle import kmeans as ok
+    from synth import gen
+    flops, dt, done = 0, 0.0, []
+    for r in range(wl.B * wl.H):
+        b, h = divmod(r, wl.H)
+        for name, C in (("k", wl.n_k_clusters), ("q", wl.n_q_clusters)):
+            x = gen.to_f64(d[name][b, h], wl.dtype)
+            t0 = time.perf_counter()
+            lab, _ = ok.lloyd(x, d["centres_" + name][r].astype("float64"), wl.kmeans_iters)
+            ok.cluster_order(lab, C)
+            dt += time.perf_counter() - t0
+            flops += 2 * wl.N * C * wl.D * (wl.kmeans_iters + 1)
+            done.append(f"{name}{r}")
+            if dt >= budget_s:
+                break
+        if dt >= budget_s:
+            break
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s (distance products)",
+            "cores": int(_oracle_threads()), "kind": "oracle",
+            "sample": f"k-means of {', '.join(done)} (tensor, head) in order: {dt:.1f} s, float64 numpy"}
+
+
+def bench_kmeans(args, wl):
+    """Token clustering: one step = k-means of Q (Cq) and K (Ck), 10 Lloyd steps
+    each, Q, K, V gathered into cluster order and one output-sized tensor
+    scattered back to token order."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_gmm_tokens(wl)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    Cq, Ck, T = wl.n_q_clusters, wl.n_k_clusters, wl.kmeans_iters
+    init_q = torch.from_numpy(d["centres_q"]).to(dev)
+    init_k = torch.from_numpy(d["centres_k"]).to(dev)
+    ws_q = torch.empty(bsa.kmeans_workspace(q, Cq), dtype=torch.uint8, device=dev)
+    ws_k = torch.empty(bsa.kmeans_workspace(k, Ck), dtype=torch.uint8, device=dev)
+    qp, kp, vp, ob = (torch.empty_like(q) for _ in range(4))
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        _, _, perm_k, _ = bsa.kmeans(k, Ck, T, init_k, workspace=ws_k)
+        if evs is not None:
+            evs[1].record()
+        _, _, perm_q, _ = bsa.kmeans(q, Cq, T, init_q, workspace=ws_q)
+        if evs is not None:
+            evs[2].record()
+        bsa.gather_rows(q, perm_q, out=qp)
+        bsa.gather_rows(k, perm_k, out=kp)
+        bsa.gather_rows(v, perm_k, out=vp)
+        bsa.scatter_rows(qp, perm_q, out=ob)
+        if evs is not None:
+            evs[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    k_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    q_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    p_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    bh = wl.B * wl.H
+    fl_k = 2 * bh * wl.N * Ck * wl.D * (T + 1)
+    fl_q = 2 * bh * wl.N * Cq * wl.D * (T + 1)
+    achieved = fl_k / (k_ms * 1e-3) / 1e12
+    perm_bytes = 4 * 2 * bh * wl.N * wl.D * 2           # three gathers and one scatter, read + write
+    d_host = d if args.cpu_seconds > 0 else None
+    result = {
+        "metric": "effective TFLOP/s of SVG-EAR token clustering (k-means distance products) at 32K tokens",
+        "value": round((fl_k + fl_q) * args.steps / (t1 - t0) / 1e12, 3),
+        "unit": "TFLOP/s (2 N C D per assignment; k-means of Q and K, 10 steps each, plus permutes, per step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_kmeans_keys": round(k_ms, 4), "ms_kmeans_queries": round(q_ms, 4),
+        "ms_permute": round(p_ms, 4),
+        "permute_gbs": round(perm_bytes / (p_ms * 1e-3) / 1e9, 1),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "Cq": Cq, "Ck": Ck,
+                   "lloyd_steps": T},
+        "roofline": {"bound": "mfma", "kernel": "bsa_kmeans of the keys (assign + scan + place + update launches)",
+                     "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if d_host is not None:
+        result["cpu_baseline"] = cpu_baseline_kmeans(wl, d_host, args.cpu_seconds)
+    return result
+
+
 def bench_lipar(args, wl):
     """Latent inter-frame pruning + restoration: one step = bsa_lipar_prune of the
     sequence, then bsa_lipar_restore of the pruned rows back to full length."""
@@ -712,6 +821,9 @@ def main():
         return
     if wl.op == "mixed":
         print(json.dumps(bench_mixed(args, wl)), flush=True)
+        return
+    if wl.op == "kmeans":
+        print(json.dumps(bench_kmeans(args, wl)), flush=True)
         return
     if wl.values == "iid":
         print(json.dumps(bench_linear(args, wl)), flush=True)

@@ -10,25 +10,31 @@
 // Ties go to the lowest centre index.  The assignment compares
 // |c_b|^2 - 2 x . c_b with c_b the centre rounded to bf16: x . c_b is an fp32
 // MFMA accumulation of exact bf16 products, |c_b|^2 is fp32.  The means are
-// fp32 sums in token order divided by the count.
+// fp32 sums divided by the count (a fixed summation order: row group g sums
+// rows g, g + 16, ... of the cluster in order, then the 16 group sums are added
+// in group order).
 //
 // One Lloyd step is four launches, all deterministic:
 //   assign : grid (256-token tiles, B*H).  Each wave holds 64 tokens as MFMA B
 //            operands; the bf16 centres stream through LDS in 32-row chunks
 //            (buffer loads one chunk ahead); S^T = C_chunk X^T with
 //            32x32x16 MFMA, then a per-lane running (distance, index) minimum
-//            over the lane's 16 centres per chunk, and one exchange between
+//            over the lane's 16 centres per chunk (the chunk minimum first, the
+//            index only where it improves), and one exchange between
 //            the two lane halves at the end.  Labels go to global memory and a
 //            per-tile label histogram (LDS integer atomics) to the workspace.
 //   scan   : one workgroup per sequence: per cluster, the exclusive prefix of
 //            the tile histograms in tile order, and the cluster offsets.
-//   place  : one wave per tile: the stable rank of each token among the equal
-//            labels of its tile (a 64-lane compare per batch of 64 tokens and
-//            per-label counters in LDS), giving its position in the cluster
+//   place  : one workgroup per tile: the stable rank of each token among the
+//            equal labels of its tile (a 64-lane compare inside each wave and
+//            per-wave label counts in LDS), giving its position in the cluster
 //            order.
-//   update : one wave per cluster sums its rows in cluster order (fp32, two
-//            dims per lane), divides by the count, and writes the fp32 centre,
-//            its bf16 copy and |c_b|^2 for the next assignment.
+//   update : one workgroup per cluster: 16 row groups x 16 chunks of 8 dims
+//            sum the cluster's rows (every 16th row in cluster order, fp32,
+//            16-byte loads), the group sums are added in group order and
+//            divided by the count; the
+//            fp32 centre, its bf16 copy and |c_b|^2 go out for the next
+//            assignment.
 
 #include "launch.h"
 
@@ -111,16 +117,24 @@ __global__ void __launch_bounds__(256) km_assign_d128_kernel(KmAssignArgs a) {
 #pragma unroll
       for (int u = 0; u < 2; ++u) s[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, xf[u][t], s[u], 0, 0, 0);
     }
+    // the chunk's minimum first; only a lane that improves looks for its index
+    // (the lowest of equal distances: the lane's centres rise with r)
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      float d[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float d = __builtin_fmaf(-2.f, s[u][r], cq[r >> 2][r & 3]);
-        if (d < best[u]) {
-          best[u] = d;
-          bidx[u] = 32 * k + 8 * (r >> 2) + 4 * hi + (r & 3);
-        }
+      for (int r = 0; r < 16; ++r) d[r] = __builtin_fmaf(-2.f, s[u][r], cq[r >> 2][r & 3]);
+      float m = d[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) m = fminf(m, d[r]);
+      if (m < best[u]) {
+        int ix = 15;
+#pragma unroll
+        for (int r = 14; r >= 0; --r) ix = d[r] == m ? r : ix;
+        best[u] = m;
+        bidx[u] = 32 * k + 8 * (ix >> 2) + 4 * hi + (ix & 3);
       }
+    }
   };
   dma(S0, 0);
   int k = 0;
@@ -156,24 +170,39 @@ __global__ void __launch_bounds__(256) km_assign_d128_kernel(KmAssignArgs a) {
 
 struct KmOrderArgs {
   const int32_t* labels;  // [BH][N]
-  int32_t* hist;          // [BH][tiles][C]: counts in, exclusive tile prefix per cluster out
+  const int32_t* hist;    // [BH][tiles][C] label counts per tile
+  int32_t* tbase;         // [BH][tiles][C] exclusive prefix over tiles, per cluster
   int32_t* off;           // [BH][C + 1]
   int32_t* perm;          // [BH][N]
   int N, C, tiles;
 };
 
-// one workgroup of kMaxKmClusters threads per sequence
+// one workgroup of kMaxKmClusters threads per sequence (thread c = cluster c);
+// the tile loop keeps eight loads in flight
 __global__ void __launch_bounds__(kMaxKmClusters) km_scan_kernel(KmOrderArgs a) {
   __shared__ int sc[kMaxKmClusters];
   const int c = threadIdx.x, bh = blockIdx.x;
-  int32_t* h = a.hist + (int64_t)bh * a.tiles * a.C;
+  const int32_t* __restrict__ h = a.hist + (int64_t)bh * a.tiles * a.C + c;
+  int32_t* __restrict__ tb = a.tbase + (int64_t)bh * a.tiles * a.C + c;
   int run = 0;
-  if (c < a.C)
-    for (int t = 0; t < a.tiles; ++t) {
-      const int v = h[(int64_t)t * a.C + c];
-      h[(int64_t)t * a.C + c] = run;
+  if (c < a.C) {
+    int t = 0;
+    for (; t + 8 <= a.tiles; t += 8) {
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = h[(int64_t)(t + u) * a.C];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        tb[(int64_t)(t + u) * a.C] = run;
+        run += v[u];
+      }
+    }
+    for (; t < a.tiles; ++t) {
+      const int v = h[(int64_t)t * a.C];
+      tb[(int64_t)t * a.C] = run;
       run += v;
     }
+  }
   // inclusive scan of the cluster counts (Hillis-Steele in LDS)
   sc[c] = run;
   __syncthreads();
@@ -188,28 +217,34 @@ __global__ void __launch_bounds__(kMaxKmClusters) km_scan_kernel(KmOrderArgs a) 
   if (c == a.C - 1) o[a.C] = sc[c];
 }
 
-// one wave per tile: stable positions of the tile's tokens in the cluster order
-__global__ void __launch_bounds__(64) km_place_kernel(KmOrderArgs a) {
-  __shared__ int cnt[kMaxKmClusters];
-  const int lane = threadIdx.x, tile = blockIdx.x, bh = blockIdx.y;
-  for (int i = lane; i < a.C; i += 64) cnt[i] = 0;
-  __syncthreads();
-  const int32_t* lab = a.labels + (int64_t)bh * a.N;
-  const int32_t* base = a.hist + ((int64_t)bh * a.tiles + tile) * a.C;
+// one workgroup per tile, wave b placing tokens 64 b .. 64 b + 63 of the tile:
+// the tile's bases (cluster offset + earlier tiles) are staged in LDS, each
+// wave counts its labels, and a token's position adds the counts of the
+// earlier waves and its rank among the equal labels of its own wave
+__global__ void __launch_bounds__(256) km_place_kernel(KmOrderArgs a) {
+  __shared__ int base[kMaxKmClusters];
+  __shared__ int cnt[4][kMaxKmClusters];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, tile = blockIdx.x, bh = blockIdx.y;
+  const int32_t* tb = a.tbase + ((int64_t)bh * a.tiles + tile) * a.C;
   const int32_t* o = a.off + (int64_t)bh * (a.C + 1);
-  int32_t* perm = a.perm + (int64_t)bh * a.N;
-  for (int b = 0; b < kKmTile / 64; ++b) {
-    const int n = tile * kKmTile + 64 * b + lane;
-    const int l = n < a.N ? lab[n] : -1;
-    int rank = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int lj = __builtin_amdgcn_readlane(l, j);
-      rank += (j < lane && lj == l) ? 1 : 0;
-    }
-    if (l >= 0) {
-      perm[o[l] + base[l] + cnt[l] + rank] = n;
-      atomicAdd(&cnt[l], 1);  // after every lane's read of cnt (one wave, LDS order)
-    }
+  for (int i = tid; i < a.C; i += 256) {
+    base[i] = o[i] + tb[i];
+    cnt[0][i] = cnt[1][i] = cnt[2][i] = cnt[3][i] = 0;
+  }
+  const int n = tile * kKmTile + 64 * wave + lane;
+  const int l = n < a.N ? a.labels[(int64_t)bh * a.N + n] : -1;
+  int rank = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int lj = __builtin_amdgcn_readlane(l, j);
+    rank += (j < lane && lj == l) ? 1 : 0;
+  }
+  __syncthreads();
+  if (l >= 0) atomicAdd(&cnt[wave][l], 1);
+  __syncthreads();
+  if (l >= 0) {
+    int pos = base[l] + rank;
+    for (int w = 0; w < wave; ++w) pos += cnt[w][l];
+    a.perm[(int64_t)bh * a.N + pos] = n;
   }
 }
 
@@ -234,51 +269,66 @@ __device__ __forceinline__ void km_store_centre(const KmUpdateArgs& a, int bh, i
   if (lane == 0) a.cn[(int64_t)bh * a.Cp + c] = q;
 }
 
-// one wave per cluster (mode 0: mean of the cluster's rows, mode 1: the bf16
-// copy and norm of the given fp32 centres; rows C..Cp-1 are padded)
-template <int MODE>
-__global__ void __launch_bounds__(256) km_update_d128_kernel(KmUpdateArgs a) {
+// the bf16 copy and norm of given fp32 centres, one wave per centre (rows
+// C..Cp-1 are padding: zero, and an infinite norm so they never win)
+__global__ void __launch_bounds__(256) km_prepare_d128_kernel(KmUpdateArgs a) {
   constexpr int D = 128;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int c = blockIdx.x * 4 + wave, bh = blockIdx.y;
   if (c >= a.Cp) return;
-  if (c >= a.C) {  // padding: never the nearest centre
+  if (c >= a.C) {
     *(uint32_t*)&a.cb[((int64_t)bh * a.Cp + c) * D + 2 * lane] = 0u;
     if (lane == 0) a.cn[(int64_t)bh * a.Cp + c] = __builtin_inff();
     return;
   }
   const f32x2 old = *(const f32x2*)&a.cent[((int64_t)bh * a.C + c) * D + 2 * lane];
-  if (MODE == 1) {
-    km_store_centre(a, bh, c, lane, old[0], old[1]);
-    return;
-  }
+  km_store_centre(a, bh, c, lane, old[0], old[1]);
+}
+
+// one workgroup per cluster: thread (row group g = tid / 16, chunk cc =
+// tid % 16) sums head dims 8 cc .. 8 cc + 7 of the cluster's rows g, g + 16,
+// g + 32, ... in order (16-byte loads, four rows in flight); the 16 row-group
+// sums are then added in group order and divided by the count
+__global__ void __launch_bounds__(256) km_update_d128_kernel(KmUpdateArgs a) {
+  constexpr int D = 128;
+  __shared__ __attribute__((aligned(16))) float part[16][D];
+  const int tid = threadIdx.x, cc = tid & 15, g = tid >> 4;
+  const int c = blockIdx.x, bh = blockIdx.y;
   const int32_t* o = a.off + (int64_t)bh * (a.C + 1);
   const int i0 = o[c], i1 = o[c + 1];
-  if (i1 == i0) {
-    km_store_centre(a, bh, c, lane, old[0], old[1]);
+  if (i1 == i0) {  // empty: the centre stays (its bf16 copy and norm are current)
     return;
   }
   const int32_t* perm = a.perm + (int64_t)bh * a.N;
-  const uint16_t* xh = a.x + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + 2 * lane;
-  float s0 = 0.f, s1 = 0.f;
-  int i = i0;
-  for (; i + 4 <= i1; i += 4) {  // four rows in flight, summed in cluster order
-    uint32_t w[4];
+  const uint16_t* xh = a.x + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + 8 * cc;
+  float acc[8];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = *(const uint32_t*)(xh + (int64_t)perm[i + u] * a.sn);
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int i = i0 + g; i < i1; i += 64) {
+    u32x4 w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s0 += bf16_lo(w[u]);
-      s1 += bf16_hi(w[u]);
-    }
+    for (int u = 0; u < 4; ++u)
+      w[u] = i + 16 * u < i1 ? *(const u32x4*)(xh + (int64_t)perm[i + 16 * u] * a.sn) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        acc[2 * e] += bf16_lo(w[u][e]);
+        acc[2 * e + 1] += bf16_hi(w[u][e]);
+      }
   }
-  for (; i < i1; ++i) {
-    const uint32_t w = *(const uint32_t*)(xh + (int64_t)perm[i] * a.sn);
-    s0 += bf16_lo(w);
-    s1 += bf16_hi(w);
+  *(f32x4*)&part[g][8 * cc] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  *(f32x4*)&part[g][8 * cc + 4] = f32x4{acc[4], acc[5], acc[6], acc[7]};
+  __syncthreads();
+  if (tid >= 64) return;
+  float t0 = 0.f, t1 = 0.f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) {
+    t0 += part[q][2 * tid];
+    t1 += part[q][2 * tid + 1];
   }
   const float n = (float)(i1 - i0);
-  km_store_centre(a, bh, c, lane, s0 / n, s1 / n);
+  km_store_centre(a, bh, c, tid, t0 / n, t1 / n);
 }
 
 // ---- row gather / scatter through a permutation ------------------------------
@@ -292,18 +342,19 @@ struct RowPermArgs {
   int scatter;         // 0: dst[i] = src[perm[i]]; 1: dst[perm[i]] = src[i]
 };
 
-// one wave per row; perm entries outside [0, N) are skipped
+// one thread per 16-byte chunk of an output row (consecutive threads walk a
+// row's chunks, then the next row); perm entries outside [0, N) are skipped
 __global__ void __launch_bounds__(256) rows_permute_kernel(RowPermArgs a) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int i = blockIdx.x * 4 + wave, bh = blockIdx.y;
+  const int64_t item = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  const int i = (int)(item / a.chunks), ch = (int)(item % a.chunks);
   if (i >= a.N) return;
   const int p = a.perm[(int64_t)bh * a.N + i];
   if (p < 0 || p >= a.N) return;
   const int64_t head = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
   const int si = a.scatter ? i : p, di = a.scatter ? p : i;
-  const u32x4* s = (const u32x4*)(a.src + head + (int64_t)si * a.sn);
-  u32x4* d = (u32x4*)(a.dst + head + (int64_t)di * a.sn);
-  for (int c = lane; c < a.chunks; c += 64) d[c] = s[c];
+  const u32x4 v = ((const u32x4*)(a.src + head + (int64_t)si * a.sn))[ch];
+  ((u32x4*)(a.dst + head + (int64_t)di * a.sn))[ch] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -320,7 +371,8 @@ KmPlan kmeans_plan(const bsa_shape& s, int C) {
   p.off_cb = 0;
   p.off_cn = km_align(p.off_cb + bh * p.Cp * 128 * 2);
   p.off_hist = km_align(p.off_cn + bh * p.Cp * 4);
-  p.off_perm = km_align(p.off_hist + bh * p.tiles * C * 4);
+  p.off_tbase = km_align(p.off_hist + bh * p.tiles * C * 4);
+  p.off_perm = km_align(p.off_tbase + bh * p.tiles * C * 4);
   p.off_off = km_align(p.off_perm + bh * s.N * 4);
   p.total = km_align(p.off_off + bh * (C + 1) * 4);
   return p;
@@ -334,20 +386,20 @@ bsa_status launch_kmeans(const void* x, const bsa_shape& s, int C, int iters, fl
   uint16_t* cb = (uint16_t*)(w + p.off_cb);
   float* cn = (float*)(w + p.off_cn);
   int32_t* hist = (int32_t*)(w + p.off_hist);
+  int32_t* tbase = (int32_t*)(w + p.off_tbase);
   if (!perm) perm = (int32_t*)(w + p.off_perm);
   if (!offsets) offsets = (int32_t*)(w + p.off_off);
   KmAssignArgs aa{(const uint16_t*)x, s.stride_b, s.stride_h, s.stride_n, s.H, s.N, C, p.Cp, p.tiles,
                   cb, cn, labels, hist};
-  KmOrderArgs oa{labels, hist, offsets, perm, s.N, C, p.tiles};
+  KmOrderArgs oa{labels, hist, tbase, offsets, perm, s.N, C, p.tiles};
   KmUpdateArgs ua{(const uint16_t*)x, s.stride_b, s.stride_h, s.stride_n, s.H, s.N, C, p.Cp, perm, offsets,
                   cent, cb, cn};
-  const dim3 ug((p.Cp + 3) / 4, bh);
-  hipLaunchKernelGGL(km_update_d128_kernel<1>, ug, dim3(256), 0, stream, ua);
+  hipLaunchKernelGGL(km_prepare_d128_kernel, dim3((p.Cp + 3) / 4, bh), dim3(256), 0, stream, ua);
   for (int t = 0; t <= iters; ++t) {
     hipLaunchKernelGGL(km_assign_d128_kernel, dim3(p.tiles, bh), dim3(256), 0, stream, aa);
     hipLaunchKernelGGL(km_scan_kernel, dim3(bh), dim3(kMaxKmClusters), 0, stream, oa);
-    hipLaunchKernelGGL(km_place_kernel, dim3(p.tiles, bh), dim3(64), 0, stream, oa);
-    if (t < iters) hipLaunchKernelGGL(km_update_d128_kernel<0>, ug, dim3(256), 0, stream, ua);
+    hipLaunchKernelGGL(km_place_kernel, dim3(p.tiles, bh), dim3(256), 0, stream, oa);
+    if (t < iters) hipLaunchKernelGGL(km_update_d128_kernel, dim3(C, bh), dim3(256), 0, stream, ua);
   }
   return launch_ok("kmeans") ? BSA_OK : BSA_ERR_HIP;
 }
@@ -356,7 +408,8 @@ bsa_status launch_rows_permute(const void* src, const bsa_shape& s, int elem_byt
                                bool scatter, hipStream_t stream) {
   RowPermArgs a{(const uint8_t*)src, (uint8_t*)dst, s.stride_b * elem_bytes, s.stride_h * elem_bytes,
                 s.stride_n * elem_bytes, s.H, s.N, s.D * elem_bytes / 16, perm, scatter ? 1 : 0};
-  hipLaunchKernelGGL(rows_permute_kernel, dim3((s.N + 3) / 4, s.B * s.H), dim3(256), 0, stream, a);
+  const int64_t items = (int64_t)s.N * a.chunks;
+  hipLaunchKernelGGL(rows_permute_kernel, dim3((unsigned)((items + 255) / 256), s.B * s.H), dim3(256), 0, stream, a);
   return launch_ok(scatter ? "scatter_rows" : "gather_rows") ? BSA_OK : BSA_ERR_HIP;
 }
 

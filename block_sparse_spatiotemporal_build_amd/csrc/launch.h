@@ -46,7 +46,7 @@ bsa_status launch_causal_linear_attn(const void* q, const void* k, const void* v
 constexpr int kMaxKmClusters = 1024;
 struct KmPlan {
   int Cp, tiles;  // centres padded to a multiple of 32; 256-token tiles per sequence
-  size_t off_cb, off_cn, off_hist, off_perm, off_off, total;  // workspace layout (bytes)
+  size_t off_cb, off_cn, off_hist, off_tbase, off_perm, off_off, total;  // workspace layout (bytes)
 };
 KmPlan kmeans_plan(const bsa_shape& s, int C);
 bsa_status launch_kmeans(const void* x, const bsa_shape& s, int C, int iters, float* cent, int32_t* labels,

@@ -232,7 +232,7 @@ size_t bsa_kmeans_workspace(const bsa_shape* shape, int32_t C);
  *   q_off / k_off form the calls below take.
  * Precision: the assignment compares |c_b|^2 - 2 x.c_b with c_b the centre
  *   rounded to bf16 (fp32 MFMA accumulation of exact bf16 products); means are
- *   fp32 sums in cluster order divided by the count.  Deterministic.
+ *   fp32 sums in a fixed order divided by the count.  Deterministic.
  * workspace: at least bsa_kmeans_workspace(shape, C) bytes, 256-byte aligned.
  * All pointers 16-byte aligned.  Only BSA_DT_BF16 (BSA_ERR_UNSUPPORTED). */
 bsa_status bsa_kmeans(const void* x, bsa_dtype dtype, const bsa_shape* shape, int32_t C, int32_t iters,

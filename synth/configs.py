@@ -46,8 +46,9 @@ class Workload:
     ar_rho: float = 0.9
     # latent inter-frame pruning (LIPAR): threshold on the mean |difference|
     lipar_tau: float = 0.0
-    # which call a linear-attention workload runs: "" non-causal, "causal", or
-    # "mixed" (LinVideo blend with weight mix_r on the block-sparse branch)
+    # which call a workload runs where its values do not say: "causal" or
+    # "mixed" (LinVideo blend with weight mix_r on the block-sparse branch) for
+    # the linear family, "kmeans" for the token clustering
     op: str = ""
     mix_r: float = 0.0
     notes: str = field(default="", compare=False)
@@ -94,6 +95,13 @@ WORKLOADS = {
         name="svg_ear_32k", seed=3, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
         dtype="bf16", values="gmm", n_q_clusters=100, n_k_clusters=500,
         density_ppm=150000),
+    # Token clustering in front of SVG-EAR: the same inputs as svg_ear_32k in
+    # token order, k-means of queries (100 clusters) and keys (500), 10 steps
+    # each from the generating centres, then the rows into cluster order.
+    "kmeans_32k": Workload(
+        name="kmeans_32k", seed=3, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
+        dtype="bf16", values="gmm", n_q_clusters=100, n_k_clusters=500,
+        density_ppm=150000, op="kmeans"),
     # LinVideo-style elu+1 linear attention at two lengths.
     "linear_32k": Workload(
         name="linear_32k", seed=4, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,

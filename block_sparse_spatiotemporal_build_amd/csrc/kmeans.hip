@@ -177,17 +177,46 @@ struct KmOrderArgs {
   int N, C, tiles;
 };
 
-// one workgroup of kMaxKmClusters threads per sequence (thread c = cluster c);
-// the tile loop keeps eight loads in flight
+// one workgroup of kMaxKmClusters threads per sequence.  Thread (g, c), c < C,
+// g < G (G = the largest power of two with G * C <= kMaxKmClusters) covers
+// cluster c over the g-th of G contiguous tile ranges: it sums that range, the
+// range sums give its start, and a second pass writes the running tile bases
+// (eight loads in flight in both passes)
+__device__ __forceinline__ int km_sum_tiles(const int32_t* __restrict__ h, int C, int t0, int t1) {
+  int run = 0, t = t0;
+  for (; t + 8 <= t1; t += 8) {
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = h[(int64_t)(t + u) * C];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) run += v[u];
+  }
+  for (; t < t1; ++t) run += h[(int64_t)t * C];
+  return run;
+}
+
 __global__ void __launch_bounds__(kMaxKmClusters) km_scan_kernel(KmOrderArgs a) {
   __shared__ int sc[kMaxKmClusters];
-  const int c = threadIdx.x, bh = blockIdx.x;
+  __shared__ int part[kMaxKmClusters];
+  const int tid = threadIdx.x, bh = blockIdx.x;
+  int G = 1;
+  while (2 * G * a.C <= kMaxKmClusters) G *= 2;
+  const int g = tid / a.C, c = tid - g * a.C;
+  const bool act = g < G;
+  const int t0 = act ? (int)((int64_t)a.tiles * g / G) : 0, t1 = act ? (int)((int64_t)a.tiles * (g + 1) / G) : 0;
   const int32_t* __restrict__ h = a.hist + (int64_t)bh * a.tiles * a.C + c;
   int32_t* __restrict__ tb = a.tbase + (int64_t)bh * a.tiles * a.C + c;
-  int run = 0;
-  if (c < a.C) {
-    int t = 0;
-    for (; t + 8 <= a.tiles; t += 8) {
+  if (act) part[tid] = km_sum_tiles(h, a.C, t0, t1);
+  __syncthreads();
+  int run = 0, total = 0;
+  if (act) {
+    for (int q = 0; q < G; ++q) {
+      const int v = part[q * a.C + c];
+      run += q < g ? v : 0;
+      total += v;
+    }
+    int t = t0;
+    for (; t + 8 <= t1; t += 8) {
       int v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) v[u] = h[(int64_t)(t + u) * a.C];
@@ -197,24 +226,25 @@ __global__ void __launch_bounds__(kMaxKmClusters) km_scan_kernel(KmOrderArgs a) 
         run += v[u];
       }
     }
-    for (; t < a.tiles; ++t) {
+    for (; t < t1; ++t) {
       const int v = h[(int64_t)t * a.C];
       tb[(int64_t)t * a.C] = run;
       run += v;
     }
   }
-  // inclusive scan of the cluster counts (Hillis-Steele in LDS)
-  sc[c] = run;
+  // inclusive scan of the cluster counts (Hillis-Steele in LDS, thread c)
+  const int cnt_c = tid < a.C ? total : 0;
+  sc[tid] = cnt_c;
   __syncthreads();
   for (int d = 1; d < kMaxKmClusters; d <<= 1) {
-    const int v = c >= d ? sc[c - d] : 0;
+    const int v = tid >= d ? sc[tid - d] : 0;
     __syncthreads();
-    sc[c] += v;
+    sc[tid] += v;
     __syncthreads();
   }
   int32_t* o = a.off + (int64_t)bh * (a.C + 1);
-  if (c < a.C) o[c] = sc[c] - run;
-  if (c == a.C - 1) o[a.C] = sc[c];
+  if (tid < a.C) o[tid] = sc[tid] - cnt_c;
+  if (tid == a.C - 1) o[a.C] = sc[tid];
 }
 
 // one workgroup per tile, wave b placing tokens 64 b .. 64 b + 63 of the tile:

@@ -27,7 +27,8 @@ attention), ``svg_ear`` (centroids, routing scores, budget selection,
 compensated attention; the score formula is "parity unpinned" as far as the
 pages go, see that module), ``linear`` (elu+1 linear attention, causal and
 mixed forms), ``lipar`` (pruning and restoration), ``kmeans`` (the token
-clustering and cluster order in front of the SVG-EAR calls).
+clustering and cluster order in front of the SVG-EAR calls),
+``attention_bwd`` (gradients of the block-sparse attention).
 """
 
-from . import mask, attention, linear, svg_ear, lipar, kmeans  # noqa: F401
+from . import mask, attention, attention_bwd, linear, svg_ear, lipar, kmeans  # noqa: F401

@@ -19,14 +19,20 @@ Keys of skipped blocks receive nothing from that query block; a query row
 without keys has O = 0 and receives zero gradient.  Per query block the kept
 key blocks are gathered and the products are float64 matrix products, in
 query-block order.
+
+Reading (``o_dtype="bf16"``): a bf16 training step keeps the forward output as
+stored, in bf16, and takes Delta = rowsum(dO * O) from it (the identity with
+rowsum(P * dP) holds for the exact O only); the oracle then rounds its own O to
+bf16 before that row sum.  ``o_dtype=None`` uses the exact O.
 """
 
 import numpy as np
 
 from .attention import kept_keys, softmax_rows
+from .numerics import round_bf16
 
 
-def block_sparse_attention_backward(q, k, v, do, mask: np.ndarray, block: int, scale: float):
+def block_sparse_attention_backward(q, k, v, do, mask: np.ndarray, block: int, scale: float, o_dtype=None):
     """(dq, dk, dv) float64 [B, H, N, D] for float64 [B, H, N, D] q, k, v, do."""
     q, k, v, do = (np.asarray(t, np.float64) for t in (q, k, v, do))
     B, H, N, _ = q.shape
@@ -44,7 +50,10 @@ def block_sparse_attention_backward(q, k, v, do, mask: np.ndarray, block: int, s
                 p, _ = softmax_rows(scale * (qi @ kk.T))
                 dv[b, h, keys] += p.T @ doi
                 dp = doi @ vk.T
-                delta = (p * dp).sum(axis=1, keepdims=True)
+                if o_dtype == "bf16":
+                    delta = (doi * round_bf16(p @ vk)).sum(axis=1, keepdims=True)
+                else:
+                    delta = (p * dp).sum(axis=1, keepdims=True)
                 ds = p * (dp - delta)
                 dq[b, h, r0:r1] = scale * (ds @ kk)
                 dk[b, h, keys] += scale * (ds.T @ qi)

@@ -27,13 +27,7 @@ Readings (the page names the grouping, not the algorithm):
 
 import numpy as np
 
-
-def round_bf16(x):
-    """float64 -> nearest bf16 value (ties to even), returned as float64."""
-    f = np.asarray(x, np.float64).astype(np.float32)
-    b = f.view(np.uint32).astype(np.uint64)
-    b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
-    return b.astype(np.uint32).view(np.float32).astype(np.float64)
+from .numerics import round_bf16
 
 
 def assign(x, centres, centre_dtype="bf16"):

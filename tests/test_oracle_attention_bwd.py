@@ -95,3 +95,24 @@ def test_transpose_csr():
     tp, ti = ob.transpose_csr(rp, ci, 9)
     tp2, ti2 = om.to_csr(m.T)
     assert np.array_equal(tp, tp2) and np.array_equal(ti, ti2)
+
+
+def test_stored_bf16_output_changes_only_delta():
+    """With Delta taken from the bf16-rounded output, dS changes by -P * eps per
+    row (eps = rowsum(dO * (bf16(O) - O))), so dq moves by -scale * eps * (P K),
+    dk by -scale * (P * eps)^T Q and dv not at all: checked against the exact
+    gradients with P, O and eps formed from the dense masked softmax."""
+    from oracle.numerics import round_bf16
+    q, k, v, do, m = _case(48, 8, 16, 9, density=1.1)           # every block kept: plain dense attention
+    scale = 0.3
+    ex = ob.block_sparse_attention_backward(q, k, v, do, m, 16, scale)
+    bf = ob.block_sparse_attention_backward(q, k, v, do, m, 16, scale, o_dtype="bf16")
+    s = scale * np.einsum("bhnd,bhmd->bhnm", q, k)
+    p = np.exp(s - s.max(-1, keepdims=True))
+    p /= p.sum(-1, keepdims=True)
+    o = p @ v
+    eps = (do * (round_bf16(o) - o)).sum(-1, keepdims=True)
+    assert np.allclose(bf[0] - ex[0], -scale * eps * (p @ k), rtol=1e-9, atol=1e-12)
+    assert np.allclose(bf[1] - ex[1], -scale * np.einsum("bhnm,bhnd->bhmd", p * eps, q), rtol=1e-9, atol=1e-12)
+    assert np.array_equal(bf[2], ex[2])
+    assert np.abs(eps).max() > 0

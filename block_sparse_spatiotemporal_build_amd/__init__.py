@@ -44,6 +44,11 @@ _SIGNATURES = {
     "bsa_block_sparse_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int,
                                                  ctypes.POINTER(Shape), _P, _P, _P, ctypes.c_int32,
                                                  ctypes.c_float, _P]),
+    "bsa_transpose_block_mask": (ctypes.c_int, [_P, _P, ctypes.c_int32, _P, _P, ctypes.c_int64, _P]),
+    "bsa_block_sparse_attn_bwd_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
+    "bsa_block_sparse_attn_bwd": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
+                                                 _P, _P, _P, ctypes.c_int32, ctypes.c_float, _P, _P, _P, _P,
+                                                 ctypes.c_size_t, _P]),
     "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                            _P, ctypes.c_size_t, _P]),
@@ -224,6 +229,45 @@ def _check_qkv(q, k, v):
         raise BsaError("q, k, v must share one shape and one stride layout")
     if k.dtype != q.dtype or v.dtype != q.dtype:
         raise BsaError("q, k, v must share one dtype")
+
+
+def transpose_block_mask(row_ptr, col_idx):
+    """(col_ptr, row_idx): the transposed block CSR (query blocks per key block)."""
+    lib = load()
+    nb = row_ptr.numel() - 1
+    col_ptr = torch.empty(nb + 1, dtype=torch.int32, device=row_ptr.device)
+    row_idx = torch.empty(nb * nb, dtype=torch.int32, device=row_ptr.device)
+    _check(lib.bsa_transpose_block_mask(_ptr(row_ptr), _ptr(col_idx), nb, _ptr(col_ptr), _ptr(row_idx),
+                                        row_idx.numel(), _stream(row_ptr.device)), "bsa_transpose_block_mask")
+    return col_ptr, row_idx
+
+
+def block_sparse_attn_bwd(q, k, v, o, do, lse, row_ptr, col_idx, block: int = 128, scale=None,
+                          col_ptr=None, row_idx=None, dq=None, dk=None, dv=None, workspace=None):
+    """(dq, dk, dv) of block-sparse attention (bf16, D = 128, block 128)."""
+    lib = load()
+    _check_qkv(q, k, v)
+    for t in (o, do):
+        if t.dtype != q.dtype or t.stride() != q.stride() or t.shape != q.shape:
+            raise BsaError("o and do must have the layout and dtype of q")
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise BsaError("lse must be a contiguous fp32 tensor [B, H, N]")
+    shape = _shape_of(q)
+    scale = 1.0 / math.sqrt(q.shape[3]) if scale is None else scale
+    if col_ptr is None:
+        col_ptr, row_idx = transpose_block_mask(row_ptr, col_idx)
+    outs = []
+    for t in (dq, dk, dv):
+        outs.append(torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device) if t is None else t)
+    if workspace is None:
+        need = int(lib.bsa_block_sparse_attn_bwd_workspace(ctypes.byref(shape)))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.bsa_block_sparse_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(do), _ptr(lse), _dtype_code(q),
+                                         ctypes.byref(shape), _ptr(row_ptr), _ptr(col_idx), _ptr(col_ptr),
+                                         _ptr(row_idx), int(block), float(scale), _ptr(outs[0]), _ptr(outs[1]),
+                                         _ptr(outs[2]), _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "bsa_block_sparse_attn_bwd")
+    return tuple(outs)
 
 
 def linear_attn_workspace(shape_like) -> int:

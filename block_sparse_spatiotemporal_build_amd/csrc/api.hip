@@ -130,6 +130,52 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   return launch_attn_f32(q, k, v, o, lse, *shape, row_ptr, col_idx, block, scale, (hipStream_t)stream);
 }
 
+bsa_status bsa_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int32_t nb, int32_t* col_ptr,
+                                    int32_t* row_idx, int64_t capacity, void* stream) {
+  const char* fn = "bsa_transpose_block_mask";
+  if (nb < 1 || nb > 46340) return fail(BSA_ERR_ARG, "%s: nb must be in [1, 46340]", fn);
+  if (!row_ptr || !col_idx || !col_ptr || !row_idx) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (capacity < (int64_t)nb * nb)
+    return fail(BSA_ERR_CAPACITY, "%s: capacity %lld < nb*nb = %lld", fn, (long long)capacity,
+                (long long)nb * nb);
+  g_err[0] = 0;
+  return launch_transpose_block_mask(row_ptr, col_idx, nb, col_ptr, row_idx, (hipStream_t)stream);
+}
+
+size_t bsa_block_sparse_attn_bwd_workspace(const bsa_shape* shape) {
+  if (check_shape(shape, 2, "bsa_block_sparse_attn_bwd_workspace") != BSA_OK) return 0;
+  return ((size_t)shape->B * shape->H * shape->N * 4 + 255) & ~(size_t)255;
+}
+
+bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                     const float* lse, bsa_dtype dtype, const bsa_shape* shape,
+                                     const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+                                     const int32_t* row_idx, int32_t block, float scale, void* dq, void* dk,
+                                     void* dv, void* workspace, size_t ws_bytes, void* stream) {
+  const char* fn = "bsa_block_sparse_attn_bwd";
+  if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
+  bsa_status st = check_shape(shape, 2, fn);
+  if (st != BSA_OK) return st;
+  if (shape->D != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: D must be 128 (got %d)", fn, shape->D);
+  if (block != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: block must be 128 (got %d)", fn, block);
+  if (!q || !k || !v || !o || !dO || !lse || !row_ptr || !col_idx || !col_ptr || !row_idx || !dq || !dk || !dv)
+    return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return fail(BSA_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
+  if (!__builtin_isfinite(scale) || scale == 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  if (((int64_t)shape->N + 128) * shape->stride_n * 2 >= ((int64_t)1 << 31))
+    return fail(BSA_ERR_UNSUPPORTED, "%s: a head must fit 32-bit byte offsets", fn);
+  const size_t need = bsa_block_sparse_attn_bwd_workspace(shape);
+  if (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0)
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
+                workspace ? ws_bytes : (size_t)0);
+  g_err[0] = 0;
+  return launch_attn_bwd_bf16(q, k, v, o, dO, lse, *shape, row_ptr, col_idx, col_ptr, row_idx, scale, dq, dk, dv,
+                              workspace, (hipStream_t)stream);
+}
+
 size_t bsa_linear_attn_workspace(const bsa_shape* shape) {
   if (check_shape(shape, 2, "bsa_linear_attn_workspace") != BSA_OK) return 0;
   return linear_plan(*shape).total;

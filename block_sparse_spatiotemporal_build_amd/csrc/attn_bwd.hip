@@ -1,0 +1,443 @@
+// Backward pass of block-sparse softmax attention, bf16, head_dim 128, blocks
+// of 128 tokens, for gfx950.
+//
+// Operation: the gradients of the block-sparse attention of attn_fwd.hip
+// (LVSA review page, section 1 Key Terms: block-sparse attention; needed by the
+// training uses on the Radial Attention headline (LoRA fine-tuning for longer
+// videos) and the LinVideo page (post-training)).  For query block i with kept
+// key set K(i), P = softmax(scale * Q_i K^T) is recomputed from the forward's
+// log-sum-exp, and
+//   dV_K += P^T dO_i,  dP = dO_i V_K^T,  Delta = rowsum(dO_i * O_i),
+//   dS = P * (dP - Delta),  dQ_i = scale * dS K_K,  dK_K += scale * dS^T Q_i.
+//
+// Two launches, no atomics (deterministic):
+//   dq   : grid (query blocks, B*H), 4 waves x 32 query rows.  Q and dO of the
+//          wave's rows are register-resident B operands; Delta comes from dO
+//          and O of the same rows (fp32) and is stored for the second launch.
+//          The row's kept key blocks stream through LDS in 64-key sub-tiles
+//          (K and V by buffer loads, one sub-tile ahead, rows swizzled for the
+//          transpose read).  Per sub-tile: S^T = K Q^T and dP^T = V dO^T
+//          (32x32x16 MFMA, keys x queries: each lane owns one query column),
+//          P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - Delta),
+//          and dQ^T += K^T dS^T with K^T from the transpose read and dS^T taken
+//          straight from the accumulators (the softmax kernel's P^T trick).
+//   dkdv : grid (key blocks, B*H), 4 waves x 32 key rows, walking the query
+//          blocks that keep the key block (the transposed CSR) in 32-query
+//          sub-tiles: K and V of the wave's keys are the B operands;
+//          S = Q K^T and dP = dO V^T (queries x keys: each lane owns one key
+//          column), P and dS from the staged lse and Delta of the sub-tile, and
+//          dV^T += dO^T P, dK^T += Q^T dS with the transpose reads of the
+//          staged Q and dO.
+// Accumulation is fp32; P and dS enter the MFMA as bf16; the gradients are
+// stored as bf16.
+
+#include "launch.h"
+
+namespace bsa {
+
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dO;
+  const float* lse;       // [BH][N] natural log
+  float* delta;           // [BH][N] workspace
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  const int32_t* row_ptr;
+  const int32_t* col_idx;
+  const int32_t* col_ptr;  // transposed CSR
+  const int32_t* row_idx;
+  int64_t sb, sh, sn;
+  int H, N, nb;
+  float scale, c2;         // softmax scale, scale * log2(e)
+};
+
+constexpr int kBwdBlock = 128;
+
+// transpose read of a swz_v-swizzled stage: lane (l32, hi) gets column
+// 32 dt + l32 at rows 16 ks + 8 (e / 4) + 4 hi + e % 4, e = 0..7
+__device__ __forceinline__ bf16x8 bwd_tr_frag(const uint16_t* st, int ks, int dt, int lane) {
+  constexpr int D = 128;
+  const int hi = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
+  const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
+  const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  const int half = (j16 & 1) * 4;
+  const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
+  const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+  return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+}
+
+// row fragment of a swz_v-swizzled stage: row r, head dims 16 t + 8 hi .. + 7
+__device__ __forceinline__ bf16x8 bwd_row_frag(const uint16_t* st, int r, int t, int hi) {
+  constexpr int D = 128;
+  return *(const bf16x8*)&st[r * D + (((2 * t + hi) ^ swz_v(r)) << 3)];
+}
+
+__device__ __forceinline__ void bwd_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// dQ (and Delta)
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) attn_bwd_dq_d128_kernel(BwdArgs a) {
+  constexpr int D = 128, KT = 8, DT = 4, SUB = 64, TILE = SUB * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int qblk = blockIdx.x, bh = blockIdx.y;
+  const int N = a.N;
+  const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
+  const int qrow = qblk * kBwdBlock + 32 * wave + l32;
+  const int qr = min(qrow, N - 1);
+
+  // B operands: query l32, head dims 16 t + 8 hi .. + 7; Delta from dO and O
+  bf16x8 qf[KT], gf[KT];
+  float dl = 0.f;
+  {
+    const int64_t ro = head_off + (int64_t)qr * a.sn + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      qf[t] = *(const bf16x8*)(a.q + ro + 16 * t);
+      const u32x4 g = *(const u32x4*)(a.dO + ro + 16 * t);
+      const u32x4 ov = *(const u32x4*)(a.o + ro + 16 * t);
+      gf[t] = __builtin_bit_cast(bf16x8, g);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dl = __builtin_fmaf(bf16_lo(g[e]), bf16_lo(ov[e]), dl);
+        dl = __builtin_fmaf(bf16_hi(g[e]), bf16_hi(ov[e]), dl);
+      }
+    }
+  }
+  dl = pair_sum(dl);
+  if (hi == 0 && qrow < N) a.delta[(int64_t)bh * N + qrow] = dl;
+  const float lse2 = a.lse[(int64_t)bh * N + qr] * kLog2e;
+
+  const int rbeg = a.row_ptr[qblk], rend = a.row_ptr[qblk + 1];
+  int nsub = (rend - rbeg) * 2;
+  if (nsub > 0 && a.col_idx[rend - 1] == a.nb - 1) {
+    const int last_real = N - (a.nb - 1) * kBwdBlock;
+    nsub -= 2 - (last_real + SUB - 1) / SUB;
+  }
+  auto key0_of = [&](int u) -> int { return a.col_idx[rbeg + (u >> 1)] * kBwdBlock + (u & 1) * SUB; };
+
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  // copy roles: wave w, instruction j stages rows 16 w + 4 j + lane / 16
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int key0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * wv + 4 * j + (lane >> 4);
+      const uint32_t o = (uint32_t)min(key0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+    }
+  };
+
+  f32x16 dq[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) dq[i] = f32x16{};
+
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
+    const int key0 = key0_of(u);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed
+    bwd_barrier();
+    if (u + 1 < nsub) dma(Kn, Vn, key0_of(u + 1));
+    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Kb, 32 * kt + l32, t, hi), qf[t], s[kt], 0, 0, 0);
+        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Vb, 32 * kt + l32, t, hi), gf[t], dp[kt], 0, 0, 0);
+      }
+    // s[kt][r] is key key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4 of query l32
+    bf16x8 df[4];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      float ds[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool live = key0 + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) < N;
+        const float p = live ? fast_exp2(__builtin_fmaf(s[kt][r], a.c2, -lse2)) : 0.f;
+        ds[r] = p * (dp[kt][r] - dl);
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const u32x4 w = {pack_bf16x2(ds[8 * h2], ds[8 * h2 + 1]), pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]),
+                         pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7])};
+        df[2 * kt + h2] = __builtin_bit_cast(bf16x8, w);
+      }
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Kb, ks, dt, lane), df[ks], dq[dt], 0, 0, 0);
+  };
+
+  if (nsub > 0) dma(K0, V0, key0_of(0));
+  int u = 0;
+  for (; u + 2 <= nsub; u += 2) {
+    step(K0, V0, K1, V1, u);
+    step(K1, V1, K0, V0, u + 1);
+  }
+  if (u < nsub) step(K0, V0, K1, V1, u);
+
+  // dq[dt][r] = dQ^T[32 dt + 8 (r / 4) + 4 hi + r % 4][query l32] / scale
+  if (qrow < N) {
+    uint16_t* dst = a.dq + head_off + (int64_t)qrow * a.sn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 w = {pack_bf16x2(dq[dt][4 * g] * a.scale, dq[dt][4 * g + 1] * a.scale),
+                         pack_bf16x2(dq[dt][4 * g + 2] * a.scale, dq[dt][4 * g + 3] * a.scale)};
+        *(u32x2*)(dst + 32 * dt + 8 * g + 4 * hi) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
+  constexpr int D = 128, KT = 8, DT = 4, SUB = 32, TILE = SUB * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t G0[TILE], G1[TILE];
+  __shared__ __attribute__((aligned(16))) float L[2][SUB], E[2][SUB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
+  const int kblk = blockIdx.x, bh = blockIdx.y;
+  const int N = a.N;
+  const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
+  const int krow = kblk * kBwdBlock + 32 * wave + l32;
+
+  // B operands: key l32, head dims 16 t + 8 hi .. + 7
+  bf16x8 kf[KT], vf[KT];
+  {
+    const int64_t ro = head_off + (int64_t)min(krow, N - 1) * a.sn + 8 * hi;
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      kf[t] = *(const bf16x8*)(a.k + ro + 16 * t);
+      vf[t] = *(const bf16x8*)(a.v + ro + 16 * t);
+    }
+  }
+
+  const int cbeg = a.col_ptr[kblk], cend = a.col_ptr[kblk + 1];
+  constexpr int PER = kBwdBlock / SUB;  // sub-tiles per query block
+  int nsub = (cend - cbeg) * PER;
+  if (nsub > 0 && a.row_idx[cend - 1] == a.nb - 1) {
+    const int last_real = N - (a.nb - 1) * kBwdBlock;
+    nsub -= PER - (last_real + SUB - 1) / SUB;
+  }
+  auto q0_of = [&](int u) -> int { return a.row_idx[cbeg + u / PER] * kBwdBlock + (u % PER) * SUB; };
+
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t qrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t grs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.dO + head_off), (short)0, 0x7fffffff, kBufferWord3);
+  // copy roles: wave w, instruction j stages rows 8 w + 4 j + lane / 16
+  auto dma = [&](uint16_t* qst, uint16_t* gst, int q0) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int row = 8 * wv + 4 * j + (lane >> 4);
+      const uint32_t o = (uint32_t)min(q0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)&gst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+    }
+  };
+  // lse (log2 units; +inf for rows past N, so P = 0 there) and Delta of a
+  // sub-tile's queries: loaded by wave 0 early, written to LDS late
+  const float* lse_h = a.lse + (int64_t)bh * N;
+  const float* del_h = a.delta + (int64_t)bh * N;
+  float nl = 0.f, ne = 0.f;
+  auto side_load = [&](int q0) {
+    if (wave == 0 && lane < SUB) {
+      const int qq = q0 + lane;
+      nl = qq < N ? lse_h[qq] * kLog2e : __builtin_inff();
+      ne = qq < N ? del_h[qq] : 0.f;
+    }
+  };
+  auto side_store = [&](int buf) {
+    if (wave == 0 && lane < SUB) {
+      L[buf][lane] = nl;
+      E[buf][lane] = ne;
+    }
+  };
+
+  f32x16 dk[DT], dv[DT];
+#pragma unroll
+  for (int i = 0; i < DT; ++i) dk[i] = dv[i] = f32x16{};
+
+  auto step = [&](const uint16_t* Qb, const uint16_t* Gb, uint16_t* Qn, uint16_t* Gn, int u) {
+    const int buf = u & 1;
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u and its lse / Delta landed
+    bwd_barrier();
+    if (u + 1 < nsub) {
+      dma(Qn, Gn, q0_of(u + 1));
+      side_load(q0_of(u + 1));
+    }
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int t = 0; t < KT; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Qb, l32, t, hi), kf[t], s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Gb, l32, t, hi), vf[t], dp, 0, 0, 0);
+    }
+    // s[r] is query 8 (r / 4) + 4 hi + r % 4 of the sub-tile, key l32
+    float p[16], ds[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lg = *(const f32x4*)&L[buf][8 * g + 4 * hi];
+      const f32x4 eg = *(const f32x4*)&E[buf][8 * g + 4 * hi];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        p[r] = fast_exp2(__builtin_fmaf(s[r], a.c2, -lg[j]));
+        ds[r] = p[r] * (dp[r] - eg[j]);
+      }
+    }
+    bf16x8 pf[2], df[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 wp = {pack_bf16x2(p[8 * ks], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
+                        pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7])};
+      const u32x4 wd = {pack_bf16x2(ds[8 * ks], ds[8 * ks + 1]), pack_bf16x2(ds[8 * ks + 2], ds[8 * ks + 3]),
+                        pack_bf16x2(ds[8 * ks + 4], ds[8 * ks + 5]), pack_bf16x2(ds[8 * ks + 6], ds[8 * ks + 7])};
+      pf[ks] = __builtin_bit_cast(bf16x8, wp);
+      df[ks] = __builtin_bit_cast(bf16x8, wd);
+    }
+    // dV^T += dO^T P,  dK^T += Q^T dS
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Gb, ks, dt, lane), pf[ks], dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Qb, ks, dt, lane), df[ks], dk[dt], 0, 0, 0);
+      }
+    if (u + 1 < nsub) side_store(buf ^ 1);
+  };
+
+  if (nsub > 0) {
+    dma(Q0, G0, q0_of(0));
+    side_load(q0_of(0));
+    side_store(0);
+  }
+  int u = 0;
+  for (; u + 2 <= nsub; u += 2) {
+    step(Q0, G0, Q1, G1, u);
+    step(Q1, G1, Q0, G0, u + 1);
+  }
+  if (u < nsub) step(Q0, G0, Q1, G1, u);
+
+  // dk[dt][r] = dK^T[32 dt + 8 (r / 4) + 4 hi + r % 4][key l32] / scale
+  if (krow < N) {
+    uint16_t* dkd = a.dk + head_off + (int64_t)krow * a.sn;
+    uint16_t* dvd = a.dv + head_off + (int64_t)krow * a.sn;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * dt + 8 * g + 4 * hi;
+        const u32x2 wk = {pack_bf16x2(dk[dt][4 * g] * a.scale, dk[dt][4 * g + 1] * a.scale),
+                          pack_bf16x2(dk[dt][4 * g + 2] * a.scale, dk[dt][4 * g + 3] * a.scale)};
+        const u32x2 wvv = {pack_bf16x2(dv[dt][4 * g], dv[dt][4 * g + 1]),
+                           pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
+        *(u32x2*)(dkd + d0) = wk;
+        *(u32x2*)(dvd + d0) = wvv;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// transposed block CSR
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ bool csr_has(const int32_t* cols, int b, int e, int j) {
+  while (b < e) {  // columns ascending
+    const int m = (b + e) >> 1;
+    const int c = cols[m];
+    if (c == j) return true;
+    if (c < j) b = m + 1;
+    else e = m;
+  }
+  return false;
+}
+
+// one workgroup: thread t owns key blocks [t per, (t + 1) per); counts by
+// binary search in every row, a block-wide scan, then the fill in row order
+__global__ void __launch_bounds__(1024) mask_transpose_kernel(const int32_t* row_ptr, const int32_t* col_idx, int nb,
+                                                              int32_t* col_ptr, int32_t* row_idx) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int per = (nb + 1023) / 1024;
+  const int j0 = min(t * per, nb), j1 = min(j0 + per, nb);
+  int mine = 0;
+  for (int j = j0; j < j1; ++j) {
+    int c = 0;
+    for (int i = 0; i < nb; ++i) c += csr_has(col_idx, row_ptr[i], row_ptr[i + 1], j) ? 1 : 0;
+    col_ptr[j + 1] = c;
+    mine += c;
+  }
+  part[t] = mine;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = t >= d ? part[t - d] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = part[t] - mine;
+  if (t == 0) col_ptr[0] = 0;
+  for (int j = j0; j < j1; ++j) {
+    const int c = col_ptr[j + 1];
+    int pos = run;
+    for (int i = 0; i < nb; ++i)
+      if (csr_has(col_idx, row_ptr[i], row_ptr[i + 1], j)) row_idx[pos++] = i;
+    run += c;
+    col_ptr[j + 1] = run;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+
+bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int nb, int32_t* col_ptr,
+                                       int32_t* row_idx, hipStream_t stream) {
+  hipLaunchKernelGGL(mask_transpose_kernel, dim3(1), dim3(1024), 0, stream, row_ptr, col_idx, nb, col_ptr, row_idx);
+  return launch_ok("transpose_block_mask") ? BSA_OK : BSA_ERR_HIP;
+}
+
+bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                const float* lse, const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
+                                void* dv, void* ws, hipStream_t stream) {
+  BwdArgs a;
+  a.q = (const uint16_t*)q; a.k = (const uint16_t*)k; a.v = (const uint16_t*)v;
+  a.o = (const uint16_t*)o; a.dO = (const uint16_t*)dO; a.lse = lse; a.delta = (float*)ws;
+  a.dq = (uint16_t*)dq; a.dk = (uint16_t*)dk; a.dv = (uint16_t*)dv;
+  a.row_ptr = row_ptr; a.col_idx = col_idx; a.col_ptr = col_ptr; a.row_idx = row_idx;
+  a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
+  a.H = s.H; a.N = s.N; a.nb = (s.N + kBwdBlock - 1) / kBwdBlock;
+  a.scale = scale; a.c2 = scale * kLog2e;
+  const dim3 grid(a.nb, s.B * s.H);
+  hipLaunchKernelGGL(attn_bwd_dq_d128_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_d128_kernel, grid, dim3(256), 0, stream, a);
+  return launch_ok("block_sparse_attn_bwd") ? BSA_OK : BSA_ERR_HIP;
+}
+
+}  // namespace bsa

@@ -18,6 +18,14 @@ bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o,
                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                            int block, float scale, hipStream_t stream);
 
+// ---- block-sparse attention backward (bf16, head_dim 128, block 128) ----------
+bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int nb, int32_t* col_ptr,
+                                       int32_t* row_idx, hipStream_t stream);
+bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                const float* lse, const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
+                                const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
+                                void* dv, void* ws, hipStream_t stream);
+
 // ---- linear attention ------------------------------------------------------
 struct LinPlan {
   int splits, chunk;  // state: token splits per head and tokens per split

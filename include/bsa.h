@@ -131,6 +131,41 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
                                      const int32_t* row_order, int32_t block, float scale,
                                      void* stream);
 
+/* Transposed block mask: for every key block j the query blocks i with
+ * (i, j) kept, ascending, as CSR (col_ptr int32 [nb + 1], row_idx int32, at
+ * least nb * nb entries of capacity or BSA_ERR_CAPACITY).  row_ptr / col_idx
+ * as bsa_build_block_mask writes them (device contents trusted: columns
+ * ascending and in [0, nb)).  One workgroup; meant to be run once per mask. */
+bsa_status bsa_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int32_t nb, int32_t* col_ptr,
+                                    int32_t* row_idx, int64_t capacity, void* stream);
+
+/* Workspace bytes required by bsa_block_sparse_attn_bwd (Delta, fp32 per query
+ * row); 0 if the shape is invalid. */
+size_t bsa_block_sparse_attn_bwd_workspace(const bsa_shape* shape);
+
+/* Gradients of block-sparse attention (the backward pass of
+ * bsa_block_sparse_attn_fwd).  Needed by the training uses on the pages: the
+ * LoRA fine-tuning of Radial Attention for longer videos (hyper.ai headline)
+ * and LinVideo's post-training (technical summary sections 1-2).  With
+ * P = softmax(scale * Q K^T) over each row's kept keys (recomputed from lse):
+ *   dV = P^T dO,  dS = P * (dO V^T - rowsum(dO * O)),  dQ = scale * dS K,
+ *   dK = scale * dS^T Q.
+ * q, k, v, o (the forward output), dO: bf16 device tensors with `shape`,
+ *   D = 128; dq, dk, dv: bf16 outputs with the same layout.
+ * lse: fp32 [B, H, N], natural log, as the forward writes it.
+ * row_ptr, col_idx: the forward's block CSR for block = 128; col_ptr, row_idx:
+ *   its transpose (bsa_transpose_block_mask).  Device contents trusted.
+ * Precision: fp32 accumulation; P and dS enter the MFMA as bf16; Delta uses the
+ *   bf16 forward output.  Deterministic (no atomics).  Rows without kept keys
+ *   get zero dq; keys no row keeps get zero dk and dv.
+ * workspace: at least bsa_block_sparse_attn_bwd_workspace(shape) bytes,
+ *   256-byte aligned.  Only bf16, D = 128, block = 128 (BSA_ERR_UNSUPPORTED). */
+bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                                     const float* lse, bsa_dtype dtype, const bsa_shape* shape,
+                                     const int32_t* row_ptr, const int32_t* col_idx, const int32_t* col_ptr,
+                                     const int32_t* row_idx, int32_t block, float scale, void* dq, void* dk,
+                                     void* dv, void* workspace, size_t ws_bytes, void* stream);
+
 /* Workspace bytes required by bsa_linear_attn_fwd for `shape` (0 if the shape
  * is invalid).  The workspace holds per-chunk partial states (fp32), the
  * reduced S^T in bf16 and z. */

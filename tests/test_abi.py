@@ -223,3 +223,22 @@ def test_kmeans_and_row_permute_argument_checks(lib):
     assert lib.bsa_gather_rows(p, 0, ctypes.byref(ok_), p, p, None) == 1          # in place
     assert lib.bsa_scatter_rows(p, 7, ctypes.byref(ok_), p, ctypes.c_void_p(8192), None) == 1
     assert b"bsa_scatter_rows" in lib.bsa_last_error()
+
+
+def test_attention_backward_argument_checks(lib):
+    p = ctypes.c_void_p(4096)
+    ok_ = _shape(B=1, H=2, N=1000, D=128)
+
+    def bwd(shape=ok_, block=128, dtype=0, ws=1 << 30, scale=0.1, ptr=p):
+        return lib.bsa_block_sparse_attn_bwd(ptr, p, p, p, p, p, dtype, ctypes.byref(shape), p, p, p, p, block,
+                                             ctypes.c_float(scale), p, p, p, ctypes.c_void_p(1 << 20), ws, None)
+
+    assert bwd(shape=_shape(D=64)) == 2
+    assert bwd(block=64) == 2
+    assert bwd(dtype=1) == 2
+    assert bwd(scale=float("inf")) == 1
+    assert bwd(ws=16) == 4
+    assert bwd(ptr=ctypes.c_void_p(4098)) == 1
+    assert b"bsa_block_sparse_attn_bwd" in lib.bsa_last_error()
+    assert lib.bsa_transpose_block_mask(p, p, 10, p, p, 99, None) == 3          # capacity < nb * nb
+    assert lib.bsa_transpose_block_mask(p, p, 0, p, p, 99, None) == 1

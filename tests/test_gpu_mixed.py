@@ -39,7 +39,7 @@ def _case(bsa, wl, params, r, rows=None):
 
 
 def _lvsa(wl, block=128):
-    return dict(kind=0, frames=wl.frames, frame_tokens=wl.P, block=block, window=1,
+    return dict(kind=1, frames=wl.frames, frame_tokens=wl.P, block=block, window=1,
                 anchor_period=2, anchor_step=1, anchor_rows=1, radial_w=0)
 
 

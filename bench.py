@@ -29,7 +29,10 @@ reported as algorithmic GB/s of reading Q, K, V once; compensated attention as
 effective TFLOP/s over exact plus virtual keys); kmeans_32k (the token
 clustering in front of it: k-means of queries and keys, 10 Lloyd steps each,
 rows into cluster order and one tensor back, as effective TFLOP/s of the
-distance products); lipar_32k (latent inter-frame pruning and restoration as
+distance products); lvsa_32k_bwd (the attention part of a training step on the
+LVSA workload: mask, transposed mask, forward and backward, as effective
+TFLOP/s counting 4 D per kept pair for the forward and 10 D for the backward's
+five products); lipar_32k (latent inter-frame pruning and restoration as
 algorithmic GB/s).
 """
 
@@ -56,7 +59,7 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=40)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--workload", default="lvsa_32k",
-                    choices=["lvsa_32k", "radial_196k", "linear_32k", "linear_196k", "causal_linear_32k",
+                    choices=["lvsa_32k", "lvsa_32k_bwd", "radial_196k", "linear_32k", "linear_196k", "causal_linear_32k",
                              "mixed_32k", "svg_ear_32k", "kmeans_32k", "lipar_32k"])
     ap.add_argument("--cpu-seconds", type=float, default=20.0,
                     help="wall-clock budget of the CPU oracle sample (0 disables it)")
@@ -611,6 +614,114 @@ def bench_kmeans(args, wl):
     return result
 
 
+def cpu_baseline_bwd(wl, d, do, params, budget_s: float):
+    """The backward oracle on whole heads in order until the budget is spent, as
+    effective TFLOP/s (10 D per kept pair)."""
+    import numpy as np
+    from oracle import attention_bwd as ob
+    from oracle import mask as om
+    from synth import gen
+    m = om.block_mask(om.spec_from_params(params))
+    sizes = np.minimum(wl.block, wl.N - np.arange(wl.nb) * wl.block)
+    pairs = int((m * sizes[:, None] * sizes[None, :]).sum())
+    heads, dt = 0, 0.0
+    for h in range(wl.H):
+        q, k, v = (gen.to_f64(d[n][:, h:h + 1], wl.dtype) for n in ("q", "k", "v"))
+        g = gen.to_f64(do[:, h:h + 1], wl.dtype)
+        t0 = time.perf_counter()
+        ob.block_sparse_attention_backward(q, k, v, g, m, wl.block, 1.0 / math.sqrt(wl.D), o_dtype="bf16")
+        dt += time.perf_counter() - t0
+        heads += 1
+        if dt >= budget_s:
+            break
+    return {"value": round(10 * wl.D * pairs * heads / dt / 1e12, 6),
+            "unit": "TFLOP/s (effective, 10 D per kept pair)", "cores": int(_oracle_threads()),
+            "kind": "oracle", "sample": f"heads 0..{heads - 1} of {wl.H} in order, mask step 0: {dt:.1f} s, "
+                                        "float64 numpy"}
+
+
+def bench_bwd(args, wl):
+    """Attention part of a training step: one step = the LVSA mask of step s, its
+    transpose, the forward (output and LSE) and the backward."""
+    import numpy as np
+    import torch
+
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen
+
+    bsa.load()
+    dev = torch.device("cuda:0")
+    d = gen.make_qkv(wl)
+    do_bits = gen.store(gen.normal_f32((wl.seed, 9, 0, 0, 9), (wl.B, wl.H, wl.N, wl.D)), wl.dtype)
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v, do = up(d["q"]), up(d["k"]), up(d["v"]), up(do_bits)
+    params = [wl.mask_params(s) for s in wl.anchor_steps]
+    nb = wl.nb
+    rp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    ci = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    ro = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    cp = torch.empty(nb + 1, dtype=torch.int32, device=dev)
+    ri = torch.empty(nb * nb, dtype=torch.int32, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(bsa.block_sparse_attn_bwd_workspace(q), dtype=torch.uint8, device=dev)
+    pairs = []
+    for p in params:
+        bsa.build_block_mask(p, row_ptr=rp, col_idx=ci)
+        r = rp.cpu().numpy()
+        c = ci[: int(r[-1])].cpu().numpy()
+        pairs.append(kept_flops_from_csr(r, c, wl.N, wl.block, wl.D, wl.B, wl.H) // (4 * wl.D))
+
+    def step(i, evs=None):
+        bsa.build_block_mask(params[i % len(params)], row_ptr=rp, col_idx=ci, row_order=ro)
+        bsa.transpose_block_mask(rp, ci, col_ptr=cp, row_idx=ri)
+        if evs is not None:
+            evs[0].record()
+        bsa.block_sparse_attn_fwd(q, k, v, rp, ci, wl.block, out=o, lse=lse, row_order=ro)
+        if evs is not None:
+            evs[1].record()
+        bsa.block_sparse_attn_bwd(q, k, v, o, do, lse, rp, ci, wl.block, col_ptr=cp, row_idx=ri,
+                                  dq=dq, dk=dk, dv=dv, workspace=ws)
+        if evs is not None:
+            evs[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize(dev)
+    t1 = time.perf_counter()
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    bwd_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    step_pairs = [pairs[i % len(pairs)] for i in range(args.steps)]
+    bwd_tf = 10 * wl.D * float(np.mean(step_pairs)) / (bwd_ms * 1e-3) / 1e12
+    result = {
+        "metric": "effective TFLOP/s of the LVSA attention training step (forward + backward) at 32K tokens",
+        "value": round(14 * wl.D * sum(step_pairs) / (t1 - t0) / 1e12, 3),
+        "unit": "TFLOP/s (4 D per kept pair forward + 10 D backward; mask, transpose, fwd, bwd per step)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round((t1 - t0) * 1e3 / args.steps, 4),
+        "ms_forward": round(fwd_ms, 4), "ms_backward": round(bwd_ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "block": wl.block,
+                   "mask": "window +-3 frames, anchor every 8th frame rotated by step s=0..3, rows+cols"},
+        "roofline": {"bound": "mfma", "kernel": "block_sparse_attn_bwd (dq + dkdv launches)",
+                     "achieved": round(bwd_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline_bwd(wl, d, do_bits, params[0], args.cpu_seconds)
+    return result
+
+
 def bench_lipar(args, wl):
     """Latent inter-frame pruning + restoration: one step = bsa_lipar_prune of the
     sequence, then bsa_lipar_restore of the pruned rows back to full length."""
@@ -824,6 +935,9 @@ def main():
         return
     if wl.op == "kmeans":
         print(json.dumps(bench_kmeans(args, wl)), flush=True)
+        return
+    if wl.op == "bwd":
+        print(json.dumps(bench_bwd(args, wl)), flush=True)
         return
     if wl.values == "iid":
         print(json.dumps(bench_linear(args, wl)), flush=True)

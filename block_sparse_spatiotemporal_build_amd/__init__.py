@@ -231,15 +231,21 @@ def _check_qkv(q, k, v):
         raise BsaError("q, k, v must share one dtype")
 
 
-def transpose_block_mask(row_ptr, col_idx):
+def transpose_block_mask(row_ptr, col_idx, col_ptr=None, row_idx=None):
     """(col_ptr, row_idx): the transposed block CSR (query blocks per key block)."""
     lib = load()
     nb = row_ptr.numel() - 1
-    col_ptr = torch.empty(nb + 1, dtype=torch.int32, device=row_ptr.device)
-    row_idx = torch.empty(nb * nb, dtype=torch.int32, device=row_ptr.device)
+    if col_ptr is None:
+        col_ptr = torch.empty(nb + 1, dtype=torch.int32, device=row_ptr.device)
+    if row_idx is None:
+        row_idx = torch.empty(nb * nb, dtype=torch.int32, device=row_ptr.device)
     _check(lib.bsa_transpose_block_mask(_ptr(row_ptr), _ptr(col_idx), nb, _ptr(col_ptr), _ptr(row_idx),
                                         row_idx.numel(), _stream(row_ptr.device)), "bsa_transpose_block_mask")
     return col_ptr, row_idx
+
+
+def block_sparse_attn_bwd_workspace(shape_like) -> int:
+    return int(load().bsa_block_sparse_attn_bwd_workspace(ctypes.byref(_shape_of(shape_like))))
 
 
 def block_sparse_attn_bwd(q, k, v, o, do, lse, row_ptr, col_idx, block: int = 128, scale=None,

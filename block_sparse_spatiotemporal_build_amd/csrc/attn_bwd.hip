@@ -10,7 +10,7 @@
 //   dV_K += P^T dO_i,  dP = dO_i V_K^T,  Delta = rowsum(dO_i * O_i),
 //   dS = P * (dP - Delta),  dQ_i = scale * dS K_K,  dK_K += scale * dS^T Q_i.
 //
-// Two launches, no atomics (deterministic):
+// Three launches, no atomics (deterministic):
 //   dq   : grid (query blocks, B*H), 4 waves x 32 query rows.  Q and dO of the
 //          wave's rows are register-resident B operands; Delta comes from dO
 //          and O of the same rows (fp32) and is stored for the second launch.
@@ -21,13 +21,15 @@
 //          P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - Delta),
 //          and dQ^T += K^T dS^T with K^T from the transpose read and dS^T taken
 //          straight from the accumulators (the softmax kernel's P^T trick).
-//   dkdv : grid (key blocks, B*H), 4 waves x 32 key rows, walking the query
-//          blocks that keep the key block (the transposed CSR) in 32-query
-//          sub-tiles: K and V of the wave's keys are the B operands;
-//          S = Q K^T and dP = dO V^T (queries x keys: each lane owns one key
-//          column), P and dS from the staged lse and Delta of the sub-tile, and
-//          dV^T += dO^T P, dK^T += Q^T dS with the transpose reads of the
-//          staged Q and dO.
+//   dv, dk : grid (key blocks, B*H), 4 waves x 32 key rows, walking the query
+//          blocks that keep the key block (the transposed CSR) in 64-query
+//          sub-tiles: K (and V for dK) of the wave's keys are the B operands;
+//          S = Q K^T (and dP = dO V^T) with queries x keys, so each lane owns one
+//          key column; P (and dS) from the staged lse (and Delta) of the
+//          sub-tile; then dV^T += dO^T P or dK^T += Q^T dS with the transpose
+//          reads of the staged dO or Q.  dV and dK are separate launches (S is
+//          recomputed once more) so that each holds one accumulator block and
+//          two waves fit a SIMD.
 // Accumulation is fp32; P and dS enter the MFMA as bf16; the gradients are
 // stored as bf16.
 
@@ -86,7 +88,8 @@ __device__ __forceinline__ void bwd_barrier() {
 // dQ (and Delta)
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) attn_bwd_dq_d128_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_dq_d128_kernel(BwdArgs a) {
   constexpr int D = 128, KT = 8, DT = 4, SUB = 64, TILE = SUB * D;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
@@ -153,38 +156,34 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_d128_kernel(BwdArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed
     bwd_barrier();
     if (u + 1 < nsub) dma(Kn, Vn, key0_of(u + 1));
-    f32x16 s[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-    for (int t = 0; t < KT; ++t)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        s[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Kb, 32 * kt + l32, t, hi), qf[t], s[kt], 0, 0, 0);
-        dp[kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Vb, 32 * kt + l32, t, hi), gf[t], dp[kt], 0, 0, 0);
-      }
-    // s[kt][r] is key key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4 of query l32
-    bf16x8 df[4];
+    // the two 32-key halves one after the other (fewer live accumulators)
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Kb, 32 * kt + l32, t, hi), qf[t], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Vb, 32 * kt + l32, t, hi), gf[t], dp, 0, 0, 0);
+      }
+      // s[r] is key key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4 of query l32
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool live = key0 + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) < N;
-        const float p = live ? fast_exp2(__builtin_fmaf(s[kt][r], a.c2, -lse2)) : 0.f;
-        ds[r] = p * (dp[kt][r] - dl);
+        const float p = live ? fast_exp2(__builtin_fmaf(s[r], a.c2, -lse2)) : 0.f;
+        ds[r] = p * (dp[r] - dl);
       }
+      // dQ^T += K^T dS^T over the half's 32 keys (k-steps 2 kt, 2 kt + 1)
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const u32x4 w = {pack_bf16x2(ds[8 * h2], ds[8 * h2 + 1]), pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]),
                          pack_bf16x2(ds[8 * h2 + 4], ds[8 * h2 + 5]), pack_bf16x2(ds[8 * h2 + 6], ds[8 * h2 + 7])};
-        df[2 * kt + h2] = __builtin_bit_cast(bf16x8, w);
+        const bf16x8 df = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Kb, 2 * kt + h2, dt, lane), df, dq[dt], 0, 0, 0);
       }
     }
-    // dQ^T += K^T dS^T
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Kb, ks, dt, lane), df[ks], dq[dt], 0, 0, 0);
   };
 
   if (nsub > 0) dma(K0, V0, key0_of(0));
@@ -210,11 +209,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_d128_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV
+// dV (MODE 0) and dK (MODE 1): one launch each, so that each fits two waves
+// per SIMD (both in one would hold K, V, dK and dV of the wave's keys)
 // ---------------------------------------------------------------------------
 
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
-  constexpr int D = 128, KT = 8, DT = 4, SUB = 32, TILE = SUB * D;
+template <int MODE>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+attn_bwd_kv_d128_kernel(BwdArgs a) {
+  constexpr int D = 128, KT = 8, DT = 4, SUB = 64, TILE = SUB * D;
+  constexpr bool DK = MODE == 1;
   __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t G0[TILE], G1[TILE];
   __shared__ __attribute__((aligned(16))) float L[2][SUB], E[2][SUB];
@@ -224,14 +227,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
   const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
   const int krow = kblk * kBwdBlock + 32 * wave + l32;
 
-  // B operands: key l32, head dims 16 t + 8 hi .. + 7
-  bf16x8 kf[KT], vf[KT];
+  // B operands: key l32, head dims 16 t + 8 hi .. + 7 (V only for dK's dP)
+  bf16x8 kf[KT], vf[DK ? KT : 1];
   {
     const int64_t ro = head_off + (int64_t)min(krow, N - 1) * a.sn + 8 * hi;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
       kf[t] = *(const bf16x8*)(a.k + ro + 16 * t);
-      vf[t] = *(const bf16x8*)(a.v + ro + 16 * t);
+      if (DK) vf[t] = *(const bf16x8*)(a.v + ro + 16 * t);
     }
   }
 
@@ -250,14 +253,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + head_off), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t grs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.dO + head_off), (short)0, 0x7fffffff, kBufferWord3);
-  // copy roles: wave w, instruction j stages rows 8 w + 4 j + lane / 16
+  // copy roles: wave w, instruction j stages rows 16 w + 4 j + lane / 16
   auto dma = [&](uint16_t* qst, uint16_t* gst, int q0) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int row = 8 * wv + 4 * j + (lane >> 4);
+    for (int j = 0; j < 4; ++j) {
+      const int row = 16 * wv + 4 * j + (lane >> 4);
       const uint32_t o = (uint32_t)min(q0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)&gst[(8 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)&gst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
     }
   };
   // lse (log2 units; +inf for rows past N, so P = 0 there) and Delta of a
@@ -269,19 +272,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
     if (wave == 0 && lane < SUB) {
       const int qq = q0 + lane;
       nl = qq < N ? lse_h[qq] * kLog2e : __builtin_inff();
-      ne = qq < N ? del_h[qq] : 0.f;
+      if (DK) ne = qq < N ? del_h[qq] : 0.f;
     }
   };
   auto side_store = [&](int buf) {
     if (wave == 0 && lane < SUB) {
       L[buf][lane] = nl;
-      E[buf][lane] = ne;
+      if (DK) E[buf][lane] = ne;
     }
   };
 
-  f32x16 dk[DT], dv[DT];
+  f32x16 acc[DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) dk[i] = dv[i] = f32x16{};
+  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
 
   auto step = [&](const uint16_t* Qb, const uint16_t* Gb, uint16_t* Qn, uint16_t* Gn, int u) {
     const int buf = u & 1;
@@ -291,43 +294,43 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
       dma(Qn, Gn, q0_of(u + 1));
       side_load(q0_of(u + 1));
     }
-    f32x16 s = f32x16{}, dp = f32x16{};
+    // the sub-tile's two 32-query tiles one after the other
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Qb, l32, t, hi), kf[t], s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Gb, l32, t, hi), vf[t], dp, 0, 0, 0);
-    }
-    // s[r] is query 8 (r / 4) + 4 hi + r % 4 of the sub-tile, key l32
-    float p[16], ds[16];
+    for (int qt = 0; qt < SUB / 32; ++qt) {
+      const uint16_t* Qt = Qb + 32 * qt * D;  // the swizzle depends on row % 16 only
+      const uint16_t* Gt = Gb + 32 * qt * D;
+      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 lg = *(const f32x4*)&L[buf][8 * g + 4 * hi];
-      const f32x4 eg = *(const f32x4*)&E[buf][8 * g + 4 * hi];
+      for (int t = 0; t < KT; ++t) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Qt, l32, t, hi), kf[t], s, 0, 0, 0);
+        if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Gt, l32, t, hi), vf[t], dp, 0, 0, 0);
+      }
+      // s[r] is query 32 qt + 8 (r / 4) + 4 hi + r % 4 of the sub-tile, key l32
+      float w[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 4 * g + j;
-        p[r] = fast_exp2(__builtin_fmaf(s[r], a.c2, -lg[j]));
-        ds[r] = p[r] * (dp[r] - eg[j]);
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 lg = *(const f32x4*)&L[buf][32 * qt + 8 * g + 4 * hi];
+        f32x4 eg = {0.f, 0.f, 0.f, 0.f};
+        if (DK) eg = *(const f32x4*)&E[buf][32 * qt + 8 * g + 4 * hi];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g + j;
+          const float p = fast_exp2(__builtin_fmaf(s[r], a.c2, -lg[j]));
+          w[r] = DK ? p * (dp[r] - eg[j]) : p;  // dS for dK, P for dV
+        }
+      }
+      // dV^T += dO^T P  or  dK^T += Q^T dS
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const u32x4 pw = {pack_bf16x2(w[8 * ks], w[8 * ks + 1]), pack_bf16x2(w[8 * ks + 2], w[8 * ks + 3]),
+                          pack_bf16x2(w[8 * ks + 4], w[8 * ks + 5]), pack_bf16x2(w[8 * ks + 6], w[8 * ks + 7])};
+        const bf16x8 bf = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt)
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(DK ? Qt : Gt, ks, dt, lane), bf, acc[dt], 0,
+                                                            0, 0);
       }
     }
-    bf16x8 pf[2], df[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4 wp = {pack_bf16x2(p[8 * ks], p[8 * ks + 1]), pack_bf16x2(p[8 * ks + 2], p[8 * ks + 3]),
-                        pack_bf16x2(p[8 * ks + 4], p[8 * ks + 5]), pack_bf16x2(p[8 * ks + 6], p[8 * ks + 7])};
-      const u32x4 wd = {pack_bf16x2(ds[8 * ks], ds[8 * ks + 1]), pack_bf16x2(ds[8 * ks + 2], ds[8 * ks + 3]),
-                        pack_bf16x2(ds[8 * ks + 4], ds[8 * ks + 5]), pack_bf16x2(ds[8 * ks + 6], ds[8 * ks + 7])};
-      pf[ks] = __builtin_bit_cast(bf16x8, wp);
-      df[ks] = __builtin_bit_cast(bf16x8, wd);
-    }
-    // dV^T += dO^T P,  dK^T += Q^T dS
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Gb, ks, dt, lane), pf[ks], dv[dt], 0, 0, 0);
-        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Qb, ks, dt, lane), df[ks], dk[dt], 0, 0, 0);
-      }
     if (u + 1 < nsub) side_store(buf ^ 1);
   };
 
@@ -343,21 +346,17 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_d128_kernel(BwdArgs a) {
   }
   if (u < nsub) step(Q0, G0, Q1, G1, u);
 
-  // dk[dt][r] = dK^T[32 dt + 8 (r / 4) + 4 hi + r % 4][key l32] / scale
+  // acc[dt][r] = dV^T or dK^T / scale at [32 dt + 8 (r / 4) + 4 hi + r % 4][key l32]
   if (krow < N) {
-    uint16_t* dkd = a.dk + head_off + (int64_t)krow * a.sn;
-    uint16_t* dvd = a.dv + head_off + (int64_t)krow * a.sn;
+    uint16_t* dst = (DK ? a.dk : a.dv) + head_off + (int64_t)krow * a.sn;
+    const float f = DK ? a.scale : 1.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int d0 = 32 * dt + 8 * g + 4 * hi;
-        const u32x2 wk = {pack_bf16x2(dk[dt][4 * g] * a.scale, dk[dt][4 * g + 1] * a.scale),
-                          pack_bf16x2(dk[dt][4 * g + 2] * a.scale, dk[dt][4 * g + 3] * a.scale)};
-        const u32x2 wvv = {pack_bf16x2(dv[dt][4 * g], dv[dt][4 * g + 1]),
-                           pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
-        *(u32x2*)(dkd + d0) = wk;
-        *(u32x2*)(dvd + d0) = wvv;
+        const u32x2 o2 = {pack_bf16x2(acc[dt][4 * g] * f, acc[dt][4 * g + 1] * f),
+                          pack_bf16x2(acc[dt][4 * g + 2] * f, acc[dt][4 * g + 3] * f)};
+        *(u32x2*)(dst + 32 * dt + 8 * g + 4 * hi) = o2;
       }
   }
 }
@@ -377,39 +376,24 @@ __device__ __forceinline__ bool csr_has(const int32_t* cols, int b, int e, int j
   return false;
 }
 
-// one workgroup: thread t owns key blocks [t per, (t + 1) per); counts by
-// binary search in every row, a block-wide scan, then the fill in row order
-__global__ void __launch_bounds__(1024) mask_transpose_kernel(const int32_t* row_ptr, const int32_t* col_idx, int nb,
-                                                              int32_t* col_ptr, int32_t* row_idx) {
-  __shared__ int part[1024];
-  const int t = threadIdx.x;
-  const int per = (nb + 1023) / 1024;
-  const int j0 = min(t * per, nb), j1 = min(j0 + per, nb);
-  int mine = 0;
-  for (int j = j0; j < j1; ++j) {
-    int c = 0;
-    for (int i = 0; i < nb; ++i) c += csr_has(col_idx, row_ptr[i], row_ptr[i + 1], j) ? 1 : 0;
-    col_ptr[j + 1] = c;
-    mine += c;
+// one wave per key block j: the lanes test 64 query blocks at a time (binary
+// search of j in the block's ascending columns) and a ballot keeps them in order
+template <bool FILL>
+__global__ void __launch_bounds__(256) mask_transpose_kernel(const int32_t* row_ptr, const int32_t* col_idx, int nb,
+                                                             int32_t* col_ptr, int32_t* row_idx) {
+  const int lane = threadIdx.x & 63;
+  const int j = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (!FILL && j == 0 && lane == 0) col_ptr[0] = 0;
+  if (j >= nb) return;
+  int pos = FILL ? col_ptr[j] : 0;
+  for (int i0 = 0; i0 < nb; i0 += 64) {
+    const int i = i0 + lane;
+    const bool has = i < nb && csr_has(col_idx, row_ptr[i], row_ptr[i + 1], j);
+    const unsigned long long bal = __ballot(has);
+    if (FILL && has) row_idx[pos + __popcll(bal & ((1ull << lane) - 1ull))] = i;
+    pos += __popcll(bal);
   }
-  part[t] = mine;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int v = t >= d ? part[t - d] : 0;
-    __syncthreads();
-    part[t] += v;
-    __syncthreads();
-  }
-  int run = part[t] - mine;
-  if (t == 0) col_ptr[0] = 0;
-  for (int j = j0; j < j1; ++j) {
-    const int c = col_ptr[j + 1];
-    int pos = run;
-    for (int i = 0; i < nb; ++i)
-      if (csr_has(col_idx, row_ptr[i], row_ptr[i + 1], j)) row_idx[pos++] = i;
-    run += c;
-    col_ptr[j + 1] = run;
-  }
+  if (!FILL && lane == 0) col_ptr[j + 1] = pos;
 }
 
 // ---------------------------------------------------------------------------
@@ -418,7 +402,10 @@ __global__ void __launch_bounds__(1024) mask_transpose_kernel(const int32_t* row
 
 bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int nb, int32_t* col_ptr,
                                        int32_t* row_idx, hipStream_t stream) {
-  hipLaunchKernelGGL(mask_transpose_kernel, dim3(1), dim3(1024), 0, stream, row_ptr, col_idx, nb, col_ptr, row_idx);
+  const dim3 g((nb + 3) / 4);
+  hipLaunchKernelGGL(mask_transpose_kernel<false>, g, dim3(256), 0, stream, row_ptr, col_idx, nb, col_ptr, row_idx);
+  launch_inclusive_scan(col_ptr, nb, stream);  // counts in col_ptr[1..nb] -> offsets
+  hipLaunchKernelGGL(mask_transpose_kernel<true>, g, dim3(256), 0, stream, row_ptr, col_idx, nb, col_ptr, row_idx);
   return launch_ok("transpose_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 
@@ -436,7 +423,8 @@ bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   a.scale = scale; a.c2 = scale * kLog2e;
   const dim3 grid(a.nb, s.B * s.H);
   hipLaunchKernelGGL(attn_bwd_dq_d128_kernel, grid, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(attn_bwd_dkdv_d128_kernel, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<0>, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<1>, grid, dim3(256), 0, stream, a);
   return launch_ok("block_sparse_attn_bwd") ? BSA_OK : BSA_ERR_HIP;
 }
 

@@ -18,6 +18,9 @@ bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o,
                            const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                            int block, float scale, hipStream_t stream);
 
+// in-place inclusive scan of a[1..n] (one workgroup; a[0] untouched)
+void launch_inclusive_scan(int32_t* a, int n, hipStream_t stream);
+
 // ---- block-sparse attention backward (bf16, head_dim 128, block 128) ----------
 bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int nb, int32_t* col_ptr,
                                        int32_t* row_idx, hipStream_t stream);

@@ -188,4 +188,8 @@ bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int
   return launch_ok("build_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 
+void launch_inclusive_scan(int32_t* a, int n, hipStream_t stream) {
+  hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a, n);
+}
+
 }  // namespace bsa

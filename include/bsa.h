@@ -135,7 +135,7 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
  * (i, j) kept, ascending, as CSR (col_ptr int32 [nb + 1], row_idx int32, at
  * least nb * nb entries of capacity or BSA_ERR_CAPACITY).  row_ptr / col_idx
  * as bsa_build_block_mask writes them (device contents trusted: columns
- * ascending and in [0, nb)).  One workgroup; meant to be run once per mask. */
+ * ascending and in [0, nb)).  Deterministic; meant to be run once per mask. */
 bsa_status bsa_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int32_t nb, int32_t* col_ptr,
                                     int32_t* row_idx, int64_t capacity, void* stream);
 

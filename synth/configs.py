@@ -48,7 +48,8 @@ class Workload:
     lipar_tau: float = 0.0
     # which call a workload runs where its values do not say: "causal" or
     # "mixed" (LinVideo blend with weight mix_r on the block-sparse branch) for
-    # the linear family, "kmeans" for the token clustering
+    # the linear family, "kmeans" for the token clustering, "bwd" for the
+    # block-sparse attention backward
     op: str = ""
     mix_r: float = 0.0
     notes: str = field(default="", compare=False)
@@ -86,6 +87,12 @@ WORKLOADS = {
         name="lvsa_32k", seed=1, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
         dtype="bf16", values="ar1", block=128, mask_kind=MASK_WINDOW_ANCHOR,
         window=3, anchor_period=8, anchor_steps=(0, 1, 2, 3), anchor_rows=1),
+    # The LVSA workload's backward pass (a training step of the attention):
+    # same inputs and masks, an N(0,1) output gradient.
+    "lvsa_32k_bwd": Workload(
+        name="lvsa_32k_bwd", seed=1, B=1, H=12, D=128, frames=21, frame_h=30, frame_w=52,
+        dtype="bf16", values="ar1", block=128, mask_kind=MASK_WINDOW_ANCHOR,
+        window=3, anchor_period=8, anchor_steps=(0, 1, 2, 3), anchor_rows=1, op="bwd"),
     # Radial: 126 latent frames (6x horizon), spatial band W / 2^floor(log2|dt|).
     "radial_196k": Workload(
         name="radial_196k", seed=2, B=1, H=12, D=128, frames=126, frame_h=30, frame_w=52,

@@ -144,7 +144,7 @@ bsa_status bsa_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_i
 
 size_t bsa_block_sparse_attn_bwd_workspace(const bsa_shape* shape) {
   if (check_shape(shape, 2, "bsa_block_sparse_attn_bwd_workspace") != BSA_OK) return 0;
-  return ((size_t)shape->B * shape->H * shape->N * 4 + 255) & ~(size_t)255;
+  return attn_bwd_workspace(*shape);
 }
 
 bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -164,7 +164,8 @@ bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v
       !aligned16(dk) || !aligned16(dv))
     return fail(BSA_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
   if (!__builtin_isfinite(scale) || scale == 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
-  if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  if ((int64_t)shape->B * shape->H * ((shape->N + 127) / 128) > 0x7fffffffLL)
+    return fail(BSA_ERR_ARG, "%s: too many (block, sequence) pairs", fn);
   if (((int64_t)shape->N + 128) * shape->stride_n * 2 >= ((int64_t)1 << 31))
     return fail(BSA_ERR_UNSUPPORTED, "%s: a head must fit 32-bit byte offsets", fn);
   const size_t need = bsa_block_sparse_attn_bwd_workspace(shape);

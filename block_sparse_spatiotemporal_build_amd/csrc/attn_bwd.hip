@@ -11,7 +11,8 @@
 //   dS = P * (dP - Delta),  dQ_i = scale * dS K_K,  dK_K += scale * dS^T Q_i.
 //
 // Three launches, no atomics (deterministic):
-//   dq   : grid (query blocks, B*H), 4 waves x 32 query rows.  Q and dO of the
+//   dq   : a workgroup per (query block, sequence), dealt to XCDs in
+//          contiguous ranges; 4 waves x 32 query rows.  Q and dO of the
 //          wave's rows are register-resident B operands; Delta comes from dO
 //          and O of the same rows (fp32) and is stored for the second launch.
 //          The row's kept key blocks stream through LDS in 64-key sub-tiles
@@ -21,7 +22,7 @@
 //          P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - Delta),
 //          and dQ^T += K^T dS^T with K^T from the transpose read and dS^T taken
 //          straight from the accumulators (the softmax kernel's P^T trick).
-//   dv, dk : grid (key blocks, B*H), 4 waves x 32 key rows, walking the query
+//   dv, dk : a workgroup per (key block, sequence), 4 waves x 32 key rows, walking the query
 //          blocks that keep the key block (the transposed CSR) in 64-query
 //          sub-tiles: K (and V for dK) of the wave's keys are the B operands;
 //          S = Q K^T (and dP = dO V^T) with queries x keys, so each lane owns one
@@ -55,7 +56,24 @@ struct BwdArgs {
   int64_t sb, sh, sn;
   int H, N, nb;
   float scale, c2;         // softmax scale, scale * log2(e)
+  int head_major;          // 1: blocks dealt in launch order; 0: each XCD takes a contiguous range
+  const int32_t* order;    // block schedule [nb + 1]: long blocks first, their count last
 };
+
+// (block, sequence) of this workgroup.  The long blocks of the schedule (rows
+// or columns with many kept blocks, e.g. anchor frames) run first, for every
+// sequence; the rest are dealt so that the workgroups the hardware sends to one
+// XCD take one contiguous range of (sequence, block), and blocks that share
+// key (or query) tiles share that XCD's L2; when eight sequences' tensors
+// would not fit the last-level cache, in launch order.
+__device__ __forceinline__ int2 bwd_item(const BwdArgs& a) {
+  const int pid = blockIdx.x, total = gridDim.x, hb = total / a.nb;
+  const int nh = a.order[a.nb], S = nh * hb;
+  if (pid < S) return int2{a.order[pid / hb], pid % hb};
+  const int rest = a.nb - nh;
+  const int item = a.head_major ? pid - S : xcd_contiguous(pid - S, S, total - S);
+  return int2{a.order[nh + item % rest], item / rest};
+}
 
 constexpr int kBwdBlock = 128;
 
@@ -94,7 +112,8 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int qblk = blockIdx.x, bh = blockIdx.y;
+  const int2 it = bwd_item(a);
+  const int qblk = it.x, bh = it.y;
   const int N = a.N;
   const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
   const int qrow = qblk * kBwdBlock + 32 * wave + l32;
@@ -222,7 +241,8 @@ attn_bwd_kv_d128_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t G0[TILE], G1[TILE];
   __shared__ __attribute__((aligned(16))) float L[2][SUB], E[2][SUB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
-  const int kblk = blockIdx.x, bh = blockIdx.y;
+  const int2 it = bwd_item(a);
+  const int kblk = it.x, bh = it.y;
   const int N = a.N;
   const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
   const int krow = kblk * kBwdBlock + 32 * wave + l32;
@@ -409,6 +429,11 @@ bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* co
   return launch_ok("transpose_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 
+size_t attn_bwd_workspace(const bsa_shape& s) {
+  const size_t nb = (s.N + kBwdBlock - 1) / kBwdBlock;
+  return ((size_t)s.B * s.H * s.N * 4 + 2 * (nb + 1) * 4 + 255) & ~(size_t)255;
+}
+
 bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                                 const float* lse, const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                                 const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,
@@ -421,8 +446,17 @@ bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   a.sb = s.stride_b; a.sh = s.stride_h; a.sn = s.stride_n;
   a.H = s.H; a.N = s.N; a.nb = (s.N + kBwdBlock - 1) / kBwdBlock;
   a.scale = scale; a.c2 = scale * kLog2e;
-  const dim3 grid(a.nb, s.B * s.H);
+  // eight sequences' K and V (or Q and dO) against the 256 MiB last-level cache
+  a.head_major = 8 * (2 * (int64_t)s.N * s.D * 2) > (256ll << 20) ? 1 : 0;
+  const dim3 grid(a.nb * s.B * s.H);
+  // block schedules: rows of the mask for dQ, columns for dK / dV
+  int32_t* row_order = (int32_t*)((char*)ws + (size_t)s.B * s.H * s.N * 4);
+  int32_t* col_order = row_order + a.nb + 1;
+  launch_block_order(row_ptr, a.nb, row_order, stream);
+  launch_block_order(col_ptr, a.nb, col_order, stream);
+  a.order = row_order;
   hipLaunchKernelGGL(attn_bwd_dq_d128_kernel, grid, dim3(256), 0, stream, a);
+  a.order = col_order;
   hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<0>, grid, dim3(256), 0, stream, a);
   hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<1>, grid, dim3(256), 0, stream, a);
   return launch_ok("block_sparse_attn_bwd") ? BSA_OK : BSA_ERR_HIP;

@@ -20,10 +20,13 @@ bsa_status launch_attn_f32(const void* q, const void* k, const void* v, void* o,
 
 // in-place inclusive scan of a[1..n] (one workgroup; a[0] untouched)
 void launch_inclusive_scan(int32_t* a, int n, hipStream_t stream);
+// block schedule of a CSR pointer array (long rows first; see mask.hip)
+void launch_block_order(const int32_t* ptr, int nb, int32_t* order, hipStream_t stream);
 
 // ---- block-sparse attention backward (bf16, head_dim 128, block 128) ----------
 bsa_status launch_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_idx, int nb, int32_t* col_ptr,
                                        int32_t* row_idx, hipStream_t stream);
+size_t attn_bwd_workspace(const bsa_shape& s);  // Delta [BH][N] + row and column schedules
 bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, const void* o, const void* dO,
                                 const float* lse, const bsa_shape& s, const int32_t* row_ptr, const int32_t* col_idx,
                                 const int32_t* col_ptr, const int32_t* row_idx, float scale, void* dq, void* dk,

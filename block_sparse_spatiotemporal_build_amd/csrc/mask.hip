@@ -188,6 +188,11 @@ bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int
   return launch_ok("build_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 
+void launch_block_order(const int32_t* ptr, int nb, int32_t* order, hipStream_t stream) {
+  hipLaunchKernelGGL(mask_order_kernel, dim3((nb + kMaskThreads - 1) / kMaskThreads), dim3(kMaskThreads), 0, stream,
+                     ptr, nb, order);
+}
+
 void launch_inclusive_scan(int32_t* a, int n, hipStream_t stream) {
   hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, a, n);
 }

@@ -140,7 +140,8 @@ bsa_status bsa_transpose_block_mask(const int32_t* row_ptr, const int32_t* col_i
                                     int32_t* row_idx, int64_t capacity, void* stream);
 
 /* Workspace bytes required by bsa_block_sparse_attn_bwd (Delta, fp32 per query
- * row); 0 if the shape is invalid. */
+ * row, and the launch schedules of the mask's rows and columns); 0 if the
+ * shape is invalid. */
 size_t bsa_block_sparse_attn_bwd_workspace(const bsa_shape* shape);
 
 /* Gradients of block-sparse attention (the backward pass of

@@ -110,17 +110,18 @@ def test_assignment_and_update_steps_on_overlapping_clusters(gpu_lib):
 
 @pytest.mark.parametrize("which", ["q", "k"])
 def test_svg_ear_32k_ten_steps(gpu_lib, which):
-    """Ten Lloyd steps on the 32,760-token workload (queries: 100 clusters, keys:
-    500), two heads: valid final labels for the final centres, the exact cluster
-    order, and agreement with the oracle run from the same centres."""
-    wl = gen.scaled(get_workload("svg_ear_32k"), H=2)
+    """Ten Lloyd steps on the 32,760-token workload as the benchmark launches
+    them (all 12 heads; queries: 100 clusters, keys: 500): for heads 0 and 7,
+    valid final labels for the final centres, the exact cluster order, and
+    agreement with the oracle run from the same centres."""
+    wl = get_workload("svg_ear_32k")
     d = gen.make_gmm_tokens(wl)
     C = wl.n_q_clusters if which == "q" else wl.n_k_clusters
     x = to_device(d[which], "bf16")
     init = d["centres_" + which]
     labels, cent, perm, off = gpu_lib.kmeans(x, C, wl.kmeans_iters, torch.from_numpy(init))
     torch.cuda.synchronize()
-    for r in range(2):
+    for r in (0, 7):
         xf = gen.to_f64(d[which][0, r], "bf16")
         lab = labels.cpu().numpy()[r]
         cen = cent.cpu().numpy()[r].astype(np.float64)

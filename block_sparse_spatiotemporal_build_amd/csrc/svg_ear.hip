@@ -1610,7 +1610,10 @@ comp_attn_d128_kernel(CompArgs p) {
   // cursor (kept-list index of the cluster holding the slot) serves all four.
   // For those rows swz_k(row) = 4j + lane/16 and swz_v(row) = 4 (lane/16) + j,
   // so the swizzled chunk offsets are one per-lane base XOR an immediate.
-  int cur = 0;
+  // The cursor's cluster bounds and first key row are kept in registers and
+  // reloaded from LDS only when the cursor moves (about once per sub-tile),
+  // so issuing a sub-tile's copies costs few LDS round trips.
+  int cur = 0, c_lo = 0, c_hi = nk > 0 ? cum[1] : 0, k_lo = nk > 0 ? kstart[0] : 0;
   const uint32_t kbase = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
   const uint32_t vbase = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
   auto dma = [&](uint16_t* kst, uint16_t* vst, int u) {
@@ -1619,8 +1622,13 @@ comp_attn_d128_kernel(CompArgs p) {
       for (int j = 0; j < 4; ++j) {
         const int row = 16 * wv + 4 * j + (lane >> 4);
         const int slot = min(u * kCaBN + row, E - 1);  // slots past E are masked below
-        while (cur + 1 < nk && cum[cur + 1] <= slot) ++cur;
-        const uint32_t ro = (uint32_t)(kstart[cur] + slot - cum[cur]) * row_bytes;
+        while (cur + 1 < nk && c_hi <= slot) {
+          ++cur;
+          c_lo = c_hi;
+          c_hi = cum[cur + 1];
+          k_lo = kstart[cur];
+        }
+        const uint32_t ro = (uint32_t)(k_lo + slot - c_lo) * row_bytes;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
                                                  ro + (kbase ^ (64u * j)), 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,

@@ -110,3 +110,14 @@ def test_deterministic(gpu_lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("B,H,frames,fh,fw", [(2, 1, 2, 5, 10), (2, 3, 1, 1, 7)])
+def test_batches_and_single_block(gpu_lib, B, H, frames, fh, fw):
+    """Batch > 1 and sequences of one (ragged) block."""
+    wl = gen.scaled(get_workload("lvsa_32k"), B=B, H=H, frames=frames, frame_h=fh, frame_w=fw, seed=70 + B + H)
+    p = dict(kind=0, frames=frames, frame_tokens=wl.P, block=128, window=0, anchor_period=0, anchor_step=0,
+             anchor_rows=0, radial_w=0)
+    got, ref, _ = _run(gpu_lib, wl, p, seed=B * 10 + H)
+    for g, r, name in zip(got, ref, ("dq", "dk", "dv")):
+        _assert_grad(g, r, f"B={B} {name}")

@@ -162,3 +162,18 @@ def test_gather_skips_out_of_range_entries(gpu_lib):
     assert torch.equal(out[0, 0, 0], x[0, 0, 3])
     assert (out[0, 0, 1:3].float() == 7.0).all()
     assert torch.equal(out[0, 0, 3:], x[0, 0, [0, 1, 2, 4, 5, 6, 7]])
+
+
+def test_batch_of_sequences(gpu_lib):
+    """B = 2 sequences of 2 heads each: every (batch, head) clusters on its own."""
+    B, H, N, C = 2, 2, 700, 20
+    bits, init = _tokens(B, H, N, C, 0.05, 77)
+    x = to_device(bits, "bf16")
+    labels, cent, perm, off = gpu_lib.kmeans(x, C, 3, torch.from_numpy(init))
+    torch.cuda.synchronize()
+    for r in range(B * H):
+        b, h = divmod(r, H)
+        xf = gen.to_f64(bits[b, h], "bf16")
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), 3)
+        assert np.array_equal(labels.cpu().numpy()[r], rl), r
+        assert np.abs(cent.cpu().numpy()[r] - rc).max() < 1e-5

@@ -177,3 +177,20 @@ def test_batch_of_sequences(gpu_lib):
         rl, rc = ok.lloyd(xf, init[r].astype(np.float64), 3)
         assert np.array_equal(labels.cpu().numpy()[r], rl), r
         assert np.abs(cent.cpu().numpy()[r] - rc).max() < 1e-5
+
+
+def test_order_outputs_are_optional(gpu_lib):
+    """perm / offsets may be NULL: labels and centres are those of the full call."""
+    import ctypes
+    bits, init = _tokens(1, 2, 1500, 30, 0.05, 78)
+    x = to_device(bits, "bf16")
+    labels, cent, _, _ = gpu_lib.kmeans(x, 30, 3, torch.from_numpy(init))
+    lib = gpu_lib.load()
+    c2 = torch.from_numpy(init).cuda().contiguous().clone()
+    l2 = torch.empty_like(labels)
+    ws = torch.empty(gpu_lib.kmeans_workspace(x, 30), dtype=torch.uint8, device="cuda")
+    st = lib.bsa_kmeans(gpu_lib._ptr(x), 0, ctypes.byref(gpu_lib._shape_of(x)), 30, 3, gpu_lib._ptr(c2),
+                        gpu_lib._ptr(l2), None, None, gpu_lib._ptr(ws), ws.numel(), gpu_lib._stream(x.device))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(l2, labels) and torch.equal(c2, cent)

@@ -713,7 +713,7 @@ def bench_bwd(args, wl):
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": wl.name, "B": wl.B, "H": wl.H, "N": wl.N, "D": wl.D, "block": wl.block,
                    "mask": "window +-3 frames, anchor every 8th frame rotated by step s=0..3, rows+cols"},
-        "roofline": {"bound": "mfma", "kernel": "block_sparse_attn_bwd (dq, dv and dk launches)",
+        "roofline": {"bound": "mfma", "kernel": "block_sparse_attn_bwd (dq and dkdv launches)",
                      "achieved": round(bwd_tf, 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(bwd_tf / BF16_PEAK_TFLOPS, 4), "traffic": None},
     }

@@ -10,7 +10,7 @@
 //   dV_K += P^T dO_i,  dP = dO_i V_K^T,  Delta = rowsum(dO_i * O_i),
 //   dS = P * (dP - Delta),  dQ_i = scale * dS K_K,  dK_K += scale * dS^T Q_i.
 //
-// Three launches, no atomics (deterministic):
+// Two launches, no atomics (deterministic):
 //   dq   : a workgroup per (query block, sequence), dealt to XCDs in
 //          contiguous ranges; 4 waves x 32 query rows.  Q and dO of the
 //          wave's rows are register-resident B operands; Delta comes from dO
@@ -22,15 +22,14 @@
 //          P^T = exp2(S^T scale log2e - lse log2e), dS^T = P^T (dP^T - Delta),
 //          and dQ^T += K^T dS^T with K^T from the transpose read and dS^T taken
 //          straight from the accumulators (the softmax kernel's P^T trick).
-//   dv, dk : a workgroup per (key block, sequence), 4 waves x 32 key rows, walking the query
-//          blocks that keep the key block (the transposed CSR) in 64-query
-//          sub-tiles: K (and V for dK) of the wave's keys are the B operands;
-//          S = Q K^T (and dP = dO V^T) with queries x keys, so each lane owns one
-//          key column; P (and dS) from the staged lse (and Delta) of the
-//          sub-tile; then dV^T += dO^T P or dK^T += Q^T dS with the transpose
-//          reads of the staged dO or Q.  dV and dK are separate launches (S is
-//          recomputed once more) so that each holds one accumulator block and
-//          two waves fit a SIMD.
+//   dkdv : a workgroup per (key block, sequence), 4 waves x 32 key rows,
+//          walking the query blocks that keep the key block (the transposed
+//          CSR) in 32-query sub-tiles.  K of the block's keys is staged once in
+//          LDS, V of the wave's keys is register-resident.  S = Q K^T and
+//          dP = dO V^T with queries x keys, so each lane owns one key column;
+//          P and dS from the staged lse and Delta of the sub-tile; then
+//          dV^T += dO^T P and dK^T += Q^T dS with the transpose reads of the
+//          staged dO and Q.  S and dP are formed once for both gradients.
 // Accumulation is fp32; P and dS enter the MFMA as bf16; the gradients are
 // stored as bf16.
 
@@ -228,15 +227,18 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// dV (MODE 0) and dK (MODE 1): one launch each, so that each fits two waves
-// per SIMD (both in one would hold K, V, dK and dV of the wave's keys)
+// dK and dV in one launch: S and dP are formed once per query tile and feed
+// both accumulators.  Two waves per SIMD still fit because K of the
+// workgroup's 128 keys is staged once in LDS (32 KB, read back as the B
+// operand of S) instead of being held in registers; V of the wave's keys stays
+// register-resident, and Q and dO stream through two 32-query stages (8 KB
+// each), so one workgroup needs about 65 KB of LDS and two share a CU.
 // ---------------------------------------------------------------------------
 
-template <int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-attn_bwd_kv_d128_kernel(BwdArgs a) {
-  constexpr int D = 128, KT = 8, DT = 4, SUB = 64, TILE = SUB * D;
-  constexpr bool DK = MODE == 1;
+attn_bwd_dkdv_d128_kernel(BwdArgs a) {
+  constexpr int D = 128, KT = 8, DT = 4, SUB = 32, TILE = SUB * D;
+  __shared__ __attribute__((aligned(1024))) uint16_t Ks[kBwdBlock * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t G0[TILE], G1[TILE];
   __shared__ __attribute__((aligned(16))) float L[2][SUB], E[2][SUB];
@@ -247,15 +249,12 @@ attn_bwd_kv_d128_kernel(BwdArgs a) {
   const int64_t head_off = (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh;
   const int krow = kblk * kBwdBlock + 32 * wave + l32;
 
-  // B operands: key l32, head dims 16 t + 8 hi .. + 7 (V only for dK's dP)
-  bf16x8 kf[KT], vf[DK ? KT : 1];
+  // B operand of dP = dO V^T: key l32, head dims 16 t + 8 hi .. + 7
+  bf16x8 vf[KT];
   {
     const int64_t ro = head_off + (int64_t)min(krow, N - 1) * a.sn + 8 * hi;
 #pragma unroll
-    for (int t = 0; t < KT; ++t) {
-      kf[t] = *(const bf16x8*)(a.k + ro + 16 * t);
-      if (DK) vf[t] = *(const bf16x8*)(a.v + ro + 16 * t);
-    }
+    for (int t = 0; t < KT; ++t) vf[t] = *(const bf16x8*)(a.v + ro + 16 * t);
   }
 
   const int cbeg = a.col_ptr[kblk], cend = a.col_ptr[kblk + 1];
@@ -269,22 +268,29 @@ attn_bwd_kv_d128_kernel(BwdArgs a) {
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t qrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.q + head_off), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t grs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.dO + head_off), (short)0, 0x7fffffff, kBufferWord3);
-  // copy roles: wave w, instruction j stages rows 16 w + 4 j + lane / 16
+  // copy roles: each instruction moves 4 rows (16 lanes per row, one 16-byte
+  // chunk each, at physical chunk lane % 16 of a swz_v-swizzled row); rows past
+  // N repeat row N - 1 (their columns or rows are masked or never stored);
+  // r0 is the (wave-uniform) first of the 4 rows
+  auto dma_rows = [&](__amdgpu_buffer_rsrc_t rs, uint16_t* st, int r0, int g0) {
+    const int row = r0 + (lane >> 4);
+    const uint32_t o = (uint32_t)min(g0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)&st[r0 * D], 16, o, 0, 0, 0);
+  };
+  // Q and dO of a 32-query sub-tile: wave w, instruction j stages rows 8 w + 4 j + lane / 16
   auto dma = [&](uint16_t* qst, uint16_t* gst, int q0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * wv + 4 * j + (lane >> 4);
-      const uint32_t o = (uint32_t)min(q0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(grs, (lds_void*)&gst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+    for (int j = 0; j < 2; ++j) {
+      dma_rows(qrs, qst, 8 * wv + 4 * j, q0);
+      dma_rows(grs, gst, 8 * wv + 4 * j, q0);
     }
   };
-  // lse (log2 units; +inf for rows past N, so P = 0 there) and Delta of a
-  // sub-tile's queries: loaded by wave 0 early, written to LDS late
   const float* lse_h = a.lse + (int64_t)bh * N;
   const float* del_h = a.delta + (int64_t)bh * N;
   float nl = 0.f, ne = 0.f;
@@ -292,69 +298,90 @@ attn_bwd_kv_d128_kernel(BwdArgs a) {
     if (wave == 0 && lane < SUB) {
       const int qq = q0 + lane;
       nl = qq < N ? lse_h[qq] * kLog2e : __builtin_inff();
-      if (DK) ne = qq < N ? del_h[qq] : 0.f;
+      ne = qq < N ? del_h[qq] : 0.f;
     }
   };
   auto side_store = [&](int buf) {
     if (wave == 0 && lane < SUB) {
       L[buf][lane] = nl;
-      if (DK) E[buf][lane] = ne;
+      E[buf][lane] = ne;
     }
   };
 
-  f32x16 acc[DT];
+  f32x16 dk[DT], dv[DT];
 #pragma unroll
-  for (int i = 0; i < DT; ++i) acc[i] = f32x16{};
+  for (int i = 0; i < DT; ++i) dk[i] = dv[i] = f32x16{};
+
+  // Per-lane LDS element offsets as one base XOR / plus immediates (the same
+  // reads as bwd_row_frag / bwd_tr_frag, so few registers stay live):
+  //   Q or dO row fragment (query l32, t):  rq ^ 16 t
+  //   K row fragment (key 32 w + l32, t):   rk ^ 16 t,  rk = rq + 4096 w
+  //   transpose fragment (ks, dt): rows r0 and r0 + 8 at 2048 ks + (tq ^ 32 dt)
+  //                                and 2048 ks + 1024 + (tq ^ 16 ^ 32 dt)
+  const int j16 = lane & 15, g16 = lane >> 4;
+  int rq = l32 * D + 8 * (hi ^ swz_v(l32));
+  int rk = rq + 32 * D * wv;
+  const int tc1 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
+  int tq = (4 * hi + (j16 >> 2)) * D + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4;
+  auto row_frag = [&](const uint16_t* st, int off) { return *(const bf16x8*)&st[off]; };
+  auto tr_frag = [&](const uint16_t* st, int ks, int dt) {
+    const u32x2 x0 = lds_tr16(&st[2048 * ks + (tq ^ (32 * dt))]);
+    const u32x2 x1 = lds_tr16(&st[2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt))]);
+    return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
+  };
 
   auto step = [&](const uint16_t* Qb, const uint16_t* Gb, uint16_t* Qn, uint16_t* Gn, int u) {
     const int buf = u & 1;
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u and its lse / Delta landed
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u (and K) landed
     bwd_barrier();
     if (u + 1 < nsub) {
       dma(Qn, Gn, q0_of(u + 1));
       side_load(q0_of(u + 1));
     }
-    // the sub-tile's two 32-query tiles one after the other
+    // the bases are opaque here, so the 24 XORed offsets are formed next to
+    // their reads instead of being hoisted out of the loop (and spilled)
+    asm volatile("" : "+v"(rq), "+v"(rk), "+v"(tq));
+    // S = Q K^T and dP = dO V^T, queries x keys: s[r] is query 8 (r / 4) + 4 hi + r % 4 of the sub-tile, key l32
+    f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
-    for (int qt = 0; qt < SUB / 32; ++qt) {
-      const uint16_t* Qt = Qb + 32 * qt * D;  // the swizzle depends on row % 16 only
-      const uint16_t* Gt = Gb + 32 * qt * D;
-      f32x16 s = f32x16{}, dp = f32x16{};
+    for (int t = 0; t < KT; ++t) {
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qb, rq ^ (16 * t)), row_frag(Ks, rk ^ (16 * t)), s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Gb, rq ^ (16 * t)), vf[t], dp, 0, 0, 0);
+    }
+    float pw[16], dw[16];
 #pragma unroll
-      for (int t = 0; t < KT; ++t) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Qt, l32, t, hi), kf[t], s, 0, 0, 0);
-        if (DK) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Gt, l32, t, hi), vf[t], dp, 0, 0, 0);
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 lg = *(const f32x4*)&L[buf][8 * g + 4 * hi];
+      const f32x4 eg = *(const f32x4*)&E[buf][8 * g + 4 * hi];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 4 * g + j;
+        const float p = fast_exp2(__builtin_fmaf(s[r], a.c2, -lg[j]));
+        pw[r] = p;
+        dw[r] = p * (dp[r] - eg[j]);
       }
-      // s[r] is query 32 qt + 8 (r / 4) + 4 hi + r % 4 of the sub-tile, key l32
-      float w[16];
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's two 16-query k-steps
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 lg = *(const f32x4*)&L[buf][32 * qt + 8 * g + 4 * hi];
-        f32x4 eg = {0.f, 0.f, 0.f, 0.f};
-        if (DK) eg = *(const f32x4*)&E[buf][32 * qt + 8 * g + 4 * hi];
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 pp = {pack_bf16x2(pw[8 * ks], pw[8 * ks + 1]), pack_bf16x2(pw[8 * ks + 2], pw[8 * ks + 3]),
+                        pack_bf16x2(pw[8 * ks + 4], pw[8 * ks + 5]), pack_bf16x2(pw[8 * ks + 6], pw[8 * ks + 7])};
+      const u32x4 dd = {pack_bf16x2(dw[8 * ks], dw[8 * ks + 1]), pack_bf16x2(dw[8 * ks + 2], dw[8 * ks + 3]),
+                        pack_bf16x2(dw[8 * ks + 4], dw[8 * ks + 5]), pack_bf16x2(dw[8 * ks + 6], dw[8 * ks + 7])};
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, pp), df = __builtin_bit_cast(bf16x8, dd);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g + j;
-          const float p = fast_exp2(__builtin_fmaf(s[r], a.c2, -lg[j]));
-          w[r] = DK ? p * (dp[r] - eg[j]) : p;  // dS for dK, P for dV
-        }
-      }
-      // dV^T += dO^T P  or  dK^T += Q^T dS
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4 pw = {pack_bf16x2(w[8 * ks], w[8 * ks + 1]), pack_bf16x2(w[8 * ks + 2], w[8 * ks + 3]),
-                          pack_bf16x2(w[8 * ks + 4], w[8 * ks + 5]), pack_bf16x2(w[8 * ks + 6], w[8 * ks + 7])};
-        const bf16x8 bf = __builtin_bit_cast(bf16x8, pw);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(DK ? Qt : Gt, ks, dt, lane), bf, acc[dt], 0,
-                                                            0, 0);
+      for (int dt = 0; dt < DT; ++dt) {
+        dv[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Gb, ks, dt), pf, dv[dt], 0, 0, 0);
+        dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Qb, ks, dt), df, dk[dt], 0, 0, 0);
       }
     }
     if (u + 1 < nsub) side_store(buf ^ 1);
   };
 
   if (nsub > 0) {
+    // K of the block's 128 keys: wave w, instruction j stages rows 32 w + 4 j + lane / 16
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dma_rows(krs, Ks, 32 * wv + 4 * j, kblk * kBwdBlock);
     dma(Q0, G0, q0_of(0));
     side_load(q0_of(0));
     side_store(0);
@@ -366,17 +393,20 @@ attn_bwd_kv_d128_kernel(BwdArgs a) {
   }
   if (u < nsub) step(Q0, G0, Q1, G1, u);
 
-  // acc[dt][r] = dV^T or dK^T / scale at [32 dt + 8 (r / 4) + 4 hi + r % 4][key l32]
+  // dk / dv[dt][r] = dK^T / scale and dV^T at [32 dt + 8 (r / 4) + 4 hi + r % 4][key l32]
   if (krow < N) {
-    uint16_t* dst = (DK ? a.dk : a.dv) + head_off + (int64_t)krow * a.sn;
-    const float f = DK ? a.scale : 1.f;
+    const int64_t ro = head_off + (int64_t)krow * a.sn;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const u32x2 o2 = {pack_bf16x2(acc[dt][4 * g] * f, acc[dt][4 * g + 1] * f),
-                          pack_bf16x2(acc[dt][4 * g + 2] * f, acc[dt][4 * g + 3] * f)};
-        *(u32x2*)(dst + 32 * dt + 8 * g + 4 * hi) = o2;
+        const int d0 = 32 * dt + 8 * g + 4 * hi;
+        const u32x2 wk = {pack_bf16x2(dk[dt][4 * g] * a.scale, dk[dt][4 * g + 1] * a.scale),
+                          pack_bf16x2(dk[dt][4 * g + 2] * a.scale, dk[dt][4 * g + 3] * a.scale)};
+        const u32x2 wvv = {pack_bf16x2(dv[dt][4 * g], dv[dt][4 * g + 1]),
+                           pack_bf16x2(dv[dt][4 * g + 2], dv[dt][4 * g + 3])};
+        *(u32x2*)(a.dk + ro + d0) = wk;
+        *(u32x2*)(a.dv + ro + d0) = wvv;
       }
   }
 }
@@ -457,8 +487,7 @@ bsa_status launch_attn_bwd_bf16(const void* q, const void* k, const void* v, con
   a.order = row_order;
   hipLaunchKernelGGL(attn_bwd_dq_d128_kernel, grid, dim3(256), 0, stream, a);
   a.order = col_order;
-  hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<0>, grid, dim3(256), 0, stream, a);
-  hipLaunchKernelGGL(attn_bwd_kv_d128_kernel<1>, grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(attn_bwd_dkdv_d128_kernel, grid, dim3(256), 0, stream, a);
   return launch_ok("block_sparse_attn_bwd") ? BSA_OK : BSA_ERR_HIP;
 }
 

@@ -115,3 +115,46 @@ def test_causal_state_fragment_swap():
         y_new = {0: x[1], 1: y[1]}
         for hi in range(2):
             assert x_new[hi] + y_new[hi] == [16 * f + 8 * hi + e for e in range(8)]
+
+
+def test_backward_dkdv_offsets_xor_form():
+    """Fused dK / dV backward kernel (`csrc/attn_bwd.hip`): stages are row-major
+    swz_v-swizzled [rows][128] bf16 (32-row Q / dO stages, the 128-row K stage).
+    Row fragment of lane l at k-step t: row r, head dims 16 t + 8 (l / 32) + 0..7,
+    with r = l % 32 (Q, dO) or 32 w + l % 32 (K of wave w): rq ^ 16 t, rk ^ 16 t.
+    Transpose read (ks, dt): rows 16 ks + 4 (l / 32) + j16 / 4 and + 8, columns
+    32 dt + 16 ((l / 16) & 1) + 4 (j16 & 3): 2048 ks + (tq ^ 32 dt) and
+    2048 ks + 1024 + (tq ^ 16 ^ 32 dt).  Every offset stays inside its stage."""
+    for w, t, lane in itertools.product(range(4), range(8), range(64)):
+        l32, hi = lane % 32, lane // 32
+        rq = l32 * 128 + 8 * (hi ^ swz_v(l32))
+        rk = rq + 32 * 128 * w
+        assert phys(l32, 16 * t + 8 * hi, swz_v) == rq ^ (16 * t) < 32 * 128
+        assert phys(32 * w + l32, 16 * t + 8 * hi, swz_v) == rk ^ (16 * t) < 128 * 128
+    for ks, dt, lane in itertools.product(range(2), range(4), range(64)):
+        hi, g16, j16 = lane // 32, lane // 16, lane % 16
+        row = 16 * ks + 4 * hi + j16 // 4
+        col = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)
+        tc1 = 2 * (g16 & 1) + ((j16 & 3) >> 1)
+        tq = (4 * hi + (j16 >> 2)) * 128 + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4
+        assert phys(row, col, swz_v) == 2048 * ks + (tq ^ (32 * dt))
+        assert phys(row + 8, col, swz_v) == 2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt))
+        assert 2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt)) + 3 < 32 * 128
+
+
+def test_backward_dkdv_copy_rows_in_stage():
+    """Copies of the fused kernel: instruction base row r0 (wave-uniform), lane l
+    lands at r0 * 128 + 8 * (l % 16) + 64 * (l / 16) elements, i.e. row
+    r0 + l / 16, physical chunk l % 16; the source is logical chunk
+    (l % 16) ^ swz_v(row).  32-row stages take r0 = 8 w + 4 j (j < 2), the K
+    stage r0 = 32 w + 4 j (j < 8): every row is written exactly once."""
+    for rows, bases in ((32, [8 * w + 4 * j for w in range(4) for j in range(2)]),
+                        (128, [32 * w + 4 * j for w in range(4) for j in range(8)])):
+        seen = set()
+        for r0, lane in itertools.product(bases, range(64)):
+            row, p = r0 + lane // 16, lane % 16
+            dst = r0 * 128 + 8 * lane
+            logical = p ^ swz_v(row)
+            assert dst == phys(row, 8 * logical, swz_v)
+            seen.add(dst)
+        assert seen == set(range(0, rows * 128, 8))

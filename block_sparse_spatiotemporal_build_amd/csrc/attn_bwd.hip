@@ -191,7 +191,9 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
         const float p = live ? fast_exp2(__builtin_fmaf(s[r], a.c2, -lse2)) : 0.f;
         ds[r] = p * (dp[r] - dl);
       }
-      // dQ^T += K^T dS^T over the half's 32 keys (k-steps 2 kt, 2 kt + 1)
+      // dQ^T += K^T dS^T over the half's 32 keys (k-steps 2 kt, 2 kt + 1), at
+      // raised wave priority as in the dK / dV kernel
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int h2 = 0; h2 < 2; ++h2) {
         const u32x4 w = {pack_bf16x2(ds[8 * h2], ds[8 * h2 + 1]), pack_bf16x2(ds[8 * h2 + 2], ds[8 * h2 + 3]),
@@ -201,6 +203,7 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
         for (int dt = 0; dt < DT; ++dt)
           dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Kb, 2 * kt + h2, dt, lane), df, dq[dt], 0, 0, 0);
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
@@ -361,7 +364,10 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
         dw[r] = p * (dp[r] - eg[j]);
       }
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's two 16-query k-steps
+    // dV^T += dO^T P and dK^T += Q^T dS over the sub-tile's two 16-query k-steps,
+    // at raised wave priority (co-resident waves drift out of phase, one's
+    // exponentials under the other's matrix work)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const u32x4 pp = {pack_bf16x2(pw[8 * ks], pw[8 * ks + 1]), pack_bf16x2(pw[8 * ks + 2], pw[8 * ks + 3]),
@@ -375,6 +381,7 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
         dk[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Qb, ks, dt), df, dk[dt], 0, 0, 0);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     if (u + 1 < nsub) side_store(buf ^ 1);
   };
 

@@ -518,19 +518,26 @@ def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out
     return (out, lse, rrow, rcol, score) if return_score else (out, lse, rrow, rcol)
 
 
-def lipar_prune(x, frames: int, tau: float):
+def lipar_prune(x, frames: int, tau: float, outputs=None):
     """Latent inter-frame pruning of x [B, H, N, D] (bf16); returns
     (keep uint8 [B*H, N], cpos int32 [B*H, N], kept_idx int32 [B*H, N],
-    n_kept int32 [B*H], x_pruned bf16 [B*H, N, D] with rows < n_kept valid)."""
+    n_kept int32 [B*H], x_pruned bf16 [B*H, N, D] with rows < n_kept valid).
+    ``outputs``: optionally that tuple, preallocated, to be written in place."""
     lib = load()
     shape = _shape_of(x)
     B, H, N, D = x.shape
     dev = x.device
-    keep = torch.empty((B * H, N), dtype=torch.uint8, device=dev)
-    cpos = torch.empty((B * H, N), dtype=torch.int32, device=dev)
-    kidx = torch.empty((B * H, N), dtype=torch.int32, device=dev)
-    nk = torch.empty((B * H,), dtype=torch.int32, device=dev)
-    xp = torch.empty((B * H, N, D), dtype=x.dtype, device=dev)
+    want = (((B * H, N), torch.uint8), ((B * H, N), torch.int32), ((B * H, N), torch.int32),
+            ((B * H,), torch.int32), ((B * H, N, D), x.dtype))
+    if outputs is None:
+        keep, cpos, kidx, nk, xp = (torch.empty(sh, dtype=dt, device=dev) for sh, dt in want)
+    else:
+        if len(outputs) != 5 or any(
+                tuple(t.shape) != sh or t.dtype != dt or t.device != dev or not t.is_contiguous()
+                for t, (sh, dt) in zip(outputs, want)):
+            raise BsaError("outputs must be contiguous (keep, cpos, kept_idx, n_kept, x_pruned) device tensors "
+                           "of the shapes and dtypes lipar_prune returns")
+        keep, cpos, kidx, nk, xp = outputs
     _check(lib.bsa_lipar_prune(_ptr(x), _dtype_code(x), ctypes.byref(shape), int(frames), float(tau), _ptr(keep),
                                _ptr(cpos), _ptr(kidx), _ptr(nk), _ptr(xp), _stream(dev)), "bsa_lipar_prune")
     return keep, cpos, kidx, nk, xp

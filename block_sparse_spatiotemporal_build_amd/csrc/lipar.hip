@@ -13,15 +13,18 @@
 // so the keep decision does not depend on the summation order.
 //
 // Launches:
-//   flag    : one wave per patch walks its frames in order, holding the previous
-//             frame's row in registers (each row is read once; the next two
-//             frames' loads are in flight while a frame is reduced).
+//   flag    : one wave per (patch, range of frames) walks its frames in order,
+//             holding the previous frame's row in registers (each row is read
+//             once, plus the row before the range; the next two frames' loads
+//             are in flight while a frame is reduced).  The ranges give the
+//             launch enough waves to keep HBM busy.
 //   positions : one workgroup per frame: the position of every token among
 //             the kept ones (in token order), the kept-token list and the
 //             kept count.
 //   gather  : one wave per pruned row copies its token's row.
 //   restore : one wave per output row finds its source frame (the latest kept
-//             frame of its patch, from the flags) and copies that pruned row.
+//             frame of its patch: one flag per lane and a ballot) and copies
+//             that pruned row.
 
 #include "launch.h"
 
@@ -32,6 +35,7 @@ struct LiparArgs {
   const uint16_t* x;   // [B, H, N, D] with strides
   int64_t sb, sh, sn;
   int H, N, D, F, P;
+  int R, FR;           // frame ranges per patch, frames per range (of frames 1 .. F - 1)
   double thr;          // tau * D
   uint8_t* keep;       // [BH][N]
   int32_t* cpos;       // [BH][N]: kept tokens before n
@@ -45,29 +49,34 @@ __device__ __forceinline__ const uint16_t* lp_row(const LiparArgs& a, int bh, in
 }
 
 // CPL = 16-byte chunks per lane (D <= 512 CPL); two frames in flight ahead of
-// the one being reduced
+// the one being reduced.  Wave w of the launch takes patch w / R and frames
+// [1 + r FR, 1 + (r + 1) FR) of it, r = w % R (the waves of one patch are
+// neighbours, so the row read at a range boundary is still cached)
 template <int CPL>
 __global__ void __launch_bounds__(256) lipar_flag_kernel(LiparArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bh = blockIdx.y, p = blockIdx.x * 4 + wave;
+  const int bh = blockIdx.y, w = blockIdx.x * 4 + wave;
+  const int p = w / a.R, r = w % a.R;
   if (p >= a.P) return;
+  const int f_beg = 1 + r * a.FR, f_end = min(a.F, f_beg + a.FR);
+  uint8_t* keep = a.keep + (int64_t)bh * a.N;
+  if (r == 0 && lane == 0) keep[p] = 1;  // frame 0 is always kept
+  if (f_beg >= f_end) return;
   const int nch = a.D / 8;  // 16-byte chunks per row
-  auto load = [&](int f, u32x4 (&r)[CPL]) {
-    const u32x4* src = (const u32x4*)lp_row(a, bh, min(f, a.F - 1) * a.P + p);
+  auto load = [&](int f, u32x4 (&dst)[CPL]) {
+    const u32x4* src = (const u32x4*)lp_row(a, bh, f * a.P + p);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = i * 64 + lane;
-      r[i] = c < nch ? src[c] : u32x4{0, 0, 0, 0};
+      dst[i] = c < nch ? src[c] : u32x4{0, 0, 0, 0};
     }
   };
-  uint8_t* keep = a.keep + (int64_t)bh * a.N;
   u32x4 prev[CPL], cur[CPL], n1[CPL], n2[CPL];
-  load(0, prev);
-  load(1, cur);
-  load(2, n1);
-  if (lane == 0) keep[p] = 1;
-  for (int f = 1; f < a.F; ++f) {
-    load(f + 2, n2);  // frames past the end re-read the last frame (unused)
+  load(f_beg - 1, prev);
+  load(f_beg, cur);
+  if (f_beg + 1 < f_end) load(f_beg + 1, n1);
+  for (int f = f_beg; f < f_end; ++f) {
+    if (f + 2 < f_end) load(f + 2, n2);
     double s = 0.0;
 #pragma unroll
     for (int i = 0; i < CPL; ++i)
@@ -101,7 +110,16 @@ __global__ void __launch_bounds__(1024) lipar_positions_kernel(LiparArgs a) {
   int32_t* kidx = a.kidx + (int64_t)bh * a.N;
   const int f0 = f * a.P;
   int c = 0;
-  for (int n = tid; n < f0; n += 1024) c += keep[n];
+  for (int n0 = 0; n0 < f0; n0 += 8 * 1024) {  // eight independent loads per round trip
+    int v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int n = n0 + u * 1024 + tid;
+      v[u] = n < f0 ? keep[n] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) c += v[u];
+  }
   for (int off = 32; off > 0; off >>= 1) c += __shfl_xor(c, off, 64);
   if (lane == 0) wsum[wave] = c;
   __syncthreads();
@@ -155,9 +173,15 @@ __global__ void __launch_bounds__(256) lipar_restore_kernel(LiparRestoreArgs a) 
   const int bh = blockIdx.y, n = blockIdx.x * 4 + wave;
   if (n >= a.N) return;
   const uint8_t* keep = a.keep + (int64_t)bh * a.N;
-  int g = n;
-  while (g >= a.P && !keep[g]) g -= a.P;  // uniform over the wave
-  const int j = a.cpos[(int64_t)bh * a.N + g];
+  const int f = n / a.P, p = n - f * a.P;
+  // the latest frame g <= f that keeps patch p: lane l looks at frame f0 + l
+  int g = 0;
+  for (int f0 = 0; f0 <= f; f0 += 64) {
+    const int ff = f0 + lane;
+    const unsigned long long bal = __ballot(ff <= f && keep[ff * a.P + p] != 0);
+    if (bal != 0ull) g = f0 + 63 - __builtin_clzll(bal);
+  }
+  const int j = a.cpos[(int64_t)bh * a.N + g * a.P + p];
   const u32x4* src = (const u32x4*)(a.y + ((int64_t)bh * a.N + j) * a.D);
   u32x4* dst = (u32x4*)(a.o + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)n * a.sn);
   const int nch = a.D / 8;
@@ -177,7 +201,13 @@ bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, flo
   a.thr = (double)tau * (double)s.D;
   a.keep = keep; a.cpos = cpos; a.kidx = kept_idx; a.nkept = n_kept; a.xp = (uint16_t*)x_pruned;
   const int bh = s.B * s.H;
-  const dim3 pg((a.P + 3) / 4, bh);
+  // frame ranges per patch: enough waves for about 4096 in the launch, each
+  // range as long as possible (one extra row read per range)
+  const int want = (4096 + a.P * bh - 1) / (a.P * bh);
+  const int ranges = std::max(1, std::min(frames - 1, want));
+  a.FR = std::max(1, (frames - 1 + ranges - 1) / ranges);
+  a.R = std::max(1, (frames - 1 + a.FR - 1) / a.FR);
+  const dim3 pg((unsigned)(((int64_t)a.P * a.R + 3) / 4), bh);
   const int cpl = (s.D / 8 + 63) / 64;
   if (cpl <= 1) hipLaunchKernelGGL(lipar_flag_kernel<1>, pg, dim3(256), 0, stream, a);
   else if (cpl <= 2) hipLaunchKernelGGL(lipar_flag_kernel<2>, pg, dim3(256), 0, stream, a);

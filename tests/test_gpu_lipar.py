@@ -45,7 +45,8 @@ def _check(bsa, x_bits, frames, tau, x_dev=None):
 
 
 @pytest.mark.parametrize("F,P,D,tau", [(5, 37, 64, 0.3), (3, 700, 8, 0.5), (7, 300, 1536, 0.05),
-                                       (2, 64, 4096, 0.1), (1, 50, 16, 0.0)])
+                                       (2, 64, 4096, 0.1), (1, 50, 16, 0.0), (70, 3, 64, 0.3),
+                                       (130, 2, 16, 0.5)])
 def test_random_and_video_like(gpu_lib, F, P, D, tau):
     r = np.random.default_rng(F * 1000 + P)
     x = np.empty((2, 2, F * P, D), np.float32)
@@ -87,3 +88,25 @@ def test_lipar_32k_full(gpu_lib):
     x = gen.make_video(wl)
     keep, nk = _check(gpu_lib, x, wl.frames, wl.lipar_tau)
     assert 0.1 < nk[0] / wl.N < 0.4
+
+
+def test_preallocated_outputs_reused(gpu_lib):
+    """Outputs passed back in are overwritten completely: a second call on other
+    data into the same buffers equals a call with fresh buffers."""
+    F, P, D = 6, 200, 64
+    r = np.random.default_rng(9)
+    xs = [_bits_to_dev(gen.store(r.standard_normal((1, 2, F * P, D)).astype(np.float32) * s, "bf16"))
+          for s in (1.0, 0.05)]
+    outs = gpu_lib.lipar_prune(xs[0], F, 0.3)
+    gpu_lib.lipar_prune(xs[1], F, 0.3, outputs=outs)
+    fresh = gpu_lib.lipar_prune(xs[1], F, 0.3)
+    torch.cuda.synchronize()
+    nk = fresh[3].cpu().numpy()
+    for i in (0, 1, 3):  # keep, cpos, n_kept: every entry
+        assert torch.equal(outs[i], fresh[i])
+    for bh in range(2):  # kept_idx and the pruned rows: the first n_kept entries are defined
+        assert 0 < nk[bh] < F * P
+        assert torch.equal(outs[2][bh, : nk[bh]], fresh[2][bh, : nk[bh]])
+        assert torch.equal(outs[4][bh, : nk[bh]], fresh[4][bh, : nk[bh]])
+    with pytest.raises(gpu_lib.BsaError):
+        gpu_lib.lipar_prune(xs[1], F, 0.3, outputs=outs[:4] + (outs[4][:, :-1],))

@@ -26,7 +26,14 @@
 
 namespace bsa {
 
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
+// elu(x) + 1 = max(1 + x, min(e^x, 1)): for x > 0 the clamped exponential is 1
+// and 1 + x wins; for x <= 0, e^x >= 1 + x (convexity) and the exponential
+// wins.  The clamp is the exp instruction's output modifier, so this is a
+// multiply, the exp, an add and a max (no compare / select); it can differ from
+// the branch form only where e^x and 1 + x agree to about an fp32 ulp (|x| < 5e-4)
+__device__ __forceinline__ float phi(float x) {
+  return fmaxf(x + 1.f, __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(x * kLog2e), 0.f, 1.f));
+}
 
 constexpr int kLinTok = 64;      // tokens per state tile
 constexpr int kLinThreads = 256;

@@ -47,7 +47,8 @@ def _tokens(B, H, N, C, sigma, seed):
     return bits, init
 
 
-@pytest.mark.parametrize("N,C,iters", [(3000, 37, 5), (257, 32, 3), (700, 100, 0), (1000, 500, 4)])
+# (20000, 600): one tile group of 79 tiles per cluster in the scan (C > 512)
+@pytest.mark.parametrize("N,C,iters", [(3000, 37, 5), (257, 32, 3), (700, 100, 0), (1000, 500, 4), (20000, 600, 2)])
 def test_well_separated_matches_oracle(gpu_lib, N, C, iters):
     B, H = 1, 3
     bits, init = _tokens(B, H, N, C, 0.05, N + C)

@@ -146,7 +146,8 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
     const int last_real = N - (a.nb - 1) * kBwdBlock;
     nsub -= 2 - (last_real + SUB - 1) / SUB;
   }
-  auto key0_of = [&](int u) -> int { return a.col_idx[rbeg + (u >> 1)] * kBwdBlock + (u & 1) * SUB; };
+  const cint_ptr cols = (cint_ptr)a.col_idx;
+  auto key0_of = [&](int u) -> int { return cols[rbeg + (u >> 1)] * kBwdBlock + (u & 1) * SUB; };
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
@@ -267,7 +268,8 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
     const int last_real = N - (a.nb - 1) * kBwdBlock;
     nsub -= PER - (last_real + SUB - 1) / SUB;
   }
-  auto q0_of = [&](int u) -> int { return a.row_idx[cbeg + u / PER] * kBwdBlock + (u % PER) * SUB; };
+  const cint_ptr ridx = (cint_ptr)a.row_idx;
+  auto q0_of = [&](int u) -> int { return ridx[cbeg + u / PER] * kBwdBlock + (u % PER) * SUB; };
 
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
@@ -297,16 +299,18 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
   const float* lse_h = a.lse + (int64_t)bh * N;
   const float* del_h = a.delta + (int64_t)bh * N;
   float nl = 0.f, ne = 0.f;
+  // (the raw values are kept until the store at the end of the step, so the
+  // loads' latency is waited for there, not before the copies are issued)
   auto side_load = [&](int q0) {
     if (wave == 0 && lane < SUB) {
       const int qq = q0 + lane;
-      nl = qq < N ? lse_h[qq] * kLog2e : __builtin_inff();
+      nl = qq < N ? lse_h[qq] : __builtin_inff();
       ne = qq < N ? del_h[qq] : 0.f;
     }
   };
   auto side_store = [&](int buf) {
     if (wave == 0 && lane < SUB) {
-      L[buf][lane] = nl;
+      L[buf][lane] = nl * kLog2e;
       E[buf][lane] = ne;
     }
   };
@@ -337,9 +341,9 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
     const int buf = u & 1;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u (and K) landed
     bwd_barrier();
-    if (u + 1 < nsub) {
-      dma(Qn, Gn, q0_of(u + 1));
+    if (u + 1 < nsub) {  // lse / Delta loads first: their use then waits for them only
       side_load(q0_of(u + 1));
+      dma(Qn, Gn, q0_of(u + 1));
     }
     // the bases are opaque here, so the 24 XORed offsets are formed next to
     // their reads instead of being hoisted out of the loop (and spilled)
@@ -387,10 +391,10 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
 
   if (nsub > 0) {
     // K of the block's 128 keys: wave w, instruction j stages rows 32 w + 4 j + lane / 16
+    side_load(q0_of(0));
 #pragma unroll
     for (int j = 0; j < 8; ++j) dma_rows(krs, Ks, 32 * wv + 4 * j, kblk * kBwdBlock);
     dma(Q0, G0, q0_of(0));
-    side_load(q0_of(0));
     side_store(0);
   }
   int u = 0;

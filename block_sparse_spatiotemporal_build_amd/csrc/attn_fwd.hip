@@ -69,8 +69,6 @@ struct AttnArgs {
   float scale_log2;  // scale * log2(e)
 };
 
-typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
-
 // Work item (query block, head, batch) of workgroup `pid`.
 //  * Rows not singled out below, default: each XCD gets a contiguous range of
 //    the (batch, head, query block) list, so the workgroups sharing an L2 walk

@@ -71,6 +71,10 @@ __device__ __forceinline__ float pair_sum(float x) {
 //   swz_v: chunk ^ (4 (row & 3) + ((row >> 2) & 3)) -- the 4 rows x 4 chunks
 //          touched by one ds_read_b64_tr_b16 over 32 lanes are distinct.
 typedef __attribute__((address_space(3))) void lds_void;
+// int32 index arrays read through the constant address space: uniform indices
+// become scalar loads (counted by lgkmcnt), so fetching the next block index
+// never makes a wave wait on its own vector-memory copies in flight
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped, stride 0) buffer loads, gfx9 family
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }

@@ -710,9 +710,14 @@ __device__ __forceinline__ float xor16_sum(float x) {
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 causal_lin_d128_kernel(CausalArgs a) {
   constexpr int D = 128, TILE = kCT * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t Q0[TILE], Q1[TILE], Q2[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE];
+  // ring stage s: Q and K tiles in QKs (Q first), V in Vs.  Six objects: the
+  // compiler tells the copies into one stage from the reads of another only
+  // for a few distinct LDS objects (with nine it made the tile reads wait for
+  // the copies of the next tiles)
+  __shared__ __attribute__((aligned(1024))) uint16_t QK0[2 * TILE], QK1[2 * TILE], QK2[2 * TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE];
+  uint16_t *const Q0 = QK0, *const Q1 = QK1, *const Q2 = QK2;
+  uint16_t *const K0 = QK0 + TILE, *const K1 = QK1 + TILE, *const K2 = QK2 + TILE;
   __shared__ __attribute__((aligned(16))) float zs[2][D];
   __shared__ __attribute__((aligned(16))) float zred[4][D];
   __shared__ float dq[kCT];
@@ -788,6 +793,10 @@ causal_lin_d128_kernel(CausalArgs a) {
       for (int r = 0; r < 16; ++r) acc[t][r] = ps[(32 * t + 8 * (r >> 2) + 4 * hi + (r & 3)) * D];
     if (tid < D) zs[0][tid] = a.pre_z[j * D + tid];
   }
+  // the state loads retire here, before any tile copy: the step waits count
+  // the copies and stores only (and the compiler then adds no wait for them
+  // inside the loop)
+  __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
   if (nch > 0) dma(Q0, K0, V0, n0);
   if (nch > 1) dma(Q1, K1, V1, n0 + kCT);
 
@@ -798,9 +807,26 @@ causal_lin_d128_kernel(CausalArgs a) {
   auto step = [&](uint16_t* Qb, uint16_t* Kb, uint16_t* Vb, uint16_t* Qn, uint16_t* Kn, uint16_t* Vn, int c) {
     const int t0 = n0 + c * kCT;
     const float* zp = zs[c & 1];
-    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6) lgkmcnt(0): the next tile may be in flight
-    else __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0) lgkmcnt(0)
+    // Wait for this step's tile.  Vector memory operations retire in issue
+    // order; a wave issues, per step, the 6 copies of the tile two ahead (right
+    // after the first barrier, when there is one) and 4 output stores (lane 0's
+    // row always exists), so after tile c's copies come: step 0: tile 1;
+    // step 1: tile 2 and step 0's stores; later: the stores of steps c - 2 and
+    // c - 1 and tile c + 1.  (lgkmcnt(0) as well.)
+    if (c == 0) {
+      if (nch > 1) __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6)
+      else __builtin_amdgcn_s_waitcnt(0x0070);          // vmcnt(0)
+    } else if (c == 1) {
+      if (nch > 2) __builtin_amdgcn_s_waitcnt(0x007A);  // vmcnt(10)
+      else __builtin_amdgcn_s_waitcnt(0x0074);          // vmcnt(4)
+    } else {
+      if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x007E);  // vmcnt(14)
+      else __builtin_amdgcn_s_waitcnt(0x0078);              // vmcnt(8)
+    }
     lds_barrier();
+    // the tile two steps ahead goes into the stage of step c - 1: every wave
+    // has passed this barrier, so none still reads it
+    if (c + 2 < nch) dma(Qn, Kn, Vn, t0 + 2 * kCT);
 
     // phi in place on the K and Q tiles; z and phi(q) . z_prev partials in fp32
     // (K rows past the split are zeroed; only a sequence's last tile has any)
@@ -810,13 +836,21 @@ causal_lin_d128_kernel(CausalArgs a) {
       for (int e = 0; e < 8; ++e) zk[e] = 0.f;
       const f32x4 z0 = *(const f32x4*)&zp[8 * cc], z1 = *(const f32x4*)&zp[8 * cc + 4];
       const float zz[8] = {z0[0], z0[1], z0[2], z0[3], z1[0], z1[1], z1[2], z1[3]};
+      // both rows' chunks are read before either is written back
+      u32x4 krr[2], qrr[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int row = prow + 16 * i;
+        const int po = row * D + ((cc ^ swz_v(row)) << 3);
+        krr[i] = *(const u32x4*)&Kb[po];
+        qrr[i] = *(const u32x4*)&Qb[po];
+      }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int row = prow + 16 * i;
         const int po = row * D + ((cc ^ swz_v(row)) << 3);
         const bool live = decltype(full)::value || t0 + row < n1;
-        const u32x4 kr = *(const u32x4*)&Kb[po];
-        const u32x4 qr = *(const u32x4*)&Qb[po];
+        const u32x4 kr = krr[i], qr = qrr[i];
         u32x4 kp, qp;
         float d = 0.f;
 #pragma unroll
@@ -913,9 +947,6 @@ causal_lin_d128_kernel(CausalArgs a) {
         *(u32x2*)(dst + 8 * g) = w;
       }
     }
-    // the tile two steps ahead goes into the stage of step c - 1 (every wave
-    // has passed this step's first barrier, so none still reads it)
-    if (c + 2 < nch) dma(Qn, Kn, Vn, t0 + 2 * kCT);
   };
 
   int c = 0;

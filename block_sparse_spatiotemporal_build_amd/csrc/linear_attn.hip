@@ -626,16 +626,24 @@ struct LinPrefixArgs {
 };
 
 // one thread per float4 column of a head's S (or z); reads every partial once,
-// in split order (deterministic)
+// in split order (deterministic).  The partials are loaded 16 splits at a time
+// (one memory round trip per 16 splits, not per split).
 template <int C4>
 __device__ __forceinline__ void prefix_column(float4* __restrict__ p, const float4* in, float4* out, int idx,
                                               int splits, int f) {
+  constexpr int U = 16;
   float4 run = in ? in[idx] : float4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int s = 0; s < splits; ++s) {
-    const float4 x = p[(int64_t)s * C4 + idx];
-    if (s % f == 0) p[(int64_t)s * C4 + idx] = run;
-    run.x += x.x; run.y += x.y; run.z += x.z; run.w += x.w;
+  for (int s0 = 0; s0 < splits; s0 += U) {
+    float4 x[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      x[u] = s0 + u < splits ? p[(int64_t)(s0 + u) * C4 + idx] : float4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int s = s0 + u;
+      if (s < splits && s % f == 0) p[(int64_t)s * C4 + idx] = run;
+      run.x += x[u].x; run.y += x[u].y; run.z += x[u].z; run.w += x[u].w;
+    }
   }
   if (out) out[idx] = run;
 }

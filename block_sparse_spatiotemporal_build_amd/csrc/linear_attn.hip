@@ -815,22 +815,13 @@ causal_lin_d128_kernel(CausalArgs a) {
   auto step = [&](uint16_t* Qb, uint16_t* Kb, uint16_t* Vb, uint16_t* Qn, uint16_t* Kn, uint16_t* Vn, int c) {
     const int t0 = n0 + c * kCT;
     const float* zp = zs[c & 1];
-    // Wait for this step's tile.  Vector memory operations retire in issue
-    // order; a wave issues, per step, the 6 copies of the tile two ahead (right
-    // after the first barrier, when there is one) and 4 output stores (lane 0's
-    // row always exists), so after tile c's copies come: step 0: tile 1;
-    // step 1: tile 2 and step 0's stores; later: the stores of steps c - 2 and
-    // c - 1 and tile c + 1.  (lgkmcnt(0) as well.)
-    if (c == 0) {
-      if (nch > 1) __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6)
-      else __builtin_amdgcn_s_waitcnt(0x0070);          // vmcnt(0)
-    } else if (c == 1) {
-      if (nch > 2) __builtin_amdgcn_s_waitcnt(0x007A);  // vmcnt(10)
-      else __builtin_amdgcn_s_waitcnt(0x0074);          // vmcnt(4)
-    } else {
-      if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x007E);  // vmcnt(14)
-      else __builtin_amdgcn_s_waitcnt(0x0078);              // vmcnt(8)
-    }
+    // Wait for this step's tile.  The copies (loads) retire in issue order;
+    // the output stores in between may retire in any order relative to them,
+    // so the count allows only the loads issued after tile c's: the 6 copies
+    // of tile c + 1 (issued at the top of step c - 1, or before the loop), if
+    // there is such a tile.  (lgkmcnt(0) as well.)
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(0x0076);  // vmcnt(6)
+    else __builtin_amdgcn_s_waitcnt(0x0070);              // vmcnt(0)
     lds_barrier();
     // the tile two steps ahead goes into the stage of step c - 1: every wave
     // has passed this barrier, so none still reads it

@@ -24,8 +24,8 @@ descriptions on the five pages:
 
 Modules: ``mask`` (block rule and CSR), ``attention`` (block-sparse softmax
 attention), ``svg_ear`` (centroids, routing scores, budget selection,
-compensated attention; the score formula is "parity unpinned" as far as the
-pages go, see that module), ``linear`` (elu+1 linear attention, causal and
+compensated attention; the score is pinned to the page's statement that the
+estimated error converges to the actual error, see that module), ``linear`` (elu+1 linear attention, causal and
 mixed forms), ``lipar`` (pruning and restoration), ``kmeans`` (the token
 clustering and cluster order in front of the SVG-EAR calls),
 ``attention_bwd`` (gradients of the block-sparse attention).

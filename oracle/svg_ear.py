@@ -23,11 +23,15 @@ cost is n_a * n_b scores.  s is the softmax scale (1/sqrt(D)).
    score_ab = n_a ||e_ab||^2 / (n_a n_b) = ||e_ab||^2 / n_b, the squared output
    error of the n_a queries per unit cost.  The page states the idea (error
    estimated by lightweight probing, error-to-cost ratio) but prints no
-   formula, so this exact score is a reading: PARITY UNPINNED against the
-   pages.  What is pinned: it vanishes when a cluster's keys all equal their
-   centroid or the cluster is a single key, it scales as |V|^2, it is invariant
-   to the order of keys inside a cluster, and it shrinks as clusters tighten
-   (the page's idea 3: error bounded by clustering quality).
+   formula, so this exact score is a reading.  It is pinned to what the page
+   does state (idea 3: as clustering tightens and sequences grow, the
+   estimated error converges to the actual error): ``actual_errors`` below
+   computes the actual per-cost output error of compensating one block, from
+   dense attention and ``compensated_attention`` alone, and the tests require
+   the ratio score / actual error to go to 1 and the two rankings to agree in
+   those limits.  Also pinned: the score vanishes when a cluster's keys all
+   equal their centroid or the cluster is a single key, it scales as |V|^2,
+   and it is invariant to the order of keys inside a cluster.
 4. Selection (idea 2, routing under a fixed density budget): over non-empty
    blocks, order by (score descending, a * Ck + b ascending) and keep the
    longest prefix whose total cost is <= floor(N * N * density_ppm / 10^6),
@@ -82,6 +86,39 @@ def route_scores(k, v, k_off, cents, scale: float):
         score[:, b] = (e * e).sum(axis=1) / nk[b]
     score[nq == 0, :] = 0.0
     return score
+
+
+def actual_errors(q, k, v, q_off, k_off, cents, scale: float, key_clusters=None):
+    """The actual compensation error of each block (a, b), per unit cost
+    (idea 3's "actual error", the quantity the routing score estimates):
+
+        err_ab = sum_{q in a} |O_b(q) - O(q)|^2 / (n_a n_b)
+
+    where O(q) is dense softmax attention of the real query q over all keys and
+    O_b(q) is the compensated output with only key cluster b replaced by its
+    virtual key (every other block exact, ``compensated_attention`` with one
+    skipped column).  Each query keeps its own max and normaliser; nothing
+    here uses the proxy centroids.  Returns [Cq, len(key_clusters)] (all key
+    clusters when None); empty clusters give 0."""
+    from . import attention as _attn
+    q, k, v = (np.asarray(x, np.float64) for x in (q, k, v))
+    nq, nk = cents["nq"], cents["nk"]
+    Cq, Ck = len(nq), len(nk)
+    cols = range(Ck) if key_clusters is None else list(key_clusters)
+    ref, _ = _attn.dense_attention(q[None, None], k[None, None], v[None, None], scale)
+    ref = ref[0, 0]
+    err = np.zeros((Cq, len(cols)))
+    for i, b in enumerate(cols):
+        if nk[b] == 0:
+            continue
+        kept = np.ones((Cq, Ck), dtype=bool)
+        kept[:, b] = False
+        out, _ = compensated_attention(q, k, v, q_off, k_off, kept, cents, scale)
+        for a in range(Cq):
+            r0, r1 = q_off[a], q_off[a + 1]
+            if r1 > r0:
+                err[a, i] = ((out[r0:r1] - ref[r0:r1]) ** 2).sum() / (nq[a] * nk[b])
+    return err
 
 
 def budget(N: int, density_ppm: int) -> int:

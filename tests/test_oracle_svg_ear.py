@@ -188,3 +188,114 @@ def test_unpermuted_output_equals_original_order():
     back[pq] = res["out"]
     ref, _ = _dense(q0, k0, v0, 0.4)
     assert np.abs(back - ref).max() < 1e-12
+
+
+# ---- the score against the actual compensation error (the page's idea 3) ----
+
+def _convergence_case(seed, N, sigma_q, D=16, Cq=4, key_cluster=8, sigma_k=0.5):
+    """Unit query / key centres at norm 2; queries spread by sigma_q around
+    theirs, keys by sigma_k (fixed, so errors stay non-zero); key clusters of
+    a fixed size, so a longer sequence has more of them."""
+    r = np.random.default_rng(seed)
+    Ck = N // key_cluster
+    lq = np.sort(r.integers(0, Cq, N))
+    lk = np.repeat(np.arange(Ck), key_cluster)
+    cq = r.standard_normal((Cq, D))
+    ck = r.standard_normal((Ck, D))
+    cq /= np.linalg.norm(cq, axis=1, keepdims=True)
+    ck /= np.linalg.norm(ck, axis=1, keepdims=True)
+    q = 2.0 * cq[lq] + sigma_q * r.standard_normal((N, D))
+    k = 2.0 * ck[lk] + sigma_k * r.standard_normal((N, D))
+    v = r.standard_normal((N, D))
+    q_off = np.concatenate([[0], np.cumsum(np.bincount(lq, minlength=Cq))]).astype(np.int64)
+    k_off = np.arange(0, N + 1, key_cluster, dtype=np.int64)
+    return q, k, v, q_off, k_off
+
+
+def _score_vs_actual(case, score_fn=None, n_cols=24):
+    q, k, v, qo, ko = case
+    s = 1.0 / math.sqrt(q.shape[1])
+    c = oe.centroids(q, k, v, qo, ko)
+    sc = (score_fn or oe.route_scores)(k, v, ko, c, s)
+    cols = np.linspace(0, len(ko) - 2, n_cols).astype(int)
+    act = oe.actual_errors(q, k, v, qo, ko, c, s, key_clusters=cols)
+    est = sc[:, cols]
+    ratio = est / act
+    return dict(agg=est.sum() / act.sum(), med=float(np.median(np.abs(ratio - 1.0))), est=est, act=act)
+
+
+def _rank_corr(x, y):
+    rx = np.argsort(np.argsort(x.ravel())).astype(float)
+    ry = np.argsort(np.argsort(y.ravel())).astype(float)
+    return float(np.corrcoef(rx, ry)[0, 1])
+
+
+def test_score_converges_to_actual_error_as_clusters_tighten():
+    """Idea 3: the estimate converges to the actual error as clustering gets
+    finer.  Query spread 0.5 -> 0.1 -> 0.02 around the proxies: the aggregate
+    ratio and the per-block ratios go to 1 and the rankings agree."""
+    res = [_score_vs_actual(_convergence_case(11, 512, sq)) for sq in (0.5, 0.1, 0.02)]
+    gaps = [abs(r["agg"] - 1.0) for r in res]
+    meds = [r["med"] for r in res]
+    assert gaps[0] > gaps[1] > gaps[2] and gaps[2] < 0.01, gaps
+    assert meds[0] > meds[1] > meds[2] and meds[2] < 0.01, meds
+    assert _rank_corr(res[2]["est"], res[2]["act"]) > 0.999
+
+
+def test_score_converges_to_actual_error_as_sequences_grow():
+    """Idea 3: ... and as the sequence grows (tight query clusters, key clusters
+    of a fixed size, so each one's share of the softmax normaliser shrinks)."""
+    meds = [_score_vs_actual(_convergence_case(12, n, 0.02))["med"] for n in (96, 384, 1536)]
+    assert meds[0] > meds[1] > meds[2] and meds[2] < 0.006, meds
+
+
+def test_selection_by_score_matches_selection_by_actual_error():
+    """The routing keeps the same blocks whether it ranks by the estimate or by
+    the actual error (tight clusters), at the 15 % density budget: at most one
+    near-tie swapped at the cut, and the actual error the estimate's selection
+    removes is within 1 % of the best selection's."""
+    q, k, v, qo, ko = _convergence_case(13, 512, 0.02)
+    s = 1.0 / math.sqrt(q.shape[1])
+    c = oe.centroids(q, k, v, qo, ko)
+    est = oe.route_scores(k, v, ko, c, s)
+    act = oe.actual_errors(q, k, v, qo, ko, c, s)
+    _, _, kept_est = oe.select_route(est, c["nq"], c["nk"], len(q), 150_000)
+    _, _, kept_act = oe.select_route(act, c["nq"], c["nk"], len(q), 150_000)
+    assert kept_act.sum() > 20
+    assert (kept_est ^ kept_act).sum() <= 2
+    cost = np.outer(c["nq"], c["nk"])
+    assert (act * cost)[kept_est].sum() >= 0.99 * (act * cost)[kept_act].sum()
+
+
+def test_convergence_pin_rejects_plausible_score_mistakes():
+    """The pin above fails a score that drops the 1/Z_a normalisation, drops the
+    1/n_b cost, keeps n_a in the numerator, or adds the compensation term with
+    the wrong sign (each written as the mistaken score it produces)."""
+    case = _convergence_case(11, 512, 0.02)
+    q, k, v, qo, ko = case
+    s = 1.0 / math.sqrt(q.shape[1])
+
+    def proxy_z(cents):
+        L = s * (cents["cq"] @ k.T)
+        return np.exp(L - L.max(axis=1, keepdims=True)).sum(axis=1)
+
+    def wrong_sign(k_, v_, ko_, cents, sc_):
+        W = np.exp(sc_ * (cents["cq"] @ k_.T))
+        out = np.zeros((len(cents["nq"]), len(cents["nk"])))
+        Z = W.sum(axis=1)
+        for b in range(len(cents["nk"])):
+            j0, j1 = ko_[b], ko_[b + 1]
+            comp = cents["nk"][b] * np.exp(sc_ * cents["cq"] @ cents["ck"][b])[:, None] * cents["vk"][b]
+            e = (W[:, j0:j1] @ v_[j0:j1] + comp) / Z[:, None]
+            out[:, b] = (e * e).sum(axis=1) / cents["nk"][b]
+        return out
+
+    mutants = {
+        "no 1/Z_a": lambda k_, v_, ko_, c_, sc_: oe.route_scores(k_, v_, ko_, c_, sc_) * proxy_z(c_)[:, None] ** 2,
+        "no 1/n_b": lambda k_, v_, ko_, c_, sc_: oe.route_scores(k_, v_, ko_, c_, sc_) * c_["nk"][None, :],
+        "n_a kept": lambda k_, v_, ko_, c_, sc_: oe.route_scores(k_, v_, ko_, c_, sc_) * c_["nq"][:, None],
+        "sign": wrong_sign,
+    }
+    for name, fn in mutants.items():
+        r = _score_vs_actual(case, fn)
+        assert abs(r["agg"] - 1.0) > 0.5 and r["med"] > 0.5, name

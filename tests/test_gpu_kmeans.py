@@ -1,10 +1,19 @@
 """GPU token clustering (k-means, cluster order, row gather / scatter) vs the oracle.
 
-Labels are integers decided by float distances: where the nearest centre is
-unique by a margin well above fp32 accumulation error they must equal the
-oracle's (which takes the decision in the kernel's precision: centres rounded
-to bf16); everywhere they must be a valid nearest centre within that error.
-The cluster order and the row copies are bit-exact."""
+Labels are integers decided by float distances.  They are checked against the
+textbook algorithm (``oracle.kmeans`` with ``centre_dtype=None``: squared
+Euclidean distances in float64 to float64 centres, the form pinned against
+scikit-learn).  The device takes the decision with the centres rounded to bf16
+and fp32 accumulation; ``_check_valid`` bounds what that rounding can change.
+Where the textbook nearest centre is unique by more than twice that bound the
+labels must equal it; everywhere they must be a textbook nearest centre
+within it.  Where the data are well separated, whole Lloyd runs must equal the
+textbook run exactly.  Ten Lloyd steps on overlapping clusters amplify single
+near-tie decisions, so there the final labels are checked for validity, the
+k-means objective against the textbook run's, and (a secondary check) the
+labels against the oracle run that takes its decisions at the device's
+precision (``centre_dtype="bf16"``).  The cluster order and the row copies are
+bit-exact."""
 
 import numpy as np
 import pytest
@@ -17,23 +26,36 @@ from synth import gen, get_workload
 pytestmark = pytest.mark.gpu
 
 
-def _dist(x, cent):
-    cb = ok.round_bf16(cent)
-    return (cb * cb).sum(1)[None, :] - 2.0 * (x @ cb.T)
+def _rounding_bound(x, cent):
+    """[N, C]: a bound on |device distance - textbook distance| per (token,
+    centre).  Rounding a centre to bf16 moves each coordinate by at most 2^-8
+    of itself, which moves |c|^2 - 2 x.c by at most 2^-7 (|c|^2 (1 + 2^-8) +
+    sum |x_i c_i|); fp32 accumulation adds at most 1e-5 (|c|^2 + 2 sum |x_i c_i|)."""
+    c2 = (cent * cent).sum(1)[None, :]
+    xc = np.abs(x) @ np.abs(cent).T
+    return 2.0 ** -7 * (c2 * (1 + 2.0 ** -8) + xc) + 1e-5 * (c2 + 2.0 * xc)
 
 
 def _check_valid(x, labels, cent):
-    """labels are nearest centres within the fp32 error bound; returns the share
-    of tokens whose nearest centre is unique by more than that bound."""
-    d = _dist(x, cent)
-    cb = ok.round_bf16(cent)
-    eps = 1e-5 * ((cb * cb).sum(1)[None, :] + 2.0 * (np.abs(x) @ np.abs(cb).T)).max()
-    dmin = d.min(axis=1)
-    assert (d[np.arange(len(x)), labels] <= dmin + eps).all()
-    srt = np.sort(d, axis=1)
-    clear = srt[:, 1] - srt[:, 0] > 2 * eps if d.shape[1] > 1 else np.ones(len(x), bool)
-    assert np.array_equal(labels[clear], d.argmin(axis=1)[clear])
+    """Each label's textbook distance interval (distance +- its bound) reaches
+    below every other centre's interval top, and where the textbook nearest
+    centre's interval lies below every other interval the label is exactly
+    that centre.  Returns the share of tokens with such a unique answer."""
+    cent = np.asarray(cent, np.float64)
+    d = (cent * cent).sum(1)[None, :] - 2.0 * (x @ cent.T)
+    eps = _rounding_bound(x, cent)
+    rows = np.arange(len(x))
+    assert (d[rows, labels] - eps[rows, labels] <= (d + eps).min(axis=1)).all()
+    best = d.argmin(axis=1)
+    lo = d - eps
+    lo[rows, best] = np.inf
+    clear = d[rows, best] + eps[rows, best] < lo.min(axis=1) if d.shape[1] > 1 else np.ones(len(x), bool)
+    assert np.array_equal(labels[clear], best[clear])
     return clear.mean()
+
+
+def _objective(x, labels, cent):
+    return float(((x - cent[labels]) ** 2).sum())
 
 
 def _tokens(B, H, N, C, sigma, seed):
@@ -58,7 +80,7 @@ def test_well_separated_matches_oracle(gpu_lib, N, C, iters):
     lab_h, cent_h, perm_h, off_h = (t.cpu().numpy() for t in (labels, cent, perm, off))
     for r in range(B * H):
         xf = gen.to_f64(bits[0, r], "bf16")
-        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), iters)
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), iters, centre_dtype=None)
         assert np.array_equal(lab_h[r], rl), r
         assert np.abs(cent_h[r] - rc).max() < 1e-5
         p, o = ok.cluster_order(lab_h[r], C)
@@ -100,7 +122,7 @@ def test_assignment_and_update_steps_on_overlapping_clusters(gpu_lib):
         xf = gen.to_f64(d["k"][0, r], "bf16")
         l0 = lab0.cpu().numpy()[r]
         assert np.array_equal(cent0.cpu().numpy()[r], d["centres_k"][r])
-        assert _check_valid(xf, l0, d["centres_k"][r].astype(np.float64)) > 0.999
+        assert _check_valid(xf, l0, d["centres_k"][r].astype(np.float64)) > 0.8
         want = ok.update(xf, l0, d["centres_k"][r].astype(np.float64))
         assert np.abs(cent1.cpu().numpy()[r] - want).max() < 1e-5
         l1 = lab1.cpu().numpy()[r]
@@ -113,8 +135,10 @@ def test_assignment_and_update_steps_on_overlapping_clusters(gpu_lib):
 def test_svg_ear_32k_ten_steps(gpu_lib, which):
     """Ten Lloyd steps on the 32,760-token workload as the benchmark launches
     them (all 12 heads; queries: 100 clusters, keys: 500): for heads 0 and 7,
-    valid final labels for the final centres, the exact cluster order, and
-    agreement with the oracle run from the same centres."""
+    valid final labels for the final centres (textbook distances), the exact
+    cluster order, a k-means objective within 1e-4 of the textbook run from
+    the same centres, and label agreement with the textbook run and (closer)
+    with the oracle run that decides at the device's precision."""
     wl = get_workload("svg_ear_32k")
     d = gen.make_gmm_tokens(wl)
     C = wl.n_q_clusters if which == "q" else wl.n_k_clusters
@@ -129,7 +153,10 @@ def test_svg_ear_32k_ten_steps(gpu_lib, which):
         _check_valid(xf, lab, cen)
         p, o = ok.cluster_order(lab, C)
         assert np.array_equal(perm.cpu().numpy()[r], p) and np.array_equal(off.cpu().numpy()[r], o)
-        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), wl.kmeans_iters)
+        tl, tc = ok.lloyd(xf, init[r].astype(np.float64), wl.kmeans_iters, centre_dtype=None)
+        assert _objective(xf, lab, cen) <= _objective(xf, tl, tc) * (1 + 1e-4)
+        assert (tl == lab).mean() > 0.95
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), wl.kmeans_iters, centre_dtype="bf16")
         assert (rl == lab).mean() > 0.999
         assert np.abs(rc - cen).max() < 1e-3
 
@@ -175,7 +202,7 @@ def test_batch_of_sequences(gpu_lib):
     for r in range(B * H):
         b, h = divmod(r, H)
         xf = gen.to_f64(bits[b, h], "bf16")
-        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), 3)
+        rl, rc = ok.lloyd(xf, init[r].astype(np.float64), 3, centre_dtype=None)
         assert np.array_equal(labels.cpu().numpy()[r], rl), r
         assert np.abs(cent.cpu().numpy()[r] - rc).max() < 1e-5
 

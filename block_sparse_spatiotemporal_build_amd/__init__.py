@@ -69,6 +69,7 @@ _SIGNATURES = {
     "bsa_route_select_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32, ctypes.c_int32]),
     "bsa_route_select": (ctypes.c_int, [_P, ctypes.POINTER(Shape), _P, ctypes.c_int32, _P, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
+    "bsa_route_budget": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
     "bsa_compensated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                 ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P,
                                                 ctypes.c_float, _P, ctypes.c_size_t, _P]),

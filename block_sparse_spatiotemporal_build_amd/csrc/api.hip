@@ -107,8 +107,7 @@ bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v
   if (!q || !k || !v || !o || !row_ptr || !col_idx) return fail(BSA_ERR_ARG, "%s: NULL tensor pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
-  if (!__builtin_isfinite(scale) || scale == 0.f)
-    return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+  if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
   if (block < 1) return fail(BSA_ERR_ARG, "%s: block must be >= 1", fn);
   if (dtype == BSA_DT_BF16) {
     if (shape->D != 64 && shape->D != 128)
@@ -163,7 +162,7 @@ bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dO) || !aligned16(dq) ||
       !aligned16(dk) || !aligned16(dv))
     return fail(BSA_ERR_ARG, "%s: tensors must be 16-byte aligned", fn);
-  if (!__builtin_isfinite(scale) || scale == 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+  if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
   if ((int64_t)shape->B * shape->H * ((shape->N + 127) / 128) > 0x7fffffffLL)
     return fail(BSA_ERR_ARG, "%s: too many (block, sequence) pairs", fn);
   if (((int64_t)shape->N + 128) * shape->stride_n * 2 >= ((int64_t)1 << 31))
@@ -250,7 +249,7 @@ bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void*
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
   if (r > 0.f) {
-    if (!__builtin_isfinite(scale) || scale == 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and non-zero", fn);
+    if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
     if (block != 64 && block != 128) return fail(BSA_ERR_UNSUPPORTED, "%s: block must be 64 or 128", fn);
   }
   if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
@@ -345,8 +344,10 @@ static bsa_status check_clusters(const bsa_shape* shape, const int32_t* q_off, i
   return BSA_OK;
 }
 
+// floor(N * N * ppm / 10^6) in 128-bit integers: N * N * ppm needs up to 82
+// bits; the result is at most N * N < 2^62
 static long long budget_of(int N, int32_t density_ppm) {
-  return (long long)N * (long long)N * (long long)density_ppm / 1000000LL;
+  return (long long)((__int128)N * N * density_ppm / 1000000);
 }
 
 bsa_status bsa_cluster_centroids(const void* q, const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
@@ -529,6 +530,11 @@ bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_sh
   if (!aligned16(y_pruned) || !aligned16(out)) return fail(BSA_ERR_ARG, "%s: y_pruned, out must be 16-byte aligned", fn);
   g_err[0] = 0;
   return launch_lipar_restore(y_pruned, *shape, frames, keep, cpos, out, (hipStream_t)stream);
+}
+
+int64_t bsa_route_budget(int32_t N, int32_t density_ppm) {
+  if (N < 0 || density_ppm < 0 || density_ppm > 1000000) return -1;
+  return budget_of(N, density_ppm);
 }
 
 const char* bsa_status_string(bsa_status s) {

@@ -82,9 +82,9 @@ __global__ void __launch_bounds__(256) lipar_flag_kernel(LiparArgs a) {
     for (int i = 0; i < CPL; ++i)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float d0 = bf16_lo(cur[i][e]) - bf16_lo(prev[i][e]);
-        const float d1 = bf16_hi(cur[i][e]) - bf16_hi(prev[i][e]);
-        s += (double)fabsf(d0) + (double)fabsf(d1);
+        const double d0 = (double)bf16_lo(cur[i][e]) - (double)bf16_lo(prev[i][e]);
+        const double d1 = (double)bf16_hi(cur[i][e]) - (double)bf16_hi(prev[i][e]);
+        s += fabs(d0) + fabs(d1);
       }
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
     if (lane == 0) keep[f * a.P + p] = s > a.thr ? 1 : 0;

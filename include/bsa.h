@@ -124,7 +124,8 @@ bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int
  *   head, row).  Without it every row is in the second group, in index order.
  *   Results are bitwise identical with or without it.  Ignored by the fp32
  *   path.  Like col_idx, its device contents are trusted.
- * scale: the softmax scale (1/sqrt(D) for standard attention). */
+ * scale: the softmax scale (1/sqrt(D) for standard attention); must be finite
+ *   and > 0 (BSA_ERR_ARG otherwise). */
 bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o,
                                      float* lse, bsa_dtype dtype, const bsa_shape* shape,
                                      const int32_t* row_ptr, const int32_t* col_idx,
@@ -159,6 +160,7 @@ size_t bsa_block_sparse_attn_bwd_workspace(const bsa_shape* shape);
  * Precision: fp32 accumulation; P and dS enter the MFMA as bf16; Delta uses the
  *   bf16 forward output.  Deterministic (no atomics).  Rows without kept keys
  *   get zero dq; keys no row keeps get zero dk and dv.
+ * scale: as in the forward, finite and > 0.
  * workspace: at least bsa_block_sparse_attn_bwd_workspace(shape) bytes,
  *   256-byte aligned.  Only bf16, D = 128, block = 128 (BSA_ERR_UNSUPPORTED). */
 bsa_status bsa_block_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
@@ -236,7 +238,8 @@ bsa_status bsa_causal_linear_attn_fwd(const void* q, const void* k, const void* 
  * linear pass blends into it row by row: each branch is rounded to bf16 once
  * before the blend (two roundings in all).
  * workspace: at least bsa_linear_attn_workspace bytes, 256-byte aligned.
- * r outside [0, 1] or NaN is rejected. */
+ * r outside [0, 1] or NaN is rejected; with r > 0, scale must be finite and
+ * > 0. */
 bsa_status bsa_mixed_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
                               const bsa_shape* shape, const int32_t* row_ptr, const int32_t* col_idx,
                               const int32_t* row_order, int32_t block, float scale, float r,
@@ -337,7 +340,7 @@ size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck
 /* Step 3 (idea 2, error-to-cost routing under a density budget): per (batch,
  * head), order the non-empty blocks by (score descending, a * Ck + b
  * ascending) and keep the longest prefix whose total cost is <=
- * floor(N * N * density_ppm / 10^6) (integer arithmetic).  Bit-exact for a given
+ * floor(N * N * density_ppm / 10^6) (integer arithmetic, bsa_route_budget).  Bit-exact for a given
  * score array.  Output CSR per (batch, head): route_row_ptr int32 [B*H][Cq + 1]
  * (offsets relative to that head's route_col segment), route_col int32
  * [B*H][Cq * Ck] with the kept key clusters of each query cluster ascending.
@@ -346,6 +349,11 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
                             int32_t Cq, const int32_t* k_off, int32_t Ck, int32_t density_ppm,
                             int32_t* route_row_ptr, int32_t* route_col, void* workspace,
                             size_t ws_bytes, void* stream);
+
+/* The density budget of bsa_route_select, in scores per (batch, head):
+ * floor(N * N * density_ppm / 10^6), computed exactly (128-bit intermediate);
+ * -1 for N < 0 or density_ppm outside [0, 10^6].  Host only. */
+int64_t bsa_route_budget(int32_t N, int32_t density_ppm);
 
 /* Step 4 (idea 1, parameter-free linear compensation): for a query q of
  * cluster a, one softmax over the exact keys of the kept clusters of route row
@@ -394,8 +402,9 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
  * token n = f * P + p.  Token (f, p), f >= 1, is kept iff
  *   sum_c |x[f, p, c] - x[f - 1, p, c]| > tau * D
  * (mean absolute difference to the same patch of the previous input frame
- * above tau), the sum taken in float64 from the bf16 values (exact for values
- * within a normal exponent range); frame 0 is always kept.  tau may be
+ * above tau), the differences and their sum taken in float64 from the bf16
+ * values (exact for values within a normal exponent range), compared with the
+ * float64 product of the float tau and D; frame 0 is always kept.  tau may be
  * negative (keep all) or +inf (keep frame 0 only); NaN is rejected.
  * The motion-detection refinement the page mentions is not specified there and
  * is not applied. */

@@ -18,7 +18,10 @@ Readings (the page gives neither a norm nor an order):
   |x[f, p] - x[f - 1, p]| against the adjacent *input* frame.  The token is kept
   iff that sum exceeds tau * D (its mean absolute difference exceeds tau).
   Frame 0 has no predecessor and is always kept.  For inputs that are exact in
-  bf16 the sum is exact in float64, so the decision has no rounding.
+  bf16 the differences and their sum are exact in float64, so the decision has
+  no rounding.
+* tau is a single-precision parameter: the threshold is its float32 value
+  times D, in float64.
 * The pruned sequence holds the kept rows in token order.
 * Restoration: a kept token takes its row of the pruned sequence; a pruned
   token (f, p) takes the restored row of (f - 1, p), i.e. the row of the latest
@@ -40,7 +43,7 @@ def keep_flags(x, frames: int, tau: float):
     keep = np.ones((frames, P), dtype=bool)
     if frames > 1:
         diff = np.abs(xf[1:] - xf[:-1]).sum(axis=2)
-        keep[1:] = diff > np.float64(tau) * D
+        keep[1:] = diff > float(np.float32(tau)) * D
     return keep.reshape(N)
 
 

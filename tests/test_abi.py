@@ -94,6 +94,8 @@ def test_attention_argument_checks(lib):
     assert _attn(lib, ptr=0) == 1
     assert _attn(lib, rp=0) == 1
     assert _attn(lib, scale=0.0) == 1
+    assert _attn(lib, scale=-0.125) == 1                        # a negative scale is rejected
+    assert _attn(lib, dtype=1, scale=-0.125) == 1
     assert _attn(lib, scale=float("inf")) == 1
     assert _attn(lib, scale=float("nan")) == 1
     assert b"bsa_block_sparse_attn_fwd" in lib.bsa_last_error()
@@ -153,9 +155,9 @@ def test_lipar_argument_checks(lib):
     assert lib.bsa_lipar_restore(p, 1, ctypes.byref(ok), 4, p, p, p, None) == 2   # fp32 not implemented
 
 
-def _mixed(lib, shape, r=0.5, block=128, ws=1 << 30, ptr=4096, mask=4096):
+def _mixed(lib, shape, r=0.5, block=128, ws=1 << 30, ptr=4096, mask=4096, scale=0.1):
     p, m = ctypes.c_void_p(ptr), ctypes.c_void_p(mask)
-    return lib.bsa_mixed_attn_fwd(p, p, p, p, 0, ctypes.byref(shape), m, m, None, block, ctypes.c_float(0.1),
+    return lib.bsa_mixed_attn_fwd(p, p, p, p, 0, ctypes.byref(shape), m, m, None, block, ctypes.c_float(scale),
                                   ctypes.c_float(r), ctypes.c_void_p(1 << 20), ws, None)
 
 
@@ -164,6 +166,7 @@ def test_mixed_attention_argument_checks(lib):
     assert _mixed(lib, ok, r=-0.1) == 1
     assert _mixed(lib, ok, r=1.5) == 1
     assert _mixed(lib, ok, r=float("nan")) == 1
+    assert _mixed(lib, ok, scale=-0.1) == 1
     assert _mixed(lib, _shape(B=1, H=2, N=1000, D=64)) == 2      # D = 128 only
     assert _mixed(lib, ok, block=32) == 2
     assert _mixed(lib, ok, mask=0) == 1                           # softmax term needs the mask
@@ -237,8 +240,21 @@ def test_attention_backward_argument_checks(lib):
     assert bwd(block=64) == 2
     assert bwd(dtype=1) == 2
     assert bwd(scale=float("inf")) == 1
+    assert bwd(scale=-0.1) == 1
     assert bwd(ws=16) == 4
     assert bwd(ptr=ctypes.c_void_p(4098)) == 1
     assert b"bsa_block_sparse_attn_bwd" in lib.bsa_last_error()
     assert lib.bsa_transpose_block_mask(p, p, 10, p, p, 99, None) == 3          # capacity < nb * nb
     assert lib.bsa_transpose_block_mask(p, p, 0, p, p, 99, None) == 1
+
+
+def test_route_budget_is_exact_up_to_the_largest_sequence(lib):
+    """floor(N * N * ppm / 10^6) with no overflow: N * N * ppm needs 82 bits at
+    N = 2^31 - 1 and ppm = 10^6 (the 64-bit product wrapped from N of about 3M)."""
+    for N in (0, 1, 32760, 196560, 3_037_000, 3_100_000, 7_800_000, 50_000_000, 2**31 - 1):
+        for ppm in (0, 1, 150_000, 999_999, 1_000_000):
+            assert lib.bsa_route_budget(N, ppm) == N * N * ppm // 1_000_000, (N, ppm)
+    assert lib.bsa_route_budget(32760, 150_000) == 160_982_640
+    assert lib.bsa_route_budget(-1, 10) == -1
+    assert lib.bsa_route_budget(10, 1_000_001) == -1
+    assert lib.bsa_route_budget(10, -1) == -1

@@ -110,3 +110,15 @@ def test_preallocated_outputs_reused(gpu_lib):
         assert torch.equal(outs[4][bh, : nk[bh]], fresh[4][bh, : nk[bh]])
     with pytest.raises(gpu_lib.BsaError):
         gpu_lib.lipar_prune(xs[1], F, 0.3, outputs=outs[:4] + (outs[4][:, :-1],))
+
+
+def test_threshold_fixtures(gpu_lib):
+    """The hand-derived cases at the threshold (a sum exactly at tau * D with far
+    apart exponents, and a sum between the float and double products of tau
+    and D): frame 1 is not kept, as the oracle's pins fix, and every output
+    equals the oracle's."""
+    from test_oracle_lipar import threshold_fixtures
+    for name, x, tau, kept in threshold_fixtures():
+        bits = gen.store(x.reshape(1, 1, 2, 8).astype(np.float32), "bf16")
+        keep, _ = _check(gpu_lib, bits, 2, tau)
+        assert keep[0].tolist() == [1, int(kept)], name

@@ -124,3 +124,44 @@ def test_brute_force_tiny(seed):
     bk, bkept, bout = _brute(x, F, tau)
     assert keep.tolist() == bk and idx.tolist() == bkept
     assert np.array_equal(ol.restore(y, keep, F), np.array(bout))
+
+
+def _bf16_exact(vals):
+    a = np.asarray(vals, np.float64)
+    assert np.array_equal(a.astype(np.float32).astype(np.float64), a)
+    b = a.astype(np.float32).view(np.uint32)
+    assert not (b & 0xFFFF).any(), "not a bf16 value"
+    return a
+
+
+def threshold_fixtures():
+    """Two hand-derived one-patch cases (D = 8, two frames), each with the keep
+    flag of frame 1 that the reading fixes:
+
+    * "sum at the threshold, far exponents": frame 0 = (2^-30, 0, ...), frame 1
+      = (1, 1, 2^-30, 0, ...), tau = 0.25.  Exactly, |1 - 2^-30| + 1 + 2^-30 = 2
+      = tau * D, so the token is not kept (kept needs > tau * D).  A difference
+      taken in float32 rounds 1 - 2^-30 to 1 and would keep it.
+    * "sum between the float and double thresholds": frame 0 = 0, frame 1 =
+      (204 * 2^-8, 204 * 2^-16, 204 * 2^-24, 7 * 2^-27, 0, ...), whose sum is
+      107374183 * 2^-27 = 0.8000000045 (each entry is a bf16 value), tau = 0.1.
+      float32(0.1) * 8 = 0.8000000119 >= the sum: not kept; the float64 value
+      of 0.1 would give 0.8 < the sum and keep it."""
+    a = np.zeros((2, 8))
+    a[0, 0] = 2.0 ** -30
+    a[1, :3] = [1.0, 1.0, 2.0 ** -30]
+    b = np.zeros((2, 8))
+    b[1, :4] = [204 * 2.0 ** -8, 204 * 2.0 ** -16, 204 * 2.0 ** -24, 7 * 2.0 ** -27]
+    assert b[1].sum() == 107374183 * 2.0 ** -27
+    return [("far exponents", _bf16_exact(a), 0.25, False), ("float tau", _bf16_exact(b), 0.1, False)]
+
+
+def test_threshold_fixtures():
+    for name, x, tau, kept in threshold_fixtures():
+        keep = ol.keep_flags(x, 2, tau)
+        assert keep[0] and keep[1] == kept, name
+    # the same cases just past the threshold are kept
+    _, x, _, _ = threshold_fixtures()[0]
+    assert ol.keep_flags(x, 2, float(np.nextafter(np.float32(0.25), np.float32(0))))[1]
+    _, x, _, _ = threshold_fixtures()[1]
+    assert ol.keep_flags(x, 2, float(np.nextafter(np.float32(0.1), np.float32(0))))[1]

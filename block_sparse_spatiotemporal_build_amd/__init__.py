@@ -52,6 +52,9 @@ _SIGNATURES = {
     "bsa_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                            _P, ctypes.c_size_t, _P]),
+    "bsa_linear_attn_fwd_noalloc": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
+                                                   _P]),
+    "bsa_linear_attn_noalloc_max_scratch": (ctypes.c_size_t, []),
     "bsa_causal_linear_attn_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape)]),
     "bsa_causal_linear_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P,
                                                   _P, _P, _P, ctypes.c_size_t, _P]),
@@ -300,6 +303,26 @@ def linear_attn_fwd(q, k, v, out=None, return_state: bool = False, workspace=Non
                                    ctypes.byref(shape), _ptr(S), _ptr(z), _ptr(workspace),
                                    workspace.numel(), _stream(q.device)),
            "bsa_linear_attn_fwd")
+    return (out, S, z) if return_state else out
+
+
+def linear_attn_fwd_noalloc(q, k, v, out=None, return_state: bool = False):
+    """linear_attn_fwd through the no-allocation entry point (the library's own
+    per-GPU scratch instead of a workspace); the caller still supplies out and,
+    with return_state, S and z are allocated here as ordinary outputs."""
+    lib = load()
+    _check_qkv(q, k, v)
+    shape = _shape_of(q)
+    if out is None:
+        out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
+    if out.stride() != q.stride() or out.dtype != q.dtype:
+        raise BsaError("out must have the layout and dtype of q")
+    B, H, N, D = q.shape
+    S = torch.empty((B, H, D, D), dtype=torch.float32, device=q.device) if return_state else None
+    z = torch.empty((B, H, D), dtype=torch.float32, device=q.device) if return_state else None
+    _check(lib.bsa_linear_attn_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _dtype_code(q),
+                                           ctypes.byref(shape), _ptr(S), _ptr(z), _stream(q.device)),
+           "bsa_linear_attn_fwd_noalloc")
     return (out, S, z) if return_state else out
 
 

@@ -181,10 +181,8 @@ size_t bsa_linear_attn_workspace(const bsa_shape* shape) {
   return linear_plan(*shape).total;
 }
 
-bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
-                               const bsa_shape* shape, float* S, float* z, void* workspace, size_t ws_bytes,
-                               void* stream) {
-  const char* fn = "bsa_linear_attn_fwd";
+static bsa_status check_linear(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                               const bsa_shape* shape, const char* fn) {
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_shape(shape, 2, fn);
   if (st != BSA_OK) return st;
@@ -194,12 +192,40 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
   if ((int64_t)shape->B * shape->H > 65535) return fail(BSA_ERR_ARG, "%s: B * H must be <= 65535", fn);
+  return BSA_OK;
+}
+
+bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                               const bsa_shape* shape, float* S, float* z, void* workspace, size_t ws_bytes,
+                               void* stream) {
+  const char* fn = "bsa_linear_attn_fwd";
+  bsa_status st = check_linear(q, k, v, o, dtype, shape, fn);
+  if (st != BSA_OK) return st;
   const size_t need = linear_plan(*shape).total;
   if (workspace == nullptr || ws_bytes < need || ((uintptr_t)workspace & 255u) != 0)
     return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required, got %zu", fn, need,
                 workspace ? ws_bytes : (size_t)0);
   g_err[0] = 0;
   return launch_linear_attn(q, k, v, o, *shape, S, z, workspace, (hipStream_t)stream);
+}
+
+size_t bsa_linear_attn_noalloc_max_scratch(void) { return kLinNoAllocBytes; }
+
+bsa_status bsa_linear_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                                       const bsa_shape* shape, float* S, float* z, void* stream) {
+  const char* fn = "bsa_linear_attn_fwd_noalloc";
+  bsa_status st = check_linear(q, k, v, o, dtype, shape, fn);
+  if (st != BSA_OK) return st;
+  const size_t need = linear_plan(*shape).total;
+  if (need > kLinNoAllocBytes)
+    return fail(BSA_ERR_UNSUPPORTED,
+                "%s: this shape needs %zu bytes of scratch, more than the %zu of the no-allocation call "
+                "(use bsa_linear_attn_fwd with a workspace)", fn, need, kLinNoAllocBytes);
+  void* ws = nullptr;
+  st = linear_noalloc_scratch(&ws);
+  if (st != BSA_OK) return st;
+  g_err[0] = 0;
+  return launch_linear_attn(q, k, v, o, *shape, S, z, ws, (hipStream_t)stream);
 }
 
 size_t bsa_causal_linear_attn_workspace(const bsa_shape* shape) {

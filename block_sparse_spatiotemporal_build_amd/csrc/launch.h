@@ -44,6 +44,13 @@ LinPlan linear_plan(const bsa_shape& s);
 bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void* o, const bsa_shape& s,
                               float* S, float* z, void* ws, hipStream_t stream, float mix_r = -1.f);
 
+// The scratch behind bsa_linear_attn_fwd_noalloc: a file-scope device array of
+// this many bytes in linear_attn.hip holding the workspace of linear_plan.
+constexpr size_t kLinNoAllocBytes = (size_t)40 << 20;
+// This device's address of that array (looked up once per device with
+// hipGetSymbolAddress; the array's name is not a device address in host code).
+bsa_status linear_noalloc_scratch(void** ptr);
+
 // causal (chunked) linear attention, head_dim 128: state partials over splits
 // of chunk_s tokens, an exclusive prefix at every f-th split, and the causal
 // walk over apply splits of chunk_a = f * chunk_s tokens

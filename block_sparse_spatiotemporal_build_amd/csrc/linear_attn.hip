@@ -22,6 +22,8 @@
 //            as the B operand straight from global memory (phi in fp32, then
 //            bf16), and the denominator phi(q).z in fp32 per lane.
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace bsa {
@@ -1023,6 +1025,46 @@ bsa_status launch_linear_attn(const void* q, const void* k, const void* v, void*
     return BSA_ERR_UNSUPPORTED;
   }
   return launch_ok("linear_attn_fwd") ? BSA_OK : BSA_ERR_HIP;
+}
+
+// ---- the no-allocation variant ---------------------------------------------
+// Workspace of bsa_linear_attn_fwd_noalloc (the linear_plan layout), held in a
+// file-scope device array: each GPU the library runs on holds its own copy
+// until the process ends, and every call on that GPU shares it.  Nothing in it
+// has to start at zero (every partial is written before it is read).  In host
+// code `scratch` names a host-side stand-in, not device memory: the device
+// address is looked up with hipGetSymbolAddress, once per device, with that
+// device current, and only that address is passed to the kernels.
+static __device__ __align__(256) unsigned char scratch[kLinNoAllocBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+bsa_status linear_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    set_error("bsa_linear_attn_fwd_noalloc: hipGetDevice failed: %s", hipGetErrorString(e));
+    return BSA_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    set_error("bsa_linear_attn_fwd_noalloc: device %d beyond the supported %d", dev, kMaxDevices);
+    return BSA_ERR_UNSUPPORTED;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("bsa_linear_attn_fwd_noalloc: hipGetSymbolAddress(scratch) failed on device %d: %s", dev,
+                hipGetErrorString(e));
+      return BSA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return BSA_OK;
 }
 
 CausalPlan causal_plan(const bsa_shape& s) {

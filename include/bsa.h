@@ -192,6 +192,26 @@ bsa_status bsa_linear_attn_fwd(const void* q, const void* k, const void* v, void
                                const bsa_shape* shape, float* S, float* z, void* workspace,
                                size_t ws_bytes, void* stream);
 
+/* bsa_linear_attn_fwd without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Same operation,
+ * arguments (minus the workspace), kernels and launch plan as
+ * bsa_linear_attn_fwd, so results are bitwise identical to it.  The scratch is
+ * a file-scope device array of bsa_linear_attn_noalloc_max_scratch() bytes
+ * (40 MiB) in the library, one per GPU, held until the process ends; its
+ * address is looked up once per device on the first call there (no
+ * hipMalloc, hipFree or allocating routine is called).  Every call on a GPU
+ * shares that GPU's array and it keeps the last call's contents, so calls
+ * that overlap on one GPU (concurrent streams or threads) race: serialise
+ * them.  A shape whose workspace (bsa_linear_attn_workspace) exceeds the
+ * array returns BSA_ERR_UNSUPPORTED before any launch (at D = 128 that is
+ * beyond about 220 (batch, head) pairs). */
+bsa_status bsa_linear_attn_fwd_noalloc(const void* q, const void* k, const void* v, void* o, bsa_dtype dtype,
+                                       const bsa_shape* shape, float* S, float* z, void* stream);
+
+/* Size in bytes of the scratch array of bsa_linear_attn_fwd_noalloc. */
+size_t bsa_linear_attn_noalloc_max_scratch(void);
+
 /* Workspace bytes required by bsa_causal_linear_attn_fwd for `shape` (0 if
  * the shape is invalid or not supported): the fp32 state partials of every
  * token split, B * H * splits * (D * D + D) * 4 bytes, splits being about

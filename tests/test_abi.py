@@ -258,3 +258,25 @@ def test_route_budget_is_exact_up_to_the_largest_sequence(lib):
     assert lib.bsa_route_budget(-1, 10) == -1
     assert lib.bsa_route_budget(10, 1_000_001) == -1
     assert lib.bsa_route_budget(10, -1) == -1
+
+
+def test_linear_no_alloc_argument_checks(lib):
+    """Validation of the no-allocation linear attention runs before any HIP call:
+    bad arguments and shapes whose workspace exceeds the library's scratch are
+    rejected with no device present."""
+    p = ctypes.c_void_p(4096)
+    assert lib.bsa_linear_attn_noalloc_max_scratch() == 40 << 20
+
+    def call(shape, dtype=0, ptr=p):
+        return lib.bsa_linear_attn_fwd_noalloc(ptr, p, p, p, dtype, ctypes.byref(shape), None, None, None)
+
+    big = _shape(B=1, H=600, N=1000, D=128)
+    assert lib.bsa_linear_attn_workspace(ctypes.byref(big)) > 40 << 20
+    assert call(big) == 2
+    assert b"scratch" in lib.bsa_last_error()
+    assert call(_shape(B=1, H=12, N=32760, D=96)) == 2           # D in {64, 128}
+    assert call(_shape(B=1, H=2, N=100, D=128), dtype=1) == 2
+    assert call(_shape(B=1, H=2, N=100, D=128), ptr=ctypes.c_void_p(4098)) == 1
+    assert call(_shape(B=1, H=2, N=0, D=128)) == 1
+    # the benchmark shape fits
+    assert lib.bsa_linear_attn_workspace(ctypes.byref(_shape(B=1, H=12, N=196560, D=128))) <= 40 << 20

@@ -849,15 +849,19 @@ def bench_svg(args, wl):
     t1 = time.perf_counter()
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
 
-    # per-step split through the step entry points (same kernels)
-    qc, kc, vc = bsa.cluster_centroids(q, k, v, qo, ko)
+    # per-step split through the step entry points, which run the fused call's
+    # kernels (query centroids; the probe, which also averages the key
+    # clusters, and the scores; the selection, whose call rebuilds the score
+    # histograms the fused call reuses; the compensated attention)
+    qc, _, _ = bsa.cluster_centroids(q, k, v, qo, ko, which="query")
+    sc, kc, vc = bsa.route_scores(k, v, qo, ko, qc, scale)
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
     split = []
     for _ in range(max(3, args.steps // 4)):
         marks[0].record()
-        bsa.cluster_centroids(q, k, v, qo, ko)
+        bsa.cluster_centroids(q, k, v, qo, ko, which="query")
         marks[1].record()
-        sc = bsa.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+        bsa.route_scores(k, v, qo, ko, qc, scale, k_cent=kc, v_cent=vc)
         marks[2].record()
         r2, c2 = bsa.route_select(sc, q, qo, ko, wl.density_ppm)
         marks[3].record()

@@ -80,7 +80,7 @@ _SIGNATURES = {
     "bsa_centroid_compensate_workspace": (ctypes.c_size_t, [ctypes.POINTER(Shape), ctypes.c_int32,
                                                             ctypes.c_int32]),
     "bsa_centroid_compensate": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
-                                               ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32,
+                                               ctypes.c_int32, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                                ctypes.c_float, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_mixed_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P, _P, _P,
                                           ctypes.c_int32, ctypes.c_float, ctypes.c_float, _P, ctypes.c_size_t,
@@ -441,23 +441,27 @@ def _check_offsets(q, q_off, k_off):
     return q_off.shape[1] - 1, k_off.shape[1] - 1
 
 
-def cluster_centroids(q, k, v, q_off, k_off):
-    """fp32 centroids (q_cent [B*H, Cq, D], k_cent, v_cent [B*H, Ck, D])."""
+def cluster_centroids(q, k, v, q_off, k_off, which: str = "all"):
+    """fp32 centroids (q_cent [B*H, Cq, D], k_cent, v_cent [B*H, Ck, D]); with
+    which="query" or "key" only that set is computed (the others are None)."""
     lib = load()
     _check_qkv(q, k, v)
     Cq, Ck = _check_offsets(q, q_off, k_off)
     B, H, N, D = q.shape
-    qc = torch.empty((B * H, Cq, D), dtype=torch.float32, device=q.device)
-    kc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device)
-    vc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device)
+    if which not in ("all", "query", "key"):
+        raise BsaError("which must be 'all', 'query' or 'key'")
+    qc = torch.empty((B * H, Cq, D), dtype=torch.float32, device=q.device) if which != "key" else None
+    kc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device) if which != "query" else None
+    vc = torch.empty((B * H, Ck, D), dtype=torch.float32, device=q.device) if which != "query" else None
     _check(lib.bsa_cluster_centroids(_ptr(q), _ptr(k), _ptr(v), _dtype_code(q), ctypes.byref(_shape_of(q)),
                                      _ptr(q_off), Cq, _ptr(k_off), Ck, _ptr(qc), _ptr(kc), _ptr(vc),
                                      _stream(q.device)), "bsa_cluster_centroids")
     return qc, kc, vc
 
 
-def route_scores(k, v, q_off, k_off, q_cent, k_cent, v_cent, scale=None):
-    """fp32 routing scores [B*H, Cq, Ck]."""
+def route_scores(k, v, q_off, k_off, q_cent, scale=None, k_cent=None, v_cent=None):
+    """fp32 routing scores [B*H, Cq, Ck] from the query centroids; returns
+    (score, k_cent, v_cent), the key / value centroids coming from the same pass."""
     lib = load()
     _check_qkv(k, k, v)
     Cq, Ck = _check_offsets(k, q_off, k_off)
@@ -465,13 +469,20 @@ def route_scores(k, v, q_off, k_off, q_cent, k_cent, v_cent, scale=None):
     shape = _shape_of(k)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     score = torch.empty((B * H, Cq, Ck), dtype=torch.float32, device=k.device)
+    if k_cent is None:
+        k_cent = torch.empty((B * H, Ck, D), dtype=torch.float32, device=k.device)
+    if v_cent is None:
+        v_cent = torch.empty((B * H, Ck, D), dtype=torch.float32, device=k.device)
+    for t, name in ((k_cent, "k_cent"), (v_cent, "v_cent")):
+        if t.dtype != torch.float32 or not t.is_contiguous() or t.numel() != B * H * Ck * D:
+            raise BsaError(f"{name} must be a contiguous float32 [B*H, Ck, D] tensor")
     ws = torch.empty(int(lib.bsa_route_scores_workspace(ctypes.byref(shape), Cq, Ck)), dtype=torch.uint8,
                      device=k.device)
     _check(lib.bsa_route_scores(_ptr(k), _ptr(v), _dtype_code(k), ctypes.byref(shape), _ptr(q_off), Cq,
-                                _ptr(k_off), Ck, _ptr(q_cent.contiguous()), _ptr(k_cent.contiguous()),
-                                _ptr(v_cent.contiguous()), float(scale), _ptr(score), _ptr(ws), ws.numel(),
-                                _stream(k.device)), "bsa_route_scores")
-    return score
+                                _ptr(k_off), Ck, _ptr(q_cent.contiguous()), _ptr(k_cent), _ptr(v_cent),
+                                float(scale), _ptr(score), _ptr(ws), ws.numel(), _stream(k.device)),
+           "bsa_route_scores")
+    return score, k_cent, v_cent
 
 
 def route_select(score, shape_like, q_off, k_off, density_ppm: int):
@@ -514,14 +525,18 @@ def compensated_attn_fwd(q, k, v, q_off, k_off, rrow, rcol, k_cent, v_cent, scal
 
 
 def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out=None, lse=None,
-                        return_score: bool = False, workspace=None, rrow=None, rcol=None, score=None):
-    """All four steps; returns (out, lse, route_row_ptr, route_col[, score])."""
+                        return_score: bool = False, workspace=None, rrow=None, rcol=None, score=None,
+                        use_given_route: bool = False):
+    """All four steps; returns (out, lse, route_row_ptr, route_col[, score]).
+    With use_given_route, rrow / rcol are the route to use (inputs)."""
     lib = load()
     _check_qkv(q, k, v)
     Cq, Ck = _check_offsets(q, q_off, k_off)
     B, H, N, D = q.shape
     shape = _shape_of(q)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
+    if use_given_route and (rrow is None or rcol is None):
+        raise BsaError("use_given_route needs rrow and rcol")
     if out is None:
         out = torch.empty_strided(q.shape, q.stride(), dtype=q.dtype, device=q.device)
     if lse is None:
@@ -537,8 +552,9 @@ def centroid_compensate(q, k, v, q_off, k_off, density_ppm: int, scale=None, out
                                 dtype=torch.uint8, device=q.device)
     _check(lib.bsa_centroid_compensate(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _dtype_code(q),
                                        ctypes.byref(shape), _ptr(q_off), Cq, _ptr(k_off), Ck, int(density_ppm),
-                                       float(scale), _ptr(rrow), _ptr(rcol), _ptr(score), _ptr(workspace),
-                                       workspace.numel(), _stream(q.device)), "bsa_centroid_compensate")
+                                       int(bool(use_given_route)), float(scale), _ptr(rrow), _ptr(rcol),
+                                       _ptr(score), _ptr(workspace), workspace.numel(), _stream(q.device)),
+           "bsa_centroid_compensate")
     return (out, lse, rrow, rcol, score) if return_score else (out, lse, rrow, rcol)
 
 

@@ -383,10 +383,15 @@ bsa_status bsa_cluster_centroids(const void* q, const void* k, const void* v, bs
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
   if (st != BSA_OK) return st;
-  if (!q || !k || !v || !q_cent || !k_cent || !v_cent) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return fail(BSA_ERR_ARG, "%s: q, k, v must be 16-byte aligned", fn);
+  const bool want_q = q_cent != nullptr, want_k = k_cent != nullptr || v_cent != nullptr;
+  if (!want_q && !want_k) return fail(BSA_ERR_ARG, "%s: no output requested", fn);
+  if (want_k && (!k_cent || !v_cent)) return fail(BSA_ERR_ARG, "%s: give both k_cent and v_cent or neither", fn);
+  if ((want_q && !q) || (want_k && (!k || !v))) return fail(BSA_ERR_ARG, "%s: NULL input", fn);
+  if ((want_q && !aligned16(q)) || (want_k && (!aligned16(k) || !aligned16(v))))
+    return fail(BSA_ERR_ARG, "%s: q, k, v must be 16-byte aligned", fn);
   g_err[0] = 0;
-  return launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, q_cent, k_cent, v_cent, (hipStream_t)stream);
+  const CentroidSet which = want_q && want_k ? kCentAll : (want_q ? kCentQuery : kCentKey);
+  return launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, q_cent, k_cent, v_cent, (hipStream_t)stream, which);
 }
 
 size_t bsa_route_scores_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
@@ -396,14 +401,15 @@ size_t bsa_route_scores_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck
 
 bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
                             const int32_t* q_off, int32_t Cq, const int32_t* k_off, int32_t Ck, const float* q_cent,
-                            const float* k_cent, const float* v_cent, float scale, float* score, void* workspace,
+                            float* k_cent, float* v_cent, float scale, float* score, void* workspace,
                             size_t ws_bytes, void* stream) {
   const char* fn = "bsa_route_scores";
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
   if (st != BSA_OK) return st;
   if (!k || !v || !q_cent || !k_cent || !v_cent || !score) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
-  if (!aligned16(k) || !aligned16(v) || !aligned16(v_cent)) return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
+  if (!aligned16(k) || !aligned16(v) || !aligned16(q_cent) || !aligned16(k_cent) || !aligned16(v_cent))
+    return fail(BSA_ERR_ARG, "%s: misaligned pointer", fn);
   if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
   const size_t need = probe_plan(*shape, Cq, Ck).total;
   if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u))
@@ -413,9 +419,10 @@ bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const
                              (hipStream_t)stream);
 }
 
+// selection workspace: the cost histograms of the scores
 size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
   if (check_shape(shape, 2, "bsa_route_select_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
-  return align256h((size_t)shape->B * shape->H * Cq * Ck);
+  return route_hist_bytes(*shape, Cq);
 }
 
 bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const int32_t* q_off, int32_t Cq,
@@ -427,10 +434,11 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
   if (!score || !route_row_ptr || !route_col) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
   if (density_ppm < 0 || density_ppm > 1000000) return fail(BSA_ERR_ARG, "%s: density_ppm must be in [0, 1e6]", fn);
   const size_t need = bsa_route_select_workspace(shape, Cq, Ck);
-  if (!workspace || ws_bytes < need) return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes required", fn, need);
+  if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u))
+    return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
   g_err[0] = 0;
   return launch_route_select(score, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
-                             route_col, (uint8_t*)workspace, (hipStream_t)stream);
+                             route_col, workspace, false, (hipStream_t)stream);
 }
 
 size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
@@ -461,9 +469,10 @@ bsa_status bsa_compensated_attn_fwd(const void* q, const void* k, const void* v,
                           scale, workspace, (hipStream_t)stream);
 }
 
-// fused call: workspace = centroids | scores | probe scratch | select flags
+// fused call: workspace = centroids | scores | probe scratch (with the cost
+// histograms) | compensated-attention workspace
 struct CompPlan {
-  size_t qc, kc, vc, sc, probe, flags, attn, total;
+  size_t qc, kc, vc, sc, probe, attn, total;
 };
 static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
   CompPlan p;
@@ -473,8 +482,7 @@ static CompPlan comp_plan(const bsa_shape& s, int Cq, int Ck) {
   p.vc = align256h(p.kc + bh * Ck * D * 4);
   p.sc = align256h(p.vc + bh * Ck * D * 4);
   p.probe = align256h(p.sc + bh * Cq * Ck * 4);
-  p.flags = align256h(p.probe + probe_plan(s, Cq, Ck).total);
-  p.attn = align256h(p.flags + bh * Cq * Ck);
+  p.attn = align256h(p.probe + probe_plan(s, Cq, Ck).total);
   p.total = align256h(p.attn + comp_attn_workspace(s, Cq, Ck));
   return p;
 }
@@ -486,8 +494,9 @@ size_t bsa_centroid_compensate_workspace(const bsa_shape* shape, int32_t Cq, int
 
 bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, void* o, float* lse, bsa_dtype dtype,
                                    const bsa_shape* shape, const int32_t* q_off, int32_t Cq, const int32_t* k_off,
-                                   int32_t Ck, int32_t density_ppm, float scale, int32_t* route_row_ptr,
-                                   int32_t* route_col, float* score, void* workspace, size_t ws_bytes, void* stream) {
+                                   int32_t Ck, int32_t density_ppm, int32_t use_given_route, float scale,
+                                   int32_t* route_row_ptr, int32_t* route_col, float* score, void* workspace,
+                                   size_t ws_bytes, void* stream) {
   const char* fn = "bsa_centroid_compensate";
   if (dtype != BSA_DT_BF16) return fail(BSA_ERR_UNSUPPORTED, "%s: only bf16 is implemented", fn);
   bsa_status st = check_clusters(shape, q_off, Cq, k_off, Ck, fn);
@@ -496,7 +505,9 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
   if (!q || !k || !v || !o || !route_row_ptr || !route_col) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o))
     return fail(BSA_ERR_ARG, "%s: q, k, v, o must be 16-byte aligned", fn);
-  if (density_ppm < 0 || density_ppm > 1000000) return fail(BSA_ERR_ARG, "%s: density_ppm must be in [0, 1e6]", fn);
+  if (use_given_route != 0 && use_given_route != 1) return fail(BSA_ERR_ARG, "%s: use_given_route must be 0 or 1", fn);
+  if (!use_given_route && (density_ppm < 0 || density_ppm > 1000000))
+    return fail(BSA_ERR_ARG, "%s: density_ppm must be in [0, 1e6]", fn);
   if (!__builtin_isfinite(scale) || scale <= 0.f) return fail(BSA_ERR_ARG, "%s: scale must be finite and > 0", fn);
   const CompPlan pl = comp_plan(*shape, Cq, Ck);
   if (!workspace || ws_bytes < pl.total || ((uintptr_t)workspace & 255u))
@@ -506,17 +517,30 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
   float* qc = (float*)(w + pl.qc);
   float* kc = (float*)(w + pl.kc);
   float* vc = (float*)(w + pl.vc);
-  float* sc = score ? score : (float*)(w + pl.sc);
   hipStream_t sm = (hipStream_t)stream;
-  st = launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, sm);
+  if (use_given_route) {
+    // the route is an input: centroids, then the compensated attention
+    st = launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, sm, kCentAll);
+    if (st != BSA_OK) return st;
+    return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale,
+                            w + pl.attn, sm);
+  }
+  float* sc = score ? score : (float*)(w + pl.sc);
+  uint16_t *kb = nullptr, *vb = nullptr;
+  comp_attn_bf16_slots(*shape, Cq, Ck, w + pl.attn, &kb, &vb);
+  const ProbePlan pp = probe_plan(*shape, Cq, Ck);
+  const bool bf16_ready = pp.fused && kb != nullptr;
+  // query centroids, then one pass over K and V for the key centroids and the scores
+  st = launch_centroids(q, k, v, *shape, q_off, Cq, k_off, Ck, qc, nullptr, nullptr, sm, kCentQuery);
   if (st != BSA_OK) return st;
-  st = launch_route_scores(k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, scale, sc, w + pl.probe, sm);
+  st = launch_route_scores(k, v, *shape, q_off, Cq, k_off, Ck, qc, kc, vc, scale, sc, w + pl.probe, sm,
+                           bf16_ready ? kb : nullptr, bf16_ready ? vb : nullptr);
   if (st != BSA_OK) return st;
   st = launch_route_select(sc, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
-                           route_col, (uint8_t*)(w + pl.flags), sm);
+                           route_col, w + pl.probe + pp.off_hist, true, sm);
   if (st != BSA_OK) return st;
   return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale,
-                          w + pl.attn, sm);
+                          w + pl.attn, sm, bf16_ready);
 }
 
 // ---- latent inter-frame pruning (LIPAR) ----------------------------------

@@ -78,26 +78,41 @@ bsa_status launch_rows_permute(const void* src, const bsa_shape& s, int elem_byt
 // ---- centroid compensation with error-aware routing ------------------------
 struct ProbePlan {
   int splits, cps;  // key-cluster splits per head and clusters per split
-  bool d128;        // head_dim 128 probe (buffer-load staging, logits precomputed)
-  size_t off_e, off_m, off_ms, off_zs, off_lc, total;  // workspace layout (bytes)
+  bool fused;       // head_dim 128: key centroids, logits and errors in one pass over K and V
+  size_t off_e, off_m, off_ms, off_zs, off_hist, total;  // workspace layout (bytes)
 };
 ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck);
+// which clusters launch_centroids averages: all, the query clusters, the key clusters
+enum CentroidSet { kCentAll = 0, kCentQuery = 1, kCentKey = 2 };
 bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,
                             int Cq, const int32_t* k_off, int Ck, float* qc, float* kc, float* vc,
-                            hipStream_t stream);
+                            hipStream_t stream, CentroidSet which = kCentAll);
+// scores from the query centroids qc; writes the key / value centroids kc, vc
+// (and their bf16 copies when kc_bf, vc_bf are given, fused path only) and
+// the scores' cost histograms (at off_hist of the workspace, the start of the
+// selection scratch)
 bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s, const int32_t* q_off, int Cq,
-                               const int32_t* k_off, int Ck, const float* qc, const float* kc, const float* vc,
-                               float scale, float* score, void* ws, hipStream_t stream);
+                               const int32_t* k_off, int Ck, const float* qc, float* kc, float* vc, float scale,
+                               float* score, void* ws, hipStream_t stream, uint16_t* kc_bf = nullptr,
+                               uint16_t* vc_bf = nullptr);
+// bytes of the selection scratch (the scores' cost histograms first, then the
+// per-head selection state, the cut-bin keys and the per-row kept counts)
+size_t route_hist_bytes(const bsa_shape& s, int Cq);
+// hist_ready: the histograms of `score` are already at the start of
+// `scratch` (launch_route_scores writes them there)
 bsa_status launch_route_select(const float* score, const bsa_shape& s, const int32_t* q_off, int Cq,
                                const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
-                               uint8_t* flags, hipStream_t stream);
+                               void* scratch, bool hist_ready, hipStream_t stream);
 // compensated attention workspace: bf16 copies of the key / value centroids
-// for the head_dim-128 kernel (0 bytes otherwise)
+// and the tile schedule of the head_dim-128 kernel (0 bytes otherwise)
 size_t comp_attn_workspace(const bsa_shape& s, int Cq, int Ck);
+// the bf16 centroid slots in that workspace (null when it has none)
+void comp_attn_bf16_slots(const bsa_shape& s, int Cq, int Ck, void* ws, uint16_t** kb, uint16_t** vb);
+// bf16_ready: the bf16 centroid copies are already in the workspace
 bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
                             const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
                             const int32_t* rcol, const float* kc, const float* vc, float scale, void* ws,
-                            hipStream_t stream);
+                            hipStream_t stream, bool bf16_ready = false);
 
 bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, float tau, uint8_t* keep,
                               int32_t* cpos, int32_t* kept_idx, int32_t* n_kept, void* x_pruned,

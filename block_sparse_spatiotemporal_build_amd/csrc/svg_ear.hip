@@ -53,11 +53,16 @@ __device__ __forceinline__ const uint16_t* head_ptr(const uint16_t* base, const 
 // centroids
 // ---------------------------------------------------------------------------
 
+// Workgroup (c0 + blockIdx.x, bh): query cluster c < Cq, else key cluster
+// c - Cq (whose key and value means it takes together).  Four rows per
+// thread are loaded before they are summed, so each thread keeps four loads in
+// flight.
 template <int D>
-__global__ void __launch_bounds__(256) centroid_kernel(SvgArgs a, float* q_cent, float* k_cent, float* v_cent) {
-  constexpr int CH = D / 8, RS = 256 / CH;
+__global__ void __launch_bounds__(256) centroid_kernel(SvgArgs a, float* q_cent, float* k_cent, float* v_cent,
+                                                       int c0) {
+  constexpr int CH = D / 8, RS = 256 / CH, U = 4;
   __shared__ float red[2][RS][D];
-  const int bh = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int bh = blockIdx.y, c = c0 + blockIdx.x, tid = threadIdx.x;
   const bool is_q = c < a.Cq;
   const int idx = is_q ? c : c - a.Cq;
   const int32_t* off = is_q ? a.q_off + (int64_t)bh * (a.Cq + 1) : a.k_off + (int64_t)bh * (a.Ck + 1);
@@ -68,21 +73,23 @@ __global__ void __launch_bounds__(256) centroid_kernel(SvgArgs a, float* q_cent,
   float s1[8], s2[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) s1[e] = s2[e] = 0.f;
-  for (int r = r0 + rg; r < r1; r += RS) {
-    const u32x4 x = *(const u32x4*)(X + (int64_t)r * a.sn + cc * 8);
+  for (int r = r0 + rg; r < r1; r += U * RS) {
+    u32x4 x[U], y[U];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      s1[2 * w] += bf16_lo(x[w]);
-      s1[2 * w + 1] += bf16_hi(x[w]);
+    for (int u = 0; u < U; ++u) {
+      const int rr = r + u * RS;
+      x[u] = rr < r1 ? *(const u32x4*)(X + (int64_t)rr * a.sn + cc * 8) : u32x4{0, 0, 0, 0};
+      y[u] = (!is_q && rr < r1) ? *(const u32x4*)(V + (int64_t)rr * a.sn + cc * 8) : u32x4{0, 0, 0, 0};
     }
-    if (!is_q) {
-      const u32x4 y = *(const u32x4*)(V + (int64_t)r * a.sn + cc * 8);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        s2[2 * w] += bf16_lo(y[w]);
-        s2[2 * w + 1] += bf16_hi(y[w]);
+        s1[2 * w] += bf16_lo(x[u][w]);
+        s1[2 * w + 1] += bf16_hi(x[u][w]);
+        s2[2 * w] += bf16_lo(y[u][w]);
+        s2[2 * w + 1] += bf16_hi(y[u][w]);
       }
-    }
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
@@ -118,7 +125,6 @@ struct ProbeArgs {
   const float* q_cent;
   const float* k_cent;
   const float* v_cent;
-  const float* lc;  // [BH][Ck][Cq] proxy-centroid logits (log2 units), head_dim 128 path
   float* e_buf;     // [BH][Cq][Ck]  squared error norm at the recorded max
   float* m_buf;     // [BH][Cq][Ck]  the max (log2 units) it was taken at
   float* m_split;   // [BH][splits][Cq]
@@ -339,79 +345,60 @@ __global__ void __launch_bounds__(256) probe_kernel(ProbeArgs p) {
   }
 }
 
-// Proxy-centroid logits lc[b][a] = s log2(e) c^_a . c_b in fp32, with c^_a
-// taken as the same bf16 hi + lo pair the probe multiplies the keys with, so
-// that the centroid weight and the key weights of the difference form share
-// one proxy.  A workgroup covers 16 proxies x 64 key clusters; thread
-// (a = tid / 16, tx = tid % 16) computes the clusters tx, tx + 16, tx + 32,
-// tx + 48 with float4 reads (row stride D + 4 floats: conflict-free).
-template <int D>
-__global__ void __launch_bounds__(256) proxy_logit_kernel(const float* q_cent, const float* k_cent, float* lc,
-                                                          int Cq, int Ck, float c2) {
-  constexpr int ST = D + 4;
-  __shared__ __attribute__((aligned(16))) float qs[16][ST];
-  __shared__ __attribute__((aligned(16))) float ks[64][ST];
-  const int bh = blockIdx.z, a0 = blockIdx.y * 16, b0 = blockIdx.x * 64, tid = threadIdx.x;
-  for (int i = tid; i < 16 * D / 4; i += 256) {
-    const int r = i / (D / 4), d = (i % (D / 4)) * 4;
-    const int a = a0 + r;
-    float4 x = {0.f, 0.f, 0.f, 0.f};
-    if (a < Cq) x = *(const float4*)&q_cent[((int64_t)bh * Cq + a) * D + d];
-    float4 y;
-    float* xs = &x.x;
-    float* ys = &y.x;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float h = bf16_lo(pack_bf16x2(xs[e], 0.f));
-      ys[e] = h + bf16_lo(pack_bf16x2(xs[e] - h, 0.f));
-    }
-    *(float4*)&qs[r][d] = y;
-  }
-  for (int i = tid; i < 64 * D / 4; i += 256) {
-    const int r = i / (D / 4), d = (i % (D / 4)) * 4;
-    const int bb = b0 + r;
-    float4 x = {0.f, 0.f, 0.f, 0.f};
-    if (bb < Ck) x = *(const float4*)&k_cent[((int64_t)bh * Ck + bb) * D + d];
-    *(float4*)&ks[r][d] = x;
-  }
-  __syncthreads();
-  const int ty = tid >> 4, tx = tid & 15;
-  float dot[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-  for (int d = 0; d < D; d += 4) {
-    const float4 q = *(const float4*)&qs[ty][d];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float4 k = *(const float4*)&ks[tx + 16 * j][d];
-      dot[j] = __builtin_fmaf(q.x, k.x, dot[j]);
-      dot[j] = __builtin_fmaf(q.y, k.y, dot[j]);
-      dot[j] = __builtin_fmaf(q.z, k.z, dot[j]);
-      dot[j] = __builtin_fmaf(q.w, k.w, dot[j]);
-    }
-  }
-  const int a = a0 + ty;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int bb = b0 + tx + 16 * j;
-    if (a < Cq && bb < Ck) lc[((int64_t)bh * Ck + bb) * Cq + a] = dot[j] * c2;
-  }
+// ---------------------------------------------------------------------------
+// fused route probe, head_dim 128
+// ---------------------------------------------------------------------------
+// One pass over the keys of a split of key clusters (split s covers clusters
+// [s cps, min((s + 1) cps, Ck)), their keys packed into 32-key tiles across
+// cluster boundaries, so a small cluster costs no padded tile).  Per tile:
+//   S^T = K (c^_hi + c^_lo)^T for the workgroup's 128 proxies (4 waves x 32),
+//   one lazily moved reference m_run and a sum l_run per proxy over every key
+//   of the split (the proxy softmax of idea 2), and for each cluster segment:
+//     U  += V_seg^T P_seg   (P = exp2(t - m_run) as bf16 hi + lo, t = c2 s)
+//     sv += column sums of V_seg, sk += column sums of K_seg (v_dot2 with a
+//           0/1 mask over the transposed LDS reads)
+//     ls += sum of t over the segment's keys.
+// When cluster b (n_b keys) ends:
+//   lc = ls / n_b = c2 c^ . c_b   (the mean logit is the logit of the mean key)
+//   e  = U - exp2(lc - m_run) sv  = sum_j (p_j - p_c) v_j,  e2 = |e|^2
+// at reference m_run.  So the key and value centroids come out of the same
+// pass (c_b = sk / n_b, vbar_b = sv / n_b) and K and V are read once.  Two LDS
+// stages, one tile copy in flight: each step waits for every vector memory
+// operation of the wave (the tile copy and the stores of the clusters that
+// ended in the step before), so result stores need no separate tracking.
+constexpr int kFpTK = 32, kFpMaxCps = 16;
+
+// acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2_f32_bf16).
+// Written as inline asm because the compiler builtin, fed 32-bit elements of a
+// vector register tuple, read the tuple's first element for every element.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  float d;
+  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
+  return d;
 }
 
-// head_dim 128 probe: same computation as probe_kernel, with K/V staged by
-// buffer loads straight to LDS (two swizzled stages as separate LDS objects,
-// loop unrolled by two), the bf16 lo halves of the proxies in LDS instead of
-// registers, the split's cluster offsets and proxy-centroid logits in LDS.
-// This keeps two waves per SIMD, so one wave's softmax overlaps the other's
-// MFMAs and the copies overlap both.
-constexpr int kPrMaxCps = 16;  // clusters per split (the plan keeps cps <= this)
+struct FusedProbeArgs {
+  SvgArgs s;
+  const float* q_cent;  // [BH][Cq][D]
+  float* e_buf;         // [BH][Cq][Ck]
+  float* m_buf;         // [BH][Cq][Ck]
+  float* m_split;       // [BH][splits][Cq]
+  float* z_split;       // [BH][splits][Cq]
+  float* k_cent;        // [BH][Ck][D] output
+  float* v_cent;        // [BH][Ck][D] output
+  uint16_t* kc_bf;      // [BH][Ck][D] bf16 copy (nullable)
+  uint16_t* vc_bf;      // [BH][Ck][D] bf16 copy (nullable)
+  int splits, cps;
+  float c2;  // scale * log2(e)
+};
 
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) probe_d128_kernel(ProbeArgs p) {
-  constexpr int D = 128, KT = 8, DT = 4, TILE = kPrBN * D;
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+probe_fused_d128_kernel(FusedProbeArgs p) {
+  constexpr int D = 128, KT = 8, DT = 4, TILE = kFpTK * D;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t CL[128 * D];  // proxy lo halves, rows swizzled (swz_k)
-  __shared__ float lcs[kPrMaxCps][128];
-  __shared__ int koffs[kPrMaxCps + 1];
+  __shared__ int koffs[kFpMaxCps + 1];
 
   const SvgArgs& a = p.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -419,22 +406,27 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
   const int prow = wave * 32 + l32;
   const int prox = blockIdx.z * 128 + prow;  // proxy (query cluster) of this lane
   const bool pvalid = prox < a.Cq;
+  const bool write_cent = blockIdx.z == 0;
   const int32_t* koff_g = a.k_off + (int64_t)bh * (a.Ck + 1);
   const uint16_t* Kh = head_ptr(a.k, a, bh);
   const uint16_t* Vh = head_ptr(a.v, a, bh);
-  const int b0 = split * p.cps, b1 = min(b0 + p.cps, a.Ck), nclu = b1 - b0;
+  const int b0 = split * p.cps, nclu = min(b0 + p.cps, a.Ck) - b0;
 
-  // proxy fragments: c^ = hi + lo (bf16 each); hi is the MFMA B operand in
-  // registers, lo is read from LDS per tile
+  // proxy fragments: c^ = hi + lo, both bf16 (about 2^-16 relative), so the
+  // logits keep the small spread of a tight cluster; hi is the MFMA B operand
+  // in registers, lo is read from LDS per tile
   bf16x8 cf[KT];
   {
+    // invalid proxies read proxy 0 (in bounds) and use zeros
     const float* src = p.q_cent + ((int64_t)bh * a.Cq + (pvalid ? prox : 0)) * D + hi * 8;
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
+      const f32x4 y0 = *(const f32x4*)&src[t * 16], y1 = *(const f32x4*)&src[t * 16 + 4];
+      const float yv[8] = {y0[0], y0[1], y0[2], y0[3], y1[0], y1[1], y1[2], y1[3]};
       u32x4 wh, wl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = pvalid ? src[t * 16 + 2 * e] : 0.f, x1 = pvalid ? src[t * 16 + 2 * e + 1] : 0.f;
+        const float x0 = pvalid ? yv[2 * e] : 0.f, x1 = pvalid ? yv[2 * e + 1] : 0.f;
         wh[e] = pack_bf16x2(x0, x1);
         wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
       }
@@ -443,99 +435,161 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
     }
   }
   for (int i = tid; i <= nclu; i += 256) koffs[i] = koff_g[b0 + i];
-  for (int i = wave; i < nclu; i += 4)
-    for (int j = lane; j < 128; j += 64) {
-      const int px = blockIdx.z * 128 + j;
-      lcs[i][j] = px < a.Cq ? p.lc[((int64_t)bh * a.Ck + b0 + i) * a.Cq + px] : 0.f;
-    }
   __syncthreads();
   retire_loads();
+  const int K0k = koffs[0], K1k = koffs[nclu];
+  const int ntiles = (K1k - K0k + kFpTK - 1) / kFpTK;
 
-  auto ntiles_of = [&](int i) { return (koffs[i + 1] - koffs[i] + kPrBN - 1) / kPrBN; };
-  int total = 0;
-  for (int i = 0; i < nclu; ++i) total += ntiles_of(i);
-
-  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane/16
+  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane / 16
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, 0x7fffffff, kBufferWord3);
-  uint32_t koff[2], voff[2];
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int u) {
+    const int key0 = K0k + u * kFpTK;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = 8 * wv + 4 * j + (lane >> 4);
-    koff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16);
-    voff[j] = (uint32_t)row * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
-  }
-  auto dma = [&](uint16_t* kst, uint16_t* vst, int key0, int kend) {
-    if (key0 + kPrBN <= kend) {
-      const uint32_t so = (uint32_t)key0 * row_bytes;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16, koff[j], so, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16, voff[j], so, 0, 0);
-      }
-    } else {  // last tile of a cluster: rows past its end are clamped to its last key (masked below)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = 8 * wv + 4 * j + (lane >> 4);
-        const uint32_t ro = (uint32_t)min(key0 + row, kend - 1) * row_bytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16,
-                                                 ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16,
-                                                 ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
-      }
+    for (int j = 0; j < 2; ++j) {
+      const int row = 8 * wv + 4 * j + (lane >> 4);
+      // rows past the split's last key repeat it (masked out below)
+      const uint32_t ro = (uint32_t)min(key0 + row, K1k - 1) * row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16,
+                                               ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16,
+                                               ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
     }
   };
 
   f32x16 U[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) U[i] = f32x16{};
-  float m_run = -1e30f, l_run = 0.f, lc2 = 0.f;
+  float sv[DT] = {0.f, 0.f, 0.f, 0.f}, sk = 0.f, ls = 0.f;
+  float m_run = -1e30f, l_run = 0.f;
   const int g16 = lane >> 4, j16 = lane & 15;
+  // per-lane LDS element offsets; each read is base ^ immediate (or + one
+  // delta), the identities are checked for every lane on the host:
+  //   K row fragment of k-step t: kb0 ^ 16 t; proxy lo fragment: cb0 ^ 16 t;
+  //   V transposed reads (ks, dt): 2048 ks + (va0 ^ 32 dt) and + vd0;
+  //   K transposed reads (column sums of this wave's 32 dims): 2048 ks + kt0 / kt1
+  const int q4 = j16 >> 2, c0 = 2 * (g16 & 1) + ((j16 >> 1) & 1), half4 = (j16 & 1) * 4;
+  const uint32_t kb0 = l32 * D + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1));
+  const uint32_t cb0 = prow * D + 16 * ((prow & 15) >> 1) + 8 * (hi ^ (prow & 1));
+  const uint32_t va0 = (4 * hi + q4) * D + 32 * q4 + 8 * (c0 ^ hi) + half4;
+  const uint32_t vd0 = 1024 + 8 * (((c0 ^ hi) ^ 2) - (c0 ^ hi));
+  const uint32_t kt0_ = (4 * hi + q4) * D + 8 * (4 * (wave ^ hi) + (c0 ^ q4)) + half4;
+  const uint32_t kt1_ = 1024 + (4 * hi + q4) * D + 8 * (4 * ((wave ^ hi) ^ 2) + (c0 ^ q4)) + half4;
 
-  // walk state: cluster (local index) and sub-tile of the tile being computed,
-  // and the prefetch cursor one tile ahead
-  int cb = 0, cst = 0;
-  while (cb < nclu && ntiles_of(cb) == 0) ++cb;
-  int fb = cb, fst = 0;
-  auto advance = [&](int& bb, int& st) {
-    ++st;
-    if (st >= ntiles_of(bb)) {
-      st = 0;
-      ++bb;
-      while (bb < nclu && ntiles_of(bb) == 0) ++bb;
+  // cluster c (local index) is complete: its error and its centroids.  The
+  // correction U -= sv (x) p_c is one MFMA per 32 dims: A holds sv of the
+  // lane's row (dim 32 dt + lane % 32) and B holds -p_c of its column (the
+  // proxy), each split into three bf16 pieces (24 bits; each of the nine
+  // products is exact in fp32), so e = U - p_c sv keeps fp32 accuracy and
+  // |e|^2 is a lane-local sum.
+  auto split3 = [](float x, float (&o)[3]) {
+    o[0] = bf16_lo(f2bf(x));
+    o[1] = bf16_lo(f2bf(x - o[0]));
+    o[2] = bf16_lo(f2bf(x - o[0] - o[1]));
+  };
+  auto finish = [&](int c) {
+    const int nb = koffs[c + 1] - koffs[c];
+    const int bg = b0 + c;
+    float svf[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) svf[dt] = pair_sum(sv[dt]);
+    const float skf = pair_sum(sk);
+    float e2 = 0.f;
+    if (nb > 0) {
+      const float lc = pair_sum(ls) / (float)nb;
+      float b3[3];
+      split3(-fast_exp2(lc - m_run), b3);
+      // k slots 0..8: (h,h) (h,m) (h,l) (m,h) (m,m) (m,l) (l,h) (l,m) (l,l);
+      // lanes 0..31 hold slots 0..7, lanes 32..63 slots 8..15
+      uint32_t bw[4];
+      if (hi == 0) {
+        bw[0] = pack_bf16x2(b3[0], b3[1]);
+        bw[1] = pack_bf16x2(b3[2], b3[0]);
+        bw[2] = pack_bf16x2(b3[1], b3[2]);
+        bw[3] = pack_bf16x2(b3[0], b3[1]);
+      } else {
+        bw[0] = pack_bf16x2(b3[2], 0.f);
+        bw[1] = bw[2] = bw[3] = 0u;
+      }
+      const bf16x8 bf = __builtin_bit_cast(bf16x8, (u32x4){bw[0], bw[1], bw[2], bw[3]});
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        float a3[3];
+        split3(svf[dt], a3);
+        uint32_t aw[4];
+        if (hi == 0) {
+          aw[0] = pack_bf16x2(a3[0], a3[0]);
+          aw[1] = pack_bf16x2(a3[0], a3[1]);
+          aw[2] = pack_bf16x2(a3[1], a3[1]);
+          aw[3] = pack_bf16x2(a3[2], a3[2]);
+        } else {
+          aw[0] = pack_bf16x2(a3[2], 0.f);
+          aw[1] = aw[2] = aw[3] = 0u;
+        }
+        const bf16x8 af = __builtin_bit_cast(bf16x8, (u32x4){aw[0], aw[1], aw[2], aw[3]});
+        U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, bf, U[dt], 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e2 = __builtin_fmaf(U[dt][r], U[dt][r], e2);
+      }
+      e2 = pair_sum(e2);
     }
+    if (pvalid && hi == 0) {
+      const int64_t o = ((int64_t)bh * a.Cq + prox) * a.Ck + bg;
+      p.e_buf[o] = e2;
+      p.m_buf[o] = nb > 0 ? m_run : -1e30f;
+    }
+    if (write_cent && lane < 32) {
+      const float inv = nb > 0 ? 1.f / (float)nb : 0.f;
+      const int64_t o = ((int64_t)bh * a.Ck + bg) * D;
+      const float kc = skf * inv;
+      p.k_cent[o + 32 * wave + lane] = kc;
+      if (p.kc_bf) p.kc_bf[o + 32 * wave + lane] = (uint16_t)f2bf(kc);
+      if (wave == 0)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const float vc = svf[dt] * inv;
+          p.v_cent[o + 32 * dt + lane] = vc;
+          if (p.vc_bf) p.vc_bf[o + 32 * dt + lane] = (uint16_t)f2bf(vc);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < DT; ++i) U[i] = f32x16{};
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) sv[dt] = 0.f;
+    sk = 0.f;
+    ls = 0.f;
   };
 
+  // the cluster being accumulated; leading empty clusters finish at once
+  int cb = 0;
+  while (cb < nclu && koffs[cb + 1] == koffs[cb]) finish(cb++);
+
   auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): tile u landed, other stage drained
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): tile u landed, earlier stores done
     __builtin_amdgcn_s_barrier();
-    if (u + 1 < total) {
-      dma(Kn, Vn, koffs[fb] + fst * kPrBN, koffs[fb + 1]);
-      advance(fb, fst);
-    }
-    const int kend = koffs[cb + 1];
-    const int key0 = koffs[cb] + cst * kPrBN;
-    if (cst == 0) {
-#pragma unroll
-      for (int i = 0; i < DT; ++i) U[i] = f32x16{};
-      lc2 = lcs[cb][prow];
-    }
+    if (u + 1 < ntiles) dma(Kn, Vn, u + 1);
+    const int key0 = K0k + u * kFpTK;
+    const int nval = min(kFpTK, K1k - key0);
+    // the bases are opaque here, so the XORed offsets are formed next to their
+    // reads instead of being held across the loop
+    uint32_t kb = kb0, clb = cb0, va = va0, vd = vd0, kt0 = kt0_, kt1 = kt1_;
+    asm volatile("" : "+v"(kb), "+v"(clb), "+v"(va), "+v"(vd), "+v"(kt0), "+v"(kt1));
     // S^T (32 keys x 32 proxies) = K (c_hi + c_lo)^T
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const bf16x8 kf = *(const bf16x8*)&Kb[l32 * D + (((2 * t + hi) ^ swz_k(l32)) << 3)];
-      const bf16x8 cl = *(const bf16x8*)&CL[prow * D + (((2 * t + hi) ^ swz_k(prow)) << 3)];
+      const bf16x8 kf = *(const bf16x8*)&Kb[kb ^ (16 * t)];
+      const bf16x8 clo = *(const bf16x8*)&CL[clb ^ (16 * t)];
       s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, cf[t], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, cl, s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, clo, s, 0, 0, 0);
     }
-    if (key0 + kPrBN > kend) {  // key of s[r]: key0 + 8 (r / 4) + 4 hi + r % 4
-      const int lim = kend - key0 - 4 * hi;
+    // key row of s[r]: 8 (r / 4) + 4 hi + r % 4
+    if (nval < kFpTK) {
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -__builtin_inff();
+        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nval) s[r] = -__builtin_inff();
     }
     float mx = s[0];
 #pragma unroll
@@ -548,126 +602,80 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))
       for (int i = 0; i < DT; ++i) U[i] *= alpha;
       m_run = m_new;
     }
-    // U accumulates sum_j (p_j - p_c) v_j (the difference form)
-    const float pc = fast_exp2(lc2 - m_run);
-    float psum = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float pr = fast_exp2(__builtin_fmaf(s[r], p.c2, -m_run));
-      psum += pr;
-      s[r] = (s[r] == -__builtin_inff()) ? 0.f : pr - pc;
-    }
-    l_run += psum;
-    // P' = hi + lo (bf16 each)
-    bf16x8 pf[2], pl[2];
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      u32x4 wh, wl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float x0 = s[8 * ks + 2 * e], x1 = s[8 * ks + 2 * e + 1];
-        wh[e] = pack_bf16x2(x0, x1);
-        wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
-      }
-      pf[ks] = __builtin_bit_cast(bf16x8, wh);
-      pl[ks] = __builtin_bit_cast(bf16x8, wl);
-    }
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
-        const int lcn = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-        const int half = (j16 & 1) * 4;
-        const u32x2 lo = lds_tr16(&Vb[r0 * D + ((lcn ^ swz_v(r0)) << 3) + half]);
-        const u32x2 h2 = lds_tr16(&Vb[r1 * D + ((lcn ^ swz_v(r1)) << 3) + half]);
-        const u32x4 w = {lo[0], lo[1], h2[0], h2[1]};
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-        U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[ks], U[dt], 0, 0, 0);
-        U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pl[ks], U[dt], 0, 0, 0);
-      }
+    for (int r = 0; r < 16; ++r) s[r] *= p.c2;  // logit t in log2 units (-inf on rows past the split)
 
-    if (cst + 1 == ntiles_of(cb)) {
-      // cluster finished: squared norm of the accumulated error (at reference m_run)
-      float e2 = 0.f;
+    // cluster segments of the tile: P = exp2(t - m_run) of the segment's keys
+    // (bf16 hi + lo, the B operand of V^T P), built per key half
+    int lo = 0;
+    while (lo < nval && cb < nclu) {
+      const int hi_end = min(koffs[cb + 1] - key0, nval);
+      if (hi_end <= lo) break;  // offsets not ascending: stop rather than loop
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
+      for (int ks = 0; ks < 2; ++ks) {
+        if (lo >= 16 * ks + 16 || hi_end <= 16 * ks) continue;
+        // this lane's 8 keys of half ks: 16 ks + 4 hi + (e & 3) + 8 (e >> 2)
+        uint32_t mw[4];
+        u32x4 wh, wl;
+        float lsum = 0.f, psum = 0.f;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e2 = __builtin_fmaf(U[dt][r], U[dt][r], e2);
-      e2 = pair_sum(e2);
-      if (pvalid && hi == 0) {
-        const int64_t o = ((int64_t)bh * a.Cq + prox) * a.Ck + b0 + cb;
-        p.e_buf[o] = e2;
-        p.m_buf[o] = m_run;
+        for (int e = 0; e < 4; ++e) {
+          const int k0 = 16 * ks + 4 * hi + ((2 * e) & 3) + 8 * ((2 * e) >> 2);
+          const bool in0 = k0 >= lo && k0 < hi_end, in1 = k0 + 1 >= lo && k0 + 1 < hi_end;
+          mw[e] = (in0 ? 0x3f80u : 0u) | (in1 ? 0x3f800000u : 0u);
+          const float t0 = s[8 * ks + 2 * e], t1 = s[8 * ks + 2 * e + 1];
+          const float x0 = in0 ? fast_exp2(t0 - m_run) : 0.f, x1 = in1 ? fast_exp2(t1 - m_run) : 0.f;
+          lsum += (in0 ? t0 : 0.f) + (in1 ? t1 : 0.f);
+          psum += x0 + x1;
+          wh[e] = pack_bf16x2(x0, x1);
+          wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+        }
+        ls += lsum;
+        l_run += psum;
+        const bf16x8 pf = __builtin_bit_cast(bf16x8, wh), plf = __builtin_bit_cast(bf16x8, wl);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint32_t vo = 2048 * ks + (va ^ (32 * dt));
+          const u32x2 v0 = lds_tr16(&Vb[vo]);
+          const u32x2 v1 = lds_tr16(&Vb[vo + vd]);
+          const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
+          U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, U[dt], 0, 0, 0);
+          U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plf, U[dt], 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sv[dt] = dot2_bf16(w[e], mw[e], sv[dt]);
+        }
+        {  // column sums of K for dims 32 wave + (lane & 31)
+          const u32x2 k0 = lds_tr16(&Kb[2048 * ks + kt0]);
+          const u32x2 k1 = lds_tr16(&Kb[2048 * ks + kt1]);
+          const u32x4 w = {k0[0], k0[1], k1[0], k1[1]};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            sk = dot2_bf16(w[e], mw[e], sk);
+        }
       }
-      cst = 0;
-      ++cb;
-      while (cb < nclu && ntiles_of(cb) == 0) ++cb;
-    } else {
-      ++cst;
+      if (key0 + hi_end == koffs[cb + 1]) {
+        finish(cb++);
+        while (cb < nclu && koffs[cb + 1] == koffs[cb]) finish(cb++);
+      }
+      lo = hi_end;
     }
   };
 
-  if (total > 0) {
-    dma(K0, V0, koffs[fb] + fst * kPrBN, koffs[fb + 1]);
-    advance(fb, fst);
-  }
+  if (ntiles > 0) dma(K0, V0, 0);
   int u = 0;
-  for (; u + 2 <= total; u += 2) {
+  for (; u + 2 <= ntiles; u += 2) {
     step(K0, V0, K1, V1, u);
     step(K1, V1, K0, V0, u + 1);
   }
-  if (u < total) step(K0, V0, K1, V1, u);
+  if (u < ntiles) step(K0, V0, K1, V1, u);
+  while (cb < nclu) finish(cb++);  // trailing empty clusters
 
   const float z = pair_sum(l_run);
   if (pvalid && hi == 0) {
     p.m_split[((int64_t)bh * p.splits + split) * a.Cq + prox] = m_run;
     p.z_split[((int64_t)bh * p.splits + split) * a.Cq + prox] = z;
-  }
-}
-
-struct FinalizeArgs {
-  const int32_t* q_off;
-  const int32_t* k_off;
-  const float* e_buf;
-  const float* m_buf;
-  const float* m_split;
-  const float* z_split;
-  float* score;  // [BH][Cq][Ck]
-  int Cq, Ck, splits;
-};
-
-__global__ void __launch_bounds__(256) probe_finalize_kernel(FinalizeArgs f) {
-  const int a = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-  __shared__ float mz[2];
-  if (tid < 64) {
-    // combine the splits' (max, normaliser) pairs of proxy a, one wave
-    float m = -1e30f;
-    for (int s = lane; s < f.splits; s += 64) m = fmaxf(m, f.m_split[((int64_t)bh * f.splits + s) * f.Cq + a]);
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    float z = 0.f;
-    for (int s = lane; s < f.splits; s += 64) {
-      const int64_t o = ((int64_t)bh * f.splits + s) * f.Cq + a;
-      z += f.z_split[o] * fast_exp2(f.m_split[o] - m);
-    }
-    for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
-    if (lane == 0) {
-      mz[0] = m;
-      mz[1] = z;
-    }
-  }
-  __syncthreads();
-  const float m = mz[0], z = mz[1];
-  const int32_t* qo = f.q_off + (int64_t)bh * (f.Cq + 1);
-  const int32_t* ko = f.k_off + (int64_t)bh * (f.Ck + 1);
-  const int na = qo[a + 1] - qo[a];
-  const float inv_z2 = z > 0.f ? 1.f / (z * z) : 0.f;
-  for (int b = tid; b < f.Ck; b += 256) {
-    const int nb = ko[b + 1] - ko[b];
-    const int64_t o = ((int64_t)bh * f.Cq + a) * f.Ck + b;
-    float sc = 0.f;
-    if (na > 0 && nb > 0) sc = f.e_buf[o] * fast_exp2(2.f * (f.m_buf[o] - m)) * inv_z2 / (float)nb;
-    f.score[o] = sc;
   }
 }
 
@@ -690,401 +698,455 @@ __device__ __forceinline__ long long wave_incl_scan64(long long x, int lane) {
   return x;
 }
 
+// ---------------------------------------------------------------------------
+// scores and their cost histogram
+// ---------------------------------------------------------------------------
+// score_ab = e2_ab 2^(2 (m_ab - M_a)) / Z_a^2 / n_b, with (M_a, Z_a) the proxy's
+// softmax reference and normaliser combined over the probe's splits (the
+// finalize of the streamed probe), or scores given by the caller.  Each of
+// kHistGroups workgroups per (batch, head) takes a range of rows and adds the
+// cost n_a n_b of every non-empty block to a histogram over bits 30..20 of
+// the score (non-negative floats order like their bit patterns); the
+// histograms are written per workgroup and summed by the selection in a fixed
+// order (integer sums: exact, so the cut does not depend on the order).
+constexpr int kHistBins = 2048, kHistGroups = 32;
+
+struct ScoreHistArgs {
+  const int32_t* q_off;
+  const int32_t* k_off;
+  const float* e_buf;    // null: the scores are given in `score`
+  const float* m_buf;
+  const float* m_split;
+  const float* z_split;
+  float* score;          // [BH][Cq][Ck]
+  unsigned long long* hist;  // [BH][kHistGroups][kHistBins]
+  int Cq, Ck, splits;
+};
+
+__device__ __forceinline__ int score_bin(uint32_t bits) {
+  return (int)min(bits >> 20, (uint32_t)(kHistBins - 1));
+}
+
+__global__ void __launch_bounds__(256) score_hist_kernel(ScoreHistArgs f) {
+  constexpr int kRows = 64;  // rows whose (M_a, 1 / Z_a^2) are combined per round
+  __shared__ unsigned long long h[kHistBins];
+  __shared__ float rm[kRows], rz[kRows];
+  const int g = blockIdx.x, bh = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int rpg = (f.Cq + kHistGroups - 1) / kHistGroups;
+  const int a0 = min(g * rpg, f.Cq), a1 = min(a0 + rpg, f.Cq);
+  const int32_t* qo = f.q_off + (int64_t)bh * (f.Cq + 1);
+  const int32_t* ko = f.k_off + (int64_t)bh * (f.Ck + 1);
+  for (int i = tid; i < kHistBins; i += 256) h[i] = 0;
+  for (int r0 = a0; r0 < a1; r0 += kRows) {
+    const int nr = min(kRows, a1 - r0);
+    if (f.e_buf) {
+      // combine the splits' (reference, normaliser) pairs of each row, one wave
+      // per row, all rows of the round in parallel
+      for (int i = wave; i < nr; i += 4) {
+        const int a = r0 + i;
+        float mm = -1e30f;
+        for (int s = lane; s < f.splits; s += 64) mm = fmaxf(mm, f.m_split[((int64_t)bh * f.splits + s) * f.Cq + a]);
+        for (int off = 32; off > 0; off >>= 1) mm = fmaxf(mm, __shfl_xor(mm, off, 64));
+        float z = 0.f;
+        for (int s = lane; s < f.splits; s += 64) {
+          const int64_t o = ((int64_t)bh * f.splits + s) * f.Cq + a;
+          z += f.z_split[o] * fast_exp2(f.m_split[o] - mm);
+        }
+        for (int off = 32; off > 0; off >>= 1) z += __shfl_xor(z, off, 64);
+        if (lane == 0) {
+          rm[i] = mm;
+          rz[i] = z > 0.f ? 1.f / (z * z) : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+    // every block of the round's rows, four per thread in flight
+    const int n = nr * f.Ck;
+    for (int e0 = tid; e0 < n; e0 += 4 * 256) {
+      float ev[4], mv[4];
+      int64_t ov[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = min(e0 + 256 * j, n - 1);
+        const int i = e / f.Ck, b = e - i * f.Ck;
+        ov[j] = ((int64_t)bh * f.Cq + r0 + i) * f.Ck + b;
+        if (f.e_buf) {
+          ev[j] = f.e_buf[ov[j]];
+          mv[j] = f.m_buf[ov[j]];
+        } else {
+          ev[j] = f.score[ov[j]];
+          mv[j] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int e = e0 + 256 * j;
+        if (e >= n) break;
+        const int i = e / f.Ck, b = e - i * f.Ck;
+        const long long na = qo[r0 + i + 1] - qo[r0 + i], nb = ko[b + 1] - ko[b];
+        float sc = ev[j];
+        if (f.e_buf) {
+          sc = 0.f;
+          if (na > 0 && nb > 0) sc = ev[j] * fast_exp2(2.f * (mv[j] - rm[i])) * rz[i] / (float)nb;
+          f.score[ov[j]] = sc;
+        }
+        const long long cost = na * nb;
+        if (cost > 0) atomicAdd(&h[score_bin(__float_as_uint(sc))], (unsigned long long)cost);
+      }
+    }
+    __syncthreads();
+  }
+  unsigned long long* out = f.hist + ((int64_t)bh * kHistGroups + g) * kHistBins;
+  for (int i = tid; i < kHistBins; i += 256) out[i] = h[i];
+}
+
+// First selection level from the histograms (one workgroup of kSelThreads):
+// the total cost of the non-empty blocks, and, unless all of them fit the
+// budget, the cut bin d (bits 30..20): the blocks of bins above d cost at most
+// the budget, adding d's blocks would exceed it.  Returns take_all; otherwise
+// sets pre = d << 20 and R = budget - (cost of the bins above d).  Thread t
+// holds bins 2t and 2t + 1.
+__device__ bool select_level1(const unsigned long long* hist, long long budget, long long* wred, long long* sh_R,
+                              unsigned* sh_prefix, unsigned& pre, long long& R) {
+  static_assert(kSelThreads * 2 == kHistBins, "two bins per thread");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned long long h0 = 0, h1 = 0;
+  for (int gg = 0; gg < kHistGroups; ++gg) {
+    h0 += hist[gg * kHistBins + 2 * tid];
+    h1 += hist[gg * kHistBins + 2 * tid + 1];
+  }
+  const long long own = (long long)(h0 + h1);
+  long long suf = own;  // inclusive suffix over the lanes >= this one
+  for (int off = 1; off < 64; off <<= 1) {
+    const long long y = __shfl_down(suf, off, 64);
+    if (lane + off < 64) suf += y;
+  }
+  if (lane == 0) wred[wave] = suf;
+  __syncthreads();
+  long long total = 0, above = suf - own;
+  for (int w = 0; w < kSelWaves; ++w) {
+    total += wred[w];
+    if (w > wave) above += wred[w];
+  }
+  const bool take_all = total <= budget;
+  if (!take_all) {
+    if (above <= budget && above + (long long)h1 > budget) {
+      *sh_R = budget - above;
+      *sh_prefix = (unsigned)(2 * tid + 1) << 20;
+    } else if (above + (long long)h1 <= budget && above + (long long)(h0 + h1) > budget) {
+      *sh_R = budget - above - (long long)h1;
+      *sh_prefix = (unsigned)(2 * tid) << 20;
+    }
+  }
+  __syncthreads();
+  pre = take_all ? 0u : *sh_prefix;
+  R = take_all ? budget : *sh_R;
+  __syncthreads();
+  return take_all;
+}
+
+// Selection state of one (batch, head), written by the level-1 and resolve
+// kernels: a block of cost > 0 is kept iff take_all, or its score bits are
+// above Tb, or equal to Tb with an index a * Ck + b up to tie_cut.
+struct SelState {
+  long long R;    // budget left for the cut bin
+  unsigned pre;   // cut bin << 20
+  int take_all;
+  unsigned Tb;
+  int tie_cut;
+  int count;      // blocks gathered from the cut bin
+  int pad;
+};
+
 struct SelectArgs {
   const float* score;   // [BH][Cq][Ck]
   const int32_t* q_off;
   const int32_t* k_off;
   int32_t* rrow;        // [BH][Cq+1]
   int32_t* rcol;        // [BH][Cq*Ck]
-  uint8_t* flags;       // [BH][Cq*Ck] workspace
+  const unsigned long long* hist;  // [BH][kHistGroups][kHistBins]
+  SelState* state;      // [BH]
+  unsigned long long* cand;        // [BH][kSelCand] cut-bin keys ~bits << 32 | index
+  int32_t* counts;      // [BH][Cq] kept blocks per row
   int Cq, Ck, N;
   long long budget;
 };
 
-// One workgroup per (batch, head).  Blocks are ranked by (score descending,
-// index a * Ck + b ascending); the kept set is the longest prefix of that order
-// whose total cost n_a n_b fits the budget.  Non-negative floats order like
-// their bit patterns, so the cut is a threshold pattern T found by a
-// cost-weighted radix select (4 passes of 8 bits, one histogram per wave):
-// every block above T is kept, and blocks equal to T are kept in index order
-// while the remaining budget lasts.  Wave w owns the contiguous rows
-// [w * rpw, (w + 1) * rpw), so index order is wave order, then row order, then
-// column order.
-__global__ void __launch_bounds__(kSelThreads) select_kernel(SelectArgs s) {
-  __shared__ unsigned long long hist[kSelWaves][256];
-  __shared__ unsigned long long htot[256];
+// Blocks are ranked by (score descending, index a * Ck + b ascending); the
+// kept set is the longest prefix of that order whose total cost n_a n_b fits
+// the budget.  Non-negative floats order like their bit patterns.  Six short
+// launches, the row-wise ones one wave per query cluster:
+//   score_hist_kernel     scores and their cost histograms (bits 30..20);
+//   select_level1_kernel  per head: the cut bin and the budget R left for it;
+//   select_gather_kernel  per row: the cut bin's blocks into a per-head list;
+//   select_resolve_kernel per head: the list sorted by (bits descending, index
+//                         ascending) as 64-bit keys (bitonic in LDS, kSelCand
+//                         at most); the kept ones are the longest prefix whose
+//                         cost fits R, which fixes Tb and tie_cut.  A cut bin
+//                         of more blocks (many equal scores) is resolved by
+//                         radix passes of 8, 8 and 4 bits over the head's
+//                         scores, the blocks equal to the final pattern taken
+//                         in index order while R lasts;
+//   select_count_kernel   per row: kept blocks;
+//   select_emit_kernel    per row: its CSR offset (sum of the earlier rows'
+//                         counts) and its ascending kept columns.
+constexpr int kSelCand = 4096;
+
+__device__ __forceinline__ bool sel_keep(const SelState& st, unsigned bits, int idx, long long cost) {
+  return cost > 0 && (st.take_all || bits > st.Tb || (bits == st.Tb && idx <= st.tie_cut));
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_level1_kernel(SelectArgs s) {
   __shared__ long long wred[kSelWaves];
-  __shared__ int nbk[kSelMaxCk];
-  __shared__ int wcnt[kSelWaves];
-  __shared__ unsigned wmin[kSelWaves], wmax[kSelWaves];
   __shared__ long long sh_R;
-  __shared__ unsigned int sh_prefix;
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Cq = s.Cq, Ck = s.Ck;
-  const int64_t M = (int64_t)Cq * Ck;
-  const unsigned* sc = (const unsigned*)(s.score + (int64_t)bh * M);
-  const int32_t* qo = s.q_off + (int64_t)bh * (Cq + 1);
-  const int32_t* ko = s.k_off + (int64_t)bh * (Ck + 1);
-  uint8_t* fl = s.flags + (int64_t)bh * M;
-  int32_t* rr = s.rrow + (int64_t)bh * (Cq + 1);
-  int32_t* rc = s.rcol + (int64_t)bh * M;
+  __shared__ unsigned sh_prefix;
+  const int bh = blockIdx.x;
+  unsigned pre = 0;
+  long long R = s.budget;
+  const bool take_all = select_level1(s.hist + (int64_t)bh * kHistGroups * kHistBins, s.budget, wred, &sh_R,
+                                      &sh_prefix, pre, R);
+  if (threadIdx.x == 0) {
+    SelState st;
+    st.R = R;
+    st.pre = pre;
+    st.take_all = take_all ? 1 : 0;
+    st.Tb = 0;
+    st.tie_cut = 0x7fffffff;
+    st.count = 0;
+    st.pad = 0;
+    s.state[bh] = st;
+  }
+}
 
-  const bool nb_lds = Ck <= kSelMaxCk;
-  if (nb_lds)
-    for (int b = tid; b < Ck; b += kSelThreads) nbk[b] = ko[b + 1] - ko[b];
-  __syncthreads();
-  auto nb_of = [&](int b) -> int { return nb_lds ? nbk[b] : ko[b + 1] - ko[b]; };
-  const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
-  const int ra0 = min(wave * rpw, Cq), ra1 = min(ra0 + rpw, Cq);
-
-  // total cost of all non-empty blocks, and the range of their score bits
-  long long part = 0;
-  unsigned bmin = 0xffffffffu, bmax = 0u;
-  for (int a = ra0; a < ra1; ++a) {
-    const long long na = qo[a + 1] - qo[a];
-    if (na == 0) continue;
-    const unsigned* row = sc + (int64_t)a * Ck;
-    for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
-      unsigned bits[kSelBatch];
+// one wave per row: visit the row's blocks in column order, the loads of a
+// batch of 64-column chunks in flight together: f(b, bits, cost)
+template <typename F>
+__device__ __forceinline__ void sel_row(const SelectArgs& s, int bh, int a, F&& f) {
+  const int lane = threadIdx.x & 63;
+  const int32_t* qo = s.q_off + (int64_t)bh * (s.Cq + 1);
+  const int32_t* ko = s.k_off + (int64_t)bh * (s.Ck + 1);
+  const long long na = qo[a + 1] - qo[a];
+  const unsigned* row = (const unsigned*)s.score + ((int64_t)bh * s.Cq + a) * s.Ck;
+  for (int b0 = 0; b0 < s.Ck; b0 += 64 * kSelBatch) {
+    unsigned bits[kSelBatch];
+    int nb[kSelBatch];
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const int b = b0 + 64 * j + lane;
-        bits[j] = b < Ck ? row[b] : 0u;
-      }
+    for (int j = 0; j < kSelBatch; ++j) {
+      const int b = b0 + 64 * j + lane;
+      bits[j] = b < s.Ck ? row[b] : 0u;
+      nb[j] = b < s.Ck ? ko[b + 1] - ko[b] : 0;
+    }
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const int b = b0 + 64 * j + lane;
-        const int nbv = b < Ck ? nb_of(b) : 0;
-        if (nbv > 0) {
-          part += na * nbv;
-          bmin = min(bmin, bits[j]);
-          bmax = max(bmax, bits[j]);
-        }
-      }
+    for (int j = 0; j < kSelBatch; ++j) {
+      if (b0 + 64 * j >= s.Ck) break;  // wave-uniform
+      f(b0 + 64 * j + lane, bits[j], na * nb[j]);
     }
   }
-  part = wave_sum64(part);
-  for (int off = 32; off > 0; off >>= 1) {
-    bmin = min(bmin, (unsigned)__shfl_xor((int)bmin, off, 64));
-    bmax = max(bmax, (unsigned)__shfl_xor((int)bmax, off, 64));
-  }
-  if (lane == 0) {
-    wred[wave] = part;
-    wmin[wave] = bmin;
-    wmax[wave] = bmax;
-  }
-  __syncthreads();
-  long long total = 0;
-  unsigned gmin = 0xffffffffu, gmax = 0u;
-  for (int w = 0; w < kSelWaves; ++w) {
-    total += wred[w];
-    gmin = min(gmin, wmin[w]);
-    gmax = max(gmax, wmax[w]);
-  }
-  const bool take_all = total <= s.budget;
+}
 
-  unsigned T = 0;
-  long long R = s.budget;
-  if (!take_all) {
-    // every counted block shares the leading bits where gmin and gmax agree,
-    // so the digits start right below them (the first digit is then spread
-    // over many bins instead of piling onto one)
-    const int lead = gmin == gmax ? 32 : __clz((int)(gmin ^ gmax));
-    unsigned msk = lead == 0 ? 0u : (lead == 32 ? 0xffffffffu : ~0u << (32 - lead));
-    unsigned pre = gmin & msk;
-    for (int low = 32 - lead; low > 0;) {
-      const int width = min(8, low);
-      const int shift = low - width;
-      const unsigned dmask = (1u << width) - 1u;
-      low = shift;
-      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
-      __builtin_amdgcn_wave_barrier();
-      for (int a = ra0; a < ra1; ++a) {
-        const long long na = qo[a + 1] - qo[a];
-        if (na == 0) continue;
-        const unsigned* row = sc + (int64_t)a * Ck;
-        for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
-          // the batch's loads are independent of the atomics below, so they are
-          // all in flight together instead of one memory latency per element
-          unsigned bits[kSelBatch];
+__global__ void __launch_bounds__(256) select_gather_kernel(SelectArgs s) {
+  const int bh = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const SelState st = s.state[bh];
+  if (st.take_all || a >= s.Cq) return;
+  unsigned long long* cand = s.cand + (int64_t)bh * kSelCand;
+  const int32_t* qo = s.q_off + (int64_t)bh * (s.Cq + 1);
+  const int32_t* ko = s.k_off + (int64_t)bh * (s.Ck + 1);
+  const long long na = qo[a + 1] - qo[a];
+  if (na == 0) return;
+  const unsigned* row = (const unsigned*)s.score + ((int64_t)bh * s.Cq + a) * s.Ck;
+  for (int b0 = 0; b0 < s.Ck; b0 += 64 * kSelBatch) {
+    // the batch's cut-bin blocks, then one counter atomic for all of them
+    unsigned bits[kSelBatch];
+    bool in[kSelBatch];
 #pragma unroll
-          for (int j = 0; j < kSelBatch; ++j) {
-            const int b = b0 + 64 * j + lane;
-            bits[j] = b < Ck ? row[b] : 0u;
-          }
+    for (int j = 0; j < kSelBatch; ++j) {
+      const int b = b0 + 64 * j + lane;
+      bits[j] = b < s.Ck ? row[b] : 0u;
+      in[j] = b < s.Ck && ko[b + 1] > ko[b] && (bits[j] >> 20) == (st.pre >> 20);
+    }
+    int total = 0;
 #pragma unroll
-          for (int j = 0; j < kSelBatch; ++j) {
-            const int b = b0 + 64 * j + lane;
-            const int nbv = b < Ck ? nb_of(b) : 0;
-            const bool in = nbv > 0 && (bits[j] & msk) == pre;
-            const unsigned dig = (bits[j] >> shift) & dmask;
-            const unsigned long long inb = __ballot(in);
-            if (inb == 0) continue;
-            const unsigned d0 = (unsigned)__shfl((int)dig, __ffsll((long long)inb) - 1, 64);
-            if (__ballot(in && dig == d0) == inb) {
-              // the whole batch element falls into one bin: one atomic for the wave
-              const long long c = wave_sum64(in ? na * nbv : 0);
-              if (lane == 0) atomicAdd(&hist[wave][d0], (unsigned long long)c);
-            } else if (in) {
-              atomicAdd(&hist[wave][dig], (unsigned long long)(na * nbv));
-            }
-          }
+    for (int j = 0; j < kSelBatch; ++j) total += __popcll(__ballot(in[j]));
+    if (total == 0) continue;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(&s.state[bh].count, total);
+    base = __shfl(base, 0, 64);
+#pragma unroll
+    for (int j = 0; j < kSelBatch; ++j) {
+      const unsigned long long bal = __ballot(in[j]);
+      const int pos = base + __popcll(bal & ((1ull << lane) - 1ull));
+      if (in[j] && pos < kSelCand)
+        cand[pos] = ((unsigned long long)(~bits[j]) << 32) | (unsigned)(a * s.Ck + b0 + 64 * j + lane);
+      base += __popcll(bal);
+    }
+  }
+}
+
+__global__ void __launch_bounds__(kSelThreads) select_resolve_kernel(SelectArgs s) {
+  __shared__ unsigned long long keys[kSelCand];  // the gathered bin; the radix passes' histograms
+  __shared__ unsigned long long hc[kSelCand];    // level-2 / level-3 histograms; the sorted ties
+  __shared__ long long wred[kSelWaves];
+  __shared__ int wcnt[kSelWaves];
+  __shared__ long long sh_R;
+  __shared__ unsigned sh_prefix;
+  __shared__ int sh_tie;
+  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const SelState st = s.state[bh];
+  if (st.take_all) return;
+  const int Cq = s.Cq, Ck = s.Ck;
+  const int32_t* qo = s.q_off + (int64_t)bh * (Cq + 1);
+  const int32_t* ko = s.k_off + (int64_t)bh * (Ck + 1);
+  long long R = st.R;
+  unsigned Tb;
+  int tie_cut;
+  const int count = st.count;
+  if (count <= kSelCand) {
+    // levels 2 and 3 (bits 19..8, then 7..0) as cost histograms over the
+    // gathered blocks, each candidate staying in LDS: keys[] holds them, hc[]
+    // the histogram; then the blocks equal to the final pattern in index order
+    const unsigned long long* cand = s.cand + (int64_t)bh * kSelCand;
+    for (int i = tid; i < count; i += kSelThreads) keys[i] = cand[i];
+    unsigned pre = st.pre, msk = 0xfff00000u;
+    for (int level = 0; level < 2; ++level) {
+      const int width = level == 0 ? 12 : 8, shift = level == 0 ? 8 : 0;
+      const int nbins = 1 << width;
+      for (int i = tid; i < nbins; i += kSelThreads) hc[i] = 0;
+      __syncthreads();
+      for (int i = tid; i < count; i += kSelThreads) {
+        const unsigned long long key = keys[i];
+        const unsigned bits = ~(unsigned)(key >> 32), idx = (unsigned)key;
+        if ((bits & msk) == pre) {
+          const int a = (int)(idx / (unsigned)Ck), b = (int)(idx % (unsigned)Ck);
+          atomicAdd(&hc[(bits >> shift) & (nbins - 1)],
+                    (unsigned long long)((long long)(qo[a + 1] - qo[a]) * (ko[b + 1] - ko[b])));
         }
       }
       __syncthreads();
-      if (tid < 256) {
-        unsigned long long t = 0;
-        for (int w = 0; w < kSelWaves; ++w) t += hist[w][tid];
-        htot[tid] = t;
+      // thread t holds bins [t * per, (t + 1) * per); the cut bin d: the bins
+      // above it fit R, adding d's cost exceeds R (bin 0 if none does)
+      const int per = nbins / kSelThreads > 0 ? nbins / kSelThreads : 1;
+      unsigned long long own = 0;
+      for (int e = 0; e < per; ++e) {
+        const int d = tid * per + e;
+        own += d < nbins ? hc[d] : 0;
       }
+      long long suf = (long long)own;  // inclusive suffix over lanes >= this one
+      for (int o = 1; o < 64; o <<= 1) {
+        const long long y = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += y;
+      }
+      if (lane == 0) wred[wave] = suf;
       __syncthreads();
-      if (wave == 0) {
-        // lane l holds digits 4l .. 4l+3; the cut digit d is the first one from
-        // the top where the cost of the digits above stays within R but adding
-        // d's own cost exceeds it (digit 0 if none does)
-        unsigned long long h[4], own = 0;
-        for (int i = 0; i < 4; ++i) {
-          h[i] = htot[4 * lane + i];
-          own += h[i];
+      long long above = suf - (long long)own;
+      for (int w = wave + 1; w < kSelWaves; ++w) above += wred[w];
+      for (int e = per - 1; e >= 0; --e) {
+        const int d = tid * per + e;
+        if (d >= nbins) continue;
+        const long long h = (long long)hc[d];
+        if (above <= R && (above + h > R || d == 0)) {
+          sh_R = R - above;
+          sh_prefix = pre | ((unsigned)d << shift);
         }
-        long long above = (long long)own;  // becomes: cost of all digits held by higher lanes
-        for (int off = 1; off < 64; off <<= 1) {
-          const long long y = __shfl_down(above, off, 64);
-          if (lane + off < 64) above += y;
-        }
-        above -= (long long)own;
-        for (int i = 3; i >= 0; --i) {
-          const int d = 4 * lane + i;
-          const bool cut = (above + (long long)h[i] > R) || d == 0;
-          if (cut && above <= R) {
-            sh_R = R - above;
-            sh_prefix = pre | ((unsigned)d << shift);
-            break;
-          }
-          above += (long long)h[i];
-        }
+        above += h;
       }
       __syncthreads();
       R = sh_R;
       pre = sh_prefix;
-      msk |= dmask << shift;
+      msk |= (unsigned)(nbins - 1) << shift;
       __syncthreads();
     }
-    T = pre;
-  }
-
-  // keep flags; ties at T in index order within the remaining budget
-  long long tc = 0;
-  if (!take_all)
-    for (int a = ra0; a < ra1; ++a) {
-      const long long na = qo[a + 1] - qo[a];
-      if (na == 0) continue;
-      const unsigned* row = sc + (int64_t)a * Ck;
-      for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
-        unsigned bits[kSelBatch];
-#pragma unroll
-        for (int j = 0; j < kSelBatch; ++j) {
-          const int b = b0 + 64 * j + lane;
-          bits[j] = b < Ck ? row[b] : 0u;
+    Tb = pre;
+    // ties: the gathered blocks equal to Tb, in index order, while R lasts.
+    // Compact their indices (usually one) and sort them (bitonic, in hc[]).
+    if (tid == 0) sh_tie = 0;
+    __syncthreads();
+    for (int i = tid; i < count; i += kSelThreads) {
+      const unsigned long long key = keys[i];
+      if (~(unsigned)(key >> 32) == Tb) hc[atomicAdd(&sh_tie, 1)] = (unsigned)key;
+    }
+    __syncthreads();
+    const int nt = sh_tie;
+    int P = 1;
+    while (P < nt) P <<= 1;
+    for (int i = nt + tid; i < P; i += kSelThreads) hc[i] = ~0ull;
+    __syncthreads();
+    for (int k = 2; k <= P; k <<= 1)
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += kSelThreads) {
+          const int l = i ^ j;
+          if (l > i) {
+            const unsigned long long x = hc[i], y = hc[l];
+            if ((x > y) == ((i & k) == 0)) {
+              hc[i] = y;
+              hc[l] = x;
+            }
+          }
         }
-#pragma unroll
-        for (int j = 0; j < kSelBatch; ++j) {
-          const int b = b0 + 64 * j + lane;
-          const int nbv = b < Ck ? nb_of(b) : 0;
-          if (nbv > 0 && bits[j] == T) tc += na * nbv;
-        }
+        __syncthreads();
       }
-    }
-  tc = wave_sum64(tc);
-  if (lane == 0) wred[wave] = tc;
-  __syncthreads();
-  long long carry = 0;
-  for (int w = 0; w < wave; ++w) carry += wred[w];
-  int wave_kept = 0;
-  for (int a = ra0; a < ra1; ++a) {
-    const long long na = qo[a + 1] - qo[a];
-    const unsigned* row = sc + (int64_t)a * Ck;
-    unsigned bits_b[kSelBatch];
-    for (int b0 = 0; b0 < Ck; b0 += 64) {
-      const int jb = (b0 / 64) % kSelBatch;
-      if (jb == 0) {
+    // the last tie whose inclusive prefix cost fits R (thread t: ties 4t..4t+3)
+    long long c4[4], run = 0;
 #pragma unroll
-        for (int j = 0; j < kSelBatch; ++j) {
-          const int bb = b0 + 64 * j + lane;
-          bits_b[j] = bb < Ck ? row[bb] : 0u;
-        }
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * tid + e;
+      long long cc = 0;
+      if (i < nt) {
+        const unsigned idx = (unsigned)hc[i];
+        const int a = (int)(idx / (unsigned)Ck), b = (int)(idx % (unsigned)Ck);
+        cc = (long long)(qo[a + 1] - qo[a]) * (ko[b + 1] - ko[b]);
       }
-      const int b = b0 + lane;
-      const bool valid = b < Ck;
-      const long long c = valid ? na * nb_of(b) : 0;
-      unsigned bits = 0u;
-#pragma unroll
-      for (int j = 0; j < kSelBatch; ++j)
-        if (j == jb) bits = bits_b[j];
-      const bool tie = !take_all && c > 0 && bits == T;
-      long long incl = 0;
-      if (__any(tie)) incl = wave_incl_scan64(tie ? c : 0, lane);
-      const bool keep = take_all ? c > 0 : (c > 0 && (bits > T || (tie && carry + incl <= R)));
-      carry += __shfl(incl, 63, 64);
-      if (valid) fl[(int64_t)a * Ck + b] = keep ? 1 : 0;
-      wave_kept += __popcll(__ballot(keep));
+      run += cc;
+      c4[e] = run;
     }
-  }
-  if (lane == 0) wcnt[wave] = wave_kept;
-  __syncthreads();
-  // CSR: wave w's rows start after the blocks kept by waves < w; columns
-  // ascending, 64 at a time with ballots (each lane re-reads only flags it wrote)
-  int start = 0;
-  for (int w = 0; w < wave; ++w) start += wcnt[w];
-  if (tid == 0) rr[0] = 0;
-  for (int a = ra0; a < ra1; ++a) {
-    for (int b0 = 0; b0 < Ck; b0 += 64 * kSelBatch) {
-      bool keep[kSelBatch];
+    const long long inc = wave_incl_scan64(run, lane);
+    if (lane == 63) wred[wave] = inc;
+    __syncthreads();
+    long long off = 0;
+    for (int w = 0; w < wave; ++w) off += wred[w];
+    const long long excl = off + inc - run;
+    int kept = 0;
 #pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const int b = b0 + 64 * j + lane;
-        keep[j] = b < Ck && fl[(int64_t)a * Ck + b] != 0;
-      }
-#pragma unroll
-      for (int j = 0; j < kSelBatch; ++j) {
-        const int b = b0 + 64 * j + lane;
-        const unsigned long long bal = __ballot(keep[j]);
-        if (keep[j]) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = b;
-        start += __popcll(bal);
-      }
-    }
-    if (lane == 0) rr[a + 1] = start;
-  }
-}
-
-// Register-resident form of select_kernel for Cq <= 16 * kSrRows and
-// Ck <= 64 * kSrCpl: the same selection and the same CSR, with every score of
-// the head loaded once into registers (lane l of wave w holds the columns
-// 64 c + l of its rows ra0 + r) and every pass run from there, instead of
-// re-reading the scores from memory in each radix pass.
-constexpr int kSrRows = 8, kSrCpl = 8;
-
-__global__ void __launch_bounds__(kSelThreads) select_reg_kernel(SelectArgs s) {
-  __shared__ unsigned long long hist[kSelWaves][256];
-  __shared__ unsigned long long htot[256];
-  __shared__ long long wred[kSelWaves];
-  __shared__ int wcnt[kSelWaves];
-  __shared__ unsigned wmin[kSelWaves], wmax[kSelWaves];
-  __shared__ long long sh_R;
-  __shared__ unsigned int sh_prefix;
-  __shared__ int nbk[64 * kSrCpl];
-  const int bh = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int Cq = s.Cq, Ck = s.Ck;
-  const int64_t M = (int64_t)Cq * Ck;
-  const unsigned* sc = (const unsigned*)(s.score + (int64_t)bh * M);
-  const int32_t* qo = s.q_off + (int64_t)bh * (Cq + 1);
-  const int32_t* ko = s.k_off + (int64_t)bh * (Ck + 1);
-  int32_t* rr = s.rrow + (int64_t)bh * (Cq + 1);
-  int32_t* rc = s.rcol + (int64_t)bh * M;
-  const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
-  const int ra0 = min(wave * rpw, Cq), nrow = min(ra0 + rpw, Cq) - ra0;
-
-  // scores in registers; key-cluster sizes in LDS (read at each use, so the
-  // compiler does not keep 64 per-lane costs live across the passes)
-  unsigned sb[kSrRows][kSrCpl];
-  int nar[kSrRows];
-  for (int b = tid; b < 64 * kSrCpl; b += kSelThreads) nbk[b] = b < Ck ? ko[b + 1] - ko[b] : 0;
-#pragma unroll
-  for (int r = 0; r < kSrRows; ++r) nar[r] = r < nrow ? qo[ra0 + r + 1] - qo[ra0 + r] : 0;
-#pragma unroll
-  for (int r = 0; r < kSrRows; ++r)
-#pragma unroll
-    for (int c = 0; c < kSrCpl; ++c) {
-      const int b = 64 * c + lane;
-      sb[r][c] = (r < nrow && b < Ck) ? sc[(int64_t)(ra0 + r) * Ck + b] : 0u;
-    }
-  __syncthreads();
-  auto cost = [&](int r, int c) -> long long { return (long long)nar[r] * nbk[64 * c + lane]; };
-
-  // total cost of the non-empty blocks and the range of their score bits
-  long long part = 0;
-  unsigned bmin = 0xffffffffu, bmax = 0u;
-#pragma unroll
-  for (int r = 0; r < kSrRows; ++r)
-#pragma unroll
-    for (int c = 0; c < kSrCpl; ++c) {
-      const long long w = cost(r, c);
-      if (w > 0) {
-        part += w;
-        bmin = min(bmin, sb[r][c]);
-        bmax = max(bmax, sb[r][c]);
-      }
-    }
-  part = wave_sum64(part);
-  for (int off = 32; off > 0; off >>= 1) {
-    bmin = min(bmin, (unsigned)__shfl_xor((int)bmin, off, 64));
-    bmax = max(bmax, (unsigned)__shfl_xor((int)bmax, off, 64));
-  }
-  if (lane == 0) {
-    wred[wave] = part;
-    wmin[wave] = bmin;
-    wmax[wave] = bmax;
-  }
-  __syncthreads();
-  long long total = 0;
-  unsigned gmin = 0xffffffffu, gmax = 0u;
-  for (int w = 0; w < kSelWaves; ++w) {
-    total += wred[w];
-    gmin = min(gmin, wmin[w]);
-    gmax = max(gmax, wmax[w]);
-  }
-  const bool take_all = total <= s.budget;
-
-  unsigned T = 0;
-  long long R = s.budget;
-  if (!take_all) {
-    // digits start below the leading bits shared by every counted score
-    const int lead = gmin == gmax ? 32 : __clz((int)(gmin ^ gmax));
-    unsigned msk = lead == 0 ? 0u : (lead == 32 ? 0xffffffffu : ~0u << (32 - lead));
-    unsigned pre = gmin & msk;
-    for (int low = 32 - lead; low > 0;) {
+    for (int e = 0; e < 4; ++e) kept += (4 * tid + e < nt && excl + c4[e] <= R) ? 1 : 0;
+    kept = (int)wave_sum64(kept);
+    if (lane == 0) wcnt[wave] = kept;
+    __syncthreads();
+    int cut = 0;
+    for (int w = 0; w < kSelWaves; ++w) cut += wcnt[w];
+    tie_cut = cut > 0 ? (int)(unsigned)hc[cut - 1] : -1;
+  } else {
+    // many equal scores in the cut bin: radix passes below the first level
+    // over the head's scores (wave w takes rows [w rpw, (w + 1) rpw)), one
+    // cost histogram per wave
+    unsigned long long* hist = keys;  // [kSelWaves][256]
+    const int rpw = (Cq + kSelWaves - 1) / kSelWaves;
+    const int ra0 = min(wave * rpw, Cq), ra1 = min(ra0 + rpw, Cq);
+    unsigned pre = st.pre, msk = 0xfff00000u;
+    for (int low = 20; low > 0;) {
       const int width = min(8, low);
       const int shift = low - width;
       const unsigned dmask = (1u << width) - 1u;
       low = shift;
-      for (int i = lane; i < 256; i += 64) hist[wave][i] = 0;
+      for (int i = lane; i < 256; i += 64) hist[wave * 256 + i] = 0;
       __builtin_amdgcn_wave_barrier();
-#pragma unroll
-      for (int r = 0; r < kSrRows; ++r)
-#pragma unroll
-        for (int c = 0; c < kSrCpl; ++c) {
-          const long long w = cost(r, c);
-          const bool in = w > 0 && (sb[r][c] & msk) == pre;
-          const unsigned dig = (sb[r][c] >> shift) & dmask;
-          const unsigned long long inb = __ballot(in);
-          if (inb == 0) continue;
-          const unsigned d0 = (unsigned)__shfl((int)dig, __ffsll((long long)inb) - 1, 64);
-          if (__ballot(in && dig == d0) == inb) {
-            const long long cw = wave_sum64(in ? w : 0);
-            if (lane == 0) atomicAdd(&hist[wave][d0], (unsigned long long)cw);
-          } else if (in) {
-            atomicAdd(&hist[wave][dig], (unsigned long long)w);
-          }
-        }
-      __syncthreads();
-      if (tid < 256) {
-        unsigned long long t = 0;
-        for (int w = 0; w < kSelWaves; ++w) t += hist[w][tid];
-        htot[tid] = t;
-      }
+      for (int a = ra0; a < ra1; ++a)
+        sel_row(s, bh, a, [&](int, unsigned bits, long long c) {
+          if (c > 0 && (bits & msk) == pre) atomicAdd(&hist[wave * 256 + ((bits >> shift) & dmask)], (unsigned long long)c);
+        });
       __syncthreads();
       if (wave == 0) {
         // lane l holds digits 4l .. 4l+3; the cut digit is the first from the
         // top whose own cost takes the cost above it past R (digit 0 if none)
         unsigned long long h[4], own = 0;
         for (int i = 0; i < 4; ++i) {
-          h[i] = htot[4 * lane + i];
-          own += h[i];
+          unsigned long long t = 0;
+          for (int w = 0; w < kSelWaves; ++w) t += hist[w * 256 + 4 * lane + i];
+          h[i] = t;
+          own += t;
         }
         long long above = (long long)own;
-        for (int off = 1; off < 64; off <<= 1) {
-          const long long y = __shfl_down(above, off, 64);
-          if (lane + off < 64) above += y;
+        for (int o = 1; o < 64; o <<= 1) {
+          const long long y = __shfl_down(above, o, 64);
+          if (lane + o < 64) above += y;
         }
         above -= (long long)own;
         for (int i = 3; i >= 0; --i) {
@@ -1104,58 +1166,70 @@ __global__ void __launch_bounds__(kSelThreads) select_reg_kernel(SelectArgs s) {
       msk |= dmask << shift;
       __syncthreads();
     }
-    T = pre;
+    Tb = pre;
+    // blocks equal to Tb in index order while R lasts: the last kept index
+    long long tc = 0;
+    for (int a = ra0; a < ra1; ++a)
+      sel_row(s, bh, a, [&](int, unsigned bits, long long c) {
+        if (c > 0 && bits == Tb) tc += c;
+      });
+    tc = wave_sum64(tc);
+    if (lane == 0) wred[wave] = tc;
+    if (tid == 0) sh_tie = -1;
+    __syncthreads();
+    long long carry = 0;
+    for (int w = 0; w < wave; ++w) carry += wred[w];
+    int last = -1;
+    for (int a = ra0; a < ra1; ++a)
+      sel_row(s, bh, a, [&](int b, unsigned bits, long long c) {
+        const bool tie = c > 0 && bits == Tb;
+        long long incl = 0;
+        if (__any(tie)) incl = wave_incl_scan64(tie ? c : 0, lane);
+        if (tie && carry + incl <= R) last = max(last, a * Ck + b);
+        carry += __shfl(incl, 63, 64);
+      });
+    for (int o = 32; o > 0; o >>= 1) last = max(last, __shfl_xor(last, o, 64));
+    if (lane == 0) atomicMax(&sh_tie, last);
+    __syncthreads();
+    tie_cut = sh_tie;
   }
+  if (tid == 0) {
+    s.state[bh].Tb = Tb;
+    s.state[bh].tie_cut = tie_cut;
+  }
+}
 
-  // cost of the ties at T held by each wave, for the index-order carry
-  long long tc = 0;
-  if (!take_all)
-#pragma unroll
-    for (int r = 0; r < kSrRows; ++r)
-#pragma unroll
-      for (int c = 0; c < kSrCpl; ++c) {
-        const long long w = cost(r, c);
-        if (w > 0 && sb[r][c] == T) tc += w;
-      }
-  tc = wave_sum64(tc);
-  if (lane == 0) wred[wave] = tc;
-  __syncthreads();
-  long long carry = 0;
-  for (int w = 0; w < wave; ++w) carry += wred[w];
-  // keep decisions in index order (row, then column), packed one bit each
-  unsigned long long keepm = 0;
-  int wave_kept = 0;
-#pragma unroll
-  for (int r = 0; r < kSrRows; ++r)
-#pragma unroll
-    for (int c = 0; c < kSrCpl; ++c) {
-      const long long w = cost(r, c);
-      const bool tie = !take_all && w > 0 && sb[r][c] == T;
-      long long incl = 0;
-      if (__any(tie)) incl = wave_incl_scan64(tie ? w : 0, lane);
-      const bool keep = take_all ? w > 0 : (w > 0 && (sb[r][c] > T || (tie && carry + incl <= R)));
-      carry += __shfl(incl, 63, 64);
-      if (keep) keepm |= 1ull << (r * kSrCpl + c);
-      wave_kept += __popcll(__ballot(keep));
-    }
-  if (lane == 0) wcnt[wave] = wave_kept;
-  __syncthreads();
-  // CSR: wave w's rows start after the blocks kept by waves < w
+__global__ void __launch_bounds__(256) select_count_kernel(SelectArgs s) {
+  const int bh = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= s.Cq) return;
+  const SelState st = s.state[bh];
+  int kept = 0;
+  sel_row(s, bh, a, [&](int b, unsigned bits, long long c) {
+    kept += __popcll(__ballot(sel_keep(st, bits, a * s.Ck + b, c)));
+  });
+  if (lane == 0) s.counts[(int64_t)bh * s.Cq + a] = kept;
+}
+
+__global__ void __launch_bounds__(256) select_emit_kernel(SelectArgs s) {
+  const int bh = blockIdx.y, a = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (a >= s.Cq) return;
+  const SelState st = s.state[bh];
+  const int32_t* cnt = s.counts + (int64_t)bh * s.Cq;
   int start = 0;
-  for (int w = 0; w < wave; ++w) start += wcnt[w];
-  if (tid == 0) rr[0] = 0;
-#pragma unroll
-  for (int r = 0; r < kSrRows; ++r) {
-    if (r >= nrow) break;
-#pragma unroll
-    for (int c = 0; c < kSrCpl; ++c) {
-      const bool keep = (keepm >> (r * kSrCpl + c)) & 1ull;
-      const unsigned long long bal = __ballot(keep);
-      if (keep) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = 64 * c + lane;
-      start += __popcll(bal);
-    }
-    if (lane == 0) rr[ra0 + r + 1] = start;
+  for (int i = lane; i < a; i += 64) start += cnt[i];
+  for (int o = 32; o > 0; o >>= 1) start += __shfl_xor(start, o, 64);
+  int32_t* rr = s.rrow + (int64_t)bh * (s.Cq + 1);
+  int32_t* rc = s.rcol + (int64_t)bh * s.Cq * s.Ck;
+  if (lane == 0) {
+    if (a == 0) rr[0] = 0;
+    rr[a + 1] = start + cnt[a];
   }
+  sel_row(s, bh, a, [&](int b, unsigned bits, long long c) {
+    const bool keep = sel_keep(st, bits, a * s.Ck + b, c);
+    const unsigned long long bal = __ballot(keep);
+    if (keep) rc[start + __popcll(bal & ((1ull << lane) - 1ull))] = b;
+    start += __popcll(bal);
+  });
 }
 
 // ---------------------------------------------------------------------------
@@ -1805,77 +1879,114 @@ static SvgArgs svg_args(const void* q, const void* k, const void* v, const bsa_s
 
 bsa_status launch_centroids(const void* q, const void* k, const void* v, const bsa_shape& s, const int32_t* q_off,
                             int Cq, const int32_t* k_off, int Ck, float* qc, float* kc, float* vc,
-                            hipStream_t stream) {
+                            hipStream_t stream, CentroidSet which) {
   SvgArgs a = svg_args(q, k, v, s, q_off, Cq, k_off, Ck);
-  dim3 grid(Cq + Ck, s.B * s.H);
-  if (s.D == 128) hipLaunchKernelGGL(centroid_kernel<128>, grid, dim3(256), 0, stream, a, qc, kc, vc);
-  else if (s.D == 64) hipLaunchKernelGGL(centroid_kernel<64>, grid, dim3(256), 0, stream, a, qc, kc, vc);
+  const int c0 = which == kCentKey ? Cq : 0;
+  const int n = which == kCentAll ? Cq + Ck : (which == kCentQuery ? Cq : Ck);
+  dim3 grid(n, s.B * s.H);
+  if (s.D == 128) hipLaunchKernelGGL(centroid_kernel<128>, grid, dim3(256), 0, stream, a, qc, kc, vc, c0);
+  else if (s.D == 64) hipLaunchKernelGGL(centroid_kernel<64>, grid, dim3(256), 0, stream, a, qc, kc, vc, c0);
   else return BSA_ERR_UNSUPPORTED;
   return launch_ok("cluster_centroids") ? BSA_OK : BSA_ERR_HIP;
 }
 
-
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// selection scratch: cost histograms [BH][8][2048] u64 | state [BH] |
+// cut-bin keys [BH][kSelCand] u64 | kept counts [BH][Cq] int32
+struct SelScratch {
+  size_t hist, state, cand, counts, total;
+};
+static SelScratch sel_scratch(const bsa_shape& s, int Cq) {
+  SelScratch w;
+  const size_t bh = (size_t)s.B * s.H;
+  w.hist = 0;
+  w.state = al256(bh * kHistGroups * kHistBins * sizeof(unsigned long long));
+  w.cand = w.state + al256(bh * sizeof(SelState));
+  w.counts = w.cand + al256(bh * kSelCand * sizeof(unsigned long long));
+  w.total = w.counts + al256(bh * Cq * sizeof(int32_t));
+  return w;
+}
+size_t route_hist_bytes(const bsa_shape& s, int Cq) { return sel_scratch(s, Cq).total; }
 
 ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck) {
   ProbePlan p;
   const int bh = s.B * s.H;
   const int groups = (Cq + 127) / 128;
-  // the head_dim-128 kernel addresses a head with 32-bit offsets
-  p.d128 = s.D == 128 && ((int64_t)s.N + kPrBN) * s.stride_n * 2 < ((int64_t)1 << 31);
+  // the fused head_dim-128 kernel addresses a head with 32-bit offsets
+  p.fused = s.D == 128 && ((int64_t)s.N + kFpTK) * s.stride_n * 2 < ((int64_t)1 << 31);
   int want = (512 + bh * groups - 1) / (bh * groups);
   if (want > Ck) want = Ck;
   if (want < 1) want = 1;
   p.cps = (Ck + want - 1) / want;
-  if (p.d128 && p.cps > kPrMaxCps) p.cps = kPrMaxCps;
+  if (p.fused && p.cps > kFpMaxCps) p.cps = kFpMaxCps;
   p.splits = (Ck + p.cps - 1) / p.cps;
   const size_t blocks = (size_t)bh * Cq * Ck;
   p.off_e = 0;
   p.off_m = al256(p.off_e + blocks * 4);
   p.off_ms = al256(p.off_m + blocks * 4);
   p.off_zs = al256(p.off_ms + (size_t)bh * p.splits * Cq * 4);
-  p.off_lc = al256(p.off_zs + (size_t)bh * p.splits * Cq * 4);
-  p.total = al256(p.off_lc + (p.d128 ? blocks * 4 : 0));
+  p.off_hist = al256(p.off_zs + (size_t)bh * p.splits * Cq * 4);
+  p.total = p.off_hist + route_hist_bytes(s, Cq);
   return p;
 }
 
 bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s, const int32_t* q_off, int Cq,
-                               const int32_t* k_off, int Ck, const float* qc, const float* kc, const float* vc,
-                               float scale, float* score, void* ws, hipStream_t stream) {
+                               const int32_t* k_off, int Ck, const float* qc, float* kc, float* vc, float scale,
+                               float* score, void* ws, hipStream_t stream, uint16_t* kc_bf, uint16_t* vc_bf) {
   const ProbePlan pl = probe_plan(s, Cq, Ck);
   char* w = (char*)ws;
-  ProbeArgs p;
-  p.s = svg_args(nullptr, k, v, s, q_off, Cq, k_off, Ck);
-  p.q_cent = qc; p.k_cent = kc; p.v_cent = vc;
-  p.lc = pl.d128 ? (const float*)(w + pl.off_lc) : nullptr;
-  p.e_buf = (float*)(w + pl.off_e); p.m_buf = (float*)(w + pl.off_m);
-  p.m_split = (float*)(w + pl.off_ms); p.z_split = (float*)(w + pl.off_zs);
-  p.splits = pl.splits; p.cps = pl.cps; p.c2 = scale * kLog2e;
+  float* e_buf = (float*)(w + pl.off_e);
+  float* m_buf = (float*)(w + pl.off_m);
+  float* m_split = (float*)(w + pl.off_ms);
+  float* z_split = (float*)(w + pl.off_zs);
+  const float c2 = scale * kLog2e;
   dim3 grid(pl.splits, s.B * s.H, (Cq + 127) / 128);
-  if (pl.d128) {
-    hipLaunchKernelGGL(proxy_logit_kernel<128>, dim3((Ck + 63) / 64, (Cq + 15) / 16, s.B * s.H), dim3(256), 0,
-                       stream, qc, kc, (float*)(w + pl.off_lc), Cq, Ck, p.c2);
-    hipLaunchKernelGGL(probe_d128_kernel, grid, dim3(256), 0, stream, p);
-  } else if (s.D == 128) {
-    hipLaunchKernelGGL(probe_kernel<128>, grid, dim3(256), 0, stream, p);
-  } else if (s.D == 64) {
-    hipLaunchKernelGGL(probe_kernel<64>, grid, dim3(256), 0, stream, p);
+  if (pl.fused) {
+    FusedProbeArgs f;
+    f.s = svg_args(nullptr, k, v, s, q_off, Cq, k_off, Ck);
+    f.q_cent = qc; f.e_buf = e_buf; f.m_buf = m_buf; f.m_split = m_split; f.z_split = z_split;
+    f.k_cent = kc; f.v_cent = vc; f.kc_bf = kc_bf; f.vc_bf = vc_bf;
+    f.splits = pl.splits; f.cps = pl.cps; f.c2 = c2;
+    hipLaunchKernelGGL(probe_fused_d128_kernel, grid, dim3(256), 0, stream, f);
   } else {
-    return BSA_ERR_UNSUPPORTED;
+    // the general probe takes the key and value centroids as inputs
+    bsa_status st = launch_centroids(nullptr, k, v, s, q_off, Cq, k_off, Ck, nullptr, kc, vc, stream, kCentKey);
+    if (st != BSA_OK) return st;
+    ProbeArgs p;
+    p.s = svg_args(nullptr, k, v, s, q_off, Cq, k_off, Ck);
+    p.q_cent = qc; p.k_cent = kc; p.v_cent = vc;
+    p.e_buf = e_buf; p.m_buf = m_buf; p.m_split = m_split; p.z_split = z_split;
+    p.splits = pl.splits; p.cps = pl.cps; p.c2 = c2;
+    if (s.D == 128) hipLaunchKernelGGL(probe_kernel<128>, grid, dim3(256), 0, stream, p);
+    else if (s.D == 64) hipLaunchKernelGGL(probe_kernel<64>, grid, dim3(256), 0, stream, p);
+    else return BSA_ERR_UNSUPPORTED;
   }
-  FinalizeArgs f{q_off, k_off, p.e_buf, p.m_buf, p.m_split, p.z_split, score, Cq, Ck, pl.splits};
-  hipLaunchKernelGGL(probe_finalize_kernel, dim3(Cq, s.B * s.H), dim3(256), 0, stream, f);
+  ScoreHistArgs h{q_off, k_off, e_buf, m_buf, m_split, z_split, score,
+                  (unsigned long long*)(w + pl.off_hist), Cq, Ck, pl.splits};
+  hipLaunchKernelGGL(score_hist_kernel, dim3(kHistGroups, s.B * s.H), dim3(256), 0, stream, h);
   return launch_ok("route_scores") ? BSA_OK : BSA_ERR_HIP;
 }
 
 bsa_status launch_route_select(const float* score, const bsa_shape& s, const int32_t* q_off, int Cq,
                                const int32_t* k_off, int Ck, long long budget, int32_t* rrow, int32_t* rcol,
-                               uint8_t* flags, hipStream_t stream) {
-  SelectArgs a{score, q_off, k_off, rrow, rcol, flags, Cq, Ck, s.N, budget};
-  if (Cq <= kSelWaves * kSrRows && Ck <= 64 * kSrCpl)
-    hipLaunchKernelGGL(select_reg_kernel, dim3(s.B * s.H), dim3(kSelThreads), 0, stream, a);
-  else
-    hipLaunchKernelGGL(select_kernel, dim3(s.B * s.H), dim3(kSelThreads), 0, stream, a);
+                               void* scratch, bool hist_ready, hipStream_t stream) {
+  const SelScratch w = sel_scratch(s, Cq);
+  char* base = (char*)scratch;
+  unsigned long long* hs = (unsigned long long*)(base + w.hist);
+  const int bh = s.B * s.H;
+  if (!hist_ready) {
+    ScoreHistArgs h{q_off, k_off, nullptr, nullptr, nullptr, nullptr, (float*)score, hs, Cq, Ck, 0};
+    hipLaunchKernelGGL(score_hist_kernel, dim3(kHistGroups, bh), dim3(256), 0, stream, h);
+  }
+  SelectArgs a{score, q_off, k_off, rrow, rcol, hs, (SelState*)(base + w.state),
+               (unsigned long long*)(base + w.cand), (int32_t*)(base + w.counts), Cq, Ck, s.N, budget};
+  const dim3 rows((Cq + 3) / 4, bh);
+  hipLaunchKernelGGL(select_level1_kernel, dim3(bh), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(select_gather_kernel, rows, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(select_resolve_kernel, dim3(bh), dim3(kSelThreads), 0, stream, a);
+  hipLaunchKernelGGL(select_count_kernel, rows, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(select_emit_kernel, rows, dim3(256), 0, stream, a);
   return launch_ok("route_select") ? BSA_OK : BSA_ERR_HIP;
 }
 
@@ -1908,10 +2019,20 @@ size_t comp_attn_workspace(const bsa_shape& s, int Cq, int Ck) {
   return comp_ws(s, Cq, Ck).total;
 }
 
+void comp_attn_bf16_slots(const bsa_shape& s, int Cq, int Ck, void* ws, uint16_t** kb, uint16_t** vb) {
+  if (!comp_d128(s)) {
+    *kb = *vb = nullptr;
+    return;
+  }
+  const CompWs w = comp_ws(s, Cq, Ck);
+  *kb = (uint16_t*)((char*)ws + w.kb);
+  *vb = (uint16_t*)((char*)ws + w.vb);
+}
+
 bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o, float* lse, const bsa_shape& s,
                             const int32_t* q_off, int Cq, const int32_t* k_off, int Ck, const int32_t* rrow,
                             const int32_t* rcol, const float* kc, const float* vc, float scale, void* ws,
-                            hipStream_t stream) {
+                            hipStream_t stream, bool bf16_ready) {
   CompArgs p;
   p.s = svg_args(q, k, v, s, q_off, Cq, k_off, Ck);
   p.o = (uint16_t*)o; p.lse = lse; p.rrow = rrow; p.rcol = rcol; p.k_cent = kc; p.v_cent = vc;
@@ -1925,8 +2046,9 @@ bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o
     uint16_t* kb = (uint16_t*)(base + w.kb);
     uint16_t* vb = (uint16_t*)(base + w.vb);
     const int64_t n2 = (int64_t)s.B * s.H * Ck * s.D / 2;
-    hipLaunchKernelGGL(centroid_bf16_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, kc, vc, kb,
-                       vb, n2);
+    if (!bf16_ready)
+      hipLaunchKernelGGL(centroid_bf16_kernel, dim3((unsigned)((n2 + 255) / 256)), dim3(256), 0, stream, kc, vc,
+                         kb, vb, n2);
     CompOrderArgs oa{q_off, k_off, rrow, rcol, Cq, Ck, s.B * s.H, w.cap, (int32_t*)(base + w.work),
                      (int32_t*)(base + w.ntile), (int32_t*)(base + w.item), (int32_t*)(base + w.x),
                      (int32_t*)(base + w.count)};

@@ -328,7 +328,10 @@ bsa_status bsa_scatter_rows(const void* y, bsa_dtype dtype, const bsa_shape* sha
 
 /* Step 1 (idea 1, cluster centroids): q_cent[a] = mean of the q rows of cluster
  * a; k_cent[b], v_cent[b] = means of the k and v rows of key cluster b (fp32
- * accumulation; an empty cluster gets zeros). */
+ * accumulation; an empty cluster gets zeros).  q_cent may be NULL (then q is
+ * not read), or k_cent and v_cent both NULL (then k and v are not read); the
+ * route-score call computes the key and value centroids itself, so the
+ * routing path asks for the query centroids only. */
 bsa_status bsa_cluster_centroids(const void* q, const void* k, const void* v, bsa_dtype dtype,
                                  const bsa_shape* shape, const int32_t* q_off, int32_t Cq,
                                  const int32_t* k_off, int32_t Ck, float* q_cent, float* k_cent,
@@ -342,17 +345,21 @@ size_t bsa_route_scores_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck
  * all keys j, m_a = max_j l_aj, Z_a = sum_j exp(l_aj - m_a),
  *   e_ab = (sum_{j in b} exp(l_aj - m_a) v_j - n_b exp(scale c^_a . c_b - m_a) vbar_b) / Z_a,
  *   score[a][b] = |e_ab|^2 / n_b  (squared output error per unit cost),
- * and 0 when cluster a or b is empty.  The sum is accumulated as
- * sum_{j in b} (exp(l_aj - m_a) - exp(scale c^_a.c_b - m_a)) v_j (n_b vbar_b =
- * sum_j v_j), with the proxies and the weight differences split into two bf16
- * MFMA operands each (about 16 significant bits); everything else is fp32.
- * workspace: at least
- * bsa_route_scores_workspace bytes, 256-byte aligned. */
+ * and 0 when cluster a or b is empty.  q_cent (input) holds the query
+ * centroids c^_a (bsa_cluster_centroids); the key and value centroids c_b,
+ * vbar_b (idea 1) are computed in the same pass over k and v and written to
+ * k_cent and v_cent (outputs, as bsa_cluster_centroids would give them up to
+ * fp32 rounding order), so k and v are read once.  Head_dim 128: the pass
+ * accumulates U_ab = sum_{j in b} exp(l_aj - m_a) v_j with the proxies and the
+ * weights split into two bf16 MFMA operands each (about 16 significant bits),
+ * takes scale c^_a . c_b as the mean of the keys' logits, and forms
+ * U_ab - n_b exp(scale c^_a . c_b - m_a) vbar_b in fp32; head_dim 64 takes the
+ * centroids first and accumulates the difference directly.
+ * workspace: at least bsa_route_scores_workspace bytes, 256-byte aligned. */
 bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const bsa_shape* shape,
                             const int32_t* q_off, int32_t Cq, const int32_t* k_off, int32_t Ck,
-                            const float* q_cent, const float* k_cent, const float* v_cent,
-                            float scale, float* score, void* workspace, size_t ws_bytes,
-                            void* stream);
+                            const float* q_cent, float* k_cent, float* v_cent, float scale, float* score,
+                            void* workspace, size_t ws_bytes, void* stream);
 
 /* Workspace bytes of bsa_route_select (0 for an invalid shape). */
 size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
@@ -364,7 +371,10 @@ size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck
  * score array.  Output CSR per (batch, head): route_row_ptr int32 [B*H][Cq + 1]
  * (offsets relative to that head's route_col segment), route_col int32
  * [B*H][Cq * Ck] with the kept key clusters of each query cluster ascending.
- * density_ppm in [0, 10^6]. */
+ * density_ppm in [0, 10^6].  Scores must be non-negative and not NaN (the
+ * order is taken on their bit patterns).  workspace: at least
+ * bsa_route_select_workspace bytes, 256-byte aligned (keep flags and the cost
+ * histograms of the first selection level). */
 bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const int32_t* q_off,
                             int32_t Cq, const int32_t* k_off, int32_t Ck, int32_t density_ppm,
                             int32_t* route_row_ptr, int32_t* route_col, void* workspace,
@@ -401,15 +411,21 @@ size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_
 /* Workspace bytes of bsa_centroid_compensate (0 for an invalid shape). */
 size_t bsa_centroid_compensate_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck);
 
-/* Steps 1-4 in one call: centroids, route scores, route selection at
- * density_ppm, compensated attention.  route_row_ptr / route_col receive the
- * route; score (nullable) receives the scores.  workspace: at least
- * bsa_centroid_compensate_workspace bytes, 256-byte aligned. */
+/* Steps 1-4 in one call.  use_given_route = 0: query centroids, route scores
+ * (with the key and value centroids from the same pass), route selection at
+ * density_ppm, compensated attention; route_row_ptr / route_col receive the
+ * route and score (nullable) the scores.  use_given_route = 1: route_row_ptr
+ * / route_col are inputs (a route from an earlier call, or any route of the
+ * form bsa_route_select writes); the call takes the centroids and runs the
+ * compensated attention on that route (density_ppm and score are ignored).
+ * workspace: at least bsa_centroid_compensate_workspace bytes, 256-byte
+ * aligned. */
 bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, void* o, float* lse,
                                    bsa_dtype dtype, const bsa_shape* shape, const int32_t* q_off,
                                    int32_t Cq, const int32_t* k_off, int32_t Ck, int32_t density_ppm,
-                                   float scale, int32_t* route_row_ptr, int32_t* route_col,
-                                   float* score, void* workspace, size_t ws_bytes, void* stream);
+                                   int32_t use_given_route, float scale, int32_t* route_row_ptr,
+                                   int32_t* route_col, float* score, void* workspace, size_t ws_bytes,
+                                   void* stream);
 
 /* ---- latent inter-frame pruning and restoration --------------------------
  * Source: "LIPAR: 비디오 생성 AI 를 위한 '스마트 스킵' 기술" (summary of the

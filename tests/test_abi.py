@@ -121,7 +121,7 @@ def test_workspace_queries_do_not_crash_and_are_aligned(lib):
                 assert rw > 0 and rw % 256 == 0
                 assert rw >= 2 * H * Cq * Ck * 4                # e and m of every block at least
                 fw = lib.bsa_centroid_compensate_workspace(ctypes.byref(sh), Cq, Ck)
-                assert fw >= rw + H * Cq * Ck * (4 + 1)         # plus scores and select flags
+                assert fw >= rw + H * Cq * Ck * 4               # plus the scores
 
 
 def test_each_struct_is_defined_once_in_the_native_sources():
@@ -280,3 +280,36 @@ def test_linear_no_alloc_argument_checks(lib):
     assert call(_shape(B=1, H=2, N=0, D=128)) == 1
     # the benchmark shape fits
     assert lib.bsa_linear_attn_workspace(ctypes.byref(_shape(B=1, H=12, N=196560, D=128))) <= 40 << 20
+
+
+def test_cluster_centroids_output_choice(lib):
+    """bsa_cluster_centroids computes the query set, the key set or both; the
+    argument checks run before any HIP call."""
+    p = ctypes.c_void_p(4096)
+    sh = _shape(B=1, H=2, N=1000, D=128)
+
+    def cc(qc, kc, vc, q=p):
+        return lib.bsa_cluster_centroids(q, p, p, 0, ctypes.byref(sh), p, 10, p, 20, qc, kc, vc, None)
+
+    assert cc(None, None, None) == 1                         # nothing asked for
+    assert cc(None, p, None) == 1                            # k_cent without v_cent
+    assert cc(p, None, None, q=None) == 1                    # query centroids need q
+    assert cc(p, None, None, q=ctypes.c_void_p(4098)) == 1   # misaligned q
+    assert b"bsa_cluster_centroids" in lib.bsa_last_error()
+
+
+def test_fused_compensation_argument_checks(lib):
+    p = ctypes.c_void_p(4096)
+    sh = _shape(B=1, H=2, N=1000, D=128)
+
+    def fused(use_given=0, ppm=150000, ws=1 << 30):
+        return lib.bsa_centroid_compensate(p, p, p, p, None, 0, ctypes.byref(sh), p, 10, p, 20, ppm, use_given,
+                                           ctypes.c_float(0.1), p, p, None, ctypes.c_void_p(1 << 20), ws, None)
+
+    assert fused(use_given=2) == 1
+    assert fused(ppm=-1) == 1
+    assert fused(ws=16) == 4
+    assert b"bsa_centroid_compensate" in lib.bsa_last_error()
+    need = lib.bsa_centroid_compensate_workspace(ctypes.byref(sh), 10, 20)
+    assert need % 256 == 0 and need >= lib.bsa_route_scores_workspace(ctypes.byref(sh), 10, 20)
+    assert lib.bsa_route_select_workspace(ctypes.byref(sh), 10, 20) >= 2 * 8 * 2048 * 8   # cost histograms

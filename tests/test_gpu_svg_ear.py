@@ -44,8 +44,8 @@ def _head(d, r):
 def _check_steps(bsa, wl, d, ppm, attn_clusters=None):
     q, k, v, qo, ko = _dev(d)
     scale = 1.0 / math.sqrt(wl.D)
-    qc, kc, vc = bsa.cluster_centroids(q, k, v, qo, ko)
-    score = bsa.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+    qc, kc0, vc0 = bsa.cluster_centroids(q, k, v, qo, ko)
+    score, kc, vc = bsa.route_scores(k, v, qo, ko, qc, scale)
     torch.cuda.synchronize()
     nh = wl.B * wl.H
     oracle_scores32 = np.empty((nh, wl.n_q_clusters, wl.n_k_clusters), np.float32)
@@ -53,7 +53,8 @@ def _check_steps(bsa, wl, d, ppm, attn_clusters=None):
     for r in range(nh):
         hq, hk, hv, hqo, hko = _head(d, r)
         cents = oe.centroids(hq, hk, hv, hqo, hko)
-        for name, got in (("cq", qc[r]), ("ck", kc[r]), ("vk", vc[r])):
+        # centroids from the centroid call and (keys, values) from the score pass
+        for name, got in (("cq", qc[r]), ("ck", kc0[r]), ("vk", vc0[r]), ("ck", kc[r]), ("vk", vc[r])):
             g = to_f64(got)
             assert np.abs(g - cents[name]).max() <= 1e-5 * max(1.0, np.abs(cents[name]).max()), name
         sc = oe.route_scores(hk, hv, hko, cents, scale)
@@ -119,8 +120,8 @@ def test_fused_call_matches_steps(gpu_lib):
     q, k, v, qo, ko = _dev(d)
     scale = 1.0 / math.sqrt(wl.D)
     out, lse, rrow, rcol, score = gpu_lib.centroid_compensate(q, k, v, qo, ko, 150000, return_score=True)
-    qc, kc, vc = gpu_lib.cluster_centroids(q, k, v, qo, ko)
-    s2 = gpu_lib.route_scores(k, v, qo, ko, qc, kc, vc, scale)
+    qc, _, _ = gpu_lib.cluster_centroids(q, k, v, qo, ko, which="query")
+    s2, kc, vc = gpu_lib.route_scores(k, v, qo, ko, qc, scale)
     r2, c2 = gpu_lib.route_select(s2, q, qo, ko, 150000)
     o2, l2 = gpu_lib.compensated_attn_fwd(q, k, v, qo, ko, r2, c2, kc, vc, scale)
     torch.cuda.synchronize()
@@ -177,3 +178,67 @@ def test_svg_ear_32k(gpu_lib, svg_full):
         jac.append(len(mine & ref) / max(1, len(mine | ref)))
     print("route Jaccard per head:", [round(j, 4) for j in jac])
     assert min(jac) > 0.9
+
+
+def test_fused_call_with_given_route(gpu_lib):
+    """use_given_route = 1: the route is an input.  Given back the route of an
+    earlier call, the output is bitwise the step-by-step attention on it (the
+    same centroid and attention kernels), and within the bf16 bar of the
+    earlier call's output (whose key centroids came from the score pass).  A
+    route keeping every block gives dense attention."""
+    wl, d = _small(seed=56)
+    q, k, v, qo, ko = _dev(d)
+    scale = 1.0 / math.sqrt(wl.D)
+    out0, lse0, rrow, rcol = gpu_lib.centroid_compensate(q, k, v, qo, ko, 150000)
+    rr_in, rc_in = rrow.clone(), rcol.clone()
+    out1, lse1, rr_after, rc_after = gpu_lib.centroid_compensate(q, k, v, qo, ko, 0, rrow=rr_in, rcol=rc_in,
+                                                                 use_given_route=True)
+    qc, kc, vc = gpu_lib.cluster_centroids(q, k, v, qo, ko)
+    o2, l2 = gpu_lib.compensated_attn_fwd(q, k, v, qo, ko, rrow, rcol, kc, vc, scale)
+    torch.cuda.synchronize()
+    assert torch.equal(rr_after, rrow) and torch.equal(rc_after, rcol)      # inputs left untouched
+    assert torch.equal(out1.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse1, l2)
+    assert_parity(to_f64(out1), to_f64(out0), "bf16", "given route vs routed call")
+
+    # every block kept: dense attention in cluster order
+    nh, Cq, Ck = wl.B * wl.H, wl.n_q_clusters, wl.n_k_clusters
+    full_rp = torch.arange(0, (Cq + 1) * Ck, Ck, dtype=torch.int32).repeat(nh, 1).cuda()
+    full_col = torch.arange(Ck, dtype=torch.int32).repeat(nh, Cq).cuda()
+    out3, _, _, _ = gpu_lib.centroid_compensate(q, k, v, qo, ko, 0, rrow=full_rp, rcol=full_col,
+                                                use_given_route=True)
+    torch.cuda.synchronize()
+    ref, _ = oa.dense_attention(gen.to_f64(d["q"], "bf16"), gen.to_f64(d["k"], "bf16"),
+                                gen.to_f64(d["v"], "bf16"), scale)
+    assert_parity(to_f64(out3), ref, "bf16", "given full route = dense attention")
+
+
+@pytest.mark.parametrize("kind", ["equal", "three_values", "one_bin", "log_uniform"])
+def test_selection_ties_and_large_cut_bins(gpu_lib, kind):
+    """The selection on given scores, bit-exact against the oracle's sorted-prefix
+    selection, where the cut falls among many equal scores ("equal",
+    "three_values": the radix passes and the index-order ties), among 50,000
+    distinct scores inside one first-level bin ("one_bin"), and among scores
+    spread over six decades ("log_uniform": the gathered, sorted bin)."""
+    r = np.random.default_rng(81)
+    H, Cq, Ck, N = 2, 100, 500, 20000
+    shp = torch.empty((1, H, N, 128), dtype=torch.bfloat16, device="cuda")
+    q_off = np.stack([np.concatenate([[0], np.sort(r.integers(0, N, Cq - 1)), [N]]) for _ in range(H)]).astype(np.int32)
+    k_off = np.stack([np.concatenate([[0], np.sort(r.integers(0, N, Ck - 1)), [N]]) for _ in range(H)]).astype(np.int32)
+    if kind == "equal":
+        sc = np.ones((H, Cq, Ck), np.float32)
+    elif kind == "three_values":
+        sc = r.choice(np.array([1.0, 2.0, 3.0], np.float32), (H, Cq, Ck))
+    elif kind == "one_bin":
+        sc = (1.0 + 0.05 * r.random((H, Cq, Ck))).astype(np.float32)
+    else:
+        sc = (10.0 ** r.uniform(-6, 0, (H, Cq, Ck))).astype(np.float32)
+    qo, ko = torch.from_numpy(q_off).cuda(), torch.from_numpy(k_off).cuda()
+    for ppm in (150000, 1000, 999999):
+        rrow, rcol = gpu_lib.route_select(torch.from_numpy(sc).cuda(), shp, qo, ko, ppm)
+        torch.cuda.synchronize()
+        rr, rc = rrow.cpu().numpy(), rcol.cpu().numpy()
+        for h in range(H):
+            want_rp, want_col, _ = oe.select_route(sc[h].astype(np.float64), np.diff(q_off[h]), np.diff(k_off[h]),
+                                                   N, ppm)
+            assert np.array_equal(rr[h], want_rp), (kind, ppm, h)
+            assert np.array_equal(rc[h][: want_rp[-1]], want_col), (kind, ppm, h)

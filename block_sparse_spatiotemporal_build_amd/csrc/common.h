@@ -76,6 +76,35 @@ typedef __attribute__((address_space(3))) void lds_void;
 // never makes a wave wait on its own vector-memory copies in flight
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped, stride 0) buffer loads, gfx9 family
+// Raw buffer descriptor as four scalar words (base, stride 0, size, format),
+// for copies issued from inline assembly.
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4;
+__device__ __forceinline__ i32x4 raw_buffer_desc(const void* base, uint32_t bytes) {
+  const uint64_t b = (uint64_t)base;
+  return i32x4{(int32_t)(uint32_t)b, (int32_t)((b >> 32) & 0xffffu), (int32_t)bytes, kBufferWord3};
+}
+// buffer_load_dwordx4 ... lds: lane i copies 16 bytes at byte offset voff of
+// the buffer to LDS byte address lds + 16 i (lds is wave-uniform).  Issued from
+// assembly so the compiler's wait insertion does not see it: it cannot tell
+// which LDS stage such a copy writes and would otherwise wait for copies still
+// in flight before reading any stage.  The caller orders every read of the
+// destination after an explicit vmcnt wait (which counts these copies) and a
+// barrier; the copy writes no register.
+// The copy writes M0, which the compiler treats as reserved: a kernel that
+// uses it must not also use the compiler's LDS-copy builtins (which keep their
+// LDS address in M0) or anything else that holds a value in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)p;
+}
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 

@@ -348,25 +348,30 @@ __global__ void __launch_bounds__(256) probe_kernel(ProbeArgs p) {
 // ---------------------------------------------------------------------------
 // fused route probe, head_dim 128
 // ---------------------------------------------------------------------------
-// One pass over the keys of a split of key clusters (split s covers clusters
-// [s cps, min((s + 1) cps, Ck)), their keys packed into 32-key tiles across
-// cluster boundaries, so a small cluster costs no padded tile).  Per tile:
+// One pass over the keys of a split of key clusters.  Split s of S takes the
+// clusters whose first key lies in [K0 + s T / S, K0 + (s + 1) T / S) (T keys
+// in the head, K0 its first), so splits hold about equal numbers of keys.
+// Each cluster's keys are cut into groups of 16, the k-step of the value
+// product; the last group of a cluster is padded with copies of its last key,
+// and two consecutive groups form one 32-key tile, so a tile may hold two
+// clusters but a k-step never does.  Per tile:
 //   S^T = K (c^_hi + c^_lo)^T for the workgroup's 128 proxies (4 waves x 32),
+//         with c^ scaled by c2 = scale log2(e) beforehand, so S is the logit t
+//         in log2 units;
 //   one lazily moved reference m_run and a sum l_run per proxy over every key
-//   of the split (the proxy softmax of idea 2), and for each cluster segment:
-//     U  += V_seg^T P_seg   (P = exp2(t - m_run) as bf16 hi + lo, t = c2 s)
-//     sv += column sums of V_seg, sk += column sums of K_seg (v_dot2 with a
-//           0/1 mask over the transposed LDS reads)
-//     ls += sum of t over the segment's keys.
-// When cluster b (n_b keys) ends:
+//   of the split (the proxy softmax of idea 2); and per group g:
+//     U  += V_g^T P_g   (P = exp2(t - m_run) as bf16 hi + lo)
+//     sv += column sums of V_g, sk += column sums of K_g, both over this
+//           wave's 32 dims (v_dot2 with 0/1 masks that drop the padding)
+//     ls += sum of t over the group's keys.
+// When cluster b (n_b keys) ends, the waves exchange their sv through LDS and
 //   lc = ls / n_b = c2 c^ . c_b   (the mean logit is the logit of the mean key)
-//   e  = U - exp2(lc - m_run) sv  = sum_j (p_j - p_c) v_j,  e2 = |e|^2
-// at reference m_run.  So the key and value centroids come out of the same
-// pass (c_b = sk / n_b, vbar_b = sv / n_b) and K and V are read once.  Two LDS
-// stages, one tile copy in flight: each step waits for every vector memory
-// operation of the wave (the tile copy and the stores of the clusters that
-// ended in the step before), so result stores need no separate tracking.
-constexpr int kFpTK = 32, kFpMaxCps = 16;
+//   e  = U - exp2(lc - m_run) sv = sum_j (p_j - p_c) v_j,  e2 = |e|^2
+// at reference m_run.  The key and value centroids come out of the same pass
+// (c_b = sk / n_b, vbar_b = sv / n_b), so K and V are read once.  Padding
+// copies a key of the same tile, so the tile maximum needs no mask.  Four LDS
+// stages, three tile copies in flight.
+constexpr int kFpTK = 32, kFpGK = 16;
 
 // acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2_f32_bf16).
 // Written as inline asm because the compiler builtin, fed 32-bit elements of a
@@ -388,17 +393,27 @@ struct FusedProbeArgs {
   float* v_cent;        // [BH][Ck][D] output
   uint16_t* kc_bf;      // [BH][Ck][D] bf16 copy (nullable)
   uint16_t* vc_bf;      // [BH][Ck][D] bf16 copy (nullable)
-  int splits, cps;
+  int splits;
   float c2;  // scale * log2(e)
 };
+
+// Position of a group walk: local cluster c, key offset off of the group in
+// it, and the cluster's key range [k0, k1).  c == nclu: past the last cluster.
+struct FpCursor {
+  int c, off, k0, k1;
+};
+
+// LDS element at a byte offset from a stage base
+__device__ __forceinline__ const uint16_t* lds_byte(const uint16_t* base, uint32_t off) {
+  return (const uint16_t*)((const char*)base + off);
+}
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 probe_fused_d128_kernel(FusedProbeArgs p) {
   constexpr int D = 128, KT = 8, DT = 4, TILE = kFpTK * D;
-  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t CL[128 * D];  // proxy lo halves, rows swizzled (swz_k)
-  __shared__ int koffs[kFpMaxCps + 1];
+  __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE], K2[TILE], K3[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE], V2[TILE], V3[TILE];
+  __shared__ float svx[2][D];  // value column sums of a finished cluster (two slots)
 
   const SvgArgs& a = p.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -407,15 +422,37 @@ probe_fused_d128_kernel(FusedProbeArgs p) {
   const int prox = blockIdx.z * 128 + prow;  // proxy (query cluster) of this lane
   const bool pvalid = prox < a.Cq;
   const bool write_cent = blockIdx.z == 0;
-  const int32_t* koff_g = a.k_off + (int64_t)bh * (a.Ck + 1);
+  // the head's cluster offsets, read through the constant address space
+  // (scalar loads, uniform across the workgroup)
+  const cint_ptr koffs = (cint_ptr)(a.k_off + (int64_t)bh * (a.Ck + 1));
   const uint16_t* Kh = head_ptr(a.k, a, bh);
   const uint16_t* Vh = head_ptr(a.v, a, bh);
-  const int b0 = split * p.cps, nclu = min(b0 + p.cps, a.Ck) - b0;
+  int b0, nclu;
+  {
+    // clusters whose first key lies below each bound (offsets ascend): every
+    // lane tests 1/64 of the offsets, the ballots count
+    const int kfirst = koffs[0], total = koffs[a.Ck] - kfirst;
+    const int lo = kfirst + (int)((int64_t)split * total / p.splits);
+    const int hi_k = kfirst + (int)((int64_t)(split + 1) * total / p.splits);
+    const int32_t* offs = a.k_off + (int64_t)bh * (a.Ck + 1);
+    int n_lo = 0, n_hi = 0;
+#pragma unroll 8
+    for (int base = 0; base < a.Ck; base += 64) {
+      const int i = base + lane;
+      const int o = i < a.Ck ? offs[i] : INT32_MAX;
+      n_lo += __popcll(__ballot(o < lo));
+      n_hi += __popcll(__ballot(o < hi_k));
+    }
+    b0 = split == 0 ? 0 : n_lo;
+    const int b1 = split + 1 == p.splits ? a.Ck : n_hi;
+    nclu = max(b1 - b0, 0);
+  }
+  auto koff = [&](int c) -> int { return koffs[b0 + c]; };
 
-  // proxy fragments: c^ = hi + lo, both bf16 (about 2^-16 relative), so the
-  // logits keep the small spread of a tight cluster; hi is the MFMA B operand
-  // in registers, lo is read from LDS per tile
-  bf16x8 cf[KT];
+  // proxy fragments (MFMA B operands, in registers): c2 c^ = hi + lo, both
+  // bf16 (about 2^-16 relative), so the logits keep the small spread of a
+  // tight cluster
+  bf16x8 cf[KT], cl[KT];
   {
     // invalid proxies read proxy 0 (in bounds) and use zeros
     const float* src = p.q_cent + ((int64_t)bh * a.Cq + (pvalid ? prox : 0)) * D + hi * 8;
@@ -426,78 +463,114 @@ probe_fused_d128_kernel(FusedProbeArgs p) {
       u32x4 wh, wl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x0 = pvalid ? yv[2 * e] : 0.f, x1 = pvalid ? yv[2 * e + 1] : 0.f;
+        const float x0 = pvalid ? p.c2 * yv[2 * e] : 0.f, x1 = pvalid ? p.c2 * yv[2 * e + 1] : 0.f;
         wh[e] = pack_bf16x2(x0, x1);
         wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
       }
       cf[t] = __builtin_bit_cast(bf16x8, wh);
-      *(u32x4*)&CL[prow * D + (((2 * t + hi) ^ swz_k(prow)) << 3)] = wl;
+      cl[t] = __builtin_bit_cast(bf16x8, wl);
     }
   }
-  for (int i = tid; i <= nclu; i += 256) koffs[i] = koff_g[b0 + i];
   __syncthreads();
   retire_loads();
-  const int K0k = koffs[0], K1k = koffs[nclu];
-  const int ntiles = (K1k - K0k + kFpTK - 1) / kFpTK;
+  const int K1k = nclu > 0 ? koff(nclu) : 0;
 
-  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane / 16
+  // cluster walk: start at cluster c (key k0), skipping empty clusters
+  auto enter = [&](FpCursor& g, int c, int k0) {
+    g.c = c;
+    g.off = 0;
+    g.k0 = k0;
+    g.k1 = c < nclu ? max(koff(c + 1), k0) : k0;
+  };
+  auto skip_empty = [&](FpCursor& g) {
+    while (g.c < nclu && g.k1 == g.k0) enter(g, g.c + 1, g.k1);
+  };
+  // keys in the group at the cursor (0 past the last cluster)
+  auto count_of = [&](const FpCursor& g) { return g.c < nclu ? min(kFpGK, g.k1 - g.k0 - g.off) : 0; };
+
+  // copy roles: wave w, instruction j covers tile rows 8w + 4j + lane / 16, so
+  // waves 0-1 copy the tile's first group and waves 2-3 its second
   const int wv = __builtin_amdgcn_readfirstlane(wave);
   const uint32_t row_bytes = (uint32_t)a.sn * 2u;
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, 0x7fffffff, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, 0x7fffffff, kBufferWord3);
-  auto dma = [&](uint16_t* kst, uint16_t* vst, int u) {
-    const int key0 = K0k + u * kFpTK;
+  const i32x4 krs = raw_buffer_desc(Kh, 0x7fffffffu), vrs = raw_buffer_desc(Vh, 0x7fffffffu);
+  FpCursor dg;  // first group of the next tile to copy
+  enter(dg, 0, nclu > 0 ? koff(0) : 0);
+  skip_empty(dg);
+  auto dma_next = [&](FpCursor& g) {
+    if (g.c >= nclu) return;
+    g.off += kFpGK;
+    if (g.k0 + g.off >= g.k1) {
+      enter(g, g.c + 1, g.k1);
+      skip_empty(g);
+    }
+  };
+  int issued = 0;  // tiles whose copies have been issued
+  auto dma = [&](uint16_t* kst, uint16_t* vst) __attribute__((always_inline)) {
+    if (dg.c >= nclu) return;  // the split's groups are all copied
+    ++issued;
+    FpCursor g = dg;
+    dma_next(dg);
+    if (wv >= 2) g = dg;
+    dma_next(dg);
+    const int cnt = count_of(g), start = g.k0 + g.off;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int row = 8 * wv + 4 * j + (lane >> 4);
-      // rows past the split's last key repeat it (masked out below)
-      const uint32_t ro = (uint32_t)min(key0 + row, K1k - 1) * row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(8 * wv + 4 * j) * D], 16,
-                                               ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16), 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(8 * wv + 4 * j) * D], 16,
-                                               ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16), 0, 0, 0);
+      // padding repeats the group's last key; an empty group (past the
+      // split's last cluster) repeats the split's last key
+      const int r = 8 * (wv & 1) + 4 * j + (lane >> 4);
+      const int key = cnt > 0 ? start + min(r, cnt - 1) : K1k - 1;
+      const uint32_t ro = (uint32_t)key * row_bytes;
+      lds_copy16(krs, ro + (uint32_t)(((lane & 15) ^ swz_k(row)) * 16),
+                 __builtin_amdgcn_readfirstlane(lds_addr(&kst[(8 * wv + 4 * j) * D])));
+      lds_copy16(vrs, ro + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16),
+                 __builtin_amdgcn_readfirstlane(lds_addr(&vst[(8 * wv + 4 * j) * D])));
     }
   };
 
   f32x16 U[DT];
 #pragma unroll
   for (int i = 0; i < DT; ++i) U[i] = f32x16{};
-  float sv[DT] = {0.f, 0.f, 0.f, 0.f}, sk = 0.f, ls = 0.f;
+  float sv = 0.f, sk = 0.f, ls = 0.f;  // sv, sk: dim 32 wave + lane % 32
   float m_run = -1e30f, l_run = 0.f;
+  int par = 0;  // svx slot of the next finished cluster
   const int g16 = lane >> 4, j16 = lane & 15;
-  // per-lane LDS element offsets; each read is base ^ immediate (or + one
-  // delta), the identities are checked for every lane on the host:
-  //   K row fragment of k-step t: kb0 ^ 16 t; proxy lo fragment: cb0 ^ 16 t;
-  //   V transposed reads (ks, dt): 2048 ks + (va0 ^ 32 dt) and + vd0;
-  //   K transposed reads (column sums of this wave's 32 dims): 2048 ks + kt0 / kt1
+  // per-lane LDS byte offsets within a stage; every read is base ^ immediate,
+  // the identities are checked for every lane on the host:
+  //   K row fragment of k-step t:            kb2 ^ 32 t
+  //   V transposed reads (ks, dt):           va2 ^ (4096 ks + 64 dt), rows + 8: ^ 2080 more
+  //   V column sums of this wave's 32 dims:  the (ks, dt = wave) reads
+  //   K transposed reads (same dims):        kt2 ^ 4096 ks, rows + 8: ^ 2176 more
   const int q4 = j16 >> 2, c0 = 2 * (g16 & 1) + ((j16 >> 1) & 1), half4 = (j16 & 1) * 4;
-  const uint32_t kb0 = l32 * D + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1));
-  const uint32_t cb0 = prow * D + 16 * ((prow & 15) >> 1) + 8 * (hi ^ (prow & 1));
-  const uint32_t va0 = (4 * hi + q4) * D + 32 * q4 + 8 * (c0 ^ hi) + half4;
-  const uint32_t vd0 = 1024 + 8 * (((c0 ^ hi) ^ 2) - (c0 ^ hi));
-  const uint32_t kt0_ = (4 * hi + q4) * D + 8 * (4 * (wave ^ hi) + (c0 ^ q4)) + half4;
-  const uint32_t kt1_ = 1024 + (4 * hi + q4) * D + 8 * (4 * ((wave ^ hi) ^ 2) + (c0 ^ q4)) + half4;
+  const uint32_t kb2 = 2 * (l32 * D + 16 * ((l32 & 15) >> 1) + 8 * (hi ^ (l32 & 1)));
+  const uint32_t va2 = 2 * ((4 * hi + q4) * D + 32 * q4 + 8 * (c0 ^ hi) + half4);
+  const uint32_t vw2 = va2 ^ (64 * wave);
+  const uint32_t kt2 = 2 * ((4 * hi + q4) * D + 8 * (4 * (wave ^ hi) + (c0 ^ q4)) + half4);
 
-  // cluster c (local index) is complete: its error and its centroids.  The
-  // correction U -= sv (x) p_c is one MFMA per 32 dims: A holds sv of the
+  // cluster c (local index, n_b keys) is complete: its error and centroids.
+  // The correction U -= sv (x) p_c is one MFMA per 32 dims: A holds sv of the
   // lane's row (dim 32 dt + lane % 32) and B holds -p_c of its column (the
   // proxy), each split into three bf16 pieces (24 bits; each of the nine
   // products is exact in fp32), so e = U - p_c sv keeps fp32 accuracy and
-  // |e|^2 is a lane-local sum.
+  // |e|^2 is a lane-local sum.  Called at the same point by every wave.
   auto split3 = [](float x, float (&o)[3]) {
     o[0] = bf16_lo(f2bf(x));
     o[1] = bf16_lo(f2bf(x - o[0]));
     o[2] = bf16_lo(f2bf(x - o[0] - o[1]));
   };
-  auto finish = [&](int c) {
-    const int nb = koffs[c + 1] - koffs[c];
+  auto finish = [&](int c, int nb) __attribute__((always_inline)) {
     const int bg = b0 + c;
-    float svf[DT];
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) svf[dt] = pair_sum(sv[dt]);
-    const float skf = pair_sum(sk);
+    const float svo = pair_sum(sv), skf = pair_sum(sk);
     float e2 = 0.f;
     if (nb > 0) {
+      if (lane < 32) svx[par][32 * wave + lane] = svo;
+      // wait for this wave's LDS write only, then meet the other waves: a
+      // fence would also wait for the tile copies in flight (they write LDS)
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      float svf[DT];
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) svf[dt] = svx[par][32 * dt + l32];
+      par ^= 1;
       const float lc = pair_sum(ls) / (float)nb;
       float b3[3];
       split3(-fast_exp2(lc - m_run), b3);
@@ -542,59 +615,143 @@ probe_fused_d128_kernel(FusedProbeArgs p) {
     }
     if (write_cent && lane < 32) {
       const float inv = nb > 0 ? 1.f / (float)nb : 0.f;
-      const int64_t o = ((int64_t)bh * a.Ck + bg) * D;
-      const float kc = skf * inv;
-      p.k_cent[o + 32 * wave + lane] = kc;
-      if (p.kc_bf) p.kc_bf[o + 32 * wave + lane] = (uint16_t)f2bf(kc);
-      if (wave == 0)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const float vc = svf[dt] * inv;
-          p.v_cent[o + 32 * dt + lane] = vc;
-          if (p.vc_bf) p.vc_bf[o + 32 * dt + lane] = (uint16_t)f2bf(vc);
-        }
+      const int64_t o = ((int64_t)bh * a.Ck + bg) * D + 32 * wave + lane;
+      const float kc = skf * inv, vc = svo * inv;
+      p.k_cent[o] = kc;
+      p.v_cent[o] = vc;
+      if (p.kc_bf) p.kc_bf[o] = (uint16_t)f2bf(kc);
+      if (p.vc_bf) p.vc_bf[o] = (uint16_t)f2bf(vc);
     }
 #pragma unroll
     for (int i = 0; i < DT; ++i) U[i] = f32x16{};
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) sv[dt] = 0.f;
-    sk = 0.f;
-    ls = 0.f;
+    sv = sk = ls = 0.f;
   };
 
-  // the cluster being accumulated; leading empty clusters finish at once
-  int cb = 0;
-  while (cb < nclu && koffs[cb + 1] == koffs[cb]) finish(cb++);
+  // compute walk: the group being accumulated; leading empty clusters finish
+  // at once
+  FpCursor cg;
+  enter(cg, 0, nclu > 0 ? koff(0) : 0);
+  while (cg.c < nclu && cg.k1 == cg.k0) {
+    finish(cg.c, 0);
+    enter(cg, cg.c + 1, cg.k1);
+  }
 
-  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
-    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): tile u landed, earlier stores done
-    __builtin_amdgcn_s_barrier();
-    if (u + 1 < ntiles) dma(Kn, Vn, u + 1);
-    const int key0 = K0k + u * kFpTK;
-    const int nval = min(kFpTK, K1k - key0);
+  // group ks (keys 16 ks .. 16 ks + 15 of the tile) at the compute cursor;
+  // s holds the tile's logits, the bases are per-step opaque copies
+  auto group = [&](const uint16_t* Kb, const uint16_t* Vb, const f32x16& s, int ks, uint32_t va,
+                   uint32_t vw, uint32_t kt) __attribute__((always_inline)) {
+    const int cnt = count_of(cg);
+    if (cnt == 0) return;
+    // the group's V^T operands and the column-sum reads go out first; P is
+    // built while they are in flight
+    u32x4 vfr[DT];
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t o = 4096 * ks + 64 * dt;
+      const u32x2 v0 = lds_tr16(lds_byte(Vb, va ^ o)), v1 = lds_tr16(lds_byte(Vb, va ^ (o + 2080)));
+      vfr[dt] = u32x4{v0[0], v0[1], v1[0], v1[1]};
+    }
+    u32x4 wvv, wk;
+    {
+      const u32x2 v0 = lds_tr16(lds_byte(Vb, vw ^ (4096 * ks))), v1 = lds_tr16(lds_byte(Vb, vw ^ (4096 * ks + 2080)));
+      const u32x2 k0 = lds_tr16(lds_byte(Kb, kt ^ (4096 * ks))), k1 = lds_tr16(lds_byte(Kb, kt ^ (4096 * ks + 2176)));
+      wvv = u32x4{v0[0], v0[1], v1[0], v1[1]};
+      wk = u32x4{k0[0], k0[1], k1[0], k1[1]};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // this lane's 8 keys of the group: 4 hi + (e & 3) + 8 (e >> 2), e = 0..7,
+    // logits s[8 ks + e]
+    u32x4 wh, wl, mw;
+    float lsum = 0.f, psum = 0.f;
+    if (cnt == kFpGK) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float t0 = s[8 * ks + 2 * e], t1 = s[8 * ks + 2 * e + 1];
+        const float x0 = fast_exp2(t0 - m_run), x1 = fast_exp2(t1 - m_run);
+        lsum += t0 + t1;
+        psum += x0 + x1;
+        wh[e] = pack_bf16x2(x0, x1);
+        wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+        mw[e] = 0x3f803f80u;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int k0 = 4 * hi + ((2 * e) & 3) + 8 * ((2 * e) >> 2);
+        const bool in0 = k0 < cnt, in1 = k0 + 1 < cnt;
+        const float t0 = s[8 * ks + 2 * e], t1 = s[8 * ks + 2 * e + 1];
+        const float x0 = in0 ? fast_exp2(t0 - m_run) : 0.f, x1 = in1 ? fast_exp2(t1 - m_run) : 0.f;
+        lsum += (in0 ? t0 : 0.f) + (in1 ? t1 : 0.f);
+        psum += x0 + x1;
+        wh[e] = pack_bf16x2(x0, x1);
+        wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
+        mw[e] = (in0 ? 0x3f80u : 0u) | (in1 ? 0x3f800000u : 0u);
+      }
+    }
+    ls += lsum;
+    l_run += psum;
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, wh), plf = __builtin_bit_cast(bf16x8, wl);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, vfr[dt]);
+      U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, U[dt], 0, 0, 0);
+      U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plf, U[dt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sv = dot2_bf16(wvv[e], mw[e], sv);
+      sk = dot2_bf16(wk[e], mw[e], sk);
+    }
+    // advance; the group that ends a cluster finishes it (and any empty
+    // clusters after it)
+    cg.off += kFpGK;
+    if (cg.k0 + cg.off >= cg.k1) {
+      finish(cg.c, cg.k1 - cg.k0);
+      enter(cg, cg.c + 1, cg.k1);
+      while (cg.c < nclu && cg.k1 == cg.k0) {
+        finish(cg.c, 0);
+        enter(cg, cg.c + 1, cg.k1);
+      }
+    }
+  };
+
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u)
+                  __attribute__((always_inline)) {
+    // tile u landed.  Loads return in order, so while a copy of tile u is
+    // outstanding all copies of the later tiles (issued after it, four per
+    // tile) are too: waiting until at most 4 (one later tile issued) or 8 (two)
+    // operations remain covers tile u even with result stores in between
+    // (which only make it wait longer)
+    const int ahead = issued - u - 1;
+    if (ahead >= 2) asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else if (ahead == 1) asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     // the bases are opaque here, so the XORed offsets are formed next to their
     // reads instead of being held across the loop
-    uint32_t kb = kb0, clb = cb0, va = va0, vd = vd0, kt0 = kt0_, kt1 = kt1_;
-    asm volatile("" : "+v"(kb), "+v"(clb), "+v"(va), "+v"(vd), "+v"(kt0), "+v"(kt1));
-    // S^T (32 keys x 32 proxies) = K (c_hi + c_lo)^T
+    uint32_t kb = kb2, va = va2, vw = vw2, kt = kt2;
+    asm volatile("" : "+v"(kb), "+v"(va), "+v"(vw), "+v"(kt));
+    // S^T (32 keys x 32 proxies) = K (c_hi + c_lo)^T, in log2 units: all K
+    // reads first, then the MFMA chain
+    bf16x8 kf[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) kf[t] = *(const bf16x8*)lds_byte(Kb, kb ^ (32 * t));
+    __builtin_amdgcn_sched_barrier(0);
     f32x16 s = f32x16{};
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      const bf16x8 kf = *(const bf16x8*)&Kb[kb ^ (16 * t)];
-      const bf16x8 clo = *(const bf16x8*)&CL[clb ^ (16 * t)];
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, cf[t], s, 0, 0, 0);
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, clo, s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], cf[t], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], cl[t], s, 0, 0, 0);
     }
-    // key row of s[r]: 8 (r / 4) + 4 hi + r % 4
-    if (nval < kFpTK) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (8 * (r >> 2) + 4 * hi + (r & 3) >= nval) s[r] = -__builtin_inff();
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the next copy (tile u + 3, if any) goes out while the chain runs (stage
+    // Kn was released by the barrier above)
+    dma(Kn, Vn);
+    // key row of s[r]: 8 (r / 4) + 4 hi + r % 4; padding rows repeat a key of
+    // this tile, so they never raise the maximum
     float mx = s[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
-    const float m_new = fmaxf(m_run, pair_max(mx) * p.c2);
+    const float m_new = fmaxf(m_run, pair_max(mx));
     if (__any(m_new - m_run > kLazyRescaleLog2)) {
       const float alpha = fast_exp2(m_run - m_new);
       l_run *= alpha;
@@ -602,75 +759,25 @@ probe_fused_d128_kernel(FusedProbeArgs p) {
       for (int i = 0; i < DT; ++i) U[i] *= alpha;
       m_run = m_new;
     }
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[r] *= p.c2;  // logit t in log2 units (-inf on rows past the split)
-
-    // cluster segments of the tile: P = exp2(t - m_run) of the segment's keys
-    // (bf16 hi + lo, the B operand of V^T P), built per key half
-    int lo = 0;
-    while (lo < nval && cb < nclu) {
-      const int hi_end = min(koffs[cb + 1] - key0, nval);
-      if (hi_end <= lo) break;  // offsets not ascending: stop rather than loop
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (lo >= 16 * ks + 16 || hi_end <= 16 * ks) continue;
-        // this lane's 8 keys of half ks: 16 ks + 4 hi + (e & 3) + 8 (e >> 2)
-        uint32_t mw[4];
-        u32x4 wh, wl;
-        float lsum = 0.f, psum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int k0 = 16 * ks + 4 * hi + ((2 * e) & 3) + 8 * ((2 * e) >> 2);
-          const bool in0 = k0 >= lo && k0 < hi_end, in1 = k0 + 1 >= lo && k0 + 1 < hi_end;
-          mw[e] = (in0 ? 0x3f80u : 0u) | (in1 ? 0x3f800000u : 0u);
-          const float t0 = s[8 * ks + 2 * e], t1 = s[8 * ks + 2 * e + 1];
-          const float x0 = in0 ? fast_exp2(t0 - m_run) : 0.f, x1 = in1 ? fast_exp2(t1 - m_run) : 0.f;
-          lsum += (in0 ? t0 : 0.f) + (in1 ? t1 : 0.f);
-          psum += x0 + x1;
-          wh[e] = pack_bf16x2(x0, x1);
-          wl[e] = pack_bf16x2(x0 - bf16_lo(wh[e]), x1 - bf16_hi(wh[e]));
-        }
-        ls += lsum;
-        l_run += psum;
-        const bf16x8 pf = __builtin_bit_cast(bf16x8, wh), plf = __builtin_bit_cast(bf16x8, wl);
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint32_t vo = 2048 * ks + (va ^ (32 * dt));
-          const u32x2 v0 = lds_tr16(&Vb[vo]);
-          const u32x2 v1 = lds_tr16(&Vb[vo + vd]);
-          const u32x4 w = {v0[0], v0[1], v1[0], v1[1]};
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, w);
-          U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, U[dt], 0, 0, 0);
-          U[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, plf, U[dt], 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sv[dt] = dot2_bf16(w[e], mw[e], sv[dt]);
-        }
-        {  // column sums of K for dims 32 wave + (lane & 31)
-          const u32x2 k0 = lds_tr16(&Kb[2048 * ks + kt0]);
-          const u32x2 k1 = lds_tr16(&Kb[2048 * ks + kt1]);
-          const u32x4 w = {k0[0], k0[1], k1[0], k1[1]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            sk = dot2_bf16(w[e], mw[e], sk);
-        }
-      }
-      if (key0 + hi_end == koffs[cb + 1]) {
-        finish(cb++);
-        while (cb < nclu && koffs[cb + 1] == koffs[cb]) finish(cb++);
-      }
-      lo = hi_end;
-    }
+    group(Kb, Vb, s, 0, va, vw, kt);
+    group(Kb, Vb, s, 1, va, vw, kt);
   };
 
-  if (ntiles > 0) dma(K0, V0, 0);
-  int u = 0;
-  for (; u + 2 <= ntiles; u += 2) {
-    step(K0, V0, K1, V1, u);
+  dma(K0, V0);
+  dma(K1, V1);
+  dma(K2, V2);
+  // tile u exists iff u < issued (copies run three tiles ahead); issued is
+  // uniform, so every wave leaves at the same step
+  for (int u = 0;; u += 4) {
+    if (u >= issued) break;
+    step(K0, V0, K3, V3, u);
+    if (u + 1 >= issued) break;
     step(K1, V1, K0, V0, u + 1);
+    if (u + 2 >= issued) break;
+    step(K2, V2, K1, V1, u + 2);
+    if (u + 3 >= issued) break;
+    step(K3, V3, K2, V2, u + 3);
   }
-  if (u < ntiles) step(K0, V0, K1, V1, u);
-  while (cb < nclu) finish(cb++);  // trailing empty clusters
 
   const float z = pair_sum(l_run);
   if (pvalid && hi == 0) {
@@ -1915,12 +2022,16 @@ ProbePlan probe_plan(const bsa_shape& s, int Cq, int Ck) {
   const int groups = (Cq + 127) / 128;
   // the fused head_dim-128 kernel addresses a head with 32-bit offsets
   p.fused = s.D == 128 && ((int64_t)s.N + kFpTK) * s.stride_n * 2 < ((int64_t)1 << 31);
-  int want = (512 + bh * groups - 1) / (bh * groups);
+  // about 512 workgroups: two resident on each of the 256 compute units (the
+  // fused kernel's LDS and registers allow two), rounded down so that no
+  // workgroup waits for a second round
+  int want = 512 / (bh * groups);
   if (want > Ck) want = Ck;
   if (want < 1) want = 1;
+  // the fused kernel balances its splits by key count, the general one by
+  // cluster count (cps clusters per split)
   p.cps = (Ck + want - 1) / want;
-  if (p.fused && p.cps > kFpMaxCps) p.cps = kFpMaxCps;
-  p.splits = (Ck + p.cps - 1) / p.cps;
+  p.splits = p.fused ? want : (Ck + p.cps - 1) / p.cps;
   const size_t blocks = (size_t)bh * Cq * Ck;
   p.off_e = 0;
   p.off_m = al256(p.off_e + blocks * 4);
@@ -1947,7 +2058,7 @@ bsa_status launch_route_scores(const void* k, const void* v, const bsa_shape& s,
     f.s = svg_args(nullptr, k, v, s, q_off, Cq, k_off, Ck);
     f.q_cent = qc; f.e_buf = e_buf; f.m_buf = m_buf; f.m_split = m_split; f.z_split = z_split;
     f.k_cent = kc; f.v_cent = vc; f.kc_bf = kc_bf; f.vc_bf = vc_bf;
-    f.splits = pl.splits; f.cps = pl.cps; f.c2 = c2;
+    f.splits = pl.splits; f.c2 = c2;
     hipLaunchKernelGGL(probe_fused_d128_kernel, grid, dim3(256), 0, stream, f);
   } else {
     // the general probe takes the key and value centroids as inputs

@@ -162,21 +162,24 @@ def test_backward_dkdv_copy_rows_in_stage():
 
 def test_fused_probe_offsets_xor_form():
     """Fused route probe (`csrc/svg_ear.hip`): 32-row K and V stages (K rows
-    swz_k, V rows swz_v) and the proxy lo-half array (128 rows, swz_k).
-    K (and proxy) row fragment of lane l at k-step t: row l % 32 (proxy row p),
-    head dims 16 t + 8 (l / 32) + 0..7: kb ^ 16 t.  Transposed reads (ks, dt) of
-    V: 2048 ks + (va ^ 32 dt) and + vd for the rows 8 further; transposed reads
-    of K for the column sums of wave w (columns 32 w + ...): 2048 ks + kt0 and
-    2048 ks + kt1.  Every offset stays inside its array."""
+    swz_k, V rows swz_v), byte offsets.  K row fragment of lane l at k-step t:
+    row l % 32, head dims 16 t + 8 (l / 32) + 0..7: kb2 ^ 32 t.  Transposed
+    reads (ks, dt) of V: va2 ^ (4096 ks + 64 dt), and ^ 2080 more for the rows
+    8 further; this wave's V column sums (wave w) are the dt = w reads,
+    vw2 = va2 ^ 64 w.  Transposed reads of K for the column sums of wave w
+    (columns 32 w + ...): kt2 ^ 4096 ks, and ^ 2176 more for the rows 8
+    further.  Each immediate's bits are disjoint from the others it is
+    combined with, so ^ and + agree there, and every offset stays inside its
+    8 KiB stage."""
     def rowfrag(r, hi):
         return r * 128 + 16 * ((r & 15) >> 1) + 8 * (hi ^ (r & 1))
 
+    stage = 32 * 128 * 2
     for t, lane in itertools.product(range(8), range(64)):
         l32, hi = lane % 32, lane // 32
-        assert phys(l32, 16 * t + 8 * hi, swz_k) == rowfrag(l32, hi) ^ (16 * t) < 32 * 128
-        for w in range(4):
-            p = 32 * w + l32
-            assert phys(p, 16 * t + 8 * hi, swz_k) == rowfrag(p, hi) ^ (16 * t) < 128 * 128
+        kb2 = 2 * rowfrag(l32, hi)
+        assert 2 * phys(l32, 16 * t + 8 * hi, swz_k) == kb2 ^ (32 * t)
+        assert (kb2 ^ (32 * t)) + 16 <= stage
     for ks, dt, w, lane in itertools.product(range(2), range(4), range(4), range(64)):
         hi, g16, j16 = lane // 32, lane // 16, lane % 16
         row = 16 * ks + 4 * hi + j16 // 4
@@ -184,16 +187,19 @@ def test_fused_probe_offsets_xor_form():
         half = (j16 & 1) * 4
         # V (swz_v)
         col = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)
-        vc1 = c0 ^ hi
-        va = (4 * hi + q) * 128 + 32 * q + 8 * vc1 + half
-        vd = 1024 + 8 * ((vc1 ^ 2) - vc1)
-        assert phys(row, col, swz_v) == 2048 * ks + (va ^ (32 * dt))
-        assert phys(row + 8, col, swz_v) == 2048 * ks + (va ^ (32 * dt)) + vd
-        assert 2048 * ks + (va ^ (32 * dt)) + vd + 3 < 32 * 128
+        va2 = 2 * ((4 * hi + q) * 128 + 32 * q + 8 * (c0 ^ hi) + half)
+        o = 4096 * ks + 64 * dt
+        assert o + 2080 == o ^ 2080
+        assert 2 * phys(row, col, swz_v) == va2 ^ o
+        assert 2 * phys(row + 8, col, swz_v) == va2 ^ (o + 2080)
+        assert max(va2 ^ o, va2 ^ (o + 2080)) + 8 <= stage
+        if dt == w:
+            vw2 = va2 ^ (64 * w)
+            assert vw2 ^ (4096 * ks) == va2 ^ o
         # K (swz_k), columns of wave w
         colk = 32 * w + 16 * (g16 & 1) + 4 * (j16 & 3)
-        kt0 = (4 * hi + q) * 128 + 8 * (4 * (w ^ hi) + (c0 ^ q)) + half
-        kt1 = 1024 + (4 * hi + q) * 128 + 8 * (4 * ((w ^ hi) ^ 2) + (c0 ^ q)) + half
-        assert phys(row, colk, swz_k) == 2048 * ks + kt0
-        assert phys(row + 8, colk, swz_k) == 2048 * ks + kt1
-        assert 2048 * ks + kt1 + 3 < 32 * 128
+        kt2 = 2 * ((4 * hi + q) * 128 + 8 * (4 * (w ^ hi) + (c0 ^ q)) + half)
+        assert 4096 * ks + 2176 == (4096 * ks) ^ 2176
+        assert 2 * phys(row, colk, swz_k) == kt2 ^ (4096 * ks)
+        assert 2 * phys(row + 8, colk, swz_k) == kt2 ^ (4096 * ks + 2176)
+        assert (kt2 ^ (4096 * ks + 2176)) + 8 <= stage

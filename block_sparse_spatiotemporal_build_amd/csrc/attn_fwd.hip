@@ -376,7 +376,11 @@ attn_bf16_d128_kernel(AttnArgs a) {
     const int last_real = N - (a.nb - 1) * BM;
     nsub -= 2 - (last_real + kBN - 1) / kBN;
   }
-  auto key0_of = [&](int u) -> int { return cols[rbeg + (u >> 1)] * BM + (u & 1) * kBN; };
+  // key blocks of the row: the current one (sub-tiles 2 i, 2 i + 1) and the
+  // next, held in scalar registers; the one after is loaded a step before it
+  // is needed
+  const int nblk = rend - rbeg;
+  int blk_cur = nblk > 0 ? cols[rbeg] : 0, blk_nxt = nblk > 1 ? cols[rbeg + 1] : 0;
 
   // Copy roles: wave w, instruction j covers tile rows 16w + 4j + lane/16 at
   // physical chunk lane%16 (i.e. logical chunk (lane%16) ^ swizzle(row)).  The
@@ -436,11 +440,13 @@ attn_bf16_d128_kernel(AttnArgs a) {
   // One 64-key sub-tile u held in (Kb, Vb); the copy of sub-tile u + 1 goes to
   // (Kn, Vn) as soon as every wave has passed the barrier (they have all
   // finished reading that stage in step u - 1).
-  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u) {
-    const int key0 = key0_of(u);
+  // k = u % 2: sub-tile u is half k of block blk_cur; sub-tile u + 1 is half 1
+  // of it (k = 0) or half 0 of the next block (k = 1)
+  auto step = [&](const uint16_t* Kb, const uint16_t* Vb, uint16_t* Kn, uint16_t* Vn, int u, int k) {
+    const int key0 = blk_cur * BM + k * kBN;
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0): sub-tile u landed, other stage drained
     __builtin_amdgcn_s_barrier();
-    if (u + 1 < nsub) dma(Kn, Vn, key0_of(u + 1));
+    if (u + 1 < nsub) dma(Kn, Vn, k == 0 ? blk_cur * BM + kBN : blk_nxt * BM);
 
     // S^T = K Q^T: read the 16 K fragments, then the MFMAs (reads run four ahead)
     f32x16 s[2];
@@ -485,23 +491,22 @@ attn_bf16_d128_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float mc = m_run * c2;
-    float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
-        s[kt][r] = p;
-        psum += p;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[kt][r] = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
+    // P as bf16 (the operand of the value product); the row sum is taken over
+    // the same rounded values with v_dot2 against bf16 ones
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks >> 1, r0 = (ks & 1) * 8;
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kt][r0 + 2 * e], s[kt][r0 + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        w[e] = pack_bf16x2(s[kt][r0 + 2 * e], s[kt][r0 + 2 * e + 1]);
+        l_run = dot2_bf16(w[e], 0x3f803f80u, l_run);
+      }
       pf[ks] = __builtin_bit_cast(bf16x8, w);
     }
 
@@ -521,15 +526,20 @@ attn_bf16_d128_kernel(AttnArgs a) {
         o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, w), pf[ks], o[dt], 0, 0, 0);
       }
     __builtin_amdgcn_s_setprio(0);
+    if (k == 1) {  // the next step opens the next block
+      const int i = u >> 1;
+      blk_cur = blk_nxt;
+      blk_nxt = i + 2 < nblk ? cols[rbeg + i + 2] : 0;
+    }
   };
 
-  if (nsub > 0) dma(K0, V0, key0_of(0));
+  if (nsub > 0) dma(K0, V0, blk_cur * BM);
   int u = 0;
   for (; u + 2 <= nsub; u += 2) {
-    step(K0, V0, K1, V1, u);
-    step(K1, V1, K0, V0, u + 1);
+    step(K0, V0, K1, V1, u, 0);
+    step(K1, V1, K0, V0, u + 1, 1);
   }
-  if (u < nsub) step(K0, V0, K1, V1, u);
+  if (u < nsub) step(K0, V0, K1, V1, u, 0);
 
   const float l_tot = pair_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

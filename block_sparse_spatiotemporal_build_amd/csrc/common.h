@@ -35,6 +35,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2_f32_bf16).
+// Written as inline asm because the compiler builtin, fed 32-bit elements of a
+// vector register tuple, read the tuple's first element for every element.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
+  float d;
+  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
+  return d;
+}
+
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
@@ -101,9 +110,20 @@ __device__ __forceinline__ void lds_copy16(i32x4 rsrc, uint32_t voff, uint32_t l
                : "v"(voff), "s"(rsrc), "s"(lds)
                : "memory", "m0");
 }
+// The same with a uniform byte offset soff added to every lane's voff.
+__device__ __forceinline__ void lds_copy16_so(i32x4 rsrc, uint32_t voff, uint32_t soff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds), "s"(soff)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)p;
+}
+// LDS element at a byte offset from a stage base
+__device__ __forceinline__ const uint16_t* lds_byte(const uint16_t* base, uint32_t off) {
+  return (const uint16_t*)((const char*)base + off);
 }
 __device__ __forceinline__ int swz_k(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }

@@ -373,14 +373,6 @@ __global__ void __launch_bounds__(256) probe_kernel(ProbeArgs p) {
 // stages, three tile copies in flight.
 constexpr int kFpTK = 32, kFpGK = 16;
 
-// acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2_f32_bf16).
-// Written as inline asm because the compiler builtin, fed 32-bit elements of a
-// vector register tuple, read the tuple's first element for every element.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
-  float d;
-  asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
-  return d;
-}
 
 struct FusedProbeArgs {
   SvgArgs s;
@@ -403,10 +395,6 @@ struct FpCursor {
   int c, off, k0, k1;
 };
 
-// LDS element at a byte offset from a stage base
-__device__ __forceinline__ const uint16_t* lds_byte(const uint16_t* base, uint32_t off) {
-  return (const uint16_t*)((const char*)base + off);
-}
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 probe_fused_d128_kernel(FusedProbeArgs p) {

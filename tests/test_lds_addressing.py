@@ -1,9 +1,11 @@
 """Host check of the LDS / copy addressing used by the head_dim-128 kernels
-(`csrc/attn_fwd.hip`, `csrc/svg_ear.hip`, `csrc/common.h`).
+(`csrc/attn_fwd.hip`, `csrc/svg_ear.hip`, `csrc/attn_bwd.hip`,
+`csrc/linear_attn.hip`, `csrc/common.h`).
 
-The kernels stage 64-row tiles of K and V (row = 128 bf16 = 16 chunks of 16 B)
-with a per-row chunk permutation, and compute every per-lane address as one
-lane base XOR / plus a compile-time immediate.  These tests restate the direct
+The kernels stage 64-row (forward and compensated attention, backward) or
+32-row (fused route probe) tiles of K and V (row = 128 bf16 = 16 chunks of
+16 B) with a per-row chunk permutation, and compute every per-lane address as
+one lane base XOR / plus a compile-time immediate.  These tests restate the direct
 definitions (swizzle of a row, MFMA operand layouts, accumulator rows) and check
 the closed forms against them for every lane, exhaustively.  No GPU involved.
 """

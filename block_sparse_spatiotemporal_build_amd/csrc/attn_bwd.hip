@@ -55,7 +55,7 @@ struct BwdArgs {
   int64_t sb, sh, sn;
   int H, N, nb;
   float scale, c2;         // softmax scale, scale * log2(e)
-  int head_major;          // 1: blocks dealt in launch order; 0: each XCD takes a contiguous range
+  int head_major;          // 1: XCD ranges within windows of launch order; 0: over the whole list
   const int32_t* order;    // block schedule [nb + 1]: long blocks first, their count last
 };
 
@@ -64,13 +64,15 @@ struct BwdArgs {
 // sequence; the rest are dealt so that the workgroups the hardware sends to one
 // XCD take one contiguous range of (sequence, block), and blocks that share
 // key (or query) tiles share that XCD's L2; when eight sequences' tensors
-// would not fit the last-level cache, in launch order.
+// would not fit the last-level cache, the same within consecutive windows of
+// launch order (one sequence at a time).
 __device__ __forceinline__ int2 bwd_item(const BwdArgs& a) {
   const int pid = blockIdx.x, total = gridDim.x, hb = total / a.nb;
   const int nh = a.order[a.nb], S = nh * hb;
   if (pid < S) return int2{a.order[pid / hb], pid % hb};
   const int rest = a.nb - nh;
-  const int item = a.head_major ? pid - S : xcd_contiguous(pid - S, S, total - S);
+  const int item = a.head_major ? xcd_windowed(pid - S, S, total - S, kXcdWindow)
+                                : xcd_contiguous(pid - S, S, total - S);
   return int2{a.order[nh + item % rest], item / rest};
 }
 

@@ -65,7 +65,7 @@ struct AttnArgs {
   const int32_t* row_order;  // nullable: schedule of query-block rows, int32[nb + 1]
   int64_t sb, sh, sn;
   int B, H, N, block, nb;
-  int head_major;    // 1: rows of one head are dealt round-robin over the XCDs (see map_work)
+  int head_major;    // 1: rows taken head by head, in windows split over the XCDs (see map_work)
   float scale_log2;  // scale * log2(e)
 };
 
@@ -74,10 +74,13 @@ struct AttnArgs {
 //    the (batch, head, query block) list, so the workgroups sharing an L2 walk
 //    neighbouring query blocks of one head and reuse their key blocks.  The
 //    eight XCDs then work on eight different heads at a time.
-//  * head_major: the list is taken in launch order, so at any time all XCDs
-//    work on neighbouring query blocks of the same head.  The launcher picks
-//    this when eight heads of K and V would not fit the last-level cache: the
-//    key blocks that miss in one XCD's L2 are then found in that cache.
+//  * head_major: the list is taken in windows of kXcdWindow items in launch
+//    order, and inside a window each XCD takes a contiguous run, so at any time
+//    all XCDs work on neighbouring query blocks of the same head and each
+//    XCD's L2 holds the key band its run of query blocks shares.  The launcher
+//    picks this when eight heads of K and V would not fit the last-level
+//    cache: the key blocks that miss in one XCD's L2 are then found in that
+//    cache.
 //  * With a row order whose first nh = row_order[nb] rows are long ones (LVSA
 //    anchor rows are about twice the mean length): those rows, for every head,
 //    take the first nh * H * B workgroups, so they start in the first wave and
@@ -97,11 +100,12 @@ __device__ __forceinline__ WorkItem map_work(const AttnArgs& a) {
       return WorkItem{ord[pid / hb], r % a.H, r / a.H};
     }
     const int rest = a.nb - nh;
-    const int item = a.head_major ? pid - S : xcd_contiguous(pid - S, S, total - S);
+    const int item = a.head_major ? xcd_windowed(pid - S, S, total - S, kXcdWindow)
+                                  : xcd_contiguous(pid - S, S, total - S);
     const int r = item / rest;
     return WorkItem{ord[nh + item % rest], r % a.H, r / a.H};
   }
-  const int item = a.head_major ? pid : xcd_contiguous(pid, 0, total);
+  const int item = a.head_major ? xcd_windowed(pid, 0, total, kXcdWindow) : xcd_contiguous(pid, 0, total);
   return WorkItem{item % a.nb, (item / a.nb) % a.H, item / (a.nb * a.H)};
 }
 

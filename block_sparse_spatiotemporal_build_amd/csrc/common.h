@@ -172,4 +172,15 @@ __device__ __forceinline__ int xcd_contiguous(int j, int S, int R) {
   return base + (j - ((x - off) & 7)) / 8;
 }
 
+// The same over consecutive windows of W items (W a multiple of 8, one
+// workgroup per CU): item order is kept from window to window, and inside a
+// window each XCD takes one contiguous run.  So the XCDs work on
+// neighbouring items (one head at a time in head-major order) while the
+// workgroups sharing an L2 still share their neighbours' tiles.
+__device__ __forceinline__ int xcd_windowed(int j, int S, int R, int W) {
+  const int base = (j / W) * W;
+  return base + xcd_contiguous(j - base, S + base, min(W, R - base));
+}
+constexpr int kXcdWindow = 256;
+
 }  // namespace bsa

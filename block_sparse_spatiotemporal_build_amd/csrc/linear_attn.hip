@@ -239,13 +239,16 @@ lin_state_d128_kernel(LinStateArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) acc[i] = f32x16{};
   float zl = 0.f;
-  // transpose-read addressing (rows of token group ks, 16-byte chunk of d block dt)
-  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> u32x4 {
-    const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
-    const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-    const int half = (j16 & 1) * 4;
-    const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
-    const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
+  // transpose reads (token group ks, 32-column block dt of the tile; rows +8
+  // for the second half of the fragment) as byte offsets base ^ immediate:
+  //   va2 ^ (4096 ks + 64 dt)  and  va2 ^ (4096 ks + 64 dt + 2080)
+  // (the K and V stages are both swizzled with swz_v; the identities are
+  // checked for every lane on the host)
+  const int q4 = j16 >> 2, c0 = 2 * (g16 & 1) + ((j16 >> 1) & 1), half4 = (j16 & 1) * 4;
+  const uint32_t va2 = 2 * ((4 * hi + q4) * D + 32 * q4 + 8 * (c0 ^ hi) + half4);
+  const uint32_t kw2 = va2 ^ (64 * wave);  // this wave's K rows d1 = 32 w + ...
+  auto tr_frag = [&](const uint16_t* st, uint32_t base, uint32_t imm) -> u32x4 {
+    const u32x2 x0 = lds_tr16(lds_byte(st, base ^ imm)), x1 = lds_tr16(lds_byte(st, base ^ (imm + 2080)));
     return u32x4{x0[0], x0[1], x1[0], x1[1]};
   };
 
@@ -261,25 +264,39 @@ lin_state_d128_kernel(LinStateArgs a) {
     else __builtin_amdgcn_s_waitcnt(0x0070);                  // vmcnt(0) lgkmcnt(0)
     __builtin_amdgcn_s_barrier();
     if (t + 4 < ntile) dma(Kn, Vn, t0 + 4 * kLinTok2);
+    uint32_t kw = kw2, va = va2;
+    asm volatile("" : "+v"(kw), "+v"(va));
     const int lim = n1 - t0 - 4 * hi;  // element e is a real token iff 16 ks + 8 (e / 4) + e % 4 < lim
+    const bool full = n1 - t0 >= kLinTok2;  // uniform: no token of the tile is past the split's end
 #pragma unroll
     for (int ks = 0; ks < kLinTok2 / 16; ++ks) {
-      const u32x4 kr = tr_frag(Kb, ks, wave);
-      u32x4 kp;
+      const u32x4 kr = tr_frag(Kb, kw, 4096 * ks);
+      u32x4 vr[4];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int e0 = 2 * w, e1 = 2 * w + 1;
-        float f0 = phi(bf16_lo(kr[w])), f1 = phi(bf16_hi(kr[w]));
-        if (16 * ks + 8 * (e0 >> 2) + (e0 & 3) >= lim) f0 = 0.f;
-        if (16 * ks + 8 * (e1 >> 2) + (e1 & 3) >= lim) f1 = 0.f;
-        zl += f0 + f1;
-        kp[w] = pack_bf16x2(f0, f1);
+      for (int dt = 0; dt < 4; ++dt) vr[dt] = tr_frag(Vb, va, 4096 * ks + 64 * dt);
+      u32x4 kp;
+      if (full) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float f0 = phi(bf16_lo(kr[w])), f1 = phi(bf16_hi(kr[w]));
+          zl += f0 + f1;
+          kp[w] = pack_bf16x2(f0, f1);
+        }
+      } else {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int e0 = 2 * w, e1 = 2 * w + 1;
+          float f0 = phi(bf16_lo(kr[w])), f1 = phi(bf16_hi(kr[w]));
+          if (16 * ks + 8 * (e0 >> 2) + (e0 & 3) >= lim) f0 = 0.f;
+          if (16 * ks + 8 * (e1 >> 2) + (e1 & 3) >= lim) f1 = 0.f;
+          zl += f0 + f1;
+          kp[w] = pack_bf16x2(f0, f1);
+        }
       }
       const bf16x8 af = __builtin_bit_cast(bf16x8, kp);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
-        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, tr_frag(Vb, ks, dt)),
-                                                          acc[dt], 0, 0, 0);
+        acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af, __builtin_bit_cast(bf16x8, vr[dt]), acc[dt], 0, 0, 0);
     }
   };
 

@@ -73,6 +73,7 @@ _SIGNATURES = {
     "bsa_route_select": (ctypes.c_int, [_P, ctypes.POINTER(Shape), _P, ctypes.c_int32, _P, ctypes.c_int32,
                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_route_budget": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
+    "bsa_check_csr": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]),
     "bsa_compensated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                 ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P,
                                                 ctypes.c_float, _P, ctypes.c_size_t, _P]),
@@ -611,3 +612,20 @@ def mixed_attn_fwd(q, k, v, r: float, row_ptr=None, col_idx=None, block: int = 1
                                   float(r), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                                   _stream(q.device)), "bsa_mixed_attn_fwd")
     return out
+
+
+def check_csr(row_ptr, col_idx, nrows: int, ncols: int, capacity=None):
+    """Host-side check of a block CSR (numpy int32 arrays): bsa_check_csr.
+    Raises BsaError naming the first violated invariant."""
+    import numpy as np
+    lib = load()
+    rp = np.ascontiguousarray(row_ptr, dtype=np.int32)
+    ci = np.ascontiguousarray(col_idx, dtype=np.int32)
+    if rp.size != nrows + 1:
+        raise BsaError(f"check_csr: row_ptr has {rp.size} entries, expected {nrows + 1}")
+    cap = int(ci.size) if capacity is None else int(capacity)
+    if cap > ci.size:
+        raise BsaError("check_csr: capacity exceeds the column array")
+    ci_p = ci.ctypes.data if ci.size else rp.ctypes.data
+    _check(lib.bsa_check_csr(rp.ctypes.data, ci_p, nrows, ncols, cap), "bsa_check_csr")
+

@@ -5,6 +5,7 @@
 
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "launch.h"
@@ -38,6 +39,66 @@ static bsa_status fail(bsa_status st, const char* fmt, ...) {
 }
 
 static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Block CSR invariants on host arrays (the checker behind bsa_check_csr).
+static bsa_status check_csr_host(const int32_t* rp, const int32_t* ci, int32_t nrows, int32_t ncols, int64_t cap,
+                                 const char* fn) {
+  if (rp == nullptr || (ci == nullptr && nrows > 0)) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (nrows < 0 || ncols < 0) return fail(BSA_ERR_ARG, "%s: negative size", fn);
+  if (rp[0] != 0) return fail(BSA_ERR_ARG, "%s: row_ptr[0] = %d, not 0", fn, rp[0]);
+  for (int32_t r = 0; r < nrows; ++r)
+    if (rp[r + 1] < rp[r])
+      return fail(BSA_ERR_ARG, "%s: row_ptr decreases at row %d (%d -> %d)", fn, r, rp[r], rp[r + 1]);
+  if ((int64_t)rp[nrows] > cap)
+    return fail(BSA_ERR_CAPACITY, "%s: %d entries exceed the capacity %lld", fn, rp[nrows], (long long)cap);
+  for (int32_t r = 0; r < nrows; ++r)
+    for (int32_t e = rp[r]; e < rp[r + 1]; ++e) {
+      if (ci[e] < 0 || ci[e] >= ncols)
+        return fail(BSA_ERR_ARG, "%s: row %d has column %d outside [0, %d)", fn, r, ci[e], ncols);
+      if (e > rp[r] && ci[e] <= ci[e - 1])
+        return fail(BSA_ERR_ARG, "%s: row %d columns not strictly ascending (%d then %d)", fn, r, ci[e - 1], ci[e]);
+    }
+  return BSA_OK;
+}
+
+// BSA_DEBUG, read at every call that can check its output
+static bool debug_mode() {
+  const char* e = getenv("BSA_DEBUG");
+  return e != nullptr && e[0] != 0 && strcmp(e, "0") != 0;
+}
+
+// Debug check of a device CSR just written on `stream`: synchronise, copy it
+// back and run the host checker; BSA_ERR_CHECK on a violation.
+static bsa_status debug_check_device_csr(const int32_t* rp_dev, const int32_t* ci_dev, int32_t nrows, int32_t ncols,
+                                         int64_t cap, hipStream_t stream, const char* fn) {
+  if (hipStreamSynchronize(stream) != hipSuccess) return fail(BSA_ERR_HIP, "%s: debug check: synchronise failed", fn);
+  int32_t* rp = (int32_t*)malloc(sizeof(int32_t) * ((size_t)nrows + 1));
+  if (rp == nullptr) return fail(BSA_ERR_CHECK, "%s: debug check: out of host memory", fn);
+  if (hipMemcpy(rp, rp_dev, sizeof(int32_t) * ((size_t)nrows + 1), hipMemcpyDeviceToHost) != hipSuccess) {
+    free(rp);
+    return fail(BSA_ERR_HIP, "%s: debug check: copy of row_ptr failed", fn);
+  }
+  const int64_t n = rp[nrows] < 0 ? 0 : (rp[nrows] > cap ? cap : rp[nrows]);
+  int32_t* ci = (int32_t*)malloc(sizeof(int32_t) * ((size_t)n + 1));
+  if (ci == nullptr) {
+    free(rp);
+    return fail(BSA_ERR_CHECK, "%s: debug check: out of host memory", fn);
+  }
+  if (n > 0 && hipMemcpy(ci, ci_dev, sizeof(int32_t) * (size_t)n, hipMemcpyDeviceToHost) != hipSuccess) {
+    free(rp);
+    free(ci);
+    return fail(BSA_ERR_HIP, "%s: debug check: copy of col_idx failed", fn);
+  }
+  bsa_status st = check_csr_host(rp, ci, nrows, ncols, cap, fn);
+  free(rp);
+  free(ci);
+  if (st != BSA_OK) {
+    char msg[512];
+    snprintf(msg, sizeof msg, "%s", g_err);
+    return fail(BSA_ERR_CHECK, "BSA_DEBUG: %s", msg);
+  }
+  return BSA_OK;
+}
 
 // Shape checks shared by the tensor calls: sizes positive, strides that keep
 // each row inside its own head, D contiguous, 16-byte aligned rows.
@@ -92,7 +153,10 @@ bsa_status bsa_build_block_mask(const bsa_mask_desc* desc, int32_t* row_ptr, int
     return fail(BSA_ERR_CAPACITY, "%s: col_capacity %lld < nb*nb = %lld", fn, (long long)col_capacity,
                 (long long)(nb * nb));
   g_err[0] = 0;
-  return launch_build_block_mask(*desc, row_ptr, col_idx, row_order, (hipStream_t)stream);
+  st = launch_build_block_mask(*desc, row_ptr, col_idx, row_order, (hipStream_t)stream);
+  if (st == BSA_OK && debug_mode())
+    st = debug_check_device_csr(row_ptr, col_idx, (int32_t)nb, (int32_t)nb, col_capacity, (hipStream_t)stream, fn);
+  return st;
 }
 
 bsa_status bsa_block_sparse_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -419,6 +483,19 @@ bsa_status bsa_route_scores(const void* k, const void* v, bsa_dtype dtype, const
                              (hipStream_t)stream);
 }
 
+// debug check of every head's route CSR: rows [BH][Cq + 1], columns
+// [BH][Cq * Ck] (each head's columns start at its own r * Cq * Ck)
+static bsa_status debug_check_route(const bsa_shape* shape, const int32_t* rrow, const int32_t* rcol, int32_t Cq,
+                                    int32_t Ck, void* stream, const char* fn) {
+  const int64_t bh = (int64_t)shape->B * shape->H;
+  for (int64_t r = 0; r < bh; ++r) {
+    bsa_status st = debug_check_device_csr(rrow + r * (Cq + 1), rcol + r * (int64_t)Cq * Ck, Cq, Ck,
+                                           (int64_t)Cq * Ck, (hipStream_t)stream, fn);
+    if (st != BSA_OK) return st;
+  }
+  return BSA_OK;
+}
+
 // selection workspace: the cost histograms of the scores
 size_t bsa_route_select_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
   if (check_shape(shape, 2, "bsa_route_select_workspace") != BSA_OK || Cq < 1 || Ck < 1) return 0;
@@ -437,8 +514,10 @@ bsa_status bsa_route_select(const float* score, const bsa_shape* shape, const in
   if (!workspace || ws_bytes < need || ((uintptr_t)workspace & 255u))
     return fail(BSA_ERR_WORKSPACE, "%s: workspace of %zu bytes (256-byte aligned) required", fn, need);
   g_err[0] = 0;
-  return launch_route_select(score, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
-                             route_col, workspace, false, (hipStream_t)stream);
+  st = launch_route_select(score, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
+                           route_col, workspace, false, (hipStream_t)stream);
+  if (st == BSA_OK && debug_mode()) st = debug_check_route(shape, route_row_ptr, route_col, Cq, Ck, stream, fn);
+  return st;
 }
 
 size_t bsa_compensated_attn_workspace(const bsa_shape* shape, int32_t Cq, int32_t Ck) {
@@ -538,6 +617,7 @@ bsa_status bsa_centroid_compensate(const void* q, const void* k, const void* v, 
   if (st != BSA_OK) return st;
   st = launch_route_select(sc, *shape, q_off, Cq, k_off, Ck, budget_of(shape->N, density_ppm), route_row_ptr,
                            route_col, w + pl.probe + pp.off_hist, true, sm);
+  if (st == BSA_OK && debug_mode()) st = debug_check_route(shape, route_row_ptr, route_col, Cq, Ck, stream, fn);
   if (st != BSA_OK) return st;
   return launch_comp_attn(q, k, v, o, lse, *shape, q_off, Cq, k_off, Ck, route_row_ptr, route_col, kc, vc, scale,
                           w + pl.attn, sm, bf16_ready);
@@ -582,6 +662,11 @@ bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_sh
   return launch_lipar_restore(y_pruned, *shape, frames, keep, cpos, out, (hipStream_t)stream);
 }
 
+bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t nrows, int32_t ncols,
+                         int64_t capacity) {
+  return check_csr_host(row_ptr, col_idx, nrows, ncols, capacity, "bsa_check_csr");
+}
+
 int64_t bsa_route_budget(int32_t N, int32_t density_ppm) {
   if (N < 0 || density_ppm < 0 || density_ppm > 1000000) return -1;
   return budget_of(N, density_ppm);
@@ -595,6 +680,7 @@ const char* bsa_status_string(bsa_status s) {
     case BSA_ERR_CAPACITY: return "output capacity too small";
     case BSA_ERR_WORKSPACE: return "workspace missing or too small";
     case BSA_ERR_HIP: return "HIP runtime error";
+    case BSA_ERR_CHECK: return "debug invariant check failed";
   }
   return "unknown status";
 }

@@ -34,15 +34,21 @@ typedef enum bsa_status {
   BSA_ERR_UNSUPPORTED = 2,  /* valid but not implemented (e.g. a head_dim)           */
   BSA_ERR_CAPACITY = 3,     /* an output buffer is too small                         */
   BSA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the query returned  */
-  BSA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed            */
+  BSA_ERR_HIP = 5,          /* a HIP runtime call or kernel launch failed            */
+  BSA_ERR_CHECK = 6,        /* a BSA_DEBUG invariant check of an output failed       */
+  BSA_STATUS_MAX = 0x7fffffff  /* range sentinel: any 32-bit value is representable  */
 } bsa_status;
 
-typedef enum bsa_dtype { BSA_DT_BF16 = 0, BSA_DT_F32 = 1 } bsa_dtype;
+/* The *_MAX enumerators are not values to pass: they make every 32-bit value
+ * representable in the enum type, so the library can receive an unknown value
+ * from a C caller and reject it without undefined behaviour. */
+typedef enum bsa_dtype { BSA_DT_BF16 = 0, BSA_DT_F32 = 1, BSA_DT_MAX = 0x7fffffff } bsa_dtype;
 
 typedef enum bsa_mask_kind {
   BSA_MASK_ALL = 0,            /* every block pair kept (dense attention)            */
   BSA_MASK_WINDOW_ANCHOR = 1,  /* local frame window + rotating global anchor frames */
-  BSA_MASK_RADIAL = 2          /* window shrinking with temporal distance            */
+  BSA_MASK_RADIAL = 2,         /* window shrinking with temporal distance            */
+  BSA_MASK_KIND_MAX = 0x7fffffff
 } bsa_mask_kind;
 
 /* Block-mask description.
@@ -465,6 +471,22 @@ bsa_status bsa_lipar_prune(const void* x, bsa_dtype dtype, const bsa_shape* shap
 bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_shape* shape,
                              int32_t frames, const uint8_t* keep, const int32_t* cpos, void* out,
                              void* stream);
+
+/* Host-side check of a block CSR held in HOST memory: row_ptr [nrows + 1]
+ * starts at 0 and never decreases, row_ptr[nrows] <= capacity, and every row's
+ * columns lie in [0, ncols) in strictly ascending order.  Returns BSA_OK, or
+ * BSA_ERR_ARG / BSA_ERR_CAPACITY naming the first violation in
+ * bsa_last_error().  Reads nothing past row_ptr[nrows] entries of col_idx.
+ *
+ * Debug mode: while the environment variable BSA_DEBUG holds a non-empty value
+ * other than "0" (read at each call), bsa_build_block_mask,
+ * bsa_route_select and bsa_centroid_compensate (routing mode) synchronise
+ * their stream after the launch, copy the CSR they wrote to the host and run
+ * this check on it, returning BSA_ERR_CHECK on a violation.  That costs a
+ * synchronisation and a copy per call; it is meant for debugging, not for
+ * stream capture. */
+bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t nrows, int32_t ncols,
+                         int64_t capacity);
 
 /* Text of a status code (static storage). */
 const char* bsa_status_string(bsa_status status);

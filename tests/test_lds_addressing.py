@@ -205,3 +205,4 @@ def test_fused_probe_offsets_xor_form():
         assert 2 * phys(row, colk, swz_k) == kt2 ^ (4096 * ks)
         assert 2 * phys(row + 8, colk, swz_k) == kt2 ^ (4096 * ks + 2176)
         assert (kt2 ^ (4096 * ks + 2176)) + 8 <= stage
+

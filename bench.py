@@ -13,8 +13,12 @@ Reported (one JSON line): effective TFLOP/s over the timed steps, counting
 4 * D * (real query rows x real key columns) of kept blocks only; ms per
 attention call; the attention kernel's roofline against the bf16 MFMA peak
 (kernel time from HIP events on the launch stream); the HBM traffic measured
-by rocprofv3 counters when a profile of the current kernel source exists; and
-the CPU oracle timed on a bounded sample of the same workload.
+by rocprofv3 counters when a profile of the current kernel source exists; the
+measured read-only HBM rate (bsa_hbm_read_probe over 2 GiB) and the sustained
+vendor GEMM rate as references; under "side", the call times of the HBM-bound
+rows on their own workloads (linear attention at 32K and 196K tokens, SVG-EAR
+routing at 32K) as algorithmic GB/s against the HBM peak; and the CPU oracle
+timed on a bounded sample of the same workload.
 
 Other workloads (``--workload``): radial_196k (Radial mask, 196,560 tokens);
 linear_32k / linear_196k (elu+1 linear attention, HBM-bound: reported as
@@ -67,6 +71,8 @@ def parse_args():
                     help="copy: run a plain device copy of known size (HBM counter calibration)")
     ap.add_argument("--no-refs", action="store_true",
                     help="skip the measured references (sustained bf16 GEMM, 1 GiB copy)")
+    ap.add_argument("--no-side", action="store_true",
+                    help="skip the side legs of the default line (linear 32K / 196K and SVG-EAR routing call times)")
     ap.add_argument("--cold-calls", type=int, default=10,
                     help="attention calls timed after a 512 MiB scratch write each (cold caches)")
     return ap.parse_args()
@@ -143,6 +149,73 @@ def measure_copy_gbs():
     dst = torch.empty_like(src)
     ms = _events_ms(lambda: dst.copy_(src), 10, 3)
     return 2 * n / (ms * 1e-3) / 1e9
+
+
+def measure_read_gbs():
+    """Read-only HBM rate: bsa_hbm_read_probe streaming a 2 GiB buffer (eight
+    times the last-level cache) once per call, as GB/s of bytes read."""
+    import torch
+    import block_sparse_spatiotemporal_build_amd as bsa
+    n = 2 << 30
+    buf = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    ms = _events_ms(lambda: bsa.hbm_read_probe(buf, sink), 10, 3)
+    del buf
+    return n / (ms * 1e-3) / 1e9
+
+
+def side_legs(args, read_gbs):
+    """Call times of the HBM-bound rows on their own workloads, reported with the
+    default line: linear attention at 32,760 and 196,560 tokens (read Q, K, V +
+    write O), and the SVG-EAR routing at 32,760 tokens (query centroids, the
+    fused key-centroid / score pass and the selection; read Q, K, V once).
+    Inputs from the same seeded recipes as their own bench lines."""
+    import numpy as np
+    import torch
+    import block_sparse_spatiotemporal_build_amd as bsa
+    from synth import gen, get_workload
+    dev = torch.device("cuda:0")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    def entry(ms, algo_bytes):
+        gbs = algo_bytes / (ms * 1e-3) / 1e9
+        e = {"ms_per_call": round(ms, 4), "algorithmic_bytes": algo_bytes, "gbs": round(gbs, 1),
+             "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
+        if read_gbs:
+            e["frac_of_measured_read"] = round(gbs / read_gbs, 4)
+        return e
+
+    out = {}
+    for name in ("linear_32k", "linear_196k"):
+        wl = get_workload(name)
+        d = gen.make_qkv(wl)
+        q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+        del d
+        o = torch.empty_like(q)
+        ws = torch.empty(bsa.linear_attn_workspace(q), dtype=torch.uint8, device=dev)
+        ms = _events_ms(lambda: bsa.linear_attn_fwd(q, k, v, out=o, workspace=ws), 20, 5)
+        out[name] = entry(ms, 4 * wl.B * wl.H * wl.N * wl.D * 2)
+        del q, k, v, o, ws
+    wl = get_workload("svg_ear_32k")
+    d = gen.make_clustered(wl)
+    q, k, v = up(d["q"]), up(d["k"]), up(d["v"])
+    qo = torch.from_numpy(d["q_off"]).to(dev)
+    ko = torch.from_numpy(d["k_off"]).to(dev)
+    del d
+    scale = 1.0 / math.sqrt(wl.D)
+    qc, _, _ = bsa.cluster_centroids(q, k, v, qo, ko, which="query")
+    sc, kc, vc = bsa.route_scores(k, v, qo, ko, qc, scale)
+
+    def routing():
+        bsa.cluster_centroids(q, k, v, qo, ko, which="query")
+        bsa.route_scores(k, v, qo, ko, qc, scale, k_cent=kc, v_cent=vc)
+        bsa.route_select(sc, q, qo, ko, wl.density_ppm)
+
+    ms = _events_ms(routing, 20, 5)
+    out["routing_svg_ear_32k"] = entry(ms, 3 * wl.B * wl.H * wl.N * wl.D * 2)
+    return out
 
 
 def cpu_baseline(wl, d, params, budget_s: float):
@@ -1064,6 +1137,12 @@ def main():
         result["measured_peak"] = {"kernel": "sustained bf16 GEMM 8192^3 (torch.matmul)",
                                    "tflops": round(gemm, 1),
                                    "attn_frac_of_measured": round(achieved / gemm, 4)}
+    read_gbs = None if args.no_refs else measure_read_gbs()
+    if read_gbs is not None:
+        result["measured_hbm_read"] = {"kernel": "bsa_hbm_read_probe, 2 GiB read once per call",
+                                       "gbs": round(read_gbs, 1), "frac_of_peak": round(read_gbs / HBM_PEAK_GBS, 4)}
+    if not args.no_side and wl.name == "lvsa_32k":
+        result["side"] = side_legs(args, read_gbs)
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(wl, d, params[0], args.cpu_seconds)
     print(json.dumps(result), flush=True)

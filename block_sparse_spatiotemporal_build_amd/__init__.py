@@ -74,6 +74,7 @@ _SIGNATURES = {
                                         ctypes.c_int32, _P, _P, _P, ctypes.c_size_t, _P]),
     "bsa_route_budget": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32]),
     "bsa_check_csr": (ctypes.c_int, [_P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64]),
+    "bsa_hbm_read_probe": (ctypes.c_int, [_P, ctypes.c_size_t, _P, _P]),
     "bsa_compensated_attn_fwd": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.c_int, ctypes.POINTER(Shape), _P,
                                                 ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P,
                                                 ctypes.c_float, _P, ctypes.c_size_t, _P]),
@@ -628,4 +629,14 @@ def check_csr(row_ptr, col_idx, nrows: int, ncols: int, capacity=None):
         raise BsaError("check_csr: capacity exceeds the column array")
     ci_p = ci.ctypes.data if ci.size else rp.ctypes.data
     _check(lib.bsa_check_csr(rp.ctypes.data, ci_p, nrows, ncols, cap), "bsa_check_csr")
+
+
+def hbm_read_probe(buf, sink):
+    """Read every byte of the device tensor `buf` once (bsa_hbm_read_probe);
+    `sink` is a device int32 tensor of at least one element."""
+    import torch
+    lib = load()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.bsa_hbm_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(),
+                                  torch.cuda.current_stream(buf.device).cuda_stream), "bsa_hbm_read_probe")
 

@@ -662,6 +662,14 @@ bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_sh
   return launch_lipar_restore(y_pruned, *shape, frames, keep, cpos, out, (hipStream_t)stream);
 }
 
+bsa_status bsa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  const char* fn = "bsa_hbm_read_probe";
+  if (!buf || !sink) return fail(BSA_ERR_ARG, "%s: NULL pointer", fn);
+  if (!aligned16(buf) || bytes % 16 != 0) return fail(BSA_ERR_ARG, "%s: buf and bytes must be 16-byte aligned", fn);
+  g_err[0] = 0;
+  return launch_hbm_read(buf, bytes, sink, (hipStream_t)stream);
+}
+
 bsa_status bsa_check_csr(const int32_t* row_ptr, const int32_t* col_idx, int32_t nrows, int32_t ncols,
                          int64_t capacity) {
   return check_csr_host(row_ptr, col_idx, nrows, ncols, capacity, "bsa_check_csr");

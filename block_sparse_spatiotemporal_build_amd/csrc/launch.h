@@ -120,4 +120,7 @@ bsa_status launch_lipar_prune(const void* x, const bsa_shape& s, int frames, flo
 bsa_status launch_lipar_restore(const void* y_pruned, const bsa_shape& s, int frames, const uint8_t* keep,
                                 const int32_t* cpos, void* out, hipStream_t stream);
 
+// read-only HBM probe (measurement reference)
+bsa_status launch_hbm_read(const void* p, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace bsa

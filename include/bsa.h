@@ -472,6 +472,13 @@ bsa_status bsa_lipar_restore(const void* y_pruned, bsa_dtype dtype, const bsa_sh
                              int32_t frames, const uint8_t* keep, const int32_t* cpos, void* out,
                              void* stream);
 
+/* Measurement reference (not part of the attention path): streams `bytes` of
+ * the device buffer `buf` once with 16-byte loads and writes nothing but, at
+ * most, one word of `sink` (device, 4 bytes).  Timed over a buffer larger than
+ * the last-level cache it gives the read-only HBM rate that the HBM-bound
+ * kernels are compared with.  buf 16-byte aligned, bytes a multiple of 16. */
+bsa_status bsa_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+
 /* Host-side check of a block CSR held in HOST memory: row_ptr [nrows + 1]
  * starts at 0 and never decreases, row_ptr[nrows] <= capacity, and every row's
  * columns lie in [0, ncols) in strictly ascending order.  Returns BSA_OK, or

@@ -204,6 +204,10 @@ int main() {
   expect(bsa_lipar_restore(P(0), BSA_DT_BF16, &good, 4, nullptr, ip, P(2), nullptr), BSA_ERR_ARG,
          "lipar restore: NULL keep");
 
+  // ---- measurement probe
+  expect(bsa_hbm_read_probe(nullptr, 1024, (uint32_t*)P(1), nullptr), BSA_ERR_ARG, "read probe: NULL buffer");
+  expect(bsa_hbm_read_probe(P(0), 1000, (uint32_t*)P(1), nullptr), BSA_ERR_ARG, "read probe: bytes not a multiple of 16");
+
   // ---- block CSR checker (host arrays)
   {
     const int32_t rp_ok[4] = {0, 2, 3, 5}, ci_ok[5] = {0, 2, 1, 0, 2};

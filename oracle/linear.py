@@ -21,12 +21,18 @@ def phi(x):
     return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
 
 
+def linear_state(k, v):
+    """The state of the sequence: S [..., D, D] = sum_n phi(k_n) v_n^T and
+    z [..., D] = sum_n phi(k_n), for float64 [..., N, D] keys and values."""
+    fk = phi(k)
+    v = np.asarray(v, np.float64)
+    return np.einsum("...nd,...ne->...de", fk, v), fk.sum(axis=-2)
+
+
 def linear_attention(q, k, v):
     """out [B, H, N, D], S [B, H, D, D], z [B, H, D] for float64 [B, H, N, D] inputs."""
-    fq, fk = phi(q), phi(k)
-    v = np.asarray(v, np.float64)
-    S = np.einsum("bhnd,bhne->bhde", fk, v)
-    z = fk.sum(axis=2)
+    fq = phi(q)
+    S, z = linear_state(k, v)
     num = np.einsum("bhnd,bhde->bhne", fq, S)
     den = np.einsum("bhnd,bhd->bhn", fq, z)
     return num / den[..., None], S, z

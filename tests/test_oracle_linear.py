@@ -41,11 +41,15 @@ def test_closed_form_equals_quadratic_form():
 def test_state_definitions_by_loops():
     q, k, v = _qkv(1, 7, 4)
     _, S, z = ol.linear_attention(q, k, v)
-    fk = ol.phi(k[0, 0])
+    S2, z2 = ol.linear_state(k[0, 0], v[0, 0])   # the state alone, on one head
     for d in range(4):
-        assert abs(z[0, 0, d] - sum(fk[n, d] for n in range(7))) < 1e-12
+        # phi by its branch definition, written out per element
+        zd = sum((k[0, 0, n, d] + 1.0) if k[0, 0, n, d] > 0 else math.exp(k[0, 0, n, d]) for n in range(7))
+        assert abs(z[0, 0, d] - zd) < 1e-12 and abs(z2[d] - zd) < 1e-12
         for e in range(4):
-            assert abs(S[0, 0, d, e] - sum(fk[n, d] * v[0, 0, n, e] for n in range(7))) < 1e-12
+            sde = sum(((k[0, 0, n, d] + 1.0) if k[0, 0, n, d] > 0 else math.exp(k[0, 0, n, d])) * v[0, 0, n, e]
+                      for n in range(7))
+            assert abs(S[0, 0, d, e] - sde) < 1e-12 and abs(S2[d, e] - sde) < 1e-12
 
 
 def test_special_cases():

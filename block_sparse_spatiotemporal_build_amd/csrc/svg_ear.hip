@@ -1347,6 +1347,7 @@ struct CompArgs {
   const int32_t* tile_item;   // head_dim 128 path: tile schedule, longest first: item bh * Cq + a,
   const int32_t* tile_x;      // tile x of that cluster (rows q_off[a] + 128 x ...),
   const int32_t* tile_count;  // and the number of tiles
+  const int32_t* runs;        // head_dim 128 path: run tables of the route rows (see comp_steps_kernel)
 };
 
 template <int D>
@@ -1604,10 +1605,15 @@ struct CompOrderArgs {
   int32_t* tile_item;
   int32_t* tile_x;
   int32_t* tile_count;
+  int32_t* runs;   // [BH][Cq * Ck] pairs, indexed like the route columns
 };
 
-// one wave per (head, cluster): E_a from the route row (indices clamped like the
-// attention kernel clamps them)
+// one wave per (head, cluster a): from the route row (indices clamped like the
+// attention kernel clamps them) E_a and the row's run table.  The exact keys
+// of cluster a are the key rows of its kept clusters concatenated in route
+// order; entry i of the table describes the i-th kept cluster b as the pair
+// (end slot, key row minus slot): slots [end_{i-1}, end_i) of the
+// concatenation hold key rows slot + delta_i, delta_i = k_off[b] - end_{i-1}.
 __global__ void __launch_bounds__(256) comp_steps_kernel(CompOrderArgs o) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bh = blockIdx.y, ca = blockIdx.x * 4 + wave;
@@ -1617,12 +1623,26 @@ __global__ void __launch_bounds__(256) comp_steps_kernel(CompOrderArgs o) {
   const int rb = max(0, min(o.rrow[(int64_t)bh * (o.Cq + 1) + ca], o.Cq * o.Ck));
   const int nk = max(0, min(o.rrow[(int64_t)bh * (o.Cq + 1) + ca + 1] - rb, min(o.Ck, o.Cq * o.Ck - rb)));
   const int32_t* cl = o.rcol + (int64_t)bh * o.Cq * o.Ck + rb;
-  int e = 0;
-  for (int i = lane; i < nk; i += 64) {
-    const int b = max(0, min(cl[i], o.Ck - 1));
-    e += ko[b + 1] - ko[b];
+  int32_t* runs = o.runs + 2 * ((int64_t)bh * o.Cq * o.Ck + rb);
+  int e = 0;  // slots before this 64-entry chunk
+  for (int i0 = 0; i0 < nk; i0 += 64) {
+    const int i = i0 + lane;
+    int b = 0, sz = 0;
+    if (i < nk) {
+      b = max(0, min(cl[i], o.Ck - 1));
+      sz = ko[b + 1] - ko[b];
+    }
+    int inc = sz;  // inclusive prefix over the chunk
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(inc, off, 64);
+      if (lane >= off) inc += y;
+    }
+    if (i < nk) {
+      runs[2 * i] = e + inc;
+      runs[2 * i + 1] = ko[b] - (e + inc - sz);
+    }
+    e += __shfl(inc, 63, 64);
   }
-  for (int off = 32; off > 0; off >>= 1) e += __shfl_xor(e, off, 64);
   if (lane == 0) {
     const int i = bh * o.Cq + ca;
     o.work[i] = (e + kCaBN - 1) / kCaBN + (o.Ck + kCaBN - 1) / kCaBN;
@@ -1675,11 +1695,11 @@ __global__ void __launch_bounds__(1024) comp_order_kernel(CompOrderArgs o) {
 // head_dim 128 compensated attention.  Same online-softmax core and staging
 // as attn_bf16_d128_kernel: 64-key sub-tiles copied straight to two swizzled
 // LDS stages (separate objects, loop unrolled by two).  Sub-tile u < ne holds
-// the concatenated keys of the kept clusters of the row's query cluster (each
-// staged row is gathered: slot -> kept cluster through a per-lane cursor over
-// the kept-size prefix cum[], -> key row); sub-tiles u >= ne hold the virtual
-// keys, one per key cluster b (bf16 centroid rows), whose logit gets the bias
-// ln(n_b) / scale, or -inf when b is kept or empty.
+// slots 64 u .. 64 u + 63 of the concatenated keys of the kept clusters of the
+// row's query cluster (each staged row is gathered through the row's run
+// table); sub-tiles u >= ne hold the virtual keys, one per key cluster b (bf16
+// centroid rows), whose logit gets the bias ln(n_b) / scale, or -inf when b is
+// kept or empty.
 constexpr int kCaMaxCk = 512;
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
@@ -1687,10 +1707,9 @@ comp_attn_d128_kernel(CompArgs p) {
   constexpr int D = 128, KT = 8, DT = 4, TILE = kCaBN * D;
   __shared__ __attribute__((aligned(1024))) uint16_t K0[TILE], K1[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t V0[TILE], V1[TILE];
-  __shared__ int cum[kCaMaxCk + 1];    // prefix of kept cluster sizes
-  __shared__ int kstart[kCaMaxCk];     // first key row of each kept cluster
-  __shared__ float bias[kCaMaxCk];     // virtual-key logit bias (raw units) or -inf
-  __shared__ int scan[256];
+  // virtual-key logit bias (raw units), -inf for kept or empty clusters and
+  // for the padding of the last virtual sub-tile
+  __shared__ __attribute__((aligned(16))) float bias[kCaMaxCk];
 
   const SvgArgs& a = p.s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hi = lane >> 5;
@@ -1716,38 +1735,15 @@ comp_attn_d128_kernel(CompArgs p) {
   const int nk = __builtin_amdgcn_readfirstlane(
       max(0, min(p.rrow[(int64_t)bh * (a.Cq + 1) + ca + 1] - rb, min(a.Ck, a.Cq * a.Ck - rb))));
   const int32_t* cl = p.rcol + (int64_t)bh * a.Cq * a.Ck + rb;
-  for (int b = tid; b < a.Ck; b += 256) {
-    const int n = ko[b + 1] - ko[b];
+  for (int b = tid; b < kCaMaxCk; b += 256) {
+    const int n = b < a.Ck ? ko[b + 1] - ko[b] : 0;
     bias[b] = n > 0 ? __logf((float)n) / p.scale : -__builtin_inff();
-  }
-  // prefix of kept sizes: thread t holds entries 2t, 2t + 1 (nk <= 512)
-  int sz[2] = {0, 0};
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int i = 2 * tid + e;
-    if (i < nk) {
-      const int b = max(0, min(cl[i], a.Ck - 1));
-      sz[e] = ko[b + 1] - ko[b];
-      kstart[i] = ko[b];
-    }
-  }
-  scan[tid] = sz[0] + sz[1];
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {
-    const int add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
-  }
-  {
-    const int ex = scan[tid] - sz[0] - sz[1];
-    if (2 * tid < nk) cum[2 * tid] = ex;
-    if (2 * tid + 1 < nk) cum[2 * tid + 1] = ex + sz[0];
-    if (tid == 255) cum[nk] = scan[255];
   }
   __syncthreads();
   for (int i = tid; i < nk; i += 256) bias[max(0, min(cl[i], a.Ck - 1))] = -__builtin_inff();
-  const int E = __builtin_amdgcn_readfirstlane(cum[nk]);
+  // run table of the row, read with scalar loads: entry i = (end slot, delta)
+  const cint_ptr runs = (cint_ptr)(p.runs + 2 * ((int64_t)bh * a.Cq * a.Ck + rb));
+  const int E = nk > 0 ? max(runs[2 * (nk - 1)], 0) : 0;
   const int ne = (E + kCaBN - 1) / kCaBN;
   const int nv = (a.Ck + kCaBN - 1) / kCaBN;
   const int nsub = ne + nv;
@@ -1762,7 +1758,7 @@ comp_attn_d128_kernel(CompArgs p) {
     for (int t = 0; t < KT; ++t) qf[t] = __builtin_bit_cast(bf16x8, *(const u32x4*)(src + t * 16));
   }
   retire_loads();
-  __syncthreads();  // cum, kstart and bias complete
+  __syncthreads();  // bias complete
 
   // ---- copy roles: wave w, instruction j covers tile rows 16w + 4j + lane/16
   const int wv = __builtin_amdgcn_readfirstlane(wave);
@@ -1775,33 +1771,68 @@ comp_attn_d128_kernel(CompArgs p) {
       (void*)(p.kc_bf + (int64_t)bh * a.Ck * D), (short)0, a.Ck * D * 2, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vcs = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(p.vc_bf + (int64_t)bh * a.Ck * D), (short)0, a.Ck * D * 2, kBufferWord3);
-  // a lane stages rows 16w + 4j + lane/16 (j = 0..3): increasing slots, so one
-  // cursor (kept-list index of the cluster holding the slot) serves all four.
-  // For those rows swz_k(row) = 4j + lane/16 and swz_v(row) = 4 (lane/16) + j,
-  // so the swizzled chunk offsets are one per-lane base XOR an immediate.
-  // The cursor's cluster bounds and first key row are kept in registers and
-  // reloaded from LDS only when the cursor moves (about once per sub-tile),
-  // so issuing a sub-tile's copies costs few LDS round trips.
-  int cur = 0, c_lo = 0, c_hi = nk > 0 ? cum[1] : 0, k_lo = nk > 0 ? kstart[0] : 0;
+  // A wave stages rows 16w + 4j + lane/16 (j = 0..3) of a sub-tile, i.e. the
+  // 16 consecutive slots s0 .. s0 + 15 (s0 = 64 u + 16 w).  A wave-uniform
+  // cursor over the run table (in scalar registers, the next entry loaded one
+  // move ahead) names the kept cluster holding s0; while the wave's slots lie
+  // in one cluster, the rows are s0 + delta + 4j + lane/16: one scalar offset
+  // and per-lane constants, as in the block-sparse kernel.  A cluster boundary
+  // inside the 16 slots (about one wave-step in four) or the end of the keys
+  // takes a per-lane path.  For these rows swz_k(row) = 4j + lane/16 and
+  // swz_v(row) = 4 (lane/16) + j, so the swizzled chunk offsets are one
+  // per-lane base XOR an immediate.
+  int cur = 0;
+  int end_cur = nk > 0 ? runs[0] : 0, d_cur = nk > 0 ? runs[1] : 0;
+  int end_nxt = nk > 1 ? runs[2] : 0, d_nxt = nk > 1 ? runs[3] : 0;
+  auto advance = [&]() __attribute__((always_inline)) {
+    ++cur;
+    end_cur = end_nxt;
+    d_cur = d_nxt;
+    if (cur + 1 < nk) {
+      end_nxt = runs[2 * (cur + 1)];
+      d_nxt = runs[2 * (cur + 1) + 1];
+    }
+  };
+  const int g4 = lane >> 4;
+  const uint32_t rbase = (uint32_t)g4 * row_bytes;
   const uint32_t kbase = (uint32_t)(((lane & 15) ^ (lane >> 4)) * 16);
   const uint32_t vbase = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
-  auto dma = [&](uint16_t* kst, uint16_t* vst, int u) {
+  auto dma = [&](uint16_t* kst, uint16_t* vst, int u) __attribute__((always_inline)) {
     if (u < ne) {
+      const int s0 = u * kCaBN + 16 * wv;
+      while (end_cur <= s0 && cur + 1 < nk) advance();
+      if (s0 + 16 <= E && (end_cur >= s0 + 16 || cur + 1 >= nk)) {
+        // one cluster holds all 16 slots
+        const uint32_t so = (uint32_t)(s0 + d_cur) * row_bytes;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int row = 16 * wv + 4 * j + (lane >> 4);
-        const int slot = min(u * kCaBN + row, E - 1);  // slots past E are masked below
-        while (cur + 1 < nk && c_hi <= slot) {
-          ++cur;
-          c_lo = c_hi;
-          c_hi = cum[cur + 1];
-          k_lo = kstart[cur];
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t ro = rbase + (uint32_t)(4 * j) * row_bytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                   ro + (kbase ^ (64u * j)), so, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                   ro + (vbase ^ (16u * j)), so, 0, 0);
         }
-        const uint32_t ro = (uint32_t)(k_lo + slot - c_lo) * row_bytes;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
-                                                 ro + (kbase ^ (64u * j)), 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
-                                                 ro + (vbase ^ (16u * j)), 0, 0, 0);
+      } else {
+        // per-lane deltas: each boundary end_cur inside the slots moves the
+        // lanes at or past it to the next kept cluster's delta (empty kept
+        // clusters are passed over the same way)
+        int dl[4] = {d_cur, d_cur, d_cur, d_cur};
+        while (end_cur < s0 + 16 && cur + 1 < nk) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (s0 + 4 * j + g4 >= end_cur) dl[j] = d_nxt;
+          advance();
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // slots past E are masked below; their rows are clamped into the sequence
+          const int row = min(max(min(s0 + 4 * j + g4, E - 1) + dl[j], 0), a.N - 1);
+          const uint32_t ro = (uint32_t)row * row_bytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16,
+                                                   ro + (kbase ^ (64u * j)), 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16,
+                                                   ro + (vbase ^ (16u * j)), 0, 0, 0);
+        }
       }
     } else {
 #pragma unroll
@@ -1873,13 +1904,15 @@ comp_attn_d128_kernel(CompArgs p) {
             if (!((vm >> (16 * kt + r)) & 1u)) s[kt][r] = -__builtin_inff();
       }
     } else {
+      // bias of clusters b = 64 (u - ne) + 32 kt + 8 g + 4 hi + 0..3 (-inf past Ck)
       const int bb = (u - ne) * kCaBN + 4 * hi;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int b = bb + kt * 32 + 8 * (r >> 2) + (r & 3);
-          s[kt][r] = b < a.Ck ? s[kt][r] + bias[b] : -__builtin_inff();
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 bv = *(const f32x4*)&bias[bb + kt * 32 + 8 * g];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[kt][4 * g + e] += bv[e];
         }
     }
     float mx = fmaxf(s[0][0], s[0][1]);
@@ -1896,23 +1929,22 @@ comp_attn_d128_kernel(CompArgs p) {
       m_run = m_new;
     }
     const float mc = m_run * c2;
-    float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pr = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
-        s[kt][r] = pr;
-        psum += pr;
-      }
-    l_run += psum;
+      for (int r = 0; r < 16; ++r) s[kt][r] = fast_exp2(__builtin_fmaf(s[kt][r], c2, -mc));
+    // P as bf16 (the operand of the value product); the row sum is taken over
+    // the same rounded values with v_dot2 against bf16 ones
     bf16x8 pf[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks >> 1, q0 = (ks & 1) * 8;
       u32x4 w;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[kt][q0 + 2 * e], s[kt][q0 + 2 * e + 1]);
+      for (int e = 0; e < 4; ++e) {
+        w[e] = pack_bf16x2(s[kt][q0 + 2 * e], s[kt][q0 + 2 * e + 1]);
+        l_run = dot2_bf16(w[e], 0x3f803f80u, l_run);
+      }
       pf[ks] = __builtin_bit_cast(bf16x8, w);
     }
     // raised issue priority over the PV block (co-resident waves drift out of
@@ -2094,9 +2126,9 @@ static bool comp_d128(const bsa_shape& s) {
 }
 
 // head_dim-128 workspace: bf16 k_cent, bf16 v_cent, per-cluster work and tile
-// counts, the tile schedule (item, x) and its length
+// counts, the tile schedule (item, x) and its length, the run tables
 struct CompWs {
-  size_t kb, vb, work, ntile, item, x, count, total;
+  size_t kb, vb, work, ntile, item, x, count, runs, total;
   int cap;  // upper bound of the tiles of all heads
 };
 static CompWs comp_ws(const bsa_shape& s, int Cq, int Ck) {
@@ -2110,7 +2142,8 @@ static CompWs comp_ws(const bsa_shape& s, int Cq, int Ck) {
   w.item = w.ntile + al256(bh * Cq * 4);
   w.x = w.item + al256((size_t)w.cap * 4);
   w.count = w.x + al256((size_t)w.cap * 4);
-  w.total = w.count + 256;
+  w.runs = w.count + 256;
+  w.total = w.runs + al256(bh * Cq * Ck * 8);
   return w;
 }
 size_t comp_attn_workspace(const bsa_shape& s, int Cq, int Ck) {
@@ -2136,7 +2169,7 @@ bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o
   p.s = svg_args(q, k, v, s, q_off, Cq, k_off, Ck);
   p.o = (uint16_t*)o; p.lse = lse; p.rrow = rrow; p.rcol = rcol; p.k_cent = kc; p.v_cent = vc;
   p.scale = scale; p.c2 = scale * kLog2e;
-  p.kc_bf = nullptr; p.vc_bf = nullptr;
+  p.kc_bf = nullptr; p.vc_bf = nullptr; p.runs = nullptr;
   const int max_tiles = (s.N + 127) / 128 + Cq;
   dim3 grid(max_tiles, s.B * s.H);
   if (comp_d128(s)) {
@@ -2150,11 +2183,11 @@ bsa_status launch_comp_attn(const void* q, const void* k, const void* v, void* o
                          kb, vb, n2);
     CompOrderArgs oa{q_off, k_off, rrow, rcol, Cq, Ck, s.B * s.H, w.cap, (int32_t*)(base + w.work),
                      (int32_t*)(base + w.ntile), (int32_t*)(base + w.item), (int32_t*)(base + w.x),
-                     (int32_t*)(base + w.count)};
+                     (int32_t*)(base + w.count), (int32_t*)(base + w.runs)};
     hipLaunchKernelGGL(comp_steps_kernel, dim3((Cq + 3) / 4, s.B * s.H), dim3(256), 0, stream, oa);
     hipLaunchKernelGGL(comp_order_kernel, dim3(1), dim3(1024), 0, stream, oa);
     p.kc_bf = kb; p.vc_bf = vb;
-    p.tile_item = oa.tile_item; p.tile_x = oa.tile_x; p.tile_count = oa.tile_count;
+    p.tile_item = oa.tile_item; p.tile_x = oa.tile_x; p.tile_count = oa.tile_count; p.runs = oa.runs;
     // 1-D grid, a multiple of 24 covering every schedule entry (see the kernel)
     const int wgs = (w.cap + 23) / 24 * 24;
     hipLaunchKernelGGL(comp_attn_d128_kernel, dim3(wgs), dim3(256), 0, stream, p);

@@ -84,6 +84,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // become scalar loads (counted by lgkmcnt), so fetching the next block index
 // never makes a wave wait on its own vector-memory copies in flight
 typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+typedef const __attribute__((address_space(4))) int64_t* cint64_ptr;
 constexpr int kBufferWord3 = 0x00020000;  // raw (untyped, stride 0) buffer loads, gfx9 family
 // Raw buffer descriptor as four scalar words (base, stride 0, size, format),
 // for copies issued from inline assembly.

@@ -1781,17 +1781,28 @@ comp_attn_d128_kernel(CompArgs p) {
   // takes a per-lane path.  For these rows swz_k(row) = 4j + lane/16 and
   // swz_v(row) = 4 (lane/16) + j, so the swizzled chunk offsets are one
   // per-lane base XOR an immediate.
-  int cur = 0;
-  int end_cur = nk > 0 ? runs[0] : 0, d_cur = nk > 0 ? runs[1] : 0;
-  int end_nxt = nk > 1 ? runs[2] : 0, d_nxt = nk > 1 ? runs[3] : 0;
+  // Past the last kept cluster the cursor sees an end of INT_MAX, so the
+  // loops compare one value; slots at or past E only occur in the last exact
+  // sub-tile, whose rows take the clamped per-lane path.
+  const cint64_ptr runs2 = (cint64_ptr)runs;
+  auto entry = [&](int i, int& end, int& d) __attribute__((always_inline)) {
+    if (i < nk) {
+      const int64_t x = runs2[i];
+      end = (int)(uint32_t)x;
+      d = (int)(x >> 32);
+    } else {
+      end = 0x7fffffff;
+      d = 0;
+    }
+  };
+  int cur = 0, end_cur, d_cur, end_nxt, d_nxt;
+  entry(0, end_cur, d_cur);
+  entry(1, end_nxt, d_nxt);
   auto advance = [&]() __attribute__((always_inline)) {
     ++cur;
     end_cur = end_nxt;
     d_cur = d_nxt;
-    if (cur + 1 < nk) {
-      end_nxt = runs[2 * (cur + 1)];
-      d_nxt = runs[2 * (cur + 1) + 1];
-    }
+    entry(cur + 1, end_nxt, d_nxt);
   };
   const int g4 = lane >> 4;
   const uint32_t rbase = (uint32_t)g4 * row_bytes;
@@ -1800,8 +1811,8 @@ comp_attn_d128_kernel(CompArgs p) {
   auto dma = [&](uint16_t* kst, uint16_t* vst, int u) __attribute__((always_inline)) {
     if (u < ne) {
       const int s0 = u * kCaBN + 16 * wv;
-      while (end_cur <= s0 && cur + 1 < nk) advance();
-      if (s0 + 16 <= E && (end_cur >= s0 + 16 || cur + 1 >= nk)) {
+      while (end_cur <= s0) advance();
+      if (end_cur >= s0 + 16 && s0 + 16 <= E) {
         // one cluster holds all 16 slots
         const uint32_t so = (uint32_t)(s0 + d_cur) * row_bytes;
 #pragma unroll
@@ -1817,7 +1828,7 @@ comp_attn_d128_kernel(CompArgs p) {
         // lanes at or past it to the next kept cluster's delta (empty kept
         // clusters are passed over the same way)
         int dl[4] = {d_cur, d_cur, d_cur, d_cur};
-        while (end_cur < s0 + 16 && cur + 1 < nk) {
+        while (end_cur < s0 + 16) {
 #pragma unroll
           for (int j = 0; j < 4; ++j)
             if (s0 + 4 * j + g4 >= end_cur) dl[j] = d_nxt;

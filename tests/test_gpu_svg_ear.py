@@ -150,6 +150,65 @@ def test_equal_keys_make_compensation_exact(gpu_lib):
         assert_parity(to_f64(out), ref, "bf16", f"equal keys ppm={ppm}")
 
 
+def test_gather_runs_tiny_and_empty_clusters(gpu_lib):
+    """Compensated attention on given routes built to walk every path of the
+    exact-key gather: kept clusters of 1-17 keys (several cluster ends inside
+    the 16 slots one wave stages), empty kept clusters in the middle and at the
+    end of a route row, clusters longer than a 64-key sub-tile, a row that keeps
+    nothing (virtual keys only), a row that keeps everything, and routes in
+    non-index order.  Against the oracle on every head and query cluster."""
+    wl, d = _small(seed=57, Cq=6, Ck=20)
+    N = wl.N
+    small = [1, 2, 3, 0, 5, 7, 15, 16, 17, 1, 1, 1, 1, 0, 33, 2, 3, 0, 64, 65, 4, 0, 9, 13, 0, 1]
+    rest = N - sum(small)
+    sizes = small + [50] * (rest // 50) + ([rest % 50] if rest % 50 else []) + [0]
+    Ck = len(sizes)
+    assert sum(sizes) == N and Ck <= 512
+    k_off = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    nh = wl.B * wl.H
+    d = dict(d)
+    d["k_off"] = np.tile(k_off, (nh, 1))
+    q, k, v, qo, ko = _dev(d)
+    Cq = d["q_off"].shape[1] - 1
+    rng = np.random.default_rng(57)
+    empties = [b for b in range(Ck) if sizes[b] == 0]
+    routes = []
+    for r in range(nh):
+        rows = [list(range(Ck)),                                   # everything
+                [],                                                # nothing: virtual keys only
+                [b for b in range(len(small))],                    # the tiny and empty ones in order
+                [b for b in reversed(range(Ck)) if b % 3 == 0] + [empties[1]],  # reversed, ends empty
+                sorted(rng.choice(Ck, size=Ck // 2, replace=False).tolist(), key=lambda _: rng.random()),
+                list(range(0, Ck, 2)) + [empties[-1]]]
+        routes.append(rows[:Cq] + [rows[2]] * max(0, Cq - len(rows)))
+    rrow = np.zeros((nh, Cq + 1), np.int32)
+    rcol = np.zeros((nh, Cq * Ck), np.int32)
+    for r in range(nh):
+        pos = 0
+        for a in range(Cq):
+            cols = list(dict.fromkeys(routes[r][a]))  # no repeats
+            rcol[r, pos:pos + len(cols)] = cols
+            pos += len(cols)
+            rrow[r, a + 1] = pos
+    scale = 1.0 / math.sqrt(wl.D)
+    qc, kc, vc = gpu_lib.cluster_centroids(q, k, v, qo, ko)
+    out, lse = gpu_lib.compensated_attn_fwd(q, k, v, qo, ko, torch.from_numpy(rrow).cuda(),
+                                            torch.from_numpy(rcol).cuda(), kc, vc, scale)
+    torch.cuda.synchronize()
+    got, glse = to_f64(out), lse.cpu().numpy()
+    for r in range(nh):
+        b, h = divmod(r, wl.H)
+        hq, hk, hv, hqo, hko = _head(d, r)
+        cents = oe.centroids(hq, hk, hv, hqo, hko)
+        kept = np.zeros((Cq, Ck), bool)
+        for a in range(Cq):
+            kept[a, rcol[r, rrow[r, a]:rrow[r, a + 1]]] = True
+        ref, rlse = oe.compensated_attention(hq, hk, hv, hqo, hko, kept, cents, scale)
+        rows = ~np.isnan(ref[:, 0])
+        assert_parity(got[b, h][rows], ref[rows], "bf16", f"gather runs head {r}")
+        assert np.abs(glse[b, h][rows] - rlse[rows]).max() < 2e-3
+
+
 @pytest.fixture(scope="module")
 def svg_full():
     wl = get_workload("svg_ear_32k")

@@ -44,10 +44,11 @@ __device__ __forceinline__ float phi(float x) {
 // 0.106 ms instead of 0.124 ms).  Cache-policy operand of the buffer copies:
 // bit 1 = nt.
 constexpr int kNt = 2;
-// The causal path keeps the default policy: its walk reads K and V again after
-// the state pass, and with non-temporal copies in the walk the call took
-// 0.29 ms instead of 0.18 ms at 32K.
-constexpr int kCausalCp = 0;
+// The causal path reads K and V twice (state pass, then the walk), so those
+// copies keep the default policy; only the walk's Q copies are non-temporal
+// (0.180 -> 0.173 ms at 32K).  Its O stores stay default as well: they are
+// 8-byte pieces of rows, and non-temporal partial-line stores made the call
+// take 0.29 ms.
 
 constexpr int kLinTok = 64;      // tokens per state tile
 constexpr int kLinThreads = 256;
@@ -749,7 +750,6 @@ __device__ __forceinline__ float xor16_sum(float x) {
 // has d1 = 16 f + 8 hi .. + 7 like the phi(Q) row fragment (one 16-byte read).
 // No copy of S goes through LDS; LDS holds the tile ring (72 KiB) and z, so
 // two workgroups fit a CU.
-template <int CP>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 causal_lin_d128_kernel(CausalArgs a) {
   constexpr int D = 128, TILE = kCT * D;
@@ -793,9 +793,9 @@ causal_lin_d128_kernel(CausalArgs a) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int r = (8 * wv + 4 * j) * D;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, off[j], so, 0, CP);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, off[j], so, 0, CP);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, off[j], so, 0, CP);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, off[j], so, 0, kNt);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, off[j], so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, off[j], so, 0, 0);
       }
     } else {  // the sequence's last tile: rows past N repeat row N - 1 (zeroed or not stored)
 #pragma unroll
@@ -804,9 +804,9 @@ causal_lin_d128_kernel(CausalArgs a) {
         const uint32_t o = (uint32_t)min(t0 + row, a.N - 1) * row_bytes +
                            (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
         const int r = (8 * wv + 4 * j) * D;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, o, 0, 0, CP);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, o, 0, 0, CP);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, o, 0, 0, CP);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(qrs, (lds_void*)&qs[r], 16, o, 0, 0, kNt);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&ks[r], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vs[r], 16, o, 0, 0, 0);
       }
     }
   };
@@ -978,8 +978,7 @@ causal_lin_d128_kernel(CausalArgs a) {
       for (int g = 0; g < 4; ++g) {
         const u32x2 w = {pack_bf16x2(o[4 * g] * inv, o[4 * g + 1] * inv),
                          pack_bf16x2(o[4 * g + 2] * inv, o[4 * g + 3] * inv)};
-        if constexpr (CP != 0) __builtin_nontemporal_store(w, (u32x2*)(dst + 8 * g));
-        else *(u32x2*)(dst + 8 * g) = w;
+        *(u32x2*)(dst + 8 * g) = w;
       }
     }
   };
@@ -1138,7 +1137,7 @@ bsa_status launch_causal_linear_attn(const void* q, const void* k, const void* v
                 s.stride_b, s.stride_h, s.stride_n, s.H, s.N, p.chunk_a, p.splits_s, p.f};
   hipLaunchKernelGGL(lin_state_d128_kernel<0>, dim3(p.splits_s, bh), dim3(kLinThreads), 0, stream, sa);
   hipLaunchKernelGGL(lin_prefix_d128_kernel, dim3(17, bh), dim3(256), 0, stream, pa);
-  hipLaunchKernelGGL(causal_lin_d128_kernel<kCausalCp>, dim3(p.splits_a, bh), dim3(256), 0, stream, ca);
+  hipLaunchKernelGGL(causal_lin_d128_kernel, dim3(p.splits_a, bh), dim3(256), 0, stream, ca);
   return launch_ok("causal_linear_attn_fwd") ? BSA_OK : BSA_ERR_HIP;
 }
 

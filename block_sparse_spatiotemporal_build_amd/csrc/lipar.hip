@@ -68,7 +68,7 @@ __global__ void __launch_bounds__(256) lipar_flag_kernel(LiparArgs a) {
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = i * 64 + lane;
-      dst[i] = c < nch ? src[c] : u32x4{0, 0, 0, 0};
+      dst[i] = c < nch ? __builtin_nontemporal_load(src + c) : u32x4{0, 0, 0, 0};  // every row read once here
     }
   };
   u32x4 prev[CPL], cur[CPL], n1[CPL], n2[CPL];
@@ -185,7 +185,8 @@ __global__ void __launch_bounds__(256) lipar_restore_kernel(LiparRestoreArgs a) 
   const u32x4* src = (const u32x4*)(a.y + ((int64_t)bh * a.N + j) * a.D);
   u32x4* dst = (u32x4*)(a.o + (int64_t)(bh / a.H) * a.sb + (int64_t)(bh % a.H) * a.sh + (int64_t)n * a.sn);
   const int nch = a.D / 8;
-  for (int c = lane; c < nch; c += 64) dst[c] = src[c];
+  // the full-length output is written once and not read back here: non-temporal
+  for (int c = lane; c < nch; c += 64) __builtin_nontemporal_store(src[c], dst + c);
 }
 
 // ---------------------------------------------------------------------------

@@ -38,6 +38,13 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 // acc + a.lo * b.lo + a.hi * b.hi for packed bf16 pairs (v_dot2_f32_bf16).
 // Written as inline asm because the compiler builtin, fed 32-bit elements of a
 // vector register tuple, read the tuple's first element for every element.
+// The hardware does not interlock a dot result: another VALU instruction that
+// reads it (other than as the accumulator of the next v_dot2) must come at least
+// three instructions later, and the compiler cannot see this inside inline asm
+// (a v_add one instruction after the last dot of a chain read the value from
+// before the chain).  So the results here only feed the next dot of a chain or
+// are read much later; a CPU test scans the compiled kernels for reads that
+// come too soon.
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float acc) {
   float d;
   asm volatile("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));

@@ -25,6 +25,10 @@ pytestmark = pytest.mark.gpu
 
 
 def _assert_grad(got, ref, what):
+    """Relative L2 <= 1e-2 and max-abs <= 2e-2 x max|ref| per gradient tensor.
+    The max-abs bar scales with the tensor: dK and dV reach max|ref| of 7-9
+    here, where rounding a stored bf16 value alone is up to 1.8e-2; measured
+    max-abs errors are 0.6-2.5e-2 and relative L2 2.3-5.8e-3."""
     ma, rl = parity(got, ref)
     scale = np.abs(ref).max()
     assert np.isfinite(got).all(), what

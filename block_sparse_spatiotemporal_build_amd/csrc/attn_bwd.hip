@@ -78,25 +78,6 @@ __device__ __forceinline__ int2 bwd_item(const BwdArgs& a) {
 
 constexpr int kBwdBlock = 128;
 
-// transpose read of a swz_v-swizzled stage: lane (l32, hi) gets column
-// 32 dt + l32 at rows 16 ks + 8 (e / 4) + 4 hi + e % 4, e = 0..7
-__device__ __forceinline__ bf16x8 bwd_tr_frag(const uint16_t* st, int ks, int dt, int lane) {
-  constexpr int D = 128;
-  const int hi = lane >> 5, g16 = lane >> 4, j16 = lane & 15;
-  const int r0 = ks * 16 + 4 * hi + (j16 >> 2), r1 = r0 + 8;
-  const int lc = 4 * dt + 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  const int half = (j16 & 1) * 4;
-  const u32x2 x0 = lds_tr16(&st[r0 * D + ((lc ^ swz_v(r0)) << 3) + half]);
-  const u32x2 x1 = lds_tr16(&st[r1 * D + ((lc ^ swz_v(r1)) << 3) + half]);
-  return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
-}
-
-// row fragment of a swz_v-swizzled stage: row r, head dims 16 t + 8 hi .. + 7
-__device__ __forceinline__ bf16x8 bwd_row_frag(const uint16_t* st, int r, int t, int hi) {
-  constexpr int D = 128;
-  return *(const bf16x8*)&st[r * D + (((2 * t + hi) ^ swz_v(r)) << 3)];
-}
-
 __device__ __forceinline__ void bwd_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -157,15 +138,46 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.k + head_off), (short)0, 0x7fffffff, kBufferWord3);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(a.v + head_off), (short)0, 0x7fffffff, kBufferWord3);
-  // copy roles: wave w, instruction j stages rows 16 w + 4 j + lane / 16
+  // copy roles: wave w, instruction j stages rows 16 w + 4 j + lane / 16, whose
+  // swz_v is 4 (lane / 16) + j: the chunk offset is one per-lane base XOR 16 j and
+  // the row offset a per-lane base plus a uniform multiple of 4 rows
+  const uint32_t rbase = (uint32_t)(16 * wv + (lane >> 4)) * row_bytes;
+  const uint32_t cbase = (uint32_t)(((lane & 15) ^ (4 * (lane >> 4))) * 16);
   auto dma = [&](uint16_t* kst, uint16_t* vst, int key0) {
+    if (key0 + SUB <= N) {
+      const uint32_t so = (uint32_t)key0 * row_bytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 16 * wv + 4 * j + (lane >> 4);
-      const uint32_t o = (uint32_t)min(key0 + row, N - 1) * row_bytes + (uint32_t)(((lane & 15) ^ swz_v(row)) * 16);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t o = rbase + (uint32_t)(4 * j) * row_bytes + (cbase ^ (16u * j));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, o, so, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, o, so, 0, 0);
+      }
+    } else {  // tail sub-tile: rows past N repeat row N - 1 (their scores are masked)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 16 * wv + 4 * j + (lane >> 4);
+        const uint32_t o = (uint32_t)min(key0 + row, N - 1) * row_bytes + (cbase ^ (16u * j));
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)&kst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)&vst[(16 * wv + 4 * j) * D], 16, o, 0, 0, 0);
+      }
     }
+  };
+
+  // LDS byte offsets of the stage reads, one per-lane base XOR an immediate:
+  //   row fragment (row 32 kt + l32, head dims 16 t + 8 hi ..): 8192 kt + (rb ^ 32 t)
+  //   transpose read (rows 16 ks + 4 hi + (lane % 16) / 4, column block dt):
+  //   4096 ks + (tb ^ 64 dt), and 8 rows on 4096 ks + 2048 + (tb ^ 32 ^ 64 dt)
+  const int j16 = lane & 15, a4 = j16 >> 2, c4 = 2 * ((lane >> 4) & 1) + ((j16 & 3) >> 1);
+  const uint32_t rb = (uint32_t)(l32 * 256 + ((hi ^ swz_v(l32)) << 4));
+  const uint32_t tb = (uint32_t)((4 * hi + a4) * 256 + 64 * a4 + 16 * (c4 ^ hi) + 8 * (j16 & 1));
+  auto row_frag = [&](const uint16_t* st, int kt, int t) -> bf16x8 {
+    return *(const bf16x8*)((const char*)st + 8192 * kt + (rb ^ (32u * t)));
+  };
+  auto tr_frag = [&](const uint16_t* st, int ks, int dt) -> bf16x8 {
+    const char* b = (const char*)st + 4096 * ks;
+    const u32x2 x0 = lds_tr16((const uint16_t*)(b + (tb ^ (64u * dt))));
+    const u32x2 x1 = lds_tr16((const uint16_t*)(b + 2048 + (tb ^ 32u ^ (64u * dt))));
+    return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
   };
 
   f32x16 dq[DT];
@@ -181,18 +193,37 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       f32x16 s = f32x16{}, dp = f32x16{};
+      bf16x8 kf[KT], vf[KT];
 #pragma unroll
       for (int t = 0; t < KT; ++t) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Kb, 32 * kt + l32, t, hi), qf[t], s, 0, 0, 0);
-        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_row_frag(Vb, 32 * kt + l32, t, hi), gf[t], dp, 0, 0, 0);
+        kf[t] = row_frag(Kb, kt, t);
+        vf[t] = row_frag(Vb, kt, t);
       }
+#pragma unroll
+      for (int t = 0; t < KT; ++t) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t], qf[t], s, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t], gf[t], dp, 0, 0, 0);
+      }
+      // reads run four ahead of the MFMAs
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 12; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       // s[r] is key key0 + 32 kt + 8 (r / 4) + 4 hi + r % 4 of query l32
       float ds[16];
+      if (key0 + 32 * kt + 32 <= N) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const bool live = key0 + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) < N;
-        const float p = live ? fast_exp2(__builtin_fmaf(s[r], a.c2, -lse2)) : 0.f;
-        ds[r] = p * (dp[r] - dl);
+        for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(s[r], a.c2, -lse2)) * (dp[r] - dl);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool live = key0 + 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) < N;
+          const float p = live ? fast_exp2(__builtin_fmaf(s[r], a.c2, -lse2)) : 0.f;
+          ds[r] = p * (dp[r] - dl);
+        }
       }
       // dQ^T += K^T dS^T over the half's 32 keys (k-steps 2 kt, 2 kt + 1), at
       // raised wave priority as in the dK / dV kernel
@@ -204,7 +235,7 @@ attn_bwd_dq_d128_kernel(BwdArgs a) {
         const bf16x8 df = __builtin_bit_cast(bf16x8, w);
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
-          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bwd_tr_frag(Kb, 2 * kt + h2, dt, lane), df, dq[dt], 0, 0, 0);
+          dq[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag(Kb, 2 * kt + h2, dt), df, dq[dt], 0, 0, 0);
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -321,21 +352,23 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < DT; ++i) dk[i] = dv[i] = f32x16{};
 
-  // Per-lane LDS element offsets as one base XOR / plus immediates (the same
-  // reads as bwd_row_frag / bwd_tr_frag, so few registers stay live):
-  //   Q or dO row fragment (query l32, t):  rq ^ 16 t
-  //   K row fragment (key 32 w + l32, t):   rk ^ 16 t,  rk = rq + 4096 w
-  //   transpose fragment (ks, dt): rows r0 and r0 + 8 at 2048 ks + (tq ^ 32 dt)
-  //                                and 2048 ks + 1024 + (tq ^ 16 ^ 32 dt)
+  // Per-lane LDS byte offsets as one base XOR / plus immediates, so few
+  // registers stay live (stages are swz_v-swizzled [rows][128] bf16):
+  //   Q or dO row fragment (query l32, head dims 16 t + 8 hi ..):  rq ^ 32 t
+  //   K row fragment (key 32 w + l32, same dims):   rk ^ 32 t,  rk = rq + 8192 w
+  //   transpose read (rows 16 ks + 4 hi + (lane % 16) / 4 and 8 more, columns
+  //   32 dt + 16 ((lane / 16) % 2) + 4 (lane % 4) ..): 4096 ks + (tq ^ 64 dt)
+  //   and 4096 ks + 2048 + (tq ^ 32 ^ 64 dt)
   const int j16 = lane & 15, g16 = lane >> 4;
-  int rq = l32 * D + 8 * (hi ^ swz_v(l32));
-  int rk = rq + 32 * D * wv;
+  int rq = 2 * (l32 * D + 8 * (hi ^ swz_v(l32)));
+  int rk = rq + 64 * D * wv;
   const int tc1 = 2 * (g16 & 1) + ((j16 & 3) >> 1);
-  int tq = (4 * hi + (j16 >> 2)) * D + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4;
-  auto row_frag = [&](const uint16_t* st, int off) { return *(const bf16x8*)&st[off]; };
+  int tq = 2 * ((4 * hi + (j16 >> 2)) * D + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4);
+  auto row_frag = [&](const uint16_t* st, int off) { return *(const bf16x8*)((const char*)st + off); };
   auto tr_frag = [&](const uint16_t* st, int ks, int dt) {
-    const u32x2 x0 = lds_tr16(&st[2048 * ks + (tq ^ (32 * dt))]);
-    const u32x2 x1 = lds_tr16(&st[2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt))]);
+    const char* b = (const char*)st + 4096 * ks;
+    const u32x2 x0 = lds_tr16((const uint16_t*)(b + (tq ^ (64 * dt))));
+    const u32x2 x1 = lds_tr16((const uint16_t*)(b + 2048 + (tq ^ 32 ^ (64 * dt))));
     return __builtin_bit_cast(bf16x8, u32x4{x0[0], x0[1], x1[0], x1[1]});
   };
 
@@ -354,9 +387,17 @@ attn_bwd_dkdv_d128_kernel(BwdArgs a) {
     f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
     for (int t = 0; t < KT; ++t) {
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qb, rq ^ (16 * t)), row_frag(Ks, rk ^ (16 * t)), s, 0, 0, 0);
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Gb, rq ^ (16 * t)), vf[t], dp, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Qb, rq ^ (32 * t)), row_frag(Ks, rk ^ (32 * t)), s, 0, 0, 0);
+      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(row_frag(Gb, rq ^ (32 * t)), vf[t], dp, 0, 0, 0);
     }
+    // reads run two k-steps ahead of the MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
     float pw[16], dw[16];
 #pragma unroll
     for (int g = 0; g < 4; ++g) {

@@ -121,27 +121,79 @@ def test_causal_state_fragment_swap():
 
 def test_backward_dkdv_offsets_xor_form():
     """Fused dK / dV backward kernel (`csrc/attn_bwd.hip`): stages are row-major
-    swz_v-swizzled [rows][128] bf16 (32-row Q / dO stages, the 128-row K stage).
-    Row fragment of lane l at k-step t: row r, head dims 16 t + 8 (l / 32) + 0..7,
-    with r = l % 32 (Q, dO) or 32 w + l % 32 (K of wave w): rq ^ 16 t, rk ^ 16 t.
-    Transpose read (ks, dt): rows 16 ks + 4 (l / 32) + j16 / 4 and + 8, columns
-    32 dt + 16 ((l / 16) & 1) + 4 (j16 & 3): 2048 ks + (tq ^ 32 dt) and
-    2048 ks + 1024 + (tq ^ 16 ^ 32 dt).  Every offset stays inside its stage."""
+    swz_v-swizzled [rows][128] bf16 (32-row Q / dO stages, the 128-row K stage);
+    offsets in bytes.  Row fragment of lane l at k-step t: row r, head dims
+    16 t + 8 (l / 32) + 0..7, with r = l % 32 (Q, dO) or 32 w + l % 32 (K of
+    wave w): rq ^ 32 t, rk ^ 32 t.  Transpose read (ks, dt): rows
+    16 ks + 4 (l / 32) + j16 / 4 and + 8, columns 32 dt + 16 ((l / 16) & 1) +
+    4 (j16 & 3): 4096 ks + (tq ^ 64 dt) and 4096 ks + 2048 + (tq ^ 32 ^ 64 dt).
+    Every offset stays inside its stage."""
     for w, t, lane in itertools.product(range(4), range(8), range(64)):
         l32, hi = lane % 32, lane // 32
-        rq = l32 * 128 + 8 * (hi ^ swz_v(l32))
-        rk = rq + 32 * 128 * w
-        assert phys(l32, 16 * t + 8 * hi, swz_v) == rq ^ (16 * t) < 32 * 128
-        assert phys(32 * w + l32, 16 * t + 8 * hi, swz_v) == rk ^ (16 * t) < 128 * 128
+        rq = 2 * (l32 * 128 + 8 * (hi ^ swz_v(l32)))
+        rk = rq + 64 * 128 * w
+        assert 2 * phys(l32, 16 * t + 8 * hi, swz_v) == rq ^ (32 * t)
+        assert (rq ^ (32 * t)) + 16 <= 2 * 32 * 128
+        assert 2 * phys(32 * w + l32, 16 * t + 8 * hi, swz_v) == rk ^ (32 * t)
+        assert (rk ^ (32 * t)) + 16 <= 2 * 128 * 128
     for ks, dt, lane in itertools.product(range(2), range(4), range(64)):
         hi, g16, j16 = lane // 32, lane // 16, lane % 16
         row = 16 * ks + 4 * hi + j16 // 4
         col = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)
         tc1 = 2 * (g16 & 1) + ((j16 & 3) >> 1)
-        tq = (4 * hi + (j16 >> 2)) * 128 + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4
-        assert phys(row, col, swz_v) == 2048 * ks + (tq ^ (32 * dt))
-        assert phys(row + 8, col, swz_v) == 2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt))
-        assert 2048 * ks + 1024 + (tq ^ 16 ^ (32 * dt)) + 3 < 32 * 128
+        tq = 2 * ((4 * hi + (j16 >> 2)) * 128 + ((tc1 ^ (4 * (j16 >> 2) + hi)) << 3) + (j16 & 1) * 4)
+        assert 2 * phys(row, col, swz_v) == 4096 * ks + (tq ^ (64 * dt))
+        assert 2 * phys(row + 8, col, swz_v) == 4096 * ks + 2048 + (tq ^ 32 ^ (64 * dt))
+        assert 4096 * ks + 2048 + (tq ^ 32 ^ (64 * dt)) + 8 <= 2 * 32 * 128
+
+
+def test_backward_dq_offsets_xor_form():
+    """dQ backward kernel (`csrc/attn_bwd.hip`): 64-row swz_v-swizzled K and V
+    stages, byte offsets.  Row fragment (A operand of S^T = K Q^T and
+    dP^T = V dO^T) of lane l in half kt at k-step t: row 32 kt + l % 32, head
+    dims 16 t + 8 (l / 32) + 0..7: 8192 kt + (rb ^ 32 t).  Transpose read of K
+    (ks = 0..3, dt): rows 16 ks + 4 (l / 32) + j16 / 4 and + 8, columns
+    32 dt + 16 ((l / 16) & 1) + 4 (j16 & 3): 4096 ks + (tb ^ 64 dt) and
+    4096 ks + 2048 + (tb ^ 32 ^ 64 dt).  Every offset stays inside the stage."""
+    stage = 2 * 64 * 128
+    for kt, t, lane in itertools.product(range(2), range(8), range(64)):
+        l32, hi = lane % 32, lane // 32
+        rb = l32 * 256 + ((hi ^ swz_v(l32)) << 4)
+        o = 8192 * kt + (rb ^ (32 * t))
+        assert 2 * phys(32 * kt + l32, 16 * t + 8 * hi, swz_v) == o
+        assert o + 16 <= stage
+    for ks, dt, lane in itertools.product(range(4), range(4), range(64)):
+        hi, g16, j16 = lane // 32, lane // 16, lane % 16
+        row = 16 * ks + 4 * hi + j16 // 4
+        col = 32 * dt + 16 * (g16 & 1) + 4 * (j16 & 3)
+        a4, c4 = j16 >> 2, 2 * (g16 & 1) + ((j16 & 3) >> 1)
+        tb = (4 * hi + a4) * 256 + 64 * a4 + 16 * (c4 ^ hi) + 8 * (j16 & 1)
+        assert 2 * phys(row, col, swz_v) == 4096 * ks + (tb ^ (64 * dt))
+        assert 2 * phys(row + 8, col, swz_v) == 4096 * ks + 2048 + (tb ^ 32 ^ (64 * dt))
+        assert 4096 * ks + 2048 + (tb ^ 32 ^ (64 * dt)) + 8 <= stage
+
+
+def test_backward_copy_offsets_scalar_form():
+    """Copies of a whole sub-tile in the backward kernels: the source offset of
+    lane l for stage row `row` (logical chunk (l % 16) ^ swz_v(row)) is a fixed
+    per-lane part plus the sub-tile's first row times the row pitch, which the
+    kernels pass as the scalar offset.  dQ (64-row K / V stages, wave w,
+    instruction j < 4, row 16 w + 4 j + l / 16): rbase + 4 j pitch +
+    (cbase ^ 16 j).  dK / dV (32-row Q / dO stages, row 8 w + 4 j + l / 16,
+    j < 2): the per-lane part formed once from that row."""
+    pitch = 128 * 2 * 3  # bytes between rows (e.g. a [B, N, H, D] layout with H = 3)
+    for key0 in (0, 64, 4096):
+        for w, j, lane in itertools.product(range(4), range(4), range(64)):
+            row = 16 * w + 4 * j + lane // 16
+            direct = (key0 + row) * pitch + 16 * ((lane % 16) ^ swz_v(row))
+            rbase = (16 * w + lane // 16) * pitch
+            cbase = ((lane & 15) ^ (4 * (lane >> 4))) * 16
+            assert direct == rbase + 4 * j * pitch + (cbase ^ (16 * j)) + key0 * pitch
+        for w, j, lane in itertools.product(range(4), range(2), range(64)):
+            row = 8 * w + 4 * j + lane // 16
+            direct = (key0 + row) * pitch + 16 * ((lane % 16) ^ swz_v(row))
+            fixed = row * pitch + 16 * ((lane & 15) ^ swz_v(row))
+            assert direct == fixed + key0 * pitch
 
 
 def test_backward_dkdv_copy_rows_in_stage():

@@ -99,6 +99,13 @@ def test_small_steps(gpu_lib, ppm):
     _check_steps(gpu_lib, wl, d, ppm)
 
 
+def test_batch2_steps(gpu_lib):
+    """Two sequences in one call: every step against the oracle for all four (batch, head) pairs."""
+    wl = gen.scaled(get_workload("svg_ear_32k"), B=2, H=2, D=128, frames=2, frame_h=10, frame_w=30,
+                    n_q_clusters=8, n_k_clusters=20, kmeans_iters=3, seed=55)
+    _check_steps(gpu_lib, wl, gen.make_clustered(wl), 150000)
+
+
 def test_small_d64_and_many_proxies(gpu_lib):
     wl, d = _small(seed=52, Cq=150, Ck=40, frames=3, fh=10, fw=40, H=1, D=64)
     _check_steps(gpu_lib, wl, d, 150000)

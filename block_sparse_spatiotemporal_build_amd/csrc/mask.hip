@@ -139,36 +139,37 @@ __global__ void __launch_bounds__(kMaskThreads) mask_fill_kernel(MaskArgs m, con
 // other rows follow in ascending index order.  Every row of length >= a long
 // row's length is long too, so a long row's rank is #rows longer + #rows of
 // equal length before it; a short row's rank is nh + #short rows before it.
-// One thread per row, row lengths staged in LDS tiles.
+// One wave per row: its lanes read 64 row lengths at a time and the counts
+// are ballots (integer, so the schedule does not depend on any order).
 __device__ __forceinline__ bool long_row(int len, int nb, int total) {
   return 2 * (int64_t)len * nb >= 3 * (int64_t)total && len > 0;
 }
 
-__global__ void __launch_bounds__(kMaskThreads) mask_order_kernel(const int32_t* row_ptr, int nb,
-                                                                  int32_t* row_order) {
-  __shared__ int len_tile[kMaskThreads];
-  const int i = blockIdx.x * kMaskThreads + threadIdx.x;
+constexpr int kOrderRowsPerBlock = 4;  // waves (rows) per workgroup
+
+__global__ void __launch_bounds__(64 * kOrderRowsPerBlock) mask_order_kernel(const int32_t* row_ptr, int nb,
+                                                                               int32_t* row_order) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * kOrderRowsPerBlock + (threadIdx.x >> 6);
+  if (i >= nb) return;  // wave-uniform; the kernel has no barrier
   const int total = row_ptr[nb];
-  const int li = i < nb ? row_ptr[i + 1] - row_ptr[i] : 0;
+  const int li = row_ptr[i + 1] - row_ptr[i];
   const bool li_long = long_row(li, nb, total);
   int longer = 0, equal_before = 0, n_long = 0, short_before = 0;
-  for (int j0 = 0; j0 < nb; j0 += kMaskThreads) {
-    const int j = j0 + threadIdx.x;
-    len_tile[threadIdx.x] = j < nb ? row_ptr[j + 1] - row_ptr[j] : -1;
-    __syncthreads();
-    const int cnt = min(kMaskThreads, nb - j0);
-    for (int t = 0; t < cnt; ++t) {
-      const int lj = len_tile[t];
-      const bool jl = long_row(lj, nb, total);
-      longer += lj > li ? 1 : 0;
-      equal_before += (lj == li && j0 + t < i) ? 1 : 0;
-      n_long += jl ? 1 : 0;
-      short_before += (!jl && j0 + t < i) ? 1 : 0;
-    }
-    __syncthreads();
+  for (int j0 = 0; j0 < nb; j0 += 64) {
+    const int j = j0 + lane;
+    const bool valid = j < nb;
+    const int lj = valid ? row_ptr[j + 1] - row_ptr[j] : -1;
+    const bool jl = valid && long_row(lj, nb, total);
+    longer += __popcll(__ballot(valid && lj > li));
+    equal_before += __popcll(__ballot(valid && lj == li && j < i));
+    n_long += __popcll(__ballot(jl));
+    short_before += __popcll(__ballot(valid && !jl && j < i));
   }
-  if (i < nb) row_order[li_long ? longer + equal_before : n_long + short_before] = i;
-  if (i == 0) row_order[nb] = n_long;
+  if (lane == 0) {
+    row_order[li_long ? longer + equal_before : n_long + short_before] = i;
+    if (i == 0) row_order[nb] = n_long;
+  }
 }
 
 bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int32_t* col_idx,
@@ -183,14 +184,14 @@ bsa_status launch_build_block_mask(const bsa_mask_desc& d, int32_t* row_ptr, int
   hipLaunchKernelGGL(mask_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, row_ptr, m.nb);
   hipLaunchKernelGGL(mask_fill_kernel, dim3(m.nb), dim3(kMaskThreads), 0, stream, m, row_ptr, col_idx);
   if (row_order != nullptr)
-    hipLaunchKernelGGL(mask_order_kernel, dim3((m.nb + kMaskThreads - 1) / kMaskThreads), dim3(kMaskThreads), 0,
-                       stream, row_ptr, m.nb, row_order);
+    hipLaunchKernelGGL(mask_order_kernel, dim3((m.nb + kOrderRowsPerBlock - 1) / kOrderRowsPerBlock),
+                       dim3(64 * kOrderRowsPerBlock), 0, stream, row_ptr, m.nb, row_order);
   return launch_ok("build_block_mask") ? BSA_OK : BSA_ERR_HIP;
 }
 
 void launch_block_order(const int32_t* ptr, int nb, int32_t* order, hipStream_t stream) {
-  hipLaunchKernelGGL(mask_order_kernel, dim3((nb + kMaskThreads - 1) / kMaskThreads), dim3(kMaskThreads), 0, stream,
-                     ptr, nb, order);
+  hipLaunchKernelGGL(mask_order_kernel, dim3((nb + kOrderRowsPerBlock - 1) / kOrderRowsPerBlock),
+                     dim3(64 * kOrderRowsPerBlock), 0, stream, ptr, nb, order);
 }
 
 void launch_inclusive_scan(int32_t* a, int n, hipStream_t stream) {
